@@ -1,0 +1,221 @@
+"""CPU oracle for the batch-1 quantized GEMV path -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product (``gemv_q4k_q6k_amd`` and
+its HIP library) never does, and the two share no code.
+
+The arithmetic lives in ``oracle.c`` (plain C, f64 accumulation, exact
+super-block decoding; see that file's header for the block formats and the
+readings they rest on).  This module only builds it with gcc, loads it with
+ctypes and converts numpy arrays.  Every function is pinned by
+``tests/test_oracle_pins.py`` against closed forms, hand-packed blocks,
+library routines (numpy float16, numpy matmul, numpy nanargmax) and brute
+force.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+Q4K_BLOCK_BYTES = 144
+Q6K_BLOCK_BYTES = 210
+QK = 256
+
+
+def build(force: bool = False) -> str:
+    """Compile liboracle.so with gcc (-O2, OpenMP, no fast-math, no FMA
+    contraction so every f64/f32 operation rounds once)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+               "-std=c11", "-Wall", "-shared", "-fPIC", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        build()
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        I64 = ctypes.c_int64
+        sig = {
+            "orc_fp16_to_f64": (ctypes.c_double, [ctypes.c_uint16]),
+            "orc_f32_to_fp16_rne": (ctypes.c_uint16, [ctypes.c_float]),
+            "orc_q4k_block": (None, [P, P]),
+            "orc_q6k_block": (None, [P, P]),
+            "orc_q4k_gemv": (None, [P, P, P, I64, I64]),
+            "orc_q6k_gemv": (None, [P, P, P, I64, I64]),
+            "orc_q6k_gemv_f64x": (None, [P, P, P, I64, I64]),
+            "orc_swiglu": (None, [P, P, P, P, P, P, I64, I64]),
+            "orc_q8_quantize": (None, [P, P, P, I64]),
+            "orc_q4k_q8_isums": (None, [P, P, P, I64, I64]),
+            "orc_q4k_q8_gemv": (None, [P, P, P, P, I64, I64]),
+            "orc_argmax_first_f64": (I64, [P, I64]),
+            "orc_argmax_first_f32": (I64, [P, I64]),
+            "orc_num_threads": (ctypes.c_int, []),
+            "orc_set_num_threads": (None, [ctypes.c_int]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+        return lib
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def _blocks(W: np.ndarray, N: int, K: int, block_bytes: int) -> np.ndarray:
+    W = np.ascontiguousarray(W, dtype=np.uint8)
+    if K % QK or W.size != N * (K // QK) * block_bytes:
+        raise ValueError("weight buffer size does not match N x K")
+    return W
+
+
+def _vec(x, dtype) -> np.ndarray:
+    return np.ascontiguousarray(x, dtype=dtype)
+
+
+# ------------------------------------------------------------------ scalars
+def fp16_to_f64(bits: int) -> float:
+    return _load().orc_fp16_to_f64(int(bits) & 0xFFFF)
+
+
+def f32_to_fp16_bits(v: float) -> int:
+    return int(_load().orc_f32_to_fp16_rne(float(np.float32(v))))
+
+
+# ------------------------------------------------------------------- blocks
+def q4k_decode_block(blk: np.ndarray) -> np.ndarray:
+    blk = np.ascontiguousarray(blk, dtype=np.uint8)
+    assert blk.size == Q4K_BLOCK_BYTES
+    w = np.empty(256, np.float64)
+    _load().orc_q4k_block(_ptr(blk), _ptr(w))
+    return w
+
+
+def q6k_decode_block(blk: np.ndarray) -> np.ndarray:
+    blk = np.ascontiguousarray(blk, dtype=np.uint8)
+    assert blk.size == Q6K_BLOCK_BYTES
+    w = np.empty(256, np.float64)
+    _load().orc_q6k_block(_ptr(blk), _ptr(w))
+    return w
+
+
+def q4k_dequantize(W: np.ndarray, N: int, K: int) -> np.ndarray:
+    """Whole N x K Q4_K matrix -> f64 (small sizes only)."""
+    W = _blocks(W, N, K, Q4K_BLOCK_BYTES).reshape(-1, Q4K_BLOCK_BYTES)
+    return np.concatenate([q4k_decode_block(b) for b in W]).reshape(N, K)
+
+
+def q6k_dequantize(W: np.ndarray, N: int, K: int) -> np.ndarray:
+    W = _blocks(W, N, K, Q6K_BLOCK_BYTES).reshape(-1, Q6K_BLOCK_BYTES)
+    return np.concatenate([q6k_decode_block(b) for b in W]).reshape(N, K)
+
+
+# -------------------------------------------------------------------- GEMVs
+def q4k_gemv(W, x, N: int, K: int) -> np.ndarray:
+    W = _blocks(W, N, K, Q4K_BLOCK_BYTES)
+    x = _vec(x, np.float32)
+    y = np.empty(N, np.float64)
+    _load().orc_q4k_gemv(_ptr(W), _ptr(x), _ptr(y), N, K)
+    return y
+
+
+def q6k_gemv(W, x, N: int, K: int) -> np.ndarray:
+    W = _blocks(W, N, K, Q6K_BLOCK_BYTES)
+    x = _vec(x, np.float32)
+    y = np.empty(N, np.float64)
+    _load().orc_q6k_gemv(_ptr(W), _ptr(x), _ptr(y), N, K)
+    return y
+
+
+def q6k_gemv_f64x(W, x, N: int, K: int) -> np.ndarray:
+    W = _blocks(W, N, K, Q6K_BLOCK_BYTES)
+    x = _vec(x, np.float64)
+    y = np.empty(N, np.float64)
+    _load().orc_q6k_gemv_f64x(_ptr(W), _ptr(x), _ptr(y), N, K)
+    return y
+
+
+def swiglu(Wg, Wu, x, N: int, K: int):
+    """Returns (h, g, u) in f64."""
+    Wg = _blocks(Wg, N, K, Q4K_BLOCK_BYTES)
+    Wu = _blocks(Wu, N, K, Q4K_BLOCK_BYTES)
+    x = _vec(x, np.float32)
+    h, g, u = (np.empty(N, np.float64) for _ in range(3))
+    _load().orc_swiglu(_ptr(Wg), _ptr(Wu), _ptr(x), _ptr(h), _ptr(g), _ptr(u), N, K)
+    return h, g, u
+
+
+def q8_quantize(x):
+    """Returns (q int8[K], d fp16 bits uint16[K/32])."""
+    x = _vec(x, np.float32)
+    K = x.size
+    if K % 32:
+        raise ValueError("K must be a multiple of 32")
+    q = np.empty(K, np.int8)
+    d = np.empty(K // 32, np.uint16)
+    _load().orc_q8_quantize(_ptr(x), _ptr(q), _ptr(d), K)
+    return q, d
+
+
+def q4k_q8_isums(W, xq, N: int, K: int) -> np.ndarray:
+    W = _blocks(W, N, K, Q4K_BLOCK_BYTES)
+    xq = _vec(xq, np.int8)
+    out = np.empty((N, K // 32), np.int32)
+    _load().orc_q4k_q8_isums(_ptr(W), _ptr(xq), _ptr(out), N, K)
+    return out
+
+
+def q4k_q8_gemv(W, xq, xd, N: int, K: int) -> np.ndarray:
+    W = _blocks(W, N, K, Q4K_BLOCK_BYTES)
+    xq = _vec(xq, np.int8)
+    xd = _vec(xd, np.uint16)
+    y = np.empty(N, np.float64)
+    _load().orc_q4k_q8_gemv(_ptr(W), _ptr(xq), _ptr(xd), _ptr(y), N, K)
+    return y
+
+
+# ------------------------------------------------------------------- argmax
+def argmax_first(v) -> int:
+    """First index of the maximum over non-NaN values; 0 if all are NaN."""
+    v = np.asarray(v)
+    if v.dtype == np.float32:
+        v = np.ascontiguousarray(v)
+        return int(_load().orc_argmax_first_f32(_ptr(v), v.size))
+    v = _vec(v, np.float64)
+    return int(_load().orc_argmax_first_f64(_ptr(v), v.size))
+
+
+def top2_gap(v) -> float:
+    """Largest minus second largest value at distinct indices (f64)."""
+    v = np.asarray(v, dtype=np.float64)
+    i = argmax_first(v)
+    rest = np.delete(v, i)
+    return float(v[i] - np.nanmax(rest))
+
+
+def num_threads() -> int:
+    return int(_load().orc_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    _load().orc_set_num_threads(int(n))

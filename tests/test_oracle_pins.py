@@ -1,0 +1,356 @@
+"""Pins of the CPU oracle against things other than itself (CPU only).
+
+Each function of oracle/oracle.c is checked against at least one of: a
+closed-form value worked by hand (tests/golden), a library routine (numpy's
+float16 conversions, numpy matmul, numpy nanargmax, scipy expit), an
+independent test-side encoder (tests/kquant_encode.py), brute force on tiny
+inputs, or an invariant of the definition.  The cases are chosen so that a
+dropped term, a wrong sign, a wrong index or a transposed operand in the
+oracle fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+from scipy.special import expit
+
+import oracle
+from tests.kquant_encode import (f16_bits, pack_q4k, pack_q6k, q4k_matrix_from_fields,
+                                 q6k_matrix_from_fields, random_q4k_fields, random_q6k_fields)
+
+
+def _golden(golden_dir, name):
+    with open(os.path.join(golden_dir, name)) as f:
+        return json.load(f)
+
+
+# ------------------------------------------------------------------ fp16
+def test_fp16_closed_forms():
+    table = {0x3C00: 1.0, 0x3800: 0.5, 0xC000: -2.0, 0x7BFF: 65504.0,
+             0x0400: 2.0 ** -14, 0x0001: 2.0 ** -24, 0x0000: 0.0}
+    for bits, val in table.items():
+        assert oracle.fp16_to_f64(bits) == val
+    neg0 = oracle.fp16_to_f64(0x8000)
+    assert neg0 == 0.0 and math.copysign(1.0, neg0) < 0
+    assert oracle.fp16_to_f64(0x7C00) == math.inf
+    assert oracle.fp16_to_f64(0xFC00) == -math.inf
+    assert math.isnan(oracle.fp16_to_f64(0x7E00))
+
+
+def test_fp16_decode_exhaustive_vs_numpy():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = np.array([oracle.fp16_to_f64(int(b)) for b in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def test_f32_to_fp16_rne_vs_numpy():
+    rng = np.random.default_rng(7)
+    vals = np.concatenate([
+        rng.standard_normal(20000).astype(np.float32) * np.float32(1000),
+        rng.uniform(1e-3, 1e-2, 20000).astype(np.float32),
+        (rng.standard_normal(5000) * 1e-6).astype(np.float32),   # subnormal fp16 range
+        np.array([0.0, -0.0, 65504.0, 65519.0, 65520.0, 1e6, -1e6, 2.0 ** -24,
+                  2.0 ** -25, 3 * 2.0 ** -26, 2.0 ** -14, 6.1e-5, np.inf, -np.inf], np.float32),
+    ])
+    # exact ties of binary16 at several exponents: (2k+1)/2 ulp
+    ties = []
+    for e in (-24, -20, -14, -10, 0, 5):
+        for m in (1, 2, 3, 1023, 2047):
+            ties.append(np.float32(m * 2.0 ** e + 2.0 ** (e - 1)))
+    vals = np.concatenate([vals, np.array(ties, np.float32)])
+    with np.errstate(over="ignore"):
+        ref = vals.astype(np.float16).view(np.uint16)
+    got = np.array([oracle.f32_to_fp16_bits(v) for v in vals], np.uint16)
+    assert np.array_equal(got, ref)
+    assert oracle.f32_to_fp16_bits(np.float32(np.nan)) & 0x7C00 == 0x7C00
+
+
+# ------------------------------------------------------------------ Q4_K
+def test_q4k_worked_block(golden_dir):
+    g = _golden(golden_dir, "q4k_worked_block.json")
+    blk = np.frombuffer(bytes.fromhex(g["bytes_hex"]), np.uint8)
+    w = oracle.q4k_decode_block(blk)
+    for i, v in g["weights"].items():
+        assert w[int(i)] == v, (i, w[int(i)], v)
+    assert w.sum() == g["sum_all_ones"]
+    y = oracle.q4k_gemv(blk, np.ones(256, np.float32), 1, 256)
+    assert y[0] == g["sum_all_ones"]
+
+
+def test_q4k_scale_packing_exhaustive():
+    """Every (sc, m) in [0,63]^2 at every sub-block position survives
+    encode (test side) -> decode (oracle)."""
+    q = np.zeros(256, int)
+    q[::32] = 1                         # weight 32j has q = 1, the rest 0
+    one = f16_bits(1.0)                 # d = dmin = 1
+    for j in range(8):
+        for s in range(64):
+            sc = [(j * 7 + 3) % 64] * 8
+            mn = [(j * 5 + 11) % 64] * 8
+            sc[j] = s
+            blk_list = []
+            for m in range(64):
+                mn_j = list(mn)
+                mn_j[j] = m
+                blk_list.append((mn_j, pack_q4k(one, one, sc, mn_j, q)))
+            for mn_j, blk in blk_list:
+                w = oracle.q4k_decode_block(blk)
+                # weight 32k has q=1: w = sc_k - m_k; weight 32k+1 has q=0: w = -m_k
+                assert np.array_equal(w[1::32], -np.array(mn_j, float))
+                assert np.array_equal(w[0::32], np.array(sc, float) - np.array(mn_j, float))
+
+
+def test_q4k_random_roundtrip():
+    rng = np.random.default_rng(1)
+    fields = random_q4k_fields(rng, 64)
+    blocks, w_ref = q4k_matrix_from_fields(fields, 64, 256)
+    for i in range(64):
+        assert np.array_equal(oracle.q4k_decode_block(blocks[i]), w_ref[i])
+
+
+def test_q4k_special_blocks():
+    zero = np.zeros(144, np.uint8)
+    w = oracle.q4k_decode_block(zero)
+    assert np.all(w == 0.0)
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal(256).astype(np.float32)
+    assert oracle.q4k_gemv(zero, x, 1, 256)[0] == 0.0
+    # constant block: every q = c, sc = s, m = mu -> y = (d*s*c - dmin*mu) * sum(x)
+    for c, s, mu, d, dm in [(15, 63, 63, 0.00999, 0.001), (7, 1, 0, 0.5, 0.25), (0, 5, 9, 0.125, 0.0625)]:
+        db, dmb = f16_bits(d), f16_bits(dm)
+        blk = pack_q4k(db, dmb, [s] * 8, [mu] * 8, [c] * 256)
+        dv = float(np.uint16(db).view(np.float16))
+        dmv = float(np.uint16(dmb).view(np.float16))
+        wv = dv * s * c - dmv * mu
+        assert np.all(oracle.q4k_decode_block(blk) == wv)
+        ones = np.ones(256, np.float32)
+        assert oracle.q4k_gemv(blk, ones, 1, 256)[0] == pytest.approx(256 * wv, rel=1e-15, abs=1e-12)
+
+
+# ------------------------------------------------------------------ Q6_K
+def test_q6k_worked_block(golden_dir):
+    g = _golden(golden_dir, "q6k_worked_block.json")
+    blk = np.frombuffer(bytes.fromhex(g["bytes_hex"]), np.uint8)
+    w = oracle.q6k_decode_block(blk)
+    for i, v in g["weights"].items():
+        assert w[int(i)] == v, (i, w[int(i)], v)
+    for i in g["negative_zero_indices"]:
+        assert w[i] == 0.0 and np.signbit(w[i])
+    assert w.sum() == g["sum_all_ones"]
+    assert oracle.q6k_gemv(blk, np.ones(256, np.float32), 1, 256)[0] == g["sum_all_ones"]
+
+
+def test_q6k_random_roundtrip():
+    rng = np.random.default_rng(3)
+    fields = random_q6k_fields(rng, 64)
+    blocks, w_ref = q6k_matrix_from_fields(fields, 64, 256)
+    for i in range(64):
+        assert np.array_equal(oracle.q6k_decode_block(blocks[i]), w_ref[i])
+
+
+def test_q6k_every_quant_value_every_position():
+    """Each of the 64 quant values at each of the 256 positions decodes to
+    d*sc*(q-32) with a distinct scale per 16-group (catches a wrong bit pair,
+    nibble or group index)."""
+    sc = [g - 8 if g != 8 else 9 for g in range(16)]   # 16 distinct nonzero scales
+    for v in range(64):
+        q = [(v + 13 * i) % 64 for i in range(256)]
+        blk = pack_q6k(f16_bits(1.0), sc, q)
+        w = oracle.q6k_decode_block(blk)
+        exp = np.array([sc[i // 16] * (q[i] - 32) for i in range(256)], float)
+        assert np.array_equal(w, exp)
+
+
+def test_q6k_zero_quants_closed_form():
+    sc = list(range(-8, 8))
+    blk = pack_q6k(f16_bits(0.25), sc, [0] * 256)   # ql = qh = 0
+    w = oracle.q6k_decode_block(blk)
+    assert np.array_equal(w, np.array([-32 * 0.25 * sc[i // 16] for i in range(256)], float))
+
+
+def test_q6k_block_size_matches_page_figure():
+    # qualiaDB resident_decode.rs: 2520 B per 3072-wide Q6_K logits row
+    assert 3072 // 256 * oracle.Q6K_BLOCK_BYTES == 2520
+
+
+# ------------------------------------------------------------------ GEMV
+@pytest.mark.parametrize("fmt", ["q4k", "q6k"])
+def test_gemv_vs_numpy_matmul(fmt):
+    rng = np.random.default_rng(4)
+    N, K = 7, 768
+    if fmt == "q4k":
+        W, Wf = q4k_matrix_from_fields(random_q4k_fields(rng, N * K // 256), N, K)
+        gemv = oracle.q4k_gemv
+    else:
+        W, Wf = q6k_matrix_from_fields(random_q6k_fields(rng, N * K // 256), N, K)
+        gemv = oracle.q6k_gemv
+    x = rng.standard_normal(K).astype(np.float32)
+    y = gemv(W, x, N, K)
+    ref = Wf @ x.astype(np.float64)
+    assert np.allclose(y, ref, rtol=1e-13, atol=1e-13 * np.abs(Wf).sum())
+    # one-hot activations extract columns exactly
+    for k in (0, 1, 255, 256, 511, 767):
+        e = np.zeros(K, np.float32)
+        e[k] = 1.0
+        assert np.array_equal(gemv(W, e, N, K), Wf[:, k])
+    assert np.all(gemv(W, np.zeros(K, np.float32), N, K) == 0.0)
+    # linearity: W(2x) = 2 W x exactly (power-of-two scaling)
+    assert np.array_equal(gemv(W, 2 * x, N, K), 2 * y)
+
+
+def test_q6k_gemv_f64x_matches_f32_path():
+    rng = np.random.default_rng(5)
+    N, K = 5, 512
+    W, Wf = q6k_matrix_from_fields(random_q6k_fields(rng, N * K // 256), N, K)
+    x = rng.standard_normal(K).astype(np.float32)
+    assert np.array_equal(oracle.q6k_gemv_f64x(W, x.astype(np.float64), N, K),
+                          oracle.q6k_gemv(W, x, N, K))
+
+
+# ------------------------------------------------------------------ SwiGLU
+def test_swiglu_vs_scipy_expit():
+    rng = np.random.default_rng(6)
+    N, K = 9, 512
+    Wg, Wgf = q4k_matrix_from_fields(random_q4k_fields(rng, N * K // 256), N, K)
+    Wu, Wuf = q4k_matrix_from_fields(random_q4k_fields(rng, N * K // 256), N, K)
+    x = rng.standard_normal(K).astype(np.float32)
+    h, g, u = oracle.swiglu(Wg, Wu, x, N, K)
+    g_ref = Wgf @ x.astype(np.float64)
+    u_ref = Wuf @ x.astype(np.float64)
+    assert np.allclose(g, g_ref, rtol=1e-13, atol=1e-12)
+    assert np.allclose(u, u_ref, rtol=1e-13, atol=1e-12)
+    assert np.allclose(h, g_ref * u_ref * expit(g_ref), rtol=1e-12, atol=1e-12)
+    # gate == up: h = g^2 * sigmoid(g)
+    h2, g2, _ = oracle.swiglu(Wg, Wg, x, N, K)
+    assert np.allclose(h2, g2 * g2 * expit(g2), rtol=1e-12, atol=1e-12)
+    # silu(0) = 0: an all-zero gate row gives h = 0
+    Wz = Wg.copy()
+    Wz[0] = 0
+    h3, g3, _ = oracle.swiglu(Wz, Wu, x, N, K)
+    assert g3[0] == 0.0 and h3[0] == 0.0
+
+
+def test_swiglu_sign_of_exponent():
+    """Large positive gate passes through (silu(z) ~ z), large negative is
+    suppressed (silu(z) ~ 0): catches e^{+z} in place of e^{-z}."""
+    K = 256
+    blk_pos = pack_q4k(f16_bits(1.0), f16_bits(0.0), [1] * 8, [0] * 8, [15] * 256)
+    ones = np.ones(K, np.float32)
+    h, g, u = oracle.swiglu(blk_pos, blk_pos, ones, 1, K)
+    assert g[0] == 15 * 256 and h[0] == pytest.approx(g[0] * u[0], rel=1e-12)
+    h, g, u = oracle.swiglu(blk_pos, blk_pos, -ones, 1, K)
+    assert g[0] == -15 * 256 and abs(h[0]) < 1e-300
+
+
+# ------------------------------------------------------------------ Q8
+def test_q8_worked_blocks(golden_dir):
+    g = _golden(golden_dir, "q8_worked_block.json")
+    x = np.zeros(64, np.float32)
+    for i, v in g["block_a"]["x_nonzero"].items():
+        x[int(i)] = v
+    q, d = oracle.q8_quantize(x)
+    exp = np.zeros(32, np.int8)
+    for i, v in g["block_a"]["expected_q_nonzero"].items():
+        exp[int(i)] = v
+    assert np.array_equal(q[:32], exp)
+    assert d[0] == int(g["block_a"]["expected_scale_bits"], 16)
+    assert np.all(q[32:] == 0) and d[1] == int(g["block_zero"]["expected_scale_bits"], 16)
+
+
+def test_q8_invariants_and_numpy():
+    rng = np.random.default_rng(8)
+    x = (rng.standard_normal(32 * 400) * np.repeat(rng.uniform(0.01, 100, 400), 32)).astype(np.float32)
+    x[:32] = 0.0
+    q, d = oracle.q8_quantize(x)
+    xb = x.reshape(-1, 32)
+    qb = q.reshape(-1, 32).astype(np.int64)
+    amax = np.abs(xb).max(axis=1)
+    d32 = (amax / np.float32(127)).astype(np.float32)          # numpy f32 division (IEEE)
+    assert np.array_equal(d, d32.astype(np.float16).view(np.uint16))
+    assert np.all(np.abs(qb) <= 127)
+    nz = amax > 0
+    assert np.all(np.abs(qb[nz]).max(axis=1) == 127)
+    assert np.all(qb[~nz] == 0)
+    t = np.zeros_like(xb)
+    t[nz] = (xb[nz] / d32[nz, None]).astype(np.float32)
+    # nearest integer, ties away from zero
+    frac = np.abs(t.astype(np.float64) - qb)
+    assert np.all(frac <= 0.5)
+    tie = frac == 0.5
+    assert np.all(np.abs(qb[tie]) > np.abs(t[tie]))
+
+
+def test_q8_rounding_ties_away_from_zero():
+    x = np.zeros(32, np.float32)
+    x[0] = 127.0
+    x[1:9] = [0.5, -0.5, 1.5, -1.5, 2.5, -2.5, 126.5, -126.5]
+    q, d = oracle.q8_quantize(x)
+    assert list(q[1:9]) == [1, -1, 2, -2, 3, -3, 127, -127]
+
+
+def test_q4k_q8_worked_dot(golden_dir):
+    g = _golden(golden_dir, "q8_worked_block.json")["q4k_dot"]
+    blk = np.frombuffer(bytes.fromhex(_golden(golden_dir, "q4k_worked_block.json")["bytes_hex"]), np.uint8)
+    x = np.ones(256, np.float32)
+    q, d = oracle.q8_quantize(x)
+    assert np.all(d == int(g["expected_scale_bits"], 16)) and np.all(q == g["expected_q"])
+    isums = oracle.q4k_q8_isums(blk, q, 1, 256)
+    assert list(isums[0]) == g["expected_isums"]
+    assert int(q[:32].astype(np.int64).sum()) == g["expected_qsum"]
+    y = oracle.q4k_q8_gemv(blk, q, d, 1, 256)
+    assert y[0] == g["expected_y"]
+
+
+def test_q4k_q8_vs_numpy():
+    rng = np.random.default_rng(9)
+    N, K = 6, 1024
+    fields = random_q4k_fields(rng, N * K // 256)
+    W, Wf = q4k_matrix_from_fields(fields, N, K)
+    x = (rng.standard_normal(K) * 3).astype(np.float32)
+    q, d = oracle.q8_quantize(x)
+    qraw = fields[4].reshape(N, K).astype(np.int64)
+    isum_ref = (qraw * q.astype(np.int64)).reshape(N, K // 32, 32).sum(axis=2)
+    assert np.array_equal(oracle.q4k_q8_isums(W, q, N, K), isum_ref)
+    xdq = np.repeat(d.view(np.float16).astype(np.float64), 32) * q
+    y = oracle.q4k_q8_gemv(W, q, d, N, K)
+    assert np.allclose(y, Wf @ xdq, rtol=1e-13, atol=1e-12)
+
+
+# ------------------------------------------------------------------ argmax
+def test_argmax_vs_nanargmax_with_ties():
+    rng = np.random.default_rng(10)
+    for trial in range(300):
+        n = int(rng.integers(1, 300))
+        v = rng.integers(-5, 5, n).astype(np.float64)     # many exact ties
+        if trial % 3 == 0:
+            v[rng.integers(0, n, max(1, n // 10))] = np.nan
+        if np.all(np.isnan(v)):
+            assert oracle.argmax_first(v) == 0
+        else:
+            assert oracle.argmax_first(v) == int(np.nanargmax(v))
+        f = v.astype(np.float32)
+        if not np.all(np.isnan(f)):
+            assert oracle.argmax_first(f) == int(np.nanargmax(f))
+
+
+def test_argmax_edges():
+    nan, inf = np.nan, np.inf
+    assert oracle.argmax_first(np.array([nan, nan])) == 0
+    assert oracle.argmax_first(np.array([nan, -inf, -inf])) == 1
+    assert oracle.argmax_first(np.array([-0.0, 0.0])) == 0
+    assert oracle.argmax_first(np.array([0.0, -0.0])) == 0
+    assert oracle.argmax_first(np.array([-1.0, -0.0, 0.0])) == 1
+    assert oracle.argmax_first(np.array([1.0, inf, nan, inf])) == 1
+    assert oracle.argmax_first(np.array([3.0, 3.0, 3.0], np.float32)) == 0
+    assert oracle.argmax_first(np.array([1.0, 2.0, 2.0], np.float32)) == 1
+
+
+def test_top2_gap():
+    assert oracle.top2_gap(np.array([1.0, 5.0, 3.0])) == 2.0
+    assert oracle.top2_gap(np.array([5.0, 1.0, 5.0])) == 0.0

@@ -1,0 +1,63 @@
+"""Seeded input generators: determinism (checksums) and distributions (CPU)."""
+import hashlib
+
+import numpy as np
+
+import synth
+
+
+def _h(*arrs):
+    m = hashlib.sha256()
+    for a in arrs:
+        m.update(np.ascontiguousarray(a).tobytes())
+    return m.hexdigest()[:16]
+
+
+def test_checksums_fixed():
+    # A change in draw order or distribution changes these; update them only
+    # together with a stated reason.
+    r = synth.rng_for(0)
+    assert _h(synth.q4k_weights(r, 64, 512), synth.activation(r, 512)) == "1a80ff6f66e325cb"
+    r = synth.rng_for(0)
+    assert _h(synth.q6k_weights(r, 64, 512), synth.activation(r, 512)) == "3822445b7cdd00f3"
+    r = synth.rng_for(0)
+    assert _h(synth.activation_outliers(r, 8192)) == "aed567af945460ea"
+    assert _h(*synth.c1_inputs(0)) == "8fd912eb75ae0192"
+
+
+def test_q4k_layout_and_ranges():
+    N, K = 50, 1024
+    W = synth.q4k_weights(synth.rng_for(1), N, K)
+    assert W.shape == (N, K // 256 * 144) and W.dtype == np.uint8
+    blk = W.reshape(N, K // 256, 144)
+    d = blk[:, :, 0:2].copy().view(np.float16).astype(np.float64)
+    dmin = blk[:, :, 2:4].copy().view(np.float16).astype(np.float64)
+    for v in (d, dmin):
+        assert v.min() >= 0.00099 and v.max() <= 0.01001
+    # the 6-bit fields of uniform bytes are uniform: mean of the low 6 bits ~ 31.5
+    assert abs((blk[:, :, 4:8] & 63).mean() - 31.5) < 1.5
+
+
+def test_q6k_layout_and_ranges():
+    N, K = 50, 1024
+    W = synth.q6k_weights(synth.rng_for(2), N, K)
+    assert W.shape == (N, K // 256 * 210)
+    blk = W.reshape(N, K // 256, 210)
+    sc = blk[:, :, 192:208].copy().view(np.int8)
+    assert sc.min() == -32 and sc.max() == 31
+    d = blk[:, :, 208:210].copy().view(np.float16).astype(np.float64)
+    assert d.min() >= 0.00099 and d.max() <= 0.01001
+
+
+def test_activation_outliers():
+    x = synth.activation_outliers(synth.rng_for(0), 8192)
+    assert x.dtype == np.float32 and x.size == 8192
+    big = np.abs(x) > 12.0        # |N(0,2)| > 12 has probability ~1e-17
+    assert 1 <= big.sum() <= 8
+    assert abs(np.var(x[~big]) - 2.0) < 0.15
+
+
+def test_shapes_of_workloads():
+    assert synth.C3_LM_HEAD == (248_320, 1024)
+    assert synth.C3_LM_HEAD[0] * 4 == 993_280   # f32 logits bytes of the unfused path
+    assert synth.C5_Q8 == (28_672, 8192)
