@@ -1,0 +1,363 @@
+#!/usr/bin/env python3
+"""Benchmark of the batch-1 quantized GEMV path on one MI355X.
+
+One step = one pass of the whole hot path over the five workloads' shapes, all
+enqueued on one stream:
+  1. Q4_K GEMV  4096x2560, 2560x9728, 9728x2560 (4B-class decode shapes)
+  2. lm_head Q6_K 248,320 x 1024 GEMV + fused first-index argmax (4-byte result)
+  3. fused gate/up SwiGLU GEMV (2 x Q4_K 9728x2560) + ffn_down Q6_K 2560x9728
+  4. Q8 quantize of an f32[8192] activation + Q4_K x Q8 GEMV 28672x8192
+Weights are seeded synthetic data with the workloads' distributions.  Two
+copies of every weight buffer alternate between steps, so each buffer is
+re-read only after ~0.85 GB of other traffic and the 256 MB Infinity Cache
+cannot serve it.
+
+Prints ONE JSON line: value = effective weight GB/s of the whole step (weight
+bytes streamed per step / time per step), plus the lm_head-argmax calls/s,
+a roofline entry for the dominant kernel (its algorithmic bytes / its average
+launch time, measured with HIP events on the launch stream inside the timed
+region) and the CPU oracle timed on the host on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Q4_K GEMV effective HBM GB/s (% of peak) + lm_head-argmax calls/sec"
+HBM_PEAK_GBS = 8000.0
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_lm_head_argmax_q6k_248320x1024.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "gemv_q4k_q6k_amd", "csrc", f) for f in
+                  ("gemvq_kernels.hip", "gemvq_device.h", "gemvq_launch.h")]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def build_workload(dev):
+    """Seeded inputs (CPU numpy) and their device copies (two weight sets)."""
+    import torch
+    import synth
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    t0 = time.time()
+    c2 = [synth.c2_inputs(i) for i in range(3)]
+    c3 = synth.c3_inputs(0)
+    c4 = synth.c4_inputs(0)
+    c5 = synth.c5_inputs(0)
+    host = {"c2": c2, "c3": c3, "c4": c4, "c5": c5}
+    sets = []
+    for copy in range(2):
+        s = {
+            "c2W": [up(W) for W, _ in c2],
+            "c3W": up(c3[0]),
+            "c4Wg": up(c4[0]), "c4Wu": up(c4[1]), "c4Wd": up(c4[2]),
+            "c5W": up(c5[0]),
+        }
+        sets.append(s)
+    vec = {
+        "c2x": [up(x) for _, x in c2],
+        "c3x": up(c3[1]),
+        "c4x": up(c4[3]),
+        "c5x": up(c5[1]),
+        "h": torch.empty(synth.C4_SWIGLU[0], dtype=torch.float32, device=dev),
+        "yd": torch.empty(synth.C4_SWIGLU[1], dtype=torch.float32, device=dev),
+        "c2y": [torch.empty(N, dtype=torch.float32, device=dev) for N, _ in synth.C2_Q4K],
+        "c5y": torch.empty(synth.C5_Q8[0], dtype=torch.float32, device=dev),
+        "xq": torch.empty(synth.C5_Q8[1], dtype=torch.int8, device=dev),
+        "xd": torch.empty(synth.C5_Q8[1] // 32, dtype=torch.int16, device=dev),
+        "idx": torch.empty(1, dtype=torch.int32, device=dev),
+        "ws": torch.zeros(0, dtype=torch.uint8, device=dev),
+    }
+    torch.cuda.synchronize()
+    log(f"workload built in {time.time() - t0:.1f}s")
+    return host, sets, vec
+
+
+def weight_bytes():
+    import synth
+    b = {}
+    b["c2"] = sum(N * K // 256 * 144 for N, K in synth.C2_Q4K)
+    N, K = synth.C3_LM_HEAD
+    b["c3"] = N * K // 256 * 210
+    N, K = synth.C4_SWIGLU
+    b["c4"] = 2 * N * K // 256 * 144 + K * N // 256 * 210
+    N, K = synth.C5_Q8
+    b["c5"] = N * K // 256 * 144
+    return b
+
+
+def lm_head_algorithmic_bytes():
+    import synth
+    N, K = synth.C3_LM_HEAD
+    return N * K // 256 * 210 + 4 * K + 4
+
+
+def step_calls(gq, s, v):
+    """The hot path of one step as pre-bound C-ABI calls (raw pointers and
+    the current stream), so the timed loop spends ~1 us of host time per
+    launch.  Every argument was validated once by the binding (check_parity
+    runs the same buffers through it).  Returns (calls, index of the lm_head
+    call)."""
+    import torch
+    import synth
+    L = gq.lib()
+    st = torch.cuda.current_stream().cuda_stream
+    calls = []
+    for i, (N, K) in enumerate(synth.C2_Q4K):
+        calls.append((L.q4k_gemv, (s["c2W"][i].data_ptr(), v["c2x"][i].data_ptr(), v["c2y"][i].data_ptr(), N, K, st)))
+    N, K = synth.C3_LM_HEAD
+    lm = len(calls)
+    calls.append((L.lm_head_argmax, (s["c3W"].data_ptr(), v["c3x"].data_ptr(), v["idx"].data_ptr(), None,
+                                     v["ws"].data_ptr(), v["ws"].numel(), N, K, st)))
+    N, K = synth.C4_SWIGLU
+    calls.append((L.swiglu_gemv, (s["c4Wg"].data_ptr(), s["c4Wu"].data_ptr(), v["c4x"].data_ptr(),
+                                  v["h"].data_ptr(), N, K, st)))
+    calls.append((L.q6k_gemv, (s["c4Wd"].data_ptr(), v["h"].data_ptr(), v["yd"].data_ptr(), K, N, st)))
+    N, K = synth.C5_Q8
+    calls.append((L.q8_quantize, (v["c5x"].data_ptr(), v["xq"].data_ptr(), v["xd"].data_ptr(), K, st)))
+    calls.append((L.q4k_q8_gemv, (s["c5W"].data_ptr(), v["xq"].data_ptr(), v["xd"].data_ptr(),
+                                  v["c5y"].data_ptr(), N, K, st)))
+    return calls, lm
+
+
+def run_calls(calls, lm=None, events=None):
+    for j, (fn, args) in enumerate(calls):
+        if j == lm and events is not None:
+            events[0].record()
+        rc = fn(*args)
+        if rc != 0:
+            raise RuntimeError(f"{fn.__name__} returned {rc}")
+        if j == lm and events is not None:
+            events[1].record()
+
+
+def run_step(gq, s, v):
+    """One pass of the hot path through the checked binding."""
+    import synth
+    for i, (N, K) in enumerate(synth.C2_Q4K):
+        gq.q4k_gemv(s["c2W"][i], v["c2x"][i], N, K, y=v["c2y"][i])
+    N, K = synth.C3_LM_HEAD
+    gq.lm_head_argmax(s["c3W"], v["c3x"], N, K, v["ws"], out_idx=v["idx"])
+    N, K = synth.C4_SWIGLU
+    gq.swiglu_gemv(s["c4Wg"], s["c4Wu"], v["c4x"], N, K, h=v["h"])
+    gq.q6k_gemv(s["c4Wd"], v["h"], K, N, y=v["yd"])
+    N, K = synth.C5_Q8
+    gq.q8_quantize(v["c5x"], xq=v["xq"], xd=v["xd"])
+    gq.q4k_q8_gemv(s["c5W"], v["xq"], v["xd"], N, K, y=v["c5y"])
+
+
+def self_check(gq, sets, v):
+    """Sanity of the benchmarked buffers without the oracle (the parity suite
+    against the oracle lives in tests/): the fused argmax must equal the
+    first-index argmax of q6k_gemv's own logits on both weight copies."""
+    import torch
+    import synth
+    N, K = synth.C3_LM_HEAD
+    ok = True
+    for s in sets:
+        run_step(gq, s, v)
+        logits = gq.q6k_gemv(s["c3W"], v["c3x"], N, K)
+        m = logits.max()
+        first = int(torch.nonzero(logits == m)[0].item())
+        ok = ok and int(v["idx"].item()) == first
+    torch.cuda.synchronize()
+    return bool(ok)
+
+
+def breakdown(gq, sets, v, reps=20):
+    """Per-call device time of each kernel: `reps` launches alternating the
+    two weight copies are captured in a HIP graph and replayed between two
+    HIP events (no host launch overhead in the measurement).  Not part of
+    `value`; rocprofv3 kernel traces are the cross-check."""
+    import torch
+    import synth
+    out = {}
+    wb = weight_bytes()
+    yl = torch.empty(synth.C3_LM_HEAD[0], dtype=torch.float32, device=v["h"].device)
+
+    def timeit(name, fn, nbytes):
+        for r in range(2):
+            fn(sets[r % 2])
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for r in range(reps):
+                fn(sets[r % 2])
+        g.replay()
+        torch.cuda.synchronize()
+        st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n_rep = 5
+        st.record()
+        for _ in range(n_rep):
+            g.replay()
+        en.record()
+        torch.cuda.synchronize()
+        us = st.elapsed_time(en) * 1000.0 / (reps * n_rep)
+        out[name] = {"us": round(us, 2), "GBps": round(nbytes / us / 1e3, 1),
+                     "frac_hbm_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
+        del g
+
+    for i, (N, K) in enumerate(synth.C2_Q4K):
+        timeit(f"q4k_gemv_{N}x{K}", lambda s, i=i, N=N, K=K: gq.q4k_gemv(s["c2W"][i], v["c2x"][i], N, K,
+                                                                           y=v["c2y"][i]),
+               N * K // 256 * 144 + 4 * (N + K))
+    N, K = synth.C3_LM_HEAD
+    timeit("lm_head_argmax_248320x1024", lambda s: gq.lm_head_argmax(s["c3W"], v["c3x"], N, K, v["ws"],
+                                                                     out_idx=v["idx"]),
+           lm_head_algorithmic_bytes())
+    timeit("q6k_gemv_248320x1024", lambda s: gq.q6k_gemv(s["c3W"], v["c3x"], N, K, y=yl),
+           N * K // 256 * 210 + 4 * (N + K))
+    N, K = synth.C4_SWIGLU
+    timeit("swiglu_gemv_9728x2560", lambda s: gq.swiglu_gemv(s["c4Wg"], s["c4Wu"], v["c4x"], N, K, h=v["h"]),
+           2 * N * K // 256 * 144 + 4 * (N + K))
+    timeit("q6k_gemv_2560x9728", lambda s: gq.q6k_gemv(s["c4Wd"], v["h"], K, N, y=v["yd"]),
+           K * N // 256 * 210 + 4 * (N + K))
+    N, K = synth.C5_Q8
+    timeit("q8_quantize_8192", lambda s: gq.q8_quantize(v["c5x"], xq=v["xq"], xd=v["xd"]), K * 4 + K + K // 16)
+    timeit("q4k_q8_gemv_28672x8192", lambda s: gq.q4k_q8_gemv(s["c5W"], v["xq"], v["xd"], N, K, y=v["c5y"]),
+           N * K // 256 * 144 + K + K // 16 + 4 * N)
+    timeit("q4k_gemv_28672x8192", lambda s: gq.q4k_gemv(s["c5W"], v["c5x"], N, K, y=v["c5y"]),
+           N * K // 256 * 144 + 4 * (N + K))
+    return out
+
+
+def cpu_baseline(host, budget_s=12.0):
+    """The oracle as it stands, on the host cores, on whole steps of the same
+    workload until about budget_s seconds have passed."""
+    import oracle
+    import synth
+    wb = sum(weight_bytes().values())
+    steps = 0
+    t0 = time.time()
+    while True:
+        for i, (N, K) in enumerate(synth.C2_Q4K):
+            oracle.q4k_gemv(host["c2"][i][0], host["c2"][i][1], N, K)
+        N, K = synth.C3_LM_HEAD
+        oracle.argmax_first(oracle.q6k_gemv(host["c3"][0], host["c3"][1], N, K))
+        Wg, Wu, Wd, x = host["c4"]
+        N, K = synth.C4_SWIGLU
+        h, _, _ = oracle.swiglu(Wg, Wu, x, N, K)
+        oracle.q6k_gemv_f64x(Wd, h, K, N)
+        W, x = host["c5"]
+        N, K = synth.C5_Q8
+        q, d = oracle.q8_quantize(x)
+        oracle.q4k_q8_gemv(W, q, d, N, K)
+        steps += 1
+        if time.time() - t0 >= budget_s:
+            break
+    dt = time.time() - t0
+    return {"value": round(wb * steps / dt / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{steps} whole steps of the same workload (all four stages, f64 oracle) in {dt:.1f}s"}
+
+
+def traffic_entry(alg_bytes):
+    """HBM bytes per lm_head launch from committed rocprofv3 counter runs, if
+    they were taken on the current kernel sources."""
+    try:
+        with open(PROFILE_TRAFFIC) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-breakdown", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the path is a single-GPU kernel library); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gemv_q4k_q6k_amd as gq
+    import synth
+
+    dev = torch.device("cuda:0")
+    gq.lib()
+    host, sets, v = build_workload(dev)
+    N, K = synth.C3_LM_HEAD
+    v["ws"] = torch.zeros(gq.lm_head_argmax_ws_bytes(N, K), dtype=torch.uint8, device=dev)
+    parity_ok = self_check(gq, sets, v)   # both copies go through the checked binding once
+    log(f"self-check of the benchmarked buffers: {'ok' if parity_ok else 'FAILED'}")
+
+    prepared = [step_calls(gq, sets[c], v) for c in range(2)]
+    for w in range(args.warmup):
+        run_calls(prepared[w % 2][0])
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for k in range(args.steps):
+        calls, lm = prepared[k % 2]
+        run_calls(calls, lm, ev[k])
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / args.steps
+    lm_us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1000.0
+
+    wb = weight_bytes()
+    step_bytes = sum(wb.values())
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    alg = lm_head_algorithmic_bytes()
+    achieved = alg / (lm_us * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_entry(alg),
+                "kernel": "lm_head_argmax Q6_K 248320x1024", "algorithmic_bytes_per_launch": alg,
+                "avg_launch_us": round(lm_us, 2)}
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic (seeded GGUF Q4_K/Q6_K blocks, f32 activations)",
+        "config": {"workload": "decode hot path: Q4_K 4096x2560+2560x9728+9728x2560; Q6_K lm_head 248320x1024 "
+                               "+ argmax; SwiGLU 2x Q4_K 9728x2560 + Q6_K 2560x9728; Q8 quantize + Q4_K "
+                               "28672x8192", "weight_bytes_per_step": step_bytes,
+                   "weight_copies": 2, "parallelism": "single GPU"},
+        "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "lm_head_argmax_calls_per_s": round(1e6 / lm_us, 1),
+        "self_check_ok": parity_ok,
+        "wall_s": round(wall, 3),
+        "roofline": roofline,
+    }
+    if not args.no_breakdown:
+        result["kernels"] = breakdown(gq, sets, v)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(host)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

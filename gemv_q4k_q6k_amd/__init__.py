@@ -1,0 +1,232 @@
+"""Python binding of libgemvq.so, the gfx950 batch-1 quantized GEMV library.
+
+Argument marshalling only: every function checks tensor dtype, device, size
+and contiguity, passes raw device pointers and the current HIP stream of the
+tensors' device to the C ABI (include/gemvq.h), and raises GemvqError on a
+non-zero status.  All arithmetic happens in the HIP kernels; there is no CPU
+fallback, and importing the functions fails loudly when the library has not
+been built (``python -m gemv_q4k_q6k_amd.build``).
+
+Layout: a weight matrix is a uint8 tensor holding N rows of K/256
+super-blocks (144 bytes each for Q4_K, 210 for Q6_K), rows back to back.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import threading
+
+__all__ = [
+    "GemvqError", "lib", "exported_names", "header_names",
+    "q4k_gemv", "q6k_gemv", "q8_quantize", "q4k_q8_gemv", "swiglu_gemv",
+    "lm_head_argmax", "lm_head_argmax_ws_bytes", "q4k_q8_isums", "strerror",
+    "Q4K_BLOCK_BYTES", "Q6K_BLOCK_BYTES", "LIB_PATH", "HEADER_PATH",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgemvq.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "gemvq.h")
+
+Q4K_BLOCK_BYTES = 144
+Q6K_BLOCK_BYTES = 210
+
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_WORKSPACE, ERR_ALIAS, ERR_HIP = range(7)
+
+
+class GemvqError(RuntimeError):
+    def __init__(self, fn: str, status: int, message: str):
+        super().__init__(f"{fn}: status {status}: {message}")
+        self.status = status
+
+
+_lock = threading.Lock()
+_lib = None
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_SIGS = {
+    "q4k_gemv": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P]),
+    "q6k_gemv": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P]),
+    "q8_quantize": (ctypes.c_int, [_P, _P, _P, _I64, _P]),
+    "q4k_q8_gemv": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _P]),
+    "swiglu_gemv": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _P]),
+    "lm_head_argmax": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_size_t, _I64, _I64, _P]),
+    "gemvq_lm_head_argmax_ws_bytes": (ctypes.c_size_t, [_I64, _I64]),
+    "gemvq_q4k_q8_isums": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P]),
+    "gemvq_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """Load libgemvq.so (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m gemv_q4k_q6k_amd.build`")
+            L = ctypes.CDLL(LIB_PATH)
+            for name, (res, args) in _SIGS.items():
+                fn = getattr(L, name)
+                fn.restype = res
+                fn.argtypes = args
+            _lib = L
+        return _lib
+
+
+def header_names() -> list[str]:
+    """Function names declared in include/gemvq.h."""
+    with open(HEADER_PATH) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([A-Za-z_][A-Za-z0-9_]*)\s*\(",
+                                 text, flags=re.M)))
+
+
+def exported_names() -> list[str]:
+    return sorted(_SIGS)
+
+
+def strerror(status: int) -> str:
+    return lib().gemvq_strerror(int(status)).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != OK:
+        raise GemvqError(fn, status, strerror(status))
+
+
+# ------------------------------------------------------------ torch helpers
+def _torch():
+    import torch
+    return torch
+
+
+def _dev_tensor(t, dtype, numel: int, what: str):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what}: expected a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{what}: must be a device tensor, got {t.device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{what}: expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what}: must be contiguous")
+    if t.numel() != numel:
+        raise ValueError(f"{what}: expected {numel} elements, got {t.numel()}")
+    return t
+
+
+def _stream(t, stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _weights(W, N: int, K: int, block: int, what: str = "W"):
+    if K % 256:
+        raise ValueError("K must be a multiple of 256")
+    return _dev_tensor(W, _torch().uint8, N * (K // 256) * block, what)
+
+
+def _out(out, device, dtype, n: int, what: str):
+    torch = _torch()
+    if out is None:
+        return torch.empty(n, dtype=dtype, device=device)
+    return _dev_tensor(out, dtype, n, what)
+
+
+# ------------------------------------------------------------- entry points
+def q4k_gemv(W, x, N: int, K: int, y=None, stream=None):
+    """y = W x for a Q4_K matrix W (uint8, N*(K/256)*144 bytes), x float32[K]."""
+    torch = _torch()
+    _weights(W, N, K, Q4K_BLOCK_BYTES)
+    _dev_tensor(x, torch.float32, K, "x")
+    y = _out(y, x.device, torch.float32, N, "y")
+    _check("q4k_gemv", lib().q4k_gemv(W.data_ptr(), x.data_ptr(), y.data_ptr(), N, K, _stream(x, stream)))
+    return y
+
+
+def q6k_gemv(W, x, N: int, K: int, y=None, stream=None):
+    """y = W x for a Q6_K matrix W (uint8, N*(K/256)*210 bytes), x float32[K]."""
+    torch = _torch()
+    _weights(W, N, K, Q6K_BLOCK_BYTES)
+    _dev_tensor(x, torch.float32, K, "x")
+    y = _out(y, x.device, torch.float32, N, "y")
+    _check("q6k_gemv", lib().q6k_gemv(W.data_ptr(), x.data_ptr(), y.data_ptr(), N, K, _stream(x, stream)))
+    return y
+
+
+def q8_quantize(x, xq=None, xd=None, stream=None):
+    """x float32[K] -> (int8[K] values, int16[K/32] fp16 scale bits)."""
+    torch = _torch()
+    K = x.numel()
+    _dev_tensor(x, torch.float32, K, "x")
+    xq = _out(xq, x.device, torch.int8, K, "xq")
+    xd = _out(xd, x.device, torch.int16, K // 32, "xd")
+    _check("q8_quantize", lib().q8_quantize(x.data_ptr(), xq.data_ptr(), xd.data_ptr(), K, _stream(x, stream)))
+    return xq, xd
+
+
+def q4k_q8_gemv(W, xq, xd, N: int, K: int, y=None, stream=None):
+    """y = W (dequantized Q8 x) with exact int8 dots; xq int8[K], xd int16[K/32]."""
+    torch = _torch()
+    _weights(W, N, K, Q4K_BLOCK_BYTES)
+    _dev_tensor(xq, torch.int8, K, "xq")
+    _dev_tensor(xd, torch.int16, K // 32, "xd")
+    y = _out(y, xq.device, torch.float32, N, "y")
+    _check("q4k_q8_gemv", lib().q4k_q8_gemv(W.data_ptr(), xq.data_ptr(), xd.data_ptr(), y.data_ptr(), N, K,
+                                            _stream(xq, stream)))
+    return y
+
+
+def swiglu_gemv(Wg, Wu, x, N: int, K: int, h=None, stream=None):
+    """h = silu(Wg x) * (Wu x), Wg and Wu Q4_K N x K."""
+    torch = _torch()
+    _weights(Wg, N, K, Q4K_BLOCK_BYTES, "Wg")
+    _weights(Wu, N, K, Q4K_BLOCK_BYTES, "Wu")
+    _dev_tensor(x, torch.float32, K, "x")
+    h = _out(h, x.device, torch.float32, N, "h")
+    _check("swiglu_gemv", lib().swiglu_gemv(Wg.data_ptr(), Wu.data_ptr(), x.data_ptr(), h.data_ptr(), N, K,
+                                            _stream(x, stream)))
+    return h
+
+
+def lm_head_argmax_ws_bytes(N: int, K: int) -> int:
+    return int(lib().gemvq_lm_head_argmax_ws_bytes(N, K))
+
+
+def lm_head_argmax(W, x, N: int, K: int, workspace, out_idx=None, out_max=None, want_max: bool = False,
+                   stream=None):
+    """First index of the largest row value of W x (Q6_K W).  Returns the
+    int32[1] device tensor holding the index (and the float32[1] maximum if
+    want_max or out_max is given).  `workspace` is a uint8 device tensor of at
+    least lm_head_argmax_ws_bytes(N, K) bytes, zero-filled before its first use
+    (torch.zeros); every call leaves it zero again."""
+    torch = _torch()
+    _weights(W, N, K, Q6K_BLOCK_BYTES)
+    _dev_tensor(x, torch.float32, K, "x")
+    if not isinstance(workspace, torch.Tensor) or workspace.device.type != "cuda" or workspace.dtype != torch.uint8:
+        raise TypeError("workspace: expected a uint8 device tensor")
+    out_idx = _out(out_idx, x.device, torch.int32, 1, "out_idx")
+    if want_max and out_max is None:
+        out_max = torch.empty(1, dtype=torch.float32, device=x.device)
+    if out_max is not None:
+        _dev_tensor(out_max, torch.float32, 1, "out_max")
+    st = lib().lm_head_argmax(W.data_ptr(), x.data_ptr(), out_idx.data_ptr(),
+                              out_max.data_ptr() if out_max is not None else None,
+                              workspace.data_ptr(), workspace.numel(), N, K, _stream(x, stream))
+    _check("lm_head_argmax", st)
+    return (out_idx, out_max) if out_max is not None else out_idx
+
+
+def q4k_q8_isums(W, xq, N: int, K: int, out=None, stream=None):
+    """Exact integer sums isums[n][j] of the Q8 path (test hook)."""
+    torch = _torch()
+    _weights(W, N, K, Q4K_BLOCK_BYTES)
+    _dev_tensor(xq, torch.int8, K, "xq")
+    out = _out(out, xq.device, torch.int32, N * (K // 32), "isums")
+    _check("gemvq_q4k_q8_isums", lib().gemvq_q4k_q8_isums(W.data_ptr(), xq.data_ptr(), out.data_ptr(), N, K,
+                                                          _stream(xq, stream)))
+    return out.view(N, K // 32)

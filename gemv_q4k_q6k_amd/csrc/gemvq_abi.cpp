@@ -1,0 +1,185 @@
+// C ABI of libgemvq.so (declared in include/gemvq.h).
+//
+// Each entry point validates every argument on the host first (so a rejected
+// call touches no HIP state and a CPU-only test can exercise every error
+// path), then looks up the CU count of the current device once, then enqueues
+// the kernels on the caller's stream and checks the launch.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/gemvq.h"
+#include "gemvq_launch.h"
+
+namespace {
+
+using gemvq::kMaxK;
+constexpr int64_t kMaxQ8K = 65536;
+constexpr int64_t kMaxN = 2147483647;
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+bool overlap(const void *a, size_t na, const void *b, size_t nb)
+{
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+// Shape of a weight matrix; on success stores its byte size.
+int check_shape(int64_t N, int64_t K, int64_t block_bytes, size_t *bytes)
+{
+    if (N < 1 || N > kMaxN || K < 256 || K > kMaxK || K % 256 != 0) return GEMVQ_ERR_SHAPE;
+    const int64_t nb = K / 256;
+    if (N > INT64_MAX / (nb * block_bytes)) return GEMVQ_ERR_SHAPE;
+    *bytes = (size_t)(N * nb * block_bytes);
+    return GEMVQ_OK;
+}
+
+// CU count of the current device, cached per device ordinal.
+std::atomic<int> g_cus[64];
+
+int device_cus(int *cus)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return GEMVQ_ERR_HIP;
+    if (dev >= 0 && dev < 64) {
+        const int c = g_cus[dev].load(std::memory_order_relaxed);
+        if (c > 0) {
+            *cus = c;
+            return GEMVQ_OK;
+        }
+    }
+    int c = 0;
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c < 1)
+        return GEMVQ_ERR_HIP;
+    if (dev >= 0 && dev < 64) g_cus[dev].store(c, std::memory_order_relaxed);
+    *cus = c;
+    return GEMVQ_OK;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? GEMVQ_OK : GEMVQ_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char *gemvq_strerror(int status)
+{
+    switch (status) {
+    case GEMVQ_OK: return "ok";
+    case GEMVQ_ERR_NULL: return "a required pointer is NULL";
+    case GEMVQ_ERR_SHAPE: return "bad shape: need 1 <= N < 2^31, 256 <= K <= 32768, K % 256 == 0";
+    case GEMVQ_ERR_ALIGN: return "misaligned pointer";
+    case GEMVQ_ERR_WORKSPACE: return "workspace too small";
+    case GEMVQ_ERR_ALIAS: return "an output overlaps an input";
+    case GEMVQ_ERR_HIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+    }
+}
+
+size_t gemvq_lm_head_argmax_ws_bytes(int64_t N, int64_t K)
+{
+    (void)N;
+    (void)K;
+    return gemvq::kArgmaxWsBytes;
+}
+
+int q4k_gemv(const void *W, const float *x, float *y, int64_t N, int64_t K, void *stream)
+{
+    if (!W || !x || !y) return GEMVQ_ERR_NULL;
+    size_t wb = 0;
+    if (int st = check_shape(N, K, 144, &wb)) return st;
+    if (!aligned(W, 16) || !aligned(x, 16) || !aligned(y, 4)) return GEMVQ_ERR_ALIGN;
+    if (overlap(y, (size_t)N * 4, W, wb) || overlap(y, (size_t)N * 4, x, (size_t)K * 4)) return GEMVQ_ERR_ALIAS;
+    int cus = 0;
+    if (int st = device_cus(&cus)) return st;
+    return status_of(gemvq::launch_q4k_gemv(W, x, y, N, K, cus, (hipStream_t)stream));
+}
+
+int q6k_gemv(const void *W, const float *x, float *y, int64_t N, int64_t K, void *stream)
+{
+    if (!W || !x || !y) return GEMVQ_ERR_NULL;
+    size_t wb = 0;
+    if (int st = check_shape(N, K, 210, &wb)) return st;
+    if (!aligned(W, 4) || !aligned(x, 16) || !aligned(y, 4)) return GEMVQ_ERR_ALIGN;
+    if (overlap(y, (size_t)N * 4, W, wb) || overlap(y, (size_t)N * 4, x, (size_t)K * 4)) return GEMVQ_ERR_ALIAS;
+    int cus = 0;
+    if (int st = device_cus(&cus)) return st;
+    return status_of(gemvq::launch_q6k_gemv(W, x, y, N, K, cus, (hipStream_t)stream));
+}
+
+int q8_quantize(const float *x, int8_t *xq, uint16_t *xd, int64_t K, void *stream)
+{
+    if (!x || !xq || !xd) return GEMVQ_ERR_NULL;
+    if (K < 32 || K > kMaxQ8K || K % 32 != 0) return GEMVQ_ERR_SHAPE;
+    if (!aligned(x, 16) || !aligned(xq, 16) || !aligned(xd, 4)) return GEMVQ_ERR_ALIGN;
+    const size_t nx = (size_t)K * 4, nq = (size_t)K, nd = (size_t)(K / 32) * 2;
+    if (overlap(xq, nq, x, nx) || overlap(xd, nd, x, nx) || overlap(xq, nq, xd, nd)) return GEMVQ_ERR_ALIAS;
+    return status_of(gemvq::launch_q8_quantize(x, xq, xd, K, (hipStream_t)stream));
+}
+
+int q4k_q8_gemv(const void *W, const int8_t *xq, const uint16_t *xd, float *y, int64_t N, int64_t K, void *stream)
+{
+    if (!W || !xq || !xd || !y) return GEMVQ_ERR_NULL;
+    size_t wb = 0;
+    if (int st = check_shape(N, K, 144, &wb)) return st;
+    if (!aligned(W, 16) || !aligned(xq, 16) || !aligned(xd, 4) || !aligned(y, 4)) return GEMVQ_ERR_ALIGN;
+    const size_t ny = (size_t)N * 4;
+    if (overlap(y, ny, W, wb) || overlap(y, ny, xq, (size_t)K) || overlap(y, ny, xd, (size_t)(K / 32) * 2))
+        return GEMVQ_ERR_ALIAS;
+    int cus = 0;
+    if (int st = device_cus(&cus)) return st;
+    return status_of(gemvq::launch_q4k_q8_gemv(W, xq, xd, y, N, K, cus, (hipStream_t)stream));
+}
+
+int swiglu_gemv(const void *Wg, const void *Wu, const float *x, float *h, int64_t N, int64_t K, void *stream)
+{
+    if (!Wg || !Wu || !x || !h) return GEMVQ_ERR_NULL;
+    size_t wb = 0;
+    if (int st = check_shape(N, K, 144, &wb)) return st;
+    if (!aligned(Wg, 16) || !aligned(Wu, 16) || !aligned(x, 16) || !aligned(h, 4)) return GEMVQ_ERR_ALIGN;
+    const size_t nh = (size_t)N * 4;
+    if (overlap(h, nh, Wg, wb) || overlap(h, nh, Wu, wb) || overlap(h, nh, x, (size_t)K * 4)) return GEMVQ_ERR_ALIAS;
+    int cus = 0;
+    if (int st = device_cus(&cus)) return st;
+    return status_of(gemvq::launch_swiglu_gemv(Wg, Wu, x, h, N, K, cus, (hipStream_t)stream));
+}
+
+int lm_head_argmax(const void *W, const float *x, uint32_t *out_idx, float *out_max, void *workspace, size_t ws_bytes,
+                   int64_t N, int64_t K, void *stream)
+{
+    if (!W || !x || !out_idx || !workspace) return GEMVQ_ERR_NULL;
+    size_t wb = 0;
+    if (int st = check_shape(N, K, 210, &wb)) return st;
+    if (!aligned(W, 4) || !aligned(x, 16) || !aligned(out_idx, 4) || (out_max && !aligned(out_max, 4)) ||
+        !aligned(workspace, 256))
+        return GEMVQ_ERR_ALIGN;
+    if (ws_bytes < gemvq::kArgmaxWsBytes) return GEMVQ_ERR_WORKSPACE;
+    const size_t nx = (size_t)K * 4;
+    if (overlap(out_idx, 4, W, wb) || overlap(out_idx, 4, x, nx) || overlap(out_idx, 4, workspace, ws_bytes))
+        return GEMVQ_ERR_ALIAS;
+    if (out_max && (overlap(out_max, 4, W, wb) || overlap(out_max, 4, x, nx) ||
+                    overlap(out_max, 4, workspace, ws_bytes) || overlap(out_max, 4, out_idx, 4)))
+        return GEMVQ_ERR_ALIAS;
+    if (overlap(workspace, ws_bytes, W, wb) || overlap(workspace, ws_bytes, x, nx)) return GEMVQ_ERR_ALIAS;
+    int cus = 0;
+    if (int st = device_cus(&cus)) return st;
+    return status_of(
+        gemvq::launch_lm_head_argmax(W, x, out_idx, out_max, workspace, N, K, cus, (hipStream_t)stream));
+}
+
+int gemvq_q4k_q8_isums(const void *W, const int8_t *xq, int32_t *isums, int64_t N, int64_t K, void *stream)
+{
+    if (!W || !xq || !isums) return GEMVQ_ERR_NULL;
+    size_t wb = 0;
+    if (int st = check_shape(N, K, 144, &wb)) return st;
+    if (N * (K / 32) > (int64_t)1 << 40) return GEMVQ_ERR_SHAPE;
+    if (!aligned(W, 16) || !aligned(xq, 16) || !aligned(isums, 4)) return GEMVQ_ERR_ALIGN;
+    const size_t ni = (size_t)N * (size_t)(K / 32) * 4;
+    if (overlap(isums, ni, W, wb) || overlap(isums, ni, xq, (size_t)K)) return GEMVQ_ERR_ALIAS;
+    return status_of(gemvq::launch_q4k_q8_isums(W, xq, isums, N, K, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,357 @@
+// Device-side building blocks of the gfx950 GEMV kernels: super-block loads,
+// in-register dequantisation + dot products, wave reductions.
+//
+// Lane geometry shared by every GEMV kernel.  A row of K weights is K/256
+// super-blocks; four lanes ("parts") share each super-block, so a row occupies
+// lanes_row = 4 * (K/256) consecutive lanes of the workgroup.  A workgroup of W
+// waves holds P = floor(64*W / lanes_row) rows at a time (a "tile").  A lane's
+// (row-in-tile, block, part) never changes while the workgroup walks its
+// tiles, so each lane loads the 64 activation values its part multiplies once
+// and keeps them in VGPRs; per tile it streams only weight bytes.
+//
+//   Q4_K part c (0..3): quant bytes qs[32c, 32c+32) = low nibbles of sub-block
+//     2c (weights 64c + i) and high nibbles of sub-block 2c+1 (64c + 32 + i).
+//   Q6_K part u (0..3), n = u>>1, l0 = 16*(u&1): ql[64n+l0, +16),
+//     ql[64n+32+l0, +16) and qh[32n+l0, +16) = weights 128n + 32s + l0 + i for
+//     s = 0..3, i < 16, one int8 scale per s.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gemvq {
+
+constexpr int kQK = 256;
+constexpr int kQ4KBytes = 144;
+constexpr int kQ6KBytes = 210;
+constexpr int kParts = 4;                 // lanes per super-block
+constexpr uint32_t kNoIndex = 0xFFFFFFFFu;
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+struct __attribute__((aligned(4))) U32x4A4 { uint32_t v[4]; };
+
+// f16 "magic" conversion: OR-ing a 10-bit integer m into the mantissa of
+// 1024.0h (0x6400) gives the exact half value 1024 + m.  Two such halves per
+// dword feed v_fma_mix_f32 directly (f16 operand, f32 accumulate).
+constexpr uint32_t kMagic2 = 0x64006400u;
+
+__device__ __forceinline__ h2_t as_h2(uint32_t v) { return __builtin_bit_cast(h2_t, v); }
+
+// (v & mask) | other in one v_and_or_b32.  gfx9 VOP3 encodings take no
+// literal constants, so the compiler otherwise splits this into a VOP2 and +
+// or pair; the mask goes in an SGPR and `other` in a VGPR.
+__device__ __forceinline__ uint32_t and_or(uint32_t v, uint32_t mask, uint32_t other)
+{
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(v), "s"(mask), "v"(other));
+    return r;
+}
+
+__device__ __forceinline__ float half_lo(uint32_t v) { return (float)as_h2(v).x; }
+__device__ __forceinline__ float half_hi(uint32_t v) { return (float)as_h2(v).y; }
+
+// ---------------------------------------------------------------- DPP
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+// Sum over the 4 lanes of a quad; every lane of the quad gets the same bits
+// (each step adds a value to its mirror partner, a commutative pair).
+__device__ __forceinline__ float quad_sum(float v)
+{
+    v += dpp_f<kDppQuadXor1>(v);
+    v += dpp_f<kDppQuadXor2>(v);
+    return v;
+}
+
+// Sum over aligned groups of `group` lanes (4, 8, 16, 32 or 64), same bits in
+// every lane of a group.  Lane groups start at multiples of `group`.
+__device__ __forceinline__ float group_sum(float v, int group)
+{
+    v = quad_sum(v);
+    if (group >= 8) v += dpp_f<kDppRowHalfMirror>(v);
+    if (group >= 16) v += dpp_f<kDppRowMirror>(v);
+    if (group >= 32) v += __shfl_xor(v, 16);
+    if (group >= 64) v += __shfl_xor(v, 32);
+    return v;
+}
+
+// ------------------------------------------------------------- argmax
+// Candidate order: NaN never wins; larger value wins; equal values (-0 == +0)
+// go to the smaller index; kNoIndex marks "no candidate".
+__device__ __forceinline__ bool better(float v, uint32_t i, float bv, uint32_t bi)
+{
+    if (v != v) return false;
+    if (bi == kNoIndex) return i != kNoIndex;
+    return v > bv || (v == bv && i < bi);
+}
+
+// 64-bit key whose unsigned order is the candidate order above: the high word
+// maps the float monotonically to an unsigned integer (-0 folded onto +0),
+// the low word is ~index so that of two equal values the smaller index has
+// the larger key.  Key 0 means "no candidate" (no real candidate maps to it).
+__device__ __forceinline__ uint64_t argmax_key(float v, uint32_t i)
+{
+    uint32_t f = __float_as_uint(v == 0.f ? 0.f : v);
+    f = (f & 0x80000000u) ? ~f : (f | 0x80000000u);
+    return ((uint64_t)f << 32) | (uint64_t)(~i);
+}
+
+__device__ __forceinline__ float argmax_key_value(uint64_t k)
+{
+    const uint32_t f = (uint32_t)(k >> 32);
+    return __uint_as_float((f & 0x80000000u) ? (f & 0x7FFFFFFFu) : ~f);
+}
+
+__device__ __forceinline__ uint32_t argmax_key_index(uint64_t k) { return ~(uint32_t)k; }
+
+// Keeps a computed value in a register (stops the compiler from recomputing
+// it inside a loop to save registers).
+__device__ __forceinline__ void pin(float &v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void pin(int32_t &v) { asm volatile("" : "+v"(v)); }
+
+// ---------------------------------------------------------------- Q4_K
+
+struct Q4KRaw {
+    u32x4 hdr;   // d | dmin<<16, scale bytes 0..3, 4..7, 8..11
+    u32x4 q0;    // quant bytes [32c, 32c+16)
+    u32x4 q1;    // quant bytes [32c+16, 32c+32)
+};
+
+// `tile` is workgroup-uniform (scalar registers) and `off` the lane's 32-bit
+// byte offset of its super-block inside the tile, so every load is one
+// global_load with an SGPR base, a VGPR offset and an immediate.
+__device__ __forceinline__ void q4k_load(Q4KRaw &r, const uint8_t *__restrict__ tile, uint32_t off, int c)
+{
+    const uint8_t *blk = tile + off;
+    r.hdr = *(const u32x4 *)(blk);
+    const uint8_t *qs = tile + (off + 32u * (uint32_t)c);
+    r.q0 = *(const u32x4 *)(qs + 16);
+    r.q1 = *(const u32x4 *)(qs + 32);
+}
+
+__device__ __forceinline__ void q4k_zero(Q4KRaw &r)
+{
+    r.hdr = u32x4{0, 0, 0, 0};
+    r.q0 = r.hdr;
+    r.q1 = r.hdr;
+}
+
+// Scale and min of sub-blocks 2c and 2c+1 from the 12 packed bytes.
+// j < 4: scale = s[j] & 63, min = s[j+4] & 63;
+// j >= 4: scale = (s[j+4] & 15) | (s[j-4] >> 6) << 4, min = (s[j+4] >> 4) | (s[j] >> 6) << 4.
+__device__ __forceinline__ void q4k_scales(const u32x4 &hdr, int c, uint32_t &sc0, uint32_t &sc1,
+                                           uint32_t &m0, uint32_t &m1)
+{
+    const uint32_t sh = (uint32_t)(c & 1) * 16u;
+    const uint32_t A = hdr.y >> sh;      // s[2(c&1)], s[2(c&1)+1]
+    const uint32_t B = hdr.z >> sh;      // s[4+2(c&1)], ...
+    const uint32_t C = hdr.w >> sh;      // s[8+2(c&1)], ...
+    if (c < 2) {
+        sc0 = A & 63u;
+        sc1 = (A >> 8) & 63u;
+        m0 = B & 63u;
+        m1 = (B >> 8) & 63u;
+    } else {
+        sc0 = (C & 15u) | ((A >> 2) & 0x30u);
+        sc1 = ((C >> 8) & 15u) | ((A >> 10) & 0x30u);
+        m0 = ((C >> 4) & 15u) | ((B >> 2) & 0x30u);
+        m1 = ((C >> 12) & 15u) | ((B >> 10) & 0x30u);
+    }
+}
+
+// Activation slice of a Q4_K part: xl = x[64c + i], xh = x[64c + 32 + i].
+struct Q4KX {
+    float xl[32];
+    float xh[32];
+    float sxl, sxh;   // sums of xl and xh
+};
+
+// Dot product of one Q4_K part with its activation slice (f32 accumulate).
+// Quants enter as exact halves 1024+q (low nibble) and 1024+16q (high nibble),
+// so acc_lo = sum q x + 1024 sum x and acc_hi = 16 sum q x + 1024 sum x; the
+// offsets are removed with the precomputed sums.
+__device__ __forceinline__ float q4k_dot(const Q4KRaw &r, const Q4KX &x, int c)
+{
+    uint32_t sc0, sc1, m0, m1;
+    q4k_scales(r.hdr, c, sc0, sc1, m0, m1);
+    const float d = half_lo(r.hdr.x);
+    const float dmin = half_hi(r.hdr.x);
+    const uint32_t w[8] = {r.q0.x, r.q0.y, r.q0.z, r.q0.w, r.q1.x, r.q1.y, r.q1.z, r.q1.w};
+    const uint32_t magic = kMagic2;
+    float aL0 = 0.f, aL1 = 0.f, aH0 = 0.f, aH1 = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const uint32_t v = w[k];
+        const uint32_t v8 = v >> 8;
+        const h2_t t0 = as_h2(and_or(v, 0x000F000Fu, magic));    // lo(b0), lo(b2)
+        const h2_t t1 = as_h2(and_or(v, 0x00F000F0u, magic));    // 16hi(b0), 16hi(b2)
+        const h2_t t2 = as_h2(and_or(v8, 0x000F000Fu, magic));   // lo(b1), lo(b3)
+        const h2_t t3 = as_h2(and_or(v8, 0x00F000F0u, magic));   // 16hi(b1), 16hi(b3)
+        aL0 = __builtin_fmaf((float)t0.x, x.xl[4 * k + 0], aL0);
+        aL1 = __builtin_fmaf((float)t2.x, x.xl[4 * k + 1], aL1);
+        aL0 = __builtin_fmaf((float)t0.y, x.xl[4 * k + 2], aL0);
+        aL1 = __builtin_fmaf((float)t2.y, x.xl[4 * k + 3], aL1);
+        aH0 = __builtin_fmaf((float)t1.x, x.xh[4 * k + 0], aH0);
+        aH1 = __builtin_fmaf((float)t3.x, x.xh[4 * k + 1], aH1);
+        aH0 = __builtin_fmaf((float)t1.y, x.xh[4 * k + 2], aH0);
+        aH1 = __builtin_fmaf((float)t3.y, x.xh[4 * k + 3], aH1);
+    }
+    const float qxl = (aL0 + aL1) - 1024.f * x.sxl;             // sum q x, low sub-block
+    const float qxh = ((aH0 + aH1) - 1024.f * x.sxh) * 0.0625f; // sum q x, high sub-block
+    const float dl = d * (float)sc0, dh = d * (float)sc1;
+    const float ml = dmin * (float)m0, mh = dmin * (float)m1;
+    return (dl * qxl - ml * x.sxl) + (dh * qxh - mh * x.sxh);
+}
+
+// ------------------------------------------------------------ Q4_K x Q8
+
+// Q8 activation slice of a Q4_K part: 32 int8 for each of sub-blocks 2c and
+// 2c+1 packed in dwords, their fp16 scales as f32, and their integer sums.
+struct Q8X {
+    uint32_t ql[8];
+    uint32_t qh[8];
+    float dl, dh;
+    int32_t sl, sh;
+};
+
+// Exact integer sums of one part: isl = sum q4*q8 over sub-block 2c, ish over 2c+1.
+__device__ __forceinline__ void q4k_q8_isums(const Q4KRaw &r, const Q8X &x, int32_t &isl, int32_t &ish)
+{
+    const uint32_t w[8] = {r.q0.x, r.q0.y, r.q0.z, r.q0.w, r.q1.x, r.q1.y, r.q1.z, r.q1.w};
+    int32_t a = 0, b = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        a = __builtin_amdgcn_sdot4((int)(w[k] & 0x0F0F0F0Fu), (int)x.ql[k], a, false);
+        b = __builtin_amdgcn_sdot4((int)((w[k] >> 4) & 0x0F0F0F0Fu), (int)x.qh[k], b, false);
+    }
+    isl = a;
+    ish = b;
+}
+
+__device__ __forceinline__ float q4k_q8_dot(const Q4KRaw &r, const Q8X &x, int c)
+{
+    uint32_t sc0, sc1, m0, m1;
+    q4k_scales(r.hdr, c, sc0, sc1, m0, m1);
+    const float d = half_lo(r.hdr.x);
+    const float dmin = half_hi(r.hdr.x);
+    int32_t isl, ish;
+    q4k_q8_isums(r, x, isl, ish);
+    const float lo = d * (float)sc0 * (float)isl - dmin * (float)m0 * (float)x.sl;
+    const float hi = d * (float)sc1 * (float)ish - dmin * (float)m1 * (float)x.sh;
+    return x.dl * lo + x.dh * hi;
+}
+
+// ---------------------------------------------------------------- Q6_K
+
+// A Q6_K block starts 2 bytes off a dword boundary when its flat index is odd.
+// Loads use dword-aligned addresses only and v_alignbyte_b32 re-aligns; every
+// dword read lies inside the block (or, for a misaligned block, in the 2 bytes
+// before it, which belong to the previous block of the same buffer).
+struct Q6KRaw {
+    uint32_t a[5];   // ql[64n+l0 .. +16) plus one dword
+    uint32_t b[5];   // ql[64n+32+l0 .. +16) plus one dword
+    uint32_t h[5];   // qh[32n+l0 .. +16) plus one dword
+    uint32_t s[3];   // scale window sc[8n .. 8n+8) plus one dword
+    uint32_t dbits;  // fp16 d in the low 16 bits
+    uint32_t shift;  // byte misalignment of the block (0 or 2)
+};
+
+__device__ __forceinline__ void load5(uint32_t (&o)[5], const uint32_t *p)
+{
+    const U32x4A4 v = *(const U32x4A4 *)p;
+    o[0] = v.v[0];
+    o[1] = v.v[1];
+    o[2] = v.v[2];
+    o[3] = v.v[3];
+    o[4] = p[4];
+}
+
+// `tile` is workgroup-uniform, `off` the lane's byte offset of its block in
+// the tile (pointer arithmetic only: an integer round trip would lose the
+// global address space and turn every load into a flat load).
+__device__ __forceinline__ void q6k_load(Q6KRaw &r, const uint8_t *__restrict__ tile, uint32_t off, int u)
+{
+    const uint32_t sh = ((uint32_t)(uintptr_t)tile + off) & 3u;
+    const uint32_t al = off - sh;                               // dword-aligned block start
+    const uint32_t n = (uint32_t)(u >> 1), l0 = 16u * (uint32_t)(u & 1);
+    load5(r.a, (const uint32_t *)(tile + (al + 64u * n + l0)));
+    load5(r.b, (const uint32_t *)(tile + (al + 64u * n + 32u + l0)));
+    load5(r.h, (const uint32_t *)(tile + (al + 128u + 32u * n + l0)));
+    const uint32_t *sp = (const uint32_t *)(tile + (al + 192u + 8u * n));
+    r.s[0] = sp[0];
+    r.s[1] = sp[1];
+    r.s[2] = sp[sh ? 2 : 1];   // the third dword is needed (and in bounds) only when misaligned
+    r.dbits = *(const uint16_t *)(tile + (off + 208u));
+    r.shift = sh;
+}
+
+__device__ __forceinline__ void q6k_zero(Q6KRaw &r)
+{
+#pragma unroll
+    for (int i = 0; i < 5; ++i) r.a[i] = r.b[i] = r.h[i] = 0u;
+    r.s[0] = r.s[1] = r.s[2] = 0u;
+    r.dbits = 0u;
+    r.shift = 0u;
+}
+
+// Activation slice of a Q6_K part: xs[s][i] = x[128n + 32s + l0 + i].
+struct Q6KX {
+    float xs[4][16];
+    float sx[4];     // sum over i of xs[s][i]
+};
+
+// Dot product of one Q6_K part: quant bytes are assembled per dword (4 quants
+// of one group s), spread into halves 1024+q with v_perm_b32 and multiplied in
+// f32.  sum (q-32) x = acc - 1056 * sum x.
+__device__ __forceinline__ float q6k_dot(const Q6KRaw &r, const Q6KX &x, int u)
+{
+    const uint32_t sh = r.shift;
+    float acc[4][2];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc[s][0] = acc[s][1] = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t a = __builtin_amdgcn_alignbyte(r.a[k + 1], r.a[k], sh);
+        const uint32_t b = __builtin_amdgcn_alignbyte(r.b[k + 1], r.b[k], sh);
+        const uint32_t h = __builtin_amdgcn_alignbyte(r.h[k + 1], r.h[k], sh);
+        uint32_t q[4];
+        q[0] = and_or(h << 4, 0x30303030u, a & 0x0F0F0F0Fu);
+        q[1] = and_or(h << 2, 0x30303030u, b & 0x0F0F0F0Fu);
+        q[2] = and_or(h, 0x30303030u, (a >> 4) & 0x0F0F0F0Fu);
+        q[3] = and_or(h >> 2, 0x30303030u, (b >> 4) & 0x0F0F0F0Fu);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            // bytes 0,2 and 1,3 of q[s] under the 0x64 exponent byte -> halves 1024+q
+            const h2_t e = as_h2(__builtin_amdgcn_perm(0x64646464u, q[s], 0x04020400u));
+            const h2_t o = as_h2(__builtin_amdgcn_perm(0x64646464u, q[s], 0x04030401u));
+            acc[s][0] = __builtin_fmaf((float)e.x, x.xs[s][4 * k + 0], acc[s][0]);
+            acc[s][1] = __builtin_fmaf((float)o.x, x.xs[s][4 * k + 1], acc[s][1]);
+            acc[s][0] = __builtin_fmaf((float)e.y, x.xs[s][4 * k + 2], acc[s][0]);
+            acc[s][1] = __builtin_fmaf((float)o.y, x.xs[s][4 * k + 3], acc[s][1]);
+        }
+    }
+    // scales sc[8n + (u&1) + 2s]: bytes (u&1) + 2s of the 8-byte window
+    const uint32_t s0 = __builtin_amdgcn_alignbyte(r.s[1], r.s[0], sh);
+    const uint32_t s1 = __builtin_amdgcn_alignbyte(r.s[2], r.s[1], sh);
+    const uint32_t bo = (uint32_t)(u & 1) * 8u;
+    const int sc0 = __builtin_amdgcn_sbfe((int)s0, bo, 8);
+    const int sc1 = __builtin_amdgcn_sbfe((int)s0, bo + 16u, 8);
+    const int sc2 = __builtin_amdgcn_sbfe((int)s1, bo, 8);
+    const int sc3 = __builtin_amdgcn_sbfe((int)s1, bo + 16u, 8);
+    const float d = half_lo(r.dbits);
+    const float t0 = (float)sc0 * ((acc[0][0] + acc[0][1]) - 1056.f * x.sx[0]);
+    const float t1 = (float)sc1 * ((acc[1][0] + acc[1][1]) - 1056.f * x.sx[1]);
+    const float t2 = (float)sc2 * ((acc[2][0] + acc[2][1]) - 1056.f * x.sx[2]);
+    const float t3 = (float)sc3 * ((acc[3][0] + acc[3][1]) - 1056.f * x.sx[3]);
+    return d * ((t0 + t1) + (t2 + t3));
+}
+
+}  // namespace gemvq

@@ -1,0 +1,661 @@
+// gfx950 kernels of the batch-1 quantized GEMV path and their launchers.
+//
+// One kernel template serves the f32-activation Q4_K and Q6_K GEMVs, the
+// fused gate/up SwiGLU GEMV, the Q4_K x Q8 integer-dot GEMV and the lm_head
+// GEMV with argmax.  Lane geometry is described in gemvq_device.h: each lane
+// owns one quarter of one super-block column of the rows in a tile and keeps
+// the 64 activation values of that quarter in registers, so the steady state
+// streams weight bytes only.  A row's value is the sum of its 4*(K/256) lane
+// partials; the summation tree depends only on K, never on which workgroup,
+// wave or tile holds the row, so equal rows give bit-identical values (the
+// argmax tie rule relies on this) and q6k_gemv's outputs are exactly the values
+// lm_head_argmax compares.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <mutex>
+
+#include "gemvq_device.h"
+#include "gemvq_launch.h"
+
+namespace gemvq {
+
+enum Kind : int { kQ4K = 0, kQ6K = 1, kQ4KQ8 = 2, kSwiglu = 3 };
+enum Epi : int { kStore = 0, kArgmax = 1 };
+
+constexpr int kPhase = 2;   // tiles in flight per lane (software pipeline depth)
+
+struct GemvArgs {
+    const uint8_t *W;      // matrix (gate matrix for SwiGLU)
+    const uint8_t *W2;     // up matrix for SwiGLU
+    const float *x;        // f32 activation
+    const int8_t *xq;      // Q8 activation values
+    const uint16_t *xd;    // Q8 activation scales (fp16 bits)
+    float *y;              // output (h for SwiGLU)
+    uint32_t *out_idx;     // argmax result
+    float *out_max;        // argmax value or nullptr
+    uint8_t *ws;           // argmax workspace
+    int64_t N;
+    int tiles;             // ceil(N / rows_tile)
+    int tiles_q, tiles_r;  // tiles per workgroup: tiles_q, plus one for the first tiles_r workgroups
+    int nb;                // super-blocks per row
+    int lanes_row;         // 4 * nb
+    uint32_t lanes_row_magic;  // ceil(2^32 / lanes_row): tid / lanes_row == umulhi(tid, magic) for tid < 1024
+    int rows_tile;         // rows per tile (P)
+    int x_in_lds;          // stage the activation (and its 16-element sums) through LDS first
+};
+
+// ------------------------------------------------------- activation setup
+
+template <int KIND>
+struct XSlice;
+template <> struct XSlice<kQ4K> { Q4KX v; };
+template <> struct XSlice<kSwiglu> { Q4KX v; };
+template <> struct XSlice<kQ6K> { Q6KX v; };
+template <> struct XSlice<kQ4KQ8> { Q8X v; };
+
+__device__ __forceinline__ void load_x_f32(float *dst, const float *src, int n)
+{
+#pragma unroll
+    for (int i = 0; i < 16; i += 4) {
+        if (i < n) {
+            const float4 v = *(const float4 *)(src + i);
+            dst[i] = v.x;
+            dst[i + 1] = v.y;
+            dst[i + 2] = v.z;
+            dst[i + 3] = v.w;
+        }
+    }
+}
+
+// Sum of 16 consecutive activation values, added in index order.  Every
+// activation sum the kernels use is built from these, whether a lane adds
+// its own slice or a workgroup precomputes them in LDS, so both give the
+// same bits.
+__device__ __forceinline__ float sum16(const float *v)
+{
+    float t = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) t += v[i];
+    return t;
+}
+
+// Q4_K part c of block b: xl = x[256b + 64c + i], xh = x[256b + 64c + 32 + i].
+// `sums` (16-element sums of x, or nullptr to add the slice here).
+__device__ __forceinline__ void setup_x(Q4KX &xs, const float *xsrc, const float *sums, int b, int c)
+{
+    const float *p = xsrc + kQK * b + 64 * c;
+#pragma unroll
+    for (int i = 0; i < 32; i += 16) {
+        load_x_f32(xs.xl + i, p + i, 16);
+        load_x_f32(xs.xh + i, p + 32 + i, 16);
+    }
+    float sl, sh;
+    if (sums) {
+        const float *q = sums + 16 * b + 4 * c;
+        sl = q[0] + q[1];
+        sh = q[2] + q[3];
+    } else {
+        sl = sum16(xs.xl) + sum16(xs.xl + 16);
+        sh = sum16(xs.xh) + sum16(xs.xh + 16);
+    }
+    pin(sl);
+    pin(sh);
+    xs.sxl = sl;
+    xs.sxh = sh;
+}
+
+// Q6_K part u of block b: xs[s][i] = x[256b + 128n + 32s + l0 + i].
+__device__ __forceinline__ void setup_x(Q6KX &xs, const float *xsrc, const float *sums, int b, int u)
+{
+    const int n = u >> 1, l0 = 16 * (u & 1);
+    const float *p = xsrc + kQK * b + 128 * n + l0;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        load_x_f32(xs.xs[s], p + 32 * s, 16);
+        float t = sums ? sums[16 * b + 8 * n + 2 * s + (u & 1)] : sum16(xs.xs[s]);
+        pin(t);
+        xs.sx[s] = t;
+    }
+}
+
+// Q8 part c of block b: 32 int8 of sub-blocks 8b+2c and 8b+2c+1, their scales.
+__device__ __forceinline__ void setup_x(Q8X &xs, const int8_t *qsrc, const uint16_t *dsrc, int b, int c)
+{
+    const uint32_t *p = (const uint32_t *)(qsrc + kQK * b + 64 * c);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        xs.ql[k] = p[k];
+        xs.qh[k] = p[8 + k];
+    }
+    int32_t sl = 0, sh = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        sl = __builtin_amdgcn_sdot4((int)xs.ql[k], 0x01010101, sl, false);
+        sh = __builtin_amdgcn_sdot4((int)xs.qh[k], 0x01010101, sh, false);
+    }
+    pin(sl);
+    pin(sh);
+    xs.sl = sl;
+    xs.sh = sh;
+    xs.dl = xs.dh = 0.f;
+    if (dsrc) {
+        const int j = 8 * b + 2 * c;
+        xs.dl = (float)__builtin_bit_cast(_Float16, dsrc[j]);
+        xs.dh = (float)__builtin_bit_cast(_Float16, dsrc[j + 1]);
+    }
+}
+
+// ------------------------------------------------------- per-kind traits
+
+template <int KIND> struct Traits;
+template <> struct Traits<kQ4K> {
+    typedef Q4KRaw Raw;
+    static constexpr int kBytes = kQ4KBytes;
+    static constexpr int kOuts = 1;
+};
+template <> struct Traits<kQ4KQ8> {
+    typedef Q4KRaw Raw;
+    static constexpr int kBytes = kQ4KBytes;
+    static constexpr int kOuts = 1;
+};
+template <> struct Traits<kQ6K> {
+    typedef Q6KRaw Raw;
+    static constexpr int kBytes = kQ6KBytes;
+    static constexpr int kOuts = 1;
+};
+template <> struct Traits<kSwiglu> {
+    typedef Q4KRaw Raw;
+    static constexpr int kBytes = kQ4KBytes;
+    static constexpr int kOuts = 2;
+};
+
+template <int KIND>
+struct RawSet {
+    typename Traits<KIND>::Raw r[Traits<KIND>::kOuts];
+};
+
+template <int KIND>
+__device__ __forceinline__ void zero_raw(RawSet<KIND> &rs)
+{
+    if constexpr (KIND == kQ6K) {
+        q6k_zero(rs.r[0]);
+    } else {
+        q4k_zero(rs.r[0]);
+        if constexpr (KIND == kSwiglu) q4k_zero(rs.r[1]);
+    }
+}
+
+template <int KIND>
+__device__ __forceinline__ void dot_raw(const RawSet<KIND> &rs, const XSlice<KIND> &xs, int part, float (&out)[2])
+{
+    if constexpr (KIND == kQ6K) {
+        out[0] = q6k_dot(rs.r[0], xs.v, part);
+    } else if constexpr (KIND == kQ4KQ8) {
+        out[0] = q4k_q8_dot(rs.r[0], xs.v, part);
+    } else {
+        out[0] = q4k_dot(rs.r[0], xs.v, part);
+        if constexpr (KIND == kSwiglu) out[1] = q4k_dot(rs.r[1], xs.v, part);
+    }
+}
+
+// ---------------------------------------------------------------- epilogue
+
+struct ArgBest {
+    float v;
+    uint32_t i;
+};
+
+template <int KIND, int EPI>
+__device__ __forceinline__ void emit_row(const GemvArgs &a, int64_t row, const float (&v)[2], ArgBest &best)
+{
+    if constexpr (EPI == kArgmax) {
+        if (better(v[0], (uint32_t)row, best.v, best.i)) {
+            best.v = v[0];
+            best.i = (uint32_t)row;
+        }
+    } else if constexpr (KIND == kSwiglu) {
+        const float g = v[0], u = v[1];
+        a.y[row] = g * u / (1.0f + expf(-g));
+    } else {
+        a.y[row] = v[0];
+    }
+}
+
+__device__ __forceinline__ void wave_best(ArgBest &b)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const float ov = __shfl_xor(b.v, off);
+        const uint32_t oi = (uint32_t)__shfl_xor((int)b.i, off);
+        if (better(ov, oi, b.v, b.i)) {
+            b.v = ov;
+            b.i = oi;
+        }
+    }
+}
+
+// Workgroup-wide best; the result is valid in thread 0.
+__device__ __forceinline__ ArgBest block_best(ArgBest b, ArgBest *s_best)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int waves = (blockDim.x + 63) >> 6;
+    wave_best(b);
+    if (lane == 0) s_best[wave] = b;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int w = 1; w < waves; ++w)
+            if (better(s_best[w].v, s_best[w].i, b.v, b.i)) b = s_best[w];
+    }
+    return b;
+}
+
+// Workspace of lm_head_argmax: [0,8) the running best key, [8,12) the count of
+// finished workgroups.  Both are zero between calls.
+__device__ __forceinline__ uint64_t *ws_key(uint8_t *ws) { return (uint64_t *)ws; }
+__device__ __forceinline__ uint32_t *ws_done(uint8_t *ws) { return (uint32_t *)(ws + 8); }
+
+// Grid-level argmax without fences: each workgroup folds its candidate into
+// one 64-bit atomic max, waits for that atomic to complete, then counts itself
+// done with an atomic add; the workgroup that counts last reads the key with
+// an atomic exchange (which also clears it for the next call), writes the
+// 4-byte result and clears the counter.  Atomics are coherent at device scope
+// across all XCDs, so no cache writeback or invalidation is needed.
+__device__ void argmax_finish(const GemvArgs &a, ArgBest best)
+{
+    __shared__ ArgBest s_best[kMaxThreads / 64];
+    best = block_best(best, s_best);
+    if (threadIdx.x == 0) {
+        if (best.i != kNoIndex) {
+            // a returning atomic: consuming its result makes the wave wait until
+            // the max has been performed before it counts itself done
+            const uint64_t old = __hip_atomic_fetch_max(ws_key(a.ws), argmax_key(best.v, best.i), __ATOMIC_RELAXED,
+                                                        __HIP_MEMORY_SCOPE_AGENT);
+            asm volatile("" ::"v"(old));
+        }
+        const uint32_t prev = __hip_atomic_fetch_add(ws_done(a.ws), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (prev == gridDim.x - 1) {
+            const uint64_t k = __hip_atomic_exchange(ws_key(a.ws), (uint64_t)0, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+            a.out_idx[0] = k ? argmax_key_index(k) : 0u;
+            if (a.out_max) a.out_max[0] = k ? argmax_key_value(k) : __builtin_nanf("");
+            __hip_atomic_store(ws_done(a.ws), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+// ------------------------------------------------------------------ kernel
+
+// WAVE_LOCAL: a row's 4*(K/256) lanes are an aligned power-of-two group inside
+// one wave (K/256 in {1,2,4,8,16}), so rows reduce with DPP only; otherwise
+// each super-block's quad sum goes through LDS and one thread per row adds the
+// K/256 block sums in order.
+template <int KIND, int EPI, bool WAVE_LOCAL>
+__global__ __launch_bounds__(kMaxThreads) void gemv_kernel(GemvArgs a)
+{
+    extern __shared__ __align__(16) unsigned char smem[];
+    constexpr int BYTES = Traits<KIND>::kBytes;
+    constexpr int OUTS = Traits<KIND>::kOuts;
+    const int tid = threadIdx.x;
+    const int p = (int)__umulhi((uint32_t)tid, a.lanes_row_magic);   // row within the tile
+    const int rr = tid - p * a.lanes_row;     // lane within the row
+    const int b = rr >> 2;                    // super-block column
+    const int part = rr & 3;                  // quarter of the super-block
+    const bool lane_on = p < a.rows_tile;
+    const int K = a.nb * kQK;
+
+    const int bid = blockIdx.x;
+    const int t_begin = bid * a.tiles_q + (bid < a.tiles_r ? bid : a.tiles_r);
+    const int t_end = t_begin + a.tiles_q + (bid < a.tiles_r ? 1 : 0);
+    // rows of the last tile that exist (the tail may be ragged)
+    const int last_rows = (int)(a.N - (a.tiles - 1) * a.rows_tile);
+    const int64_t tile_stride = (int64_t)a.rows_tile * a.nb * BYTES;   // bytes per tile
+    const uint32_t lane_off = (uint32_t)((p * a.nb + b) * BYTES);      // < tile_stride
+
+    auto valid_tile = [&](int t) {
+        return lane_on && t < t_end && (t < a.tiles - 1 || p < last_rows);
+    };
+    // Loads are unconditional so the loop stays branch-free around them: a
+    // tile past this workgroup's range is replaced by its first tile, a lane
+    // with nothing to do reads the first super-block of that tile (always in
+    // bounds), and the partial sums of both are discarded.
+    auto fetch = [&](RawSet<KIND> &rs, int t) {
+        const int64_t tt = t < t_end ? t : t_begin;
+        const uint32_t off = valid_tile(t) ? lane_off : 0u;
+        if constexpr (KIND == kQ6K) {
+            q6k_load(rs.r[0], a.W + tt * tile_stride, off, part);
+        } else {
+            q4k_load(rs.r[0], a.W + tt * tile_stride, off, part);
+            if constexpr (KIND == kSwiglu) q4k_load(rs.r[1], a.W2 + tt * tile_stride, off, part);
+        }
+    };
+
+    // first tiles in flight before the activation set-up, so the two
+    // latencies overlap
+    RawSet<KIND> ring[kPhase];
+#pragma unroll
+    for (int d = 0; d < kPhase; ++d) fetch(ring[d], t_begin + d);
+
+    // ---- activation slice into registers (through LDS when several rows of
+    // a tile share it).  The two branches keep the source pointer's address
+    // space visible to the compiler (LDS reads stay ds_read, global reads stay
+    // global_load) instead of a generic pointer that would turn both into flat
+    // loads waiting on every outstanding memory operation.
+    XSlice<KIND> xs;
+    const int xb = lane_on ? b : 0;
+    if constexpr (KIND == kQ4KQ8) {
+        if (a.x_in_lds) {
+            for (int i = tid * 16; i < K; i += blockDim.x * 16)
+                *(u32x4 *)(smem + i) = *(const u32x4 *)(a.xq + i);
+            __syncthreads();
+            setup_x(xs.v, (const int8_t *)smem, a.xd, xb, part);
+        } else {
+            setup_x(xs.v, a.xq, a.xd, xb, part);
+        }
+    } else {
+        if (a.x_in_lds) {
+            // x and its K/16 sums of 16 consecutive values, computed once per workgroup
+            float *sx = (float *)smem;
+            float *ssum = sx + K;
+            for (int i = tid * 4; i < K; i += blockDim.x * 4)
+                *(float4 *)(sx + i) = *(const float4 *)(a.x + i);
+            __syncthreads();
+            for (int g = tid; g < K / 16; g += blockDim.x) ssum[g] = sum16(sx + 16 * g);
+            __syncthreads();
+            setup_x(xs.v, (const float *)sx, (const float *)ssum, xb, part);
+        } else {
+            setup_x(xs.v, a.x, (const float *)nullptr, xb, part);
+        }
+    }
+    __syncthreads();   // LDS is reused for row reductions below
+
+    float *red = (float *)smem;   // [2][OUTS][rows_tile][nb]
+    const int red_stride = OUTS * a.rows_tile * a.nb;
+    ArgBest best{0.f, kNoIndex};
+    int buf = 0;
+    // dot, row reduction and epilogue of tile t (workgroup-uniform control flow)
+    auto process = [&](const RawSet<KIND> &rs, int t) {
+        float ps[2];
+        dot_raw<KIND>(rs, xs, part, ps);
+        const bool v = valid_tile(t);
+#pragma unroll
+        for (int o = 0; o < OUTS; ++o) ps[o] = v ? ps[o] : 0.f;
+        if constexpr (WAVE_LOCAL) {
+            float r[2];
+#pragma unroll
+            for (int o = 0; o < OUTS; ++o) r[o] = group_sum(ps[o], a.lanes_row);
+            if (rr == 0 && v) emit_row<KIND, EPI>(a, (int64_t)t * a.rows_tile + p, r, best);
+        } else {
+            float *rb = red + buf * red_stride;
+#pragma unroll
+            for (int o = 0; o < OUTS; ++o) {
+                const float q = quad_sum(ps[o]);
+                if (part == 0 && lane_on) rb[(o * a.rows_tile + p) * a.nb + b] = q;
+            }
+            __syncthreads();
+            if (tid < a.rows_tile && t < t_end) {
+                const int64_t row = (int64_t)t * a.rows_tile + tid;
+                if (row < a.N) {
+                    float r[2];
+#pragma unroll
+                    for (int o = 0; o < OUTS; ++o) {
+                        // block sums added in column order; loads issued four at a time
+                        const float *src = rb + (o * a.rows_tile + tid) * a.nb;
+                        float acc = 0.f;
+                        int c = 0;
+                        for (; c + 4 <= a.nb; c += 4) {
+                            const float v0 = src[c], v1 = src[c + 1], v2 = src[c + 2], v3 = src[c + 3];
+                            acc = (((acc + v0) + v1) + v2) + v3;
+                        }
+                        for (; c < a.nb; ++c) acc += src[c];
+                        r[o] = acc;
+                    }
+                    emit_row<KIND, EPI>(a, row, r, best);
+                }
+            }
+            buf ^= 1;   // the next tile writes the other half; one barrier per tile suffices
+        }
+    };
+
+    // ring of kPhase tiles in flight per lane: tile t+kPhase is fetched right
+    // after tile t is consumed
+    for (int t = t_begin; t < t_end; t += kPhase) {
+#pragma unroll
+        for (int d = 0; d < kPhase; ++d) {
+            process(ring[d], t + d);
+            fetch(ring[d], t + d + kPhase);
+        }
+    }
+
+    if constexpr (EPI == kArgmax) argmax_finish(a, best);
+}
+
+// --------------------------------------------------------- Q8 quantize
+
+// One 32-lane half-wave per 32-element block: amax by a lane-max tree (exact,
+// order-free), d = amax/127 and q = round(x/d) in f32 with correctly rounded
+// division (the HIP default), q rounded half away from zero (roundf).
+__global__ __launch_bounds__(256) void q8_quantize_kernel(const float *__restrict__ x, int8_t *__restrict__ xq,
+                                                         uint16_t *__restrict__ xd, int K)
+{
+    const int gid = blockIdx.x * blockDim.x + threadIdx.x;
+    const bool on = gid < K;
+    const float v = on ? x[gid] : 0.f;
+    float amax = fabsf(v);
+#pragma unroll
+    for (int m = 1; m < 32; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 32));
+    const float d = amax / 127.0f;
+    int q = 0;
+    if (d != 0.0f) {
+        float r = roundf(v / d);
+        r = fminf(fmaxf(r, -127.0f), 127.0f);
+        q = (int)r;
+    }
+    if (on) {
+        xq[gid] = (int8_t)q;
+        if ((gid & 31) == 0) xd[gid >> 5] = __builtin_bit_cast(uint16_t, (_Float16)d);
+    }
+}
+
+// ---------------------------------------------------- Q4_K x Q8 isums hook
+
+// Integer sums of every (row, 32-block) with the same decode and dot code as
+// the Q8 GEMV (q4k_load + q4k_q8_isums); one thread per (row, block, part).
+__global__ __launch_bounds__(256) void q4k_q8_isums_kernel(const uint8_t *__restrict__ W, const int8_t *__restrict__ xq,
+                                                          int32_t *__restrict__ isums, int64_t N, int nb)
+{
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t total = N * nb * kParts;
+    if (gid >= total) return;
+    const int part = (int)(gid & 3);
+    const int64_t blk = gid >> 2;   // row * nb + b
+    const int b = (int)(blk % nb);
+    Q8X xs;
+    setup_x(xs, xq, nullptr, b, part);
+    Q4KRaw r;
+    q4k_load(r, W + blk * kQ4KBytes, 0u, part);
+    int32_t isl, ish;
+    q4k_q8_isums(r, xs, isl, ish);
+    isums[blk * 8 + 2 * part] = isl;
+    isums[blk * 8 + 2 * part + 1] = ish;
+}
+
+// ------------------------------------------------------------ launch plan
+
+Plan make_plan(int64_t N, int64_t K, int kind)
+{
+    Plan pl{};
+    pl.nb = (int)(K / kQK);
+    pl.lanes_row = kParts * pl.nb;
+    pl.wave_local = (pl.lanes_row <= 64 && (pl.lanes_row & (pl.lanes_row - 1)) == 0) ? 1 : 0;
+    if (pl.wave_local) {
+        pl.waves = 4;
+    } else {
+        // fewest idle lanes over 1..kMaxThreads/64 waves (ties: fewer waves), at least one row
+        int best_w = 0;
+        double best_u = -1.0;
+        for (int w = 1; w <= kMaxThreads / 64; ++w) {
+            const int rows = 64 * w / pl.lanes_row;
+            if (rows < 1) continue;
+            const double util = (double)(rows * pl.lanes_row) / (64.0 * w);
+            if (util > best_u + 1e-9) {
+                best_u = util;
+                best_w = w;
+            }
+        }
+        pl.waves = best_w;
+    }
+    pl.threads = 64 * pl.waves;
+    pl.rows_tile = pl.threads / pl.lanes_row;
+    pl.tiles = (N + pl.rows_tile - 1) / pl.rows_tile;
+    const int outs = (kind == kSwiglu) ? 2 : 1;
+    const size_t xbytes = (kind == kQ4KQ8) ? (size_t)K : (size_t)K * 4;
+    // Staging x through LDS pays when several rows of a tile read the same
+    // slice; with one row per tile every element has a single reader.
+    const size_t sums = (kind == kQ4KQ8) ? 0 : (size_t)(K / 16) * 4;
+    pl.x_in_lds = (pl.rows_tile > 1 && xbytes + sums <= 65536) ? 1 : 0;
+    const size_t red = pl.wave_local ? 0 : (size_t)2 * outs * pl.rows_tile * pl.nb * 4;
+    pl.lds_bytes = (pl.x_in_lds ? xbytes + sums : 0);
+    if (red > pl.lds_bytes) pl.lds_bytes = red;
+    pl.grid = 0;   // set by the launcher from the occupancy
+    return pl;
+}
+
+// Resident workgroups per CU of a kernel at a block size and LDS size,
+// cached (occupancy depends only on those and the compiled kernel).
+static int occupancy(const void *fn, int threads, size_t lds)
+{
+    struct Entry { const void *fn; int threads; size_t lds; int occ; };
+    static std::mutex mu;
+    static Entry cache[64];
+    static int n = 0;
+    {
+        std::lock_guard<std::mutex> g(mu);
+        for (int i = 0; i < n; ++i)
+            if (cache[i].fn == fn && cache[i].threads == threads && cache[i].lds == lds) return cache[i].occ;
+    }
+    int occ = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, threads, lds) != hipSuccess || occ < 1) occ = 1;
+    std::lock_guard<std::mutex> g(mu);
+    if (n < 64) cache[n++] = Entry{fn, threads, lds, occ};
+    return occ;
+}
+
+// One resident wave of workgroups (persistent grid), never more workgroups than tiles.
+static int grid_for(const Plan &pl, const void *fn, int cus, int64_t cap)
+{
+    int64_t g = (int64_t)cus * occupancy(fn, pl.threads, pl.lds_bytes);
+    if (g > pl.tiles) g = pl.tiles;
+    if (g > cap) g = cap;
+    if (g < 1) g = 1;
+    return (int)g;
+}
+
+static GemvArgs base_args(const Plan &pl, int64_t N)
+{
+    GemvArgs a{};
+    a.N = N;
+    a.tiles = (int)pl.tiles;
+    a.nb = pl.nb;
+    a.lanes_row = pl.lanes_row;
+    a.lanes_row_magic = (uint32_t)((((uint64_t)1 << 32) + (uint64_t)pl.lanes_row - 1) / (uint64_t)pl.lanes_row);
+    a.rows_tile = pl.rows_tile;
+    a.x_in_lds = pl.x_in_lds;
+    return a;
+}
+
+template <int KIND, int EPI, bool WL>
+static hipError_t launch_mode(Plan &pl, GemvArgs a, int cus, hipStream_t s, int64_t cap)
+{
+    const void *fn = (const void *)gemv_kernel<KIND, EPI, WL>;
+    pl.grid = grid_for(pl, fn, cus, cap);
+    a.tiles_q = (int)(pl.tiles / pl.grid);
+    a.tiles_r = (int)(pl.tiles % pl.grid);
+    hipLaunchKernelGGL((gemv_kernel<KIND, EPI, WL>), dim3(pl.grid), dim3(pl.threads), pl.lds_bytes, s, a);
+    return hipGetLastError();
+}
+
+template <int KIND, int EPI>
+static hipError_t launch(Plan &pl, const GemvArgs &a, int cus, hipStream_t s, int64_t cap = INT64_MAX)
+{
+    return pl.wave_local ? launch_mode<KIND, EPI, true>(pl, a, cus, s, cap)
+                         : launch_mode<KIND, EPI, false>(pl, a, cus, s, cap);
+}
+
+hipError_t launch_q4k_gemv(const void *W, const float *x, float *y, int64_t N, int64_t K, int cus, hipStream_t s)
+{
+    Plan pl = make_plan(N, K, kQ4K);
+    GemvArgs a = base_args(pl, N);
+    a.W = (const uint8_t *)W;
+    a.x = x;
+    a.y = y;
+    return launch<kQ4K, kStore>(pl, a, cus, s);
+}
+
+hipError_t launch_q6k_gemv(const void *W, const float *x, float *y, int64_t N, int64_t K, int cus, hipStream_t s)
+{
+    Plan pl = make_plan(N, K, kQ6K);
+    GemvArgs a = base_args(pl, N);
+    a.W = (const uint8_t *)W;
+    a.x = x;
+    a.y = y;
+    return launch<kQ6K, kStore>(pl, a, cus, s);
+}
+
+hipError_t launch_swiglu_gemv(const void *Wg, const void *Wu, const float *x, float *h, int64_t N, int64_t K, int cus,
+                              hipStream_t s)
+{
+    Plan pl = make_plan(N, K, kSwiglu);
+    GemvArgs a = base_args(pl, N);
+    a.W = (const uint8_t *)Wg;
+    a.W2 = (const uint8_t *)Wu;
+    a.x = x;
+    a.y = h;
+    return launch<kSwiglu, kStore>(pl, a, cus, s);
+}
+
+hipError_t launch_q4k_q8_gemv(const void *W, const int8_t *xq, const uint16_t *xd, float *y, int64_t N, int64_t K,
+                              int cus, hipStream_t s)
+{
+    Plan pl = make_plan(N, K, kQ4KQ8);
+    GemvArgs a = base_args(pl, N);
+    a.W = (const uint8_t *)W;
+    a.xq = xq;
+    a.xd = xd;
+    a.y = y;
+    return launch<kQ4KQ8, kStore>(pl, a, cus, s);
+}
+
+hipError_t launch_lm_head_argmax(const void *W, const float *x, uint32_t *out_idx, float *out_max, void *ws, int64_t N,
+                                 int64_t K, int cus, hipStream_t s)
+{
+    Plan pl = make_plan(N, K, kQ6K);
+    GemvArgs a = base_args(pl, N);
+    a.W = (const uint8_t *)W;
+    a.x = x;
+    a.ws = (uint8_t *)ws;
+    a.out_idx = out_idx;
+    a.out_max = out_max;
+    return launch<kQ6K, kArgmax>(pl, a, cus, s);
+}
+
+hipError_t launch_q8_quantize(const float *x, int8_t *xq, uint16_t *xd, int64_t K, hipStream_t s)
+{
+    const int threads = 256;
+    const int blocks = (int)((K + threads - 1) / threads);
+    hipLaunchKernelGGL(q8_quantize_kernel, dim3(blocks), dim3(threads), 0, s, x, xq, xd, (int)K);
+    return hipGetLastError();
+}
+
+hipError_t launch_q4k_q8_isums(const void *W, const int8_t *xq, int32_t *isums, int64_t N, int64_t K, hipStream_t s)
+{
+    const int nb = (int)(K / kQK);
+    const int64_t total = N * nb * kParts;
+    const int threads = 256;
+    const int64_t blocks = (total + threads - 1) / threads;
+    hipLaunchKernelGGL(q4k_q8_isums_kernel, dim3((unsigned)blocks), dim3(threads), 0, s, (const uint8_t *)W, xq, isums,
+                       N, nb);
+    return hipGetLastError();
+}
+
+}  // namespace gemvq

@@ -1,0 +1,48 @@
+// Internal interface between the C ABI (gemvq_abi.cpp) and the kernels
+// (gemvq_kernels.hip).  Launchers assume validated arguments.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gemvq {
+
+// Largest workgroup of the GEMV kernels (8 waves; lets a lane use up to 256
+// VGPRs) and hence the widest row: 512 lanes = 128 super-blocks, K <= 32768.
+constexpr int kMaxThreads = 512;
+constexpr int64_t kMaxK = 32768;
+
+// lm_head_argmax workspace: a 64-bit running best key and a 32-bit counter
+// (padded to 256 bytes).
+constexpr size_t kArgmaxWsBytes = 256;
+
+// Launch geometry of the GEMV kernel template (pure function of N, K, the
+// CU count and the kernel kind).
+struct Plan {
+    int nb;          // super-blocks per row
+    int lanes_row;   // lanes per row (4 per super-block)
+    int wave_local;  // rows reduce inside one wave
+    int waves;       // waves per workgroup
+    int threads;     // 64 * waves
+    int rows_tile;   // rows per tile
+    int64_t tiles;   // ceil(N / rows_tile)
+    int x_in_lds;    // activation staged through LDS
+    size_t lds_bytes;
+    int grid;        // workgroups (one resident wave; set at launch)
+};
+
+Plan make_plan(int64_t N, int64_t K, int kind);
+
+hipError_t launch_q4k_gemv(const void *W, const float *x, float *y, int64_t N, int64_t K, int cus, hipStream_t s);
+hipError_t launch_q6k_gemv(const void *W, const float *x, float *y, int64_t N, int64_t K, int cus, hipStream_t s);
+hipError_t launch_swiglu_gemv(const void *Wg, const void *Wu, const float *x, float *h, int64_t N, int64_t K, int cus,
+                              hipStream_t s);
+hipError_t launch_q4k_q8_gemv(const void *W, const int8_t *xq, const uint16_t *xd, float *y, int64_t N, int64_t K,
+                              int cus, hipStream_t s);
+hipError_t launch_lm_head_argmax(const void *W, const float *x, uint32_t *out_idx, float *out_max, void *ws, int64_t N,
+                                 int64_t K, int cus, hipStream_t s);
+hipError_t launch_q8_quantize(const float *x, int8_t *xq, uint16_t *xd, int64_t K, hipStream_t s);
+hipError_t launch_q4k_q8_isums(const void *W, const int8_t *xq, int32_t *isums, int64_t N, int64_t K, hipStream_t s);
+
+}  // namespace gemvq

@@ -1,0 +1,144 @@
+/*
+ * gemvq -- batch-1 quantized GEMV for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libgemvq.so.  Every entry point enqueues its kernels on the
+ * caller's HIP stream and returns without synchronising; stream order is the
+ * only dependency between calls (the aprender-serve page, forward_qwen35_cuda.rs,
+ * enqueues every projection GEMV on one stream with no host sync).  No call
+ * allocates device or host memory, reads device memory on the host or keeps
+ * state between calls (aprender PR #4332, "What changed": zero per-token host
+ * and device allocations, a 4-byte download per token).
+ *
+ * Shapes and layout.  N = rows = output length, K = columns = input length
+ * (the weight handle on the aprender-serve page, `CudaQuantWeight`, carries
+ * n = out_dim and k = in_dim).  K is a multiple of 256: each row is K/256
+ * super-blocks stored back to back, rows back to back (row n starts at byte
+ * n * (K/256) * block_bytes).  Block formats are GGUF Q4_K (144 bytes per
+ * 256 weights) and Q6_K (210 bytes per 256 weights); the Q8 activation is
+ * int8 values plus one fp16 scale per 32 values.
+ *
+ * Pointers.  Every pointer argument is a DEVICE pointer owned by the caller
+ * (the library never frees or keeps one).  `stream` is a hipStream_t passed as
+ * void* (NULL = the null stream).  fp16 values are passed as their uint16_t
+ * bit patterns.
+ *
+ * Errors.  Every argument check happens on the host BEFORE any HIP call, so a
+ * rejected call has no effect on the device.  A launch failure reported by
+ * the runtime after the launch returns GEMVQ_ERR_HIP.
+ *
+ * Limits.  1 <= N <= 2^31 - 1; 256 <= K <= 32768; N * (K/256) * block_bytes
+ * must fit in 63 bits.  Alignment: weights 16 B (Q4_K) or 4 B (Q6_K), float
+ * vectors 16 B (inputs) / 4 B (outputs), int8 Q8 vector 16 B, Q8 scales 4 B.
+ * Outputs may not overlap any input.
+ */
+#ifndef GEMVQ_H
+#define GEMVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define GEMVQ_OK            0
+#define GEMVQ_ERR_NULL      1  /* a required pointer is NULL */
+#define GEMVQ_ERR_SHAPE     2  /* N < 1, K < 256, K % 256 != 0, K > 32768, size overflow */
+#define GEMVQ_ERR_ALIGN     3  /* a pointer violates the alignment above */
+#define GEMVQ_ERR_WORKSPACE 4  /* workspace too small */
+#define GEMVQ_ERR_ALIAS     5  /* an output overlaps an input */
+#define GEMVQ_ERR_HIP       6  /* the HIP runtime reported an error at launch */
+
+/*
+ * y[n] = sum_k W[n,k] * x[k] over a Q4_K matrix, f32 activation, f32 result.
+ * The float (non-int8) GEMV: the aprender-serve page pins the float Q4_K/Q6_K
+ * variants (`pin_float_gemv`, "Q4kVariant::Mwv") as the correctness default.
+ *   W: N*(K/256)*144 bytes.  x: float[K].  y: float[N] (written).
+ */
+int q4k_gemv(const void *W, const float *x, float *y, int64_t N, int64_t K, void *stream);
+
+/*
+ * Same over a Q6_K matrix (210-byte blocks): the ffn_down projection and the
+ * unfused lm_head (aprender-serve forward_qwen35_cuda.rs, the lm_head
+ * `gemv_dispatch` at the end of `forward_single`).
+ *   W: N*(K/256)*210 bytes.  x: float[K].  y: float[N].
+ * Row results are bit-identical to the row values lm_head_argmax compares.
+ */
+int q6k_gemv(const void *W, const float *x, float *y, int64_t N, int64_t K, void *stream);
+
+/*
+ * Quantize an f32 activation to Q8 (memra-engine decode.rs, `quantize_q8_1`
+ * and the "amax/127" rounding named in `ffn_swiglu_decode`): per 32-element
+ * block, d = max|x|/127 in f32 (correctly rounded), q = round-half-away-from-
+ * zero(x/d) with an f32 division, scale stored as fp16 (round to nearest
+ * even); a block of zeros gives d = 0 and q = 0.  x must be finite.
+ *   x: float[K] (K % 32 == 0, 32 <= K <= 65536).  xq: int8[K].  xd: uint16[K/32].
+ */
+int q8_quantize(const float *x, int8_t *xq, uint16_t *xd, int64_t K, void *stream);
+
+/*
+ * Q4_K x Q8 integer-dot GEMV: the approximate fast variant that quantizes the
+ * activation first (aprender-serve `pin_reference_gemv` doc comment: the int8
+ * activation path is an intentional approximation; memra-engine `matmul_pre`
+ * on a pre-quantized activation).  Per 32-block j of row n the integer sum
+ * isum = sum q4*q8 is exact; y[n] = sum_j d8_j*(d*sc_j*isum_j - dmin*m_j*sum q8).
+ *   W: Q4_K N x K.  xq, xd: the output of q8_quantize for the same K.  y: float[N].
+ */
+int q4k_q8_gemv(const void *W, const int8_t *xq, const uint16_t *xd, float *y,
+                int64_t N, int64_t K, void *stream);
+
+/*
+ * Fused gate/up SwiGLU GEMV: h[n] = silu(g[n]) * u[n], g = Wg x, u = Wu x,
+ * silu(z) = z / (1 + e^-z), both matrices read in one pass that shares x
+ * (memra-engine decode.rs `ffn_swiglu_decode`: down @ (silu(gate@z) * (up@z));
+ * qualiaDB resident_decode.rs: the fused FFN pass needs gate and up of the
+ * same type and dims).  Follow with q6k_gemv(Wd, h) for the down projection.
+ *   Wg, Wu: Q4_K N x K.  x: float[K].  h: float[N].
+ */
+int swiglu_gemv(const void *Wg, const void *Wu, const float *x, float *h,
+                int64_t N, int64_t K, void *stream);
+
+/*
+ * lm_head GEMV over Q6_K rows with an on-device argmax: writes the FIRST index
+ * of the maximum row value (NaN rows never win; -0 == +0; all-NaN gives 0) to
+ * out_idx[0] and, if out_max is not NULL, that value to out_max[0].  No logits
+ * are written anywhere; the caller downloads 4 bytes (aprender PR #4332: the
+ * tie fix keeps the first index of an exact maximum, and the download drops
+ * from 248,320 f32 logits to a 4-byte token id; memra-engine decode.rs
+ * `argmax_token_device_into`: the id stays in a persistent device word).
+ * Two stages in one kernel: every workgroup reduces its rows to one (value,
+ * index) candidate, folds it into a 64-bit atomic maximum of an order-keeping
+ * key, and the last workgroup to finish writes the result (memra-engine
+ * decode.rs names the same split, `argmax_partial_f32` + `argmax_final_f32`;
+ * qualiaDB's top-1 per block and candidate merge).
+ *   W: Q6_K N x K.  x: float[K].  out_idx: uint32[1].  out_max: float[1] or NULL.
+ *   workspace: device memory of at least gemvq_lm_head_argmax_ws_bytes(N, K)
+ *   (256) bytes, 256-B aligned.  Its first 12 bytes must be zero before the
+ *   first call; every call leaves them zero again, so one workspace serves
+ *   any number of calls in stream order (also inside a captured graph).
+ *   Calls that share a workspace must not run concurrently.
+ */
+int lm_head_argmax(const void *W, const float *x, uint32_t *out_idx, float *out_max,
+                   void *workspace, size_t ws_bytes, int64_t N, int64_t K, void *stream);
+
+/* Workspace bytes lm_head_argmax needs for an N x K call (host-only, no HIP call). */
+size_t gemvq_lm_head_argmax_ws_bytes(int64_t N, int64_t K);
+
+/*
+ * Test hook for the exactness of the int8 path: writes the integer sums
+ * isums[n][j] = sum_{i<32} q4[n][32j+i] * xq[32j+i] computed by the same
+ * device decode and dot code as q4k_q8_gemv (before any scaling).
+ *   isums: int32[N][K/32].
+ */
+int gemvq_q4k_q8_isums(const void *W, const int8_t *xq, int32_t *isums,
+                       int64_t N, int64_t K, void *stream);
+
+/* Static description of a status code (never NULL). */
+const char *gemvq_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMVQ_H */

@@ -1,0 +1,142 @@
+"""The C-ABI library on the host, with no GPU: it loads, exports every
+function include/gemvq.h declares, and rejects bad arguments with the
+documented status before any HIP call.
+
+Pointers here are fake integers; every call below is built to be rejected by
+the host-side checks, so nothing is ever dereferenced or launched."""
+import glob
+import os
+
+import pytest
+
+import gemv_q4k_q6k_amd as gq
+
+
+def _gpu_visible() -> bool:
+    try:
+        import torch
+        return torch.cuda.device_count() > 0     # counts devices without initialising HIP
+    except Exception:
+        return False
+
+
+# Fake pointers must never reach a launch: run these only where no GPU exists.
+pytestmark = pytest.mark.skipif(_gpu_visible(), reason="fake-pointer validation tests run on GPU-less hosts only")
+
+
+def test_library_is_fresh():
+    """The built library is newer than every source it is built from."""
+    srcs = glob.glob(os.path.join(os.path.dirname(gq.LIB_PATH), "csrc", "*")) + [gq.HEADER_PATH]
+    assert os.path.exists(gq.LIB_PATH), "build with python -m gemv_q4k_q6k_amd.build"
+    lib_t = os.path.getmtime(gq.LIB_PATH)
+    stale = [s for s in srcs if os.path.getmtime(s) > lib_t]
+    assert not stale, f"libgemvq.so is older than {stale}; rebuild"
+
+A = 1 << 20          # fake, 256-byte aligned "device" addresses far apart
+B = 1 << 30
+C = 1 << 34
+D = 1 << 38
+E = 1 << 42
+
+
+def _rejected(code, expected):
+    assert expected != gq.OK       # never let a test case reach a launch
+    assert code == expected, (code, gq.strerror(code))
+
+
+def test_library_loads_and_exports_header_symbols():
+    L = gq.lib()
+    names = gq.header_names()
+    assert set(names) == set(gq.exported_names())
+    for n in names:
+        assert hasattr(L, n), n
+    for n in ("q4k_gemv", "q6k_gemv", "q8_quantize", "q4k_q8_gemv", "swiglu_gemv", "lm_head_argmax"):
+        assert n in names
+
+
+def test_strerror_and_ws_bytes():
+    for s in range(7):
+        assert isinstance(gq.strerror(s), str) and gq.strerror(s)
+    assert gq.strerror(99) == "unknown status"
+    ws = gq.lm_head_argmax_ws_bytes(248_320, 1024)
+    assert ws >= 12 and ws % 8 == 0
+
+
+def test_null_pointers():
+    L = gq.lib()
+    _rejected(L.q4k_gemv(None, B, C, 4, 256, None), gq.ERR_NULL)
+    _rejected(L.q4k_gemv(A, None, C, 4, 256, None), gq.ERR_NULL)
+    _rejected(L.q4k_gemv(A, B, None, 4, 256, None), gq.ERR_NULL)
+    _rejected(L.q6k_gemv(A, B, None, 4, 256, None), gq.ERR_NULL)
+    _rejected(L.q8_quantize(A, None, C, 256, None), gq.ERR_NULL)
+    _rejected(L.q4k_q8_gemv(A, B, None, D, 4, 256, None), gq.ERR_NULL)
+    _rejected(L.swiglu_gemv(A, None, C, D, 4, 256, None), gq.ERR_NULL)
+    _rejected(L.lm_head_argmax(A, B, C, None, None, 1 << 20, 4, 256, None), gq.ERR_NULL)
+    _rejected(L.gemvq_q4k_q8_isums(A, B, None, 4, 256, None), gq.ERR_NULL)
+
+
+@pytest.mark.parametrize("N,K", [(0, 256), (-1, 256), (4, 0), (4, 255), (4, 300), (4, 128),
+                                 (4, 32768 + 256), (1 << 31, 256), (1 << 40, 32768)])
+def test_bad_shapes(N, K):
+    L = gq.lib()
+    _rejected(L.q4k_gemv(A, B, C, N, K, None), gq.ERR_SHAPE)
+    _rejected(L.q6k_gemv(A, B, C, N, K, None), gq.ERR_SHAPE)
+    _rejected(L.q4k_q8_gemv(A, B, C, D, N, K, None), gq.ERR_SHAPE)
+    _rejected(L.swiglu_gemv(A, B, C, D, N, K, None), gq.ERR_SHAPE)
+    _rejected(L.lm_head_argmax(A, B, C, D, E, 1 << 20, N, K, None), gq.ERR_SHAPE)
+    _rejected(L.gemvq_q4k_q8_isums(A, B, C, N, K, None), gq.ERR_SHAPE)
+
+
+def test_q8_bad_shapes():
+    L = gq.lib()
+    for K in (0, 16, 31, 33, 65536 + 32):
+        _rejected(L.q8_quantize(A, B, C, K, None), gq.ERR_SHAPE)
+
+
+def test_alignment():
+    L = gq.lib()
+    _rejected(L.q4k_gemv(A + 4, B, C, 4, 256, None), gq.ERR_ALIGN)      # Q4_K weights need 16 B
+    _rejected(L.q4k_gemv(A, B + 4, C, 4, 256, None), gq.ERR_ALIGN)      # x needs 16 B
+    _rejected(L.q4k_gemv(A, B, C + 2, 4, 256, None), gq.ERR_ALIGN)      # y needs 4 B
+    _rejected(L.q6k_gemv(A + 2, B, C, 4, 256, None), gq.ERR_ALIGN)      # Q6_K weights need 4 B
+    _rejected(L.q8_quantize(A, B + 8, C, 256, None), gq.ERR_ALIGN)
+    _rejected(L.q8_quantize(A, B, C + 2, 256, None), gq.ERR_ALIGN)
+    _rejected(L.q4k_q8_gemv(A, B + 1, C, D, 4, 256, None), gq.ERR_ALIGN)
+    _rejected(L.swiglu_gemv(A, B + 8, C, D, 4, 256, None), gq.ERR_ALIGN)
+    _rejected(L.lm_head_argmax(A, B, C, D, E + 16, 1 << 20, 4, 256, None), gq.ERR_ALIGN)   # workspace 256 B
+    _rejected(L.lm_head_argmax(A, B, C + 1, D, E, 1 << 20, 4, 256, None), gq.ERR_ALIGN)
+    _rejected(L.gemvq_q4k_q8_isums(A, B, C + 2, 4, 256, None), gq.ERR_ALIGN)
+
+
+def test_workspace_too_small():
+    L = gq.lib()
+    need = gq.lm_head_argmax_ws_bytes(4, 256)
+    _rejected(L.lm_head_argmax(A, B, C, D, E, need - 1, 4, 256, None), gq.ERR_WORKSPACE)
+    _rejected(L.lm_head_argmax(A, B, C, None, E, 0, 4, 256, None), gq.ERR_WORKSPACE)
+
+
+def test_aliasing():
+    L = gq.lib()
+    N, K = 64, 512
+    wbytes = N * (K // 256) * 144
+    _rejected(L.q4k_gemv(A, B, A + 64, N, K, None), gq.ERR_ALIAS)               # y inside W
+    _rejected(L.q4k_gemv(A, B, B + 4 * (K - 1), N, K, None), gq.ERR_ALIAS)      # y overlaps the end of x
+    _rejected(L.q4k_gemv(A, B, A + wbytes - 4, N, K, None), gq.ERR_ALIAS)
+    _rejected(L.q6k_gemv(A, B, B, N, K, None), gq.ERR_ALIAS)
+    _rejected(L.swiglu_gemv(A, C, B, C + 16, N, K, None), gq.ERR_ALIAS)         # h inside Wu
+    _rejected(L.q8_quantize(A, A + 16, C, K, None), gq.ERR_ALIAS)               # xq inside x
+    _rejected(L.q8_quantize(A, B, B + 16, K, None), gq.ERR_ALIAS)               # xd inside xq
+    _rejected(L.q4k_q8_gemv(A, B, C, C, N, K, None), gq.ERR_ALIAS)              # y over xd
+    ws = gq.lm_head_argmax_ws_bytes(N, K)
+    _rejected(L.lm_head_argmax(A, B, E + 8, None, E, ws, N, K, None), gq.ERR_ALIAS)   # idx inside ws
+    _rejected(L.lm_head_argmax(A, B, C, C, E, ws, N, K, None), gq.ERR_ALIAS)          # max == idx
+    _rejected(L.lm_head_argmax(A, B, C, None, A + 256, ws, N, K, None), gq.ERR_ALIAS)  # ws inside W
+    _rejected(L.gemvq_q4k_q8_isums(A, B, B, N, K, None), gq.ERR_ALIAS)
+
+
+def test_binding_rejects_host_tensors():
+    torch = pytest.importorskip("torch")
+    W = torch.zeros(144, dtype=torch.uint8)
+    x = torch.zeros(256, dtype=torch.float32)
+    with pytest.raises(ValueError):
+        gq.q4k_gemv(W, x, 1, 256)
