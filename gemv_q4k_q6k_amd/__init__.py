@@ -20,7 +20,7 @@ import threading
 __all__ = [
     "GemvqError", "lib", "exported_names", "header_names",
     "q4k_gemv", "q6k_gemv", "q8_quantize", "q4k_q8_gemv", "swiglu_gemv",
-    "lm_head_argmax", "lm_head_argmax_ws_bytes", "q4k_q8_isums", "strerror",
+    "lm_head_argmax", "lm_head_argmax_ws_bytes", "q4k_q8_isums", "strerror", "tile_geometry",
     "Q4K_BLOCK_BYTES", "Q6K_BLOCK_BYTES", "LIB_PATH", "HEADER_PATH",
 ]
 
@@ -55,6 +55,7 @@ _SIGS = {
     "gemvq_lm_head_argmax_ws_bytes": (ctypes.c_size_t, [_I64, _I64]),
     "gemvq_q4k_q8_isums": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P]),
     "gemvq_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+    "gemvq_tile_geometry": (ctypes.c_int, [ctypes.c_int, _I64, _I64, _P]),
 }
 
 
@@ -85,6 +86,17 @@ def header_names() -> list[str]:
 
 def exported_names() -> list[str]:
     return sorted(_SIGS)
+
+
+KIND_Q4K, KIND_Q6K, KIND_Q4K_Q8, KIND_SWIGLU = range(4)
+
+
+def tile_geometry(kind: int, N: int, K: int) -> dict:
+    """Launch geometry the library uses for an N x K matrix (host-only)."""
+    out = (ctypes.c_int64 * 6)()
+    _check("gemvq_tile_geometry", lib().gemvq_tile_geometry(kind, N, K, ctypes.cast(out, ctypes.c_void_p)))
+    return {"waves": out[0], "rows_tile": out[1], "tiles": out[2], "wave_local": out[3],
+            "x_in_lds": out[4], "lds_bytes": out[5]}
 
 
 def strerror(status: int) -> str:

@@ -86,6 +86,22 @@ size_t gemvq_lm_head_argmax_ws_bytes(int64_t N, int64_t K)
     return gemvq::kArgmaxWsBytes;
 }
 
+int gemvq_tile_geometry(int kind, int64_t N, int64_t K, int64_t out[6])
+{
+    if (!out) return GEMVQ_ERR_NULL;
+    if (kind < 0 || kind > 3) return GEMVQ_ERR_SHAPE;
+    size_t wb = 0;
+    if (int st = check_shape(N, K, kind == 1 ? 210 : 144, &wb)) return st;
+    const gemvq::Plan pl = gemvq::make_plan(N, K, kind);
+    out[0] = pl.waves;
+    out[1] = pl.rows_tile;
+    out[2] = pl.tiles;
+    out[3] = pl.wave_local;
+    out[4] = pl.x_in_lds;
+    out[5] = (int64_t)pl.lds_bytes;
+    return GEMVQ_OK;
+}
+
 int q4k_gemv(const void *W, const float *x, float *y, int64_t N, int64_t K, void *stream)
 {
     if (!W || !x || !y) return GEMVQ_ERR_NULL;

@@ -275,21 +275,29 @@ __device__ __forceinline__ void load5(uint32_t (&o)[5], const uint32_t *p)
 }
 
 // `tile` is workgroup-uniform, `off` the lane's byte offset of its block in
-// the tile (pointer arithmetic only: an integer round trip would lose the
-// global address space and turn every load into a flat load).
+// the tile.  Offsets are taken from the tile start rounded down to a dword
+// (`base`, still uniform), so the dword-aligned block start `al` is never
+// negative: a block that begins 2 bytes past a dword boundary at the very
+// start of a tile reads from the 2 bytes before it (the previous block of the
+// same matrix; the first block of the matrix is dword-aligned).  Pointer
+// arithmetic only: an integer round trip would lose the global address space
+// and turn every load into a flat load.
 __device__ __forceinline__ void q6k_load(Q6KRaw &r, const uint8_t *__restrict__ tile, uint32_t off, int u)
 {
-    const uint32_t sh = ((uint32_t)(uintptr_t)tile + off) & 3u;
-    const uint32_t al = off - sh;                               // dword-aligned block start
+    const uint32_t lead = (uint32_t)(uintptr_t)tile & 3u;      // uniform
+    const uint8_t *base = tile - lead;                          // dword-aligned, uniform
+    const uint32_t o = off + lead;                              // block start relative to base
+    const uint32_t sh = o & 3u;                                 // block misalignment (0 or 2)
+    const uint32_t al = o - sh;                                 // o rounded down to a dword: never below base
     const uint32_t n = (uint32_t)(u >> 1), l0 = 16u * (uint32_t)(u & 1);
-    load5(r.a, (const uint32_t *)(tile + (al + 64u * n + l0)));
-    load5(r.b, (const uint32_t *)(tile + (al + 64u * n + 32u + l0)));
-    load5(r.h, (const uint32_t *)(tile + (al + 128u + 32u * n + l0)));
-    const uint32_t *sp = (const uint32_t *)(tile + (al + 192u + 8u * n));
+    load5(r.a, (const uint32_t *)(base + (al + 64u * n + l0)));
+    load5(r.b, (const uint32_t *)(base + (al + 64u * n + 32u + l0)));
+    load5(r.h, (const uint32_t *)(base + (al + 128u + 32u * n + l0)));
+    const uint32_t *sp = (const uint32_t *)(base + (al + 192u + 8u * n));
     r.s[0] = sp[0];
     r.s[1] = sp[1];
     r.s[2] = sp[sh ? 2 : 1];   // the third dword is needed (and in bounds) only when misaligned
-    r.dbits = *(const uint16_t *)(tile + (off + 208u));
+    r.dbits = *(const uint16_t *)(base + (o + 208u));
     r.shift = sh;
 }
 

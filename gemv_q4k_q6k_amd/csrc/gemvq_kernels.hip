@@ -23,7 +23,6 @@ namespace gemvq {
 enum Kind : int { kQ4K = 0, kQ6K = 1, kQ4KQ8 = 2, kSwiglu = 3 };
 enum Epi : int { kStore = 0, kArgmax = 1 };
 
-constexpr int kPhase = 2;   // tiles in flight per lane (software pipeline depth)
 
 struct GemvArgs {
     const uint8_t *W;      // matrix (gate matrix for SwiGLU)
@@ -81,8 +80,7 @@ __device__ __forceinline__ float sum16(const float *v)
 }
 
 // Q4_K part c of block b: xl = x[256b + 64c + i], xh = x[256b + 64c + 32 + i].
-// `sums` (16-element sums of x, or nullptr to add the slice here).
-__device__ __forceinline__ void setup_x(Q4KX &xs, const float *xsrc, const float *sums, int b, int c)
+__device__ __forceinline__ void load_x(Q4KX &xs, const float *xsrc, int b, int c)
 {
     const float *p = xsrc + kQK * b + 64 * c;
 #pragma unroll
@@ -90,6 +88,12 @@ __device__ __forceinline__ void setup_x(Q4KX &xs, const float *xsrc, const float
         load_x_f32(xs.xl + i, p + i, 16);
         load_x_f32(xs.xh + i, p + 32 + i, 16);
     }
+}
+
+// The slice's two 32-element sums: from `sums` (16-element sums of x held in
+// LDS) or, when it is null, added here from the slice.
+__device__ __forceinline__ void finish_x(Q4KX &xs, const float *sums, int b, int c)
+{
     float sl, sh;
     if (sums) {
         const float *q = sums + 16 * b + 4 * c;
@@ -106,13 +110,19 @@ __device__ __forceinline__ void setup_x(Q4KX &xs, const float *xsrc, const float
 }
 
 // Q6_K part u of block b: xs[s][i] = x[256b + 128n + 32s + l0 + i].
-__device__ __forceinline__ void setup_x(Q6KX &xs, const float *xsrc, const float *sums, int b, int u)
+__device__ __forceinline__ void load_x(Q6KX &xs, const float *xsrc, int b, int u)
 {
     const int n = u >> 1, l0 = 16 * (u & 1);
     const float *p = xsrc + kQK * b + 128 * n + l0;
 #pragma unroll
+    for (int s = 0; s < 4; ++s) load_x_f32(xs.xs[s], p + 32 * s, 16);
+}
+
+__device__ __forceinline__ void finish_x(Q6KX &xs, const float *sums, int b, int u)
+{
+    const int n = u >> 1;
+#pragma unroll
     for (int s = 0; s < 4; ++s) {
-        load_x_f32(xs.xs[s], p + 32 * s, 16);
         float t = sums ? sums[16 * b + 8 * n + 2 * s + (u & 1)] : sum16(xs.xs[s]);
         pin(t);
         xs.sx[s] = t;
@@ -120,7 +130,7 @@ __device__ __forceinline__ void setup_x(Q6KX &xs, const float *xsrc, const float
 }
 
 // Q8 part c of block b: 32 int8 of sub-blocks 8b+2c and 8b+2c+1, their scales.
-__device__ __forceinline__ void setup_x(Q8X &xs, const int8_t *qsrc, const uint16_t *dsrc, int b, int c)
+__device__ __forceinline__ void load_x(Q8X &xs, const int8_t *qsrc, const uint16_t *dsrc, int b, int c)
 {
     const uint32_t *p = (const uint32_t *)(qsrc + kQK * b + 64 * c);
 #pragma unroll
@@ -128,6 +138,17 @@ __device__ __forceinline__ void setup_x(Q8X &xs, const int8_t *qsrc, const uint1
         xs.ql[k] = p[k];
         xs.qh[k] = p[8 + k];
     }
+    xs.dl = xs.dh = 0.f;
+    if (dsrc) {
+        const int j = 8 * b + 2 * c;
+        xs.dl = (float)__builtin_bit_cast(_Float16, dsrc[j]);
+        xs.dh = (float)__builtin_bit_cast(_Float16, dsrc[j + 1]);
+    }
+}
+
+// Integer sums of the slice's two Q8 blocks.
+__device__ __forceinline__ void finish_x(Q8X &xs)
+{
     int32_t sl = 0, sh = 0;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -138,12 +159,6 @@ __device__ __forceinline__ void setup_x(Q8X &xs, const int8_t *qsrc, const uint1
     pin(sh);
     xs.sl = sl;
     xs.sh = sh;
-    xs.dl = xs.dh = 0.f;
-    if (dsrc) {
-        const int j = 8 * b + 2 * c;
-        xs.dl = (float)__builtin_bit_cast(_Float16, dsrc[j]);
-        xs.dh = (float)__builtin_bit_cast(_Float16, dsrc[j + 1]);
-    }
 }
 
 // ------------------------------------------------------- per-kind traits
@@ -290,9 +305,14 @@ __device__ void argmax_finish(const GemvArgs &a, ArgBest best)
 // one wave (K/256 in {1,2,4,8,16}), so rows reduce with DPP only; otherwise
 // each super-block's quad sum goes through LDS and one thread per row adds the
 // K/256 block sums in order.
-template <int KIND, int EPI, bool WAVE_LOCAL>
+// PHASE: tiles in flight per lane (software pipeline depth); 1 for grids in
+// which workgroups own a single tile.  XLDS: the activation (and its
+// 16-element sums) is staged through LDS because several rows of a tile
+// share it; otherwise each lane reads its own slice.
+template <int KIND, int EPI, bool WAVE_LOCAL, int PHASE, bool XLDS>
 __global__ __launch_bounds__(kMaxThreads) void gemv_kernel(GemvArgs a)
 {
+    constexpr int kPhase = PHASE;
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int BYTES = Traits<KIND>::kBytes;
     constexpr int OUTS = Traits<KIND>::kOuts;
@@ -315,23 +335,47 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_kernel(GemvArgs a)
     auto valid_tile = [&](int t) {
         return lane_on && t < t_end && (t < a.tiles - 1 || p < last_rows);
     };
-    // Loads are unconditional so the loop stays branch-free around them: a
-    // tile past this workgroup's range is replaced by its first tile, a lane
-    // with nothing to do reads the first super-block of that tile (always in
-    // bounds), and the partial sums of both are discarded.
+    // Loads are unconditional so no branch surrounds them (a branch, even a
+    // uniform one, makes the compiler drain every outstanding load at the loop
+    // head): a tile past this workgroup's range re-reads its last tile (an L2
+    // hit), a lane with nothing to do reads the first super-block of the tile
+    // (always in bounds), and the partial sums of both are discarded.
     auto fetch = [&](RawSet<KIND> &rs, int t) {
-        const int64_t tt = t < t_end ? t : t_begin;
+        const int tt = t < t_end ? t : t_end - 1;
         const uint32_t off = valid_tile(t) ? lane_off : 0u;
+        const int64_t tb = (int64_t)tt * tile_stride;
         if constexpr (KIND == kQ6K) {
-            q6k_load(rs.r[0], a.W + tt * tile_stride, off, part);
+            q6k_load(rs.r[0], a.W + tb, off, part);
         } else {
-            q4k_load(rs.r[0], a.W + tt * tile_stride, off, part);
-            if constexpr (KIND == kSwiglu) q4k_load(rs.r[1], a.W2 + tt * tile_stride, off, part);
+            q4k_load(rs.r[0], a.W + tb, off, part);
+            if constexpr (KIND == kSwiglu) q4k_load(rs.r[1], a.W2 + tb, off, part);
         }
     };
 
-    // first tiles in flight before the activation set-up, so the two
-    // latencies overlap
+    // The activation's global loads go first, then the first weight tiles:
+    // vector-memory counters retire in issue order, so staging x waits only
+    // for x while the weight tiles stay in flight behind it.
+    constexpr int kXRegs = 8;   // float4 (or 16 int8) staged per thread through registers
+    u32x4 xr[kXRegs];
+    if constexpr (XLDS) {
+        const int step = KIND == kQ4KQ8 ? 16 : 4;   // elements per 16-byte load
+        const uint8_t *src = KIND == kQ4KQ8 ? (const uint8_t *)a.xq : (const uint8_t *)a.x;
+        const int esz = KIND == kQ4KQ8 ? 1 : 4;
+#pragma unroll
+        for (int r = 0; r < kXRegs; ++r) {
+            const int i = (tid + r * (int)blockDim.x) * step;
+            if (i < K) xr[r] = *(const u32x4 *)(src + (size_t)i * esz);
+        }
+    }
+    XSlice<KIND> xs;
+    const int xb = lane_on ? b : 0;
+    if constexpr (!XLDS) {
+        // each lane reads its own slice (no other lane of the tile shares it)
+        if constexpr (KIND == kQ4KQ8)
+            load_x(xs.v, a.xq, a.xd, xb, part);
+        else
+            load_x(xs.v, a.x, xb, part);
+    }
     RawSet<KIND> ring[kPhase];
 #pragma unroll
     for (int d = 0; d < kPhase; ++d) fetch(ring[d], t_begin + d);
@@ -341,30 +385,34 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_kernel(GemvArgs a)
     // space visible to the compiler (LDS reads stay ds_read, global reads stay
     // global_load) instead of a generic pointer that would turn both into flat
     // loads waiting on every outstanding memory operation.
-    XSlice<KIND> xs;
-    const int xb = lane_on ? b : 0;
-    if constexpr (KIND == kQ4KQ8) {
-        if (a.x_in_lds) {
-            for (int i = tid * 16; i < K; i += blockDim.x * 16)
-                *(u32x4 *)(smem + i) = *(const u32x4 *)(a.xq + i);
-            __syncthreads();
-            setup_x(xs.v, (const int8_t *)smem, a.xd, xb, part);
-        } else {
-            setup_x(xs.v, a.xq, a.xd, xb, part);
+    if constexpr (XLDS) {
+        // registers staged above, then any remainder straight through
+        const int step = KIND == kQ4KQ8 ? 16 : 4;
+        const uint8_t *src = KIND == kQ4KQ8 ? (const uint8_t *)a.xq : (const uint8_t *)a.x;
+        const int esz = KIND == kQ4KQ8 ? 1 : 4;
+#pragma unroll
+        for (int r = 0; r < kXRegs; ++r) {
+            const int i = (tid + r * (int)blockDim.x) * step;
+            if (i < K) *(u32x4 *)(smem + (size_t)i * esz) = xr[r];
         }
+        for (int i = (tid + kXRegs * (int)blockDim.x) * step; i < K; i += (int)blockDim.x * step)
+            *(u32x4 *)(smem + (size_t)i * esz) = *(const u32x4 *)(src + (size_t)i * esz);
+        __syncthreads();
+    }
+    if constexpr (KIND == kQ4KQ8) {
+        if constexpr (XLDS) load_x(xs.v, (const int8_t *)smem, a.xd, xb, part);
+        finish_x(xs.v);
     } else {
-        if (a.x_in_lds) {
-            // x and its K/16 sums of 16 consecutive values, computed once per workgroup
-            float *sx = (float *)smem;
-            float *ssum = sx + K;
-            for (int i = tid * 4; i < K; i += blockDim.x * 4)
-                *(float4 *)(sx + i) = *(const float4 *)(a.x + i);
-            __syncthreads();
+        if constexpr (XLDS) {
+            // K/16 sums of 16 consecutive activation values, once per workgroup
+            const float *sx = (const float *)smem;
+            float *ssum = (float *)smem + K;
             for (int g = tid; g < K / 16; g += blockDim.x) ssum[g] = sum16(sx + 16 * g);
             __syncthreads();
-            setup_x(xs.v, (const float *)sx, (const float *)ssum, xb, part);
+            load_x(xs.v, sx, xb, part);
+            finish_x(xs.v, (const float *)ssum, xb, part);
         } else {
-            setup_x(xs.v, a.x, (const float *)nullptr, xb, part);
+            finish_x(xs.v, (const float *)nullptr, xb, part);
         }
     }
     __syncthreads();   // LDS is reused for row reductions below
@@ -422,8 +470,10 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_kernel(GemvArgs a)
     for (int t = t_begin; t < t_end; t += kPhase) {
 #pragma unroll
         for (int d = 0; d < kPhase; ++d) {
-            process(ring[d], t + d);
-            fetch(ring[d], t + d + kPhase);
+            if (t + d < t_end) {   // workgroup-uniform
+                process(ring[d], t + d);
+                fetch(ring[d], t + d + kPhase);
+            }
         }
     }
 
@@ -471,7 +521,8 @@ __global__ __launch_bounds__(256) void q4k_q8_isums_kernel(const uint8_t *__rest
     const int64_t blk = gid >> 2;   // row * nb + b
     const int b = (int)(blk % nb);
     Q8X xs;
-    setup_x(xs, xq, nullptr, b, part);
+    load_x(xs, xq, nullptr, b, part);
+    finish_x(xs);
     Q4KRaw r;
     q4k_load(r, W + blk * kQ4KBytes, 0u, part);
     int32_t isl, ish;
@@ -491,10 +542,12 @@ Plan make_plan(int64_t N, int64_t K, int kind)
     if (pl.wave_local) {
         pl.waves = 4;
     } else {
-        // fewest idle lanes over 1..kMaxThreads/64 waves (ties: fewer waves), at least one row
+        // 1, 2, 4 or 8 waves (a workgroup of another size leaves SIMDs unevenly
+        // loaded and fewer workgroups fit on a CU); fewest idle lanes, ties to
+        // fewer waves; at least one row per tile
         int best_w = 0;
         double best_u = -1.0;
-        for (int w = 1; w <= kMaxThreads / 64; ++w) {
+        for (int w = 1; w <= kMaxThreads / 64; w *= 2) {
             const int rows = 64 * w / pl.lanes_row;
             if (rows < 1) continue;
             const double util = (double)(rows * pl.lanes_row) / (64.0 * w);
@@ -514,7 +567,7 @@ Plan make_plan(int64_t N, int64_t K, int kind)
     // slice; with one row per tile every element has a single reader.
     const size_t sums = (kind == kQ4KQ8) ? 0 : (size_t)(K / 16) * 4;
     pl.x_in_lds = (pl.rows_tile > 1 && xbytes + sums <= 65536) ? 1 : 0;
-    const size_t red = pl.wave_local ? 0 : (size_t)2 * outs * pl.rows_tile * pl.nb * 4;
+    const size_t red = pl.wave_local ? 0 : (size_t)2 * outs * pl.rows_tile * pl.nb * 4;   // two buffers
     pl.lds_bytes = (pl.x_in_lds ? xbytes + sums : 0);
     if (red > pl.lds_bytes) pl.lds_bytes = red;
     pl.grid = 0;   // set by the launcher from the occupancy
@@ -541,11 +594,15 @@ static int occupancy(const void *fn, int threads, size_t lds)
     return occ;
 }
 
-// One resident wave of workgroups (persistent grid), never more workgroups than tiles.
-static int grid_for(const Plan &pl, const void *fn, int cus, int64_t cap)
+// At most one resident wave of workgroups (persistent grid), and at least
+// `min_tiles` tiles per workgroup: a workgroup's start-up (activation staging,
+// first-tile latency) costs several tile times, so short grids run faster
+// with fewer, longer-lived workgroups.
+static int grid_for(const Plan &pl, const void *fn, int cus, int64_t cap, int min_tiles)
 {
     int64_t g = (int64_t)cus * occupancy(fn, pl.threads, pl.lds_bytes);
-    if (g > pl.tiles) g = pl.tiles;
+    const int64_t by_tiles = (pl.tiles + min_tiles - 1) / min_tiles;
+    if (g > by_tiles) g = by_tiles;
     if (g > cap) g = cap;
     if (g < 1) g = 1;
     return (int)g;
@@ -564,22 +621,30 @@ static GemvArgs base_args(const Plan &pl, int64_t N)
     return a;
 }
 
-template <int KIND, int EPI, bool WL>
+template <int KIND, int EPI, bool WL, bool XLDS>
 static hipError_t launch_mode(Plan &pl, GemvArgs a, int cus, hipStream_t s, int64_t cap)
 {
-    const void *fn = (const void *)gemv_kernel<KIND, EPI, WL>;
-    pl.grid = grid_for(pl, fn, cus, cap);
+    // the occupancy of the deeper-pipelined kernel sizes the grid; if that
+    // leaves at most one tile per workgroup the single-tile kernel runs
+    const void *fn2 = (const void *)gemv_kernel<KIND, EPI, WL, 2, XLDS>;
+    pl.grid = grid_for(pl, fn2, cus, cap, KIND == kSwiglu ? 2 : 4);
     a.tiles_q = (int)(pl.tiles / pl.grid);
     a.tiles_r = (int)(pl.tiles % pl.grid);
-    hipLaunchKernelGGL((gemv_kernel<KIND, EPI, WL>), dim3(pl.grid), dim3(pl.threads), pl.lds_bytes, s, a);
+    if (a.tiles_q >= 2 || (a.tiles_q == 1 && a.tiles_r > 0))
+        hipLaunchKernelGGL((gemv_kernel<KIND, EPI, WL, 2, XLDS>), dim3(pl.grid), dim3(pl.threads), pl.lds_bytes, s, a);
+    else
+        hipLaunchKernelGGL((gemv_kernel<KIND, EPI, WL, 1, XLDS>), dim3(pl.grid), dim3(pl.threads), pl.lds_bytes, s, a);
     return hipGetLastError();
 }
 
 template <int KIND, int EPI>
 static hipError_t launch(Plan &pl, const GemvArgs &a, int cus, hipStream_t s, int64_t cap = INT64_MAX)
 {
-    return pl.wave_local ? launch_mode<KIND, EPI, true>(pl, a, cus, s, cap)
-                         : launch_mode<KIND, EPI, false>(pl, a, cus, s, cap);
+    if (pl.wave_local)
+        return pl.x_in_lds ? launch_mode<KIND, EPI, true, true>(pl, a, cus, s, cap)
+                           : launch_mode<KIND, EPI, true, false>(pl, a, cus, s, cap);
+    return pl.x_in_lds ? launch_mode<KIND, EPI, false, true>(pl, a, cus, s, cap)
+                       : launch_mode<KIND, EPI, false, false>(pl, a, cus, s, cap);
 }
 
 hipError_t launch_q4k_gemv(const void *W, const float *x, float *y, int64_t N, int64_t K, int cus, hipStream_t s)

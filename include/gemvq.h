@@ -134,6 +134,17 @@ size_t gemvq_lm_head_argmax_ws_bytes(int64_t N, int64_t K);
 int gemvq_q4k_q8_isums(const void *W, const int8_t *xq, int32_t *isums,
                        int64_t N, int64_t K, void *stream);
 
+/*
+ * Launch geometry of the GEMV kernels for an N x K matrix (host-only, no HIP
+ * call; for tests and tuning).  kind: 0 = Q4_K (q4k_gemv), 1 = Q6_K (q6k_gemv,
+ * lm_head_argmax), 2 = Q4_K x Q8 (q4k_q8_gemv), 3 = SwiGLU (swiglu_gemv).
+ * out[0] = waves per workgroup, out[1] = rows per tile, out[2] = tiles,
+ * out[3] = 1 if a row's partial sums reduce inside one wave, out[4] = 1 if the
+ * activation is staged through LDS, out[5] = dynamic LDS bytes.
+ * Returns GEMVQ_ERR_SHAPE for shapes the GEMV entry points reject.
+ */
+int gemvq_tile_geometry(int kind, int64_t N, int64_t K, int64_t out[6]);
+
 /* Static description of a status code (never NULL). */
 const char *gemvq_strerror(int status);
 
