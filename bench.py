@@ -184,25 +184,33 @@ def self_check(gq, sets, v):
     return bool(ok)
 
 
-def breakdown(gq, sets, v, reps=20):
-    """Per-call device time of each kernel: `reps` launches alternating the
-    two weight copies are captured in a HIP graph and replayed between two
-    HIP events (no host launch overhead in the measurement).  Not part of
-    `value`; rocprofv3 kernel traces are the cross-check."""
+def breakdown(gq, sets, v, reps=24):
+    """Per-call device time of each kernel, not part of `value`: `reps`
+    launches are captured in a HIP graph and replayed between two HIP events
+    (no host launch overhead in the measurement).  Each kernel rotates through
+    enough device-side copies of its weights (>= 640 MB in total) that the
+    256 MB Infinity Cache cannot serve a repeat.  rocprofv3 kernel traces are
+    the cross-check."""
     import torch
     import synth
     out = {}
-    wb = weight_bytes()
-    yl = torch.empty(synth.C3_LM_HEAD[0], dtype=torch.float32, device=v["h"].device)
+    dev = v["h"].device
+    yl = torch.empty(synth.C3_LM_HEAD[0], dtype=torch.float32, device=dev)
+    min_bytes = 640 << 20
 
-    def timeit(name, fn, nbytes):
+    def copies(t):
+        n = max(2, -(-min_bytes // t.numel()))
+        return [t] + [t.clone() for _ in range(n - 1)]
+
+    def timeit(name, fn, ws, nbytes):
+        # ws: list of per-copy weight tuples
         for r in range(2):
-            fn(sets[r % 2])
+            fn(ws[r % len(ws)])
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for r in range(reps):
-                fn(sets[r % 2])
+                fn(ws[r % len(ws)])
         g.replay()
         torch.cuda.synchronize()
         st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -214,31 +222,56 @@ def breakdown(gq, sets, v, reps=20):
         torch.cuda.synchronize()
         us = st.elapsed_time(en) * 1000.0 / (reps * n_rep)
         out[name] = {"us": round(us, 2), "GBps": round(nbytes / us / 1e3, 1),
-                     "frac_hbm_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
+                     "frac_hbm_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4), "weight_copies": len(ws)}
         del g
 
+    s0 = sets[0]
     for i, (N, K) in enumerate(synth.C2_Q4K):
-        timeit(f"q4k_gemv_{N}x{K}", lambda s, i=i, N=N, K=K: gq.q4k_gemv(s["c2W"][i], v["c2x"][i], N, K,
-                                                                           y=v["c2y"][i]),
-               N * K // 256 * 144 + 4 * (N + K))
+        ws = [(w,) for w in copies(s0["c2W"][i])]
+        timeit(f"q4k_gemv_{N}x{K}", lambda w, i=i, N=N, K=K: gq.q4k_gemv(w[0], v["c2x"][i], N, K, y=v["c2y"][i]),
+               ws, N * K // 256 * 144 + 4 * (N + K))
+        del ws
     N, K = synth.C3_LM_HEAD
-    timeit("lm_head_argmax_248320x1024", lambda s: gq.lm_head_argmax(s["c3W"], v["c3x"], N, K, v["ws"],
-                                                                     out_idx=v["idx"]),
-           lm_head_algorithmic_bytes())
-    timeit("q6k_gemv_248320x1024", lambda s: gq.q6k_gemv(s["c3W"], v["c3x"], N, K, y=yl),
+    ws = [(w,) for w in copies(s0["c3W"])]
+    timeit("lm_head_argmax_248320x1024", lambda w: gq.lm_head_argmax(w[0], v["c3x"], N, K, v["ws"], out_idx=v["idx"]),
+           ws, lm_head_algorithmic_bytes())
+    timeit("q6k_gemv_248320x1024", lambda w: gq.q6k_gemv(w[0], v["c3x"], N, K, y=yl), ws,
            N * K // 256 * 210 + 4 * (N + K))
+    del ws
     N, K = synth.C4_SWIGLU
-    timeit("swiglu_gemv_9728x2560", lambda s: gq.swiglu_gemv(s["c4Wg"], s["c4Wu"], v["c4x"], N, K, h=v["h"]),
+    ws = list(zip(copies(s0["c4Wg"]), copies(s0["c4Wu"])))
+    timeit("swiglu_gemv_9728x2560", lambda w: gq.swiglu_gemv(w[0], w[1], v["c4x"], N, K, h=v["h"]), ws,
            2 * N * K // 256 * 144 + 4 * (N + K))
-    timeit("q6k_gemv_2560x9728", lambda s: gq.q6k_gemv(s["c4Wd"], v["h"], K, N, y=v["yd"]),
+    del ws
+    ws = [(w,) for w in copies(s0["c4Wd"])]
+    timeit("q6k_gemv_2560x9728", lambda w: gq.q6k_gemv(w[0], v["h"], K, N, y=v["yd"]), ws,
            K * N // 256 * 210 + 4 * (N + K))
+    del ws
     N, K = synth.C5_Q8
-    timeit("q8_quantize_8192", lambda s: gq.q8_quantize(v["c5x"], xq=v["xq"], xd=v["xd"]), K * 4 + K + K // 16)
-    timeit("q4k_q8_gemv_28672x8192", lambda s: gq.q4k_q8_gemv(s["c5W"], v["xq"], v["xd"], N, K, y=v["c5y"]),
+    timeit("q8_quantize_8192", lambda w: gq.q8_quantize(v["c5x"], xq=v["xq"], xd=v["xd"]), [()],
+           K * 4 + K + K // 16)
+    ws = [(w,) for w in copies(s0["c5W"])]
+    timeit("q4k_q8_gemv_28672x8192", lambda w: gq.q4k_q8_gemv(w[0], v["xq"], v["xd"], N, K, y=v["c5y"]), ws,
            N * K // 256 * 144 + K + K // 16 + 4 * N)
-    timeit("q4k_gemv_28672x8192", lambda s: gq.q4k_gemv(s["c5W"], v["c5x"], N, K, y=v["c5y"]),
+    timeit("q4k_gemv_28672x8192", lambda w: gq.q4k_gemv(w[0], v["c5x"], N, K, y=v["c5y"]), ws,
            N * K // 256 * 144 + 4 * (N + K))
+    del ws
+    torch.cuda.empty_cache()
     return out
+
+
+def calibration_copy(dev, mib=256, reps=6):
+    """A plain device copy of a known size (mib MiB read + mib MiB written per
+    call), run so that rocprofv3 counter runs can scale FETCH_SIZE/WRITE_SIZE
+    against known bytes."""
+    import torch
+    a = torch.empty(mib << 20, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
 
 
 def cpu_baseline(host, budget_s=12.0):
@@ -291,6 +324,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="first run a plain 256 MiB device copy six times (counter calibration for rocprofv3)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the path is a single-GPU kernel library); got --gpus {args.gpus}",
@@ -303,6 +338,8 @@ def main():
 
     dev = torch.device("cuda:0")
     gq.lib()
+    if args.calibration_copy:
+        calibration_copy(dev)
     host, sets, v = build_workload(dev)
     N, K = synth.C3_LM_HEAD
     v["ws"] = torch.zeros(gq.lm_head_argmax_ws_bytes(N, K), dtype=torch.uint8, device=dev)

@@ -84,19 +84,12 @@ __device__ __forceinline__ float group_sum(float v, int group)
 }
 
 // ------------------------------------------------------------- argmax
-// Candidate order: NaN never wins; larger value wins; equal values (-0 == +0)
-// go to the smaller index; kNoIndex marks "no candidate".
-__device__ __forceinline__ bool better(float v, uint32_t i, float bv, uint32_t bi)
-{
-    if (v != v) return false;
-    if (bi == kNoIndex) return i != kNoIndex;
-    return v > bv || (v == bv && i < bi);
-}
-
-// 64-bit key whose unsigned order is the candidate order above: the high word
-// maps the float monotonically to an unsigned integer (-0 folded onto +0),
-// the low word is ~index so that of two equal values the smaller index has
-// the larger key.  Key 0 means "no candidate" (no real candidate maps to it).
+// Argmax candidates are ordered so that NaN never wins, a larger value wins,
+// and of two equal values (-0 == +0) the smaller index wins.  The 64-bit key
+// below has exactly that unsigned order: the high word maps the float
+// monotonically to an unsigned integer (-0 folded onto +0), the low word is
+// ~index.  Key 0 means "no candidate" (no real candidate maps to it; NaN rows
+// are never keyed).
 __device__ __forceinline__ uint64_t argmax_key(float v, uint32_t i)
 {
     uint32_t f = __float_as_uint(v == 0.f ? 0.f : v);

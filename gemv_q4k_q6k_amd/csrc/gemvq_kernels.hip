@@ -216,19 +216,14 @@ __device__ __forceinline__ void dot_raw(const RawSet<KIND> &rs, const XSlice<KIN
 
 // ---------------------------------------------------------------- epilogue
 
-struct ArgBest {
-    float v;
-    uint32_t i;
-};
-
+// Running argmax of a thread: the largest key (argmax_key) of the rows it has
+// emitted; NaN rows are skipped, 0 means none.
 template <int KIND, int EPI>
-__device__ __forceinline__ void emit_row(const GemvArgs &a, int64_t row, const float (&v)[2], ArgBest &best)
+__device__ __forceinline__ void emit_row(const GemvArgs &a, int64_t row, const float (&v)[2], uint64_t &best)
 {
     if constexpr (EPI == kArgmax) {
-        if (better(v[0], (uint32_t)row, best.v, best.i)) {
-            best.v = v[0];
-            best.i = (uint32_t)row;
-        }
+        const uint64_t k = (v[0] != v[0]) ? 0ull : argmax_key(v[0], (uint32_t)row);
+        best = k > best ? k : best;
     } else if constexpr (KIND == kSwiglu) {
         const float g = v[0], u = v[1];
         a.y[row] = g * u / (1.0f + expf(-g));
@@ -237,63 +232,39 @@ __device__ __forceinline__ void emit_row(const GemvArgs &a, int64_t row, const f
     }
 }
 
-__device__ __forceinline__ void wave_best(ArgBest &b)
-{
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        const float ov = __shfl_xor(b.v, off);
-        const uint32_t oi = (uint32_t)__shfl_xor((int)b.i, off);
-        if (better(ov, oi, b.v, b.i)) {
-            b.v = ov;
-            b.i = oi;
-        }
-    }
-}
-
-// Workgroup-wide best; the result is valid in thread 0.
-__device__ __forceinline__ ArgBest block_best(ArgBest b, ArgBest *s_best)
-{
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int waves = (blockDim.x + 63) >> 6;
-    wave_best(b);
-    if (lane == 0) s_best[wave] = b;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        for (int w = 1; w < waves; ++w)
-            if (better(s_best[w].v, s_best[w].i, b.v, b.i)) b = s_best[w];
-    }
-    return b;
-}
-
 // Workspace of lm_head_argmax: [0,8) the running best key, [8,12) the count of
 // finished workgroups.  Both are zero between calls.
 __device__ __forceinline__ uint64_t *ws_key(uint8_t *ws) { return (uint64_t *)ws; }
 __device__ __forceinline__ uint32_t *ws_done(uint8_t *ws) { return (uint32_t *)(ws + 8); }
 
-// Grid-level argmax without fences: each workgroup folds its candidate into
-// one 64-bit atomic max, waits for that atomic to complete, then counts itself
-// done with an atomic add; the workgroup that counts last reads the key with
-// an atomic exchange (which also clears it for the next call), writes the
-// 4-byte result and clears the counter.  Atomics are coherent at device scope
-// across all XCDs, so no cache writeback or invalidation is needed.
-__device__ void argmax_finish(const GemvArgs &a, ArgBest best)
+// Grid-level argmax without fences: the threads' running keys are gathered
+// through LDS (one barrier) and thread 0 folds the workgroup's best into one
+// 64-bit atomic max, waits for that atomic to complete, then counts the
+// workgroup done with an atomic add; the workgroup that counts last reads the
+// key with an atomic exchange (which also clears it for the next call), writes
+// the 4-byte result and clears the counter.  Atomics are coherent at device
+// scope across all XCDs, so no cache writeback or invalidation is needed.
+// `holders` threads (0..holders-1) carry running keys.
+__device__ void argmax_finish(const GemvArgs &a, uint64_t best, int holder, int holders)
 {
-    __shared__ ArgBest s_best[kMaxThreads / 64];
-    best = block_best(best, s_best);
+    __shared__ uint64_t s_key[kMaxThreads];
+    if (holder >= 0) s_key[holder] = best;
+    __syncthreads();
     if (threadIdx.x == 0) {
-        if (best.i != kNoIndex) {
+        uint64_t k = 0;
+        for (int h = 0; h < holders; ++h) k = s_key[h] > k ? s_key[h] : k;
+        if (k) {
             // a returning atomic: consuming its result makes the wave wait until
             // the max has been performed before it counts itself done
-            const uint64_t old = __hip_atomic_fetch_max(ws_key(a.ws), argmax_key(best.v, best.i), __ATOMIC_RELAXED,
-                                                        __HIP_MEMORY_SCOPE_AGENT);
+            const uint64_t old = __hip_atomic_fetch_max(ws_key(a.ws), k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             asm volatile("" ::"v"(old));
         }
         const uint32_t prev = __hip_atomic_fetch_add(ws_done(a.ws), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (prev == gridDim.x - 1) {
-            const uint64_t k = __hip_atomic_exchange(ws_key(a.ws), (uint64_t)0, __ATOMIC_RELAXED,
+            const uint64_t g = __hip_atomic_exchange(ws_key(a.ws), (uint64_t)0, __ATOMIC_RELAXED,
                                                      __HIP_MEMORY_SCOPE_AGENT);
-            a.out_idx[0] = k ? argmax_key_index(k) : 0u;
-            if (a.out_max) a.out_max[0] = k ? argmax_key_value(k) : __builtin_nanf("");
+            a.out_idx[0] = g ? argmax_key_index(g) : 0u;
+            if (a.out_max) a.out_max[0] = g ? argmax_key_value(g) : __builtin_nanf("");
             __hip_atomic_store(ws_done(a.ws), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
@@ -419,7 +390,7 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_kernel(GemvArgs a)
 
     float *red = (float *)smem;   // [2][OUTS][rows_tile][nb]
     const int red_stride = OUTS * a.rows_tile * a.nb;
-    ArgBest best{0.f, kNoIndex};
+    uint64_t best = 0;   // running argmax key (argmax kernels)
     int buf = 0;
     // dot, row reduction and epilogue of tile t (workgroup-uniform control flow)
     auto process = [&](const RawSet<KIND> &rs, int t) {
@@ -477,7 +448,13 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_kernel(GemvArgs a)
         }
     }
 
-    if constexpr (EPI == kArgmax) argmax_finish(a, best);
+    if constexpr (EPI == kArgmax) {
+        // row leaders (wave-local) or row-sum threads (LDS reduction) hold keys
+        if constexpr (WAVE_LOCAL)
+            argmax_finish(a, best, (rr == 0 && lane_on) ? p : -1, a.rows_tile);
+        else
+            argmax_finish(a, best, tid < a.rows_tile ? tid : -1, a.rows_tile);
+    }
 }
 
 // --------------------------------------------------------- Q8 quantize
