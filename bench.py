@@ -260,18 +260,79 @@ def breakdown(gq, sets, v, reps=24):
     return out
 
 
-def calibration_copy(dev, mib=256, reps=6):
-    """A plain device copy of a known size (mib MiB read + mib MiB written per
-    call), run so that rocprofv3 counter runs can scale FETCH_SIZE/WRITE_SIZE
-    against known bytes."""
+CALIB_MIB = 256
+CALIB_TAG = "neg_kernel"        # the calibration copy is torch's elementwise negation
+
+
+def calibration_copy(dev, mib=CALIB_MIB, reps=6):
+    """A plain streaming copy of known size: `reps` launches of torch's
+    elementwise negation over mib MiB of f32 (mib MiB read, mib MiB written
+    per launch).  Run under rocprofv3 --pmc, its FETCH_SIZE/WRITE_SIZE give the
+    factors that turn those counters into bytes."""
     import torch
-    a = torch.empty(mib << 20, dtype=torch.uint8, device=dev)
+    a = torch.ones((mib << 20) // 4, dtype=torch.float32, device=dev)
     b = torch.empty_like(a)
-    a.fill_(1)
     for _ in range(reps):
-        b.copy_(a)
+        torch.neg(a, out=b)
     torch.cuda.synchronize()
     del a, b
+
+
+def _counter_means(db, counter):
+    """{kernel name: mean over dispatches of the counter's per-dispatch total}
+    from a rocprofv3 (rocpd SQLite) database."""
+    import sqlite3
+    import collections
+    c = sqlite3.connect(db)
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    for name, disp, val in c.execute(
+            "select kernel_name, dispatch_id, value from counters_collection where counter_name = ?", (counter,)):
+        per[name][disp] += val
+    c.close()
+    return {k: (sum(v.values()) / len(v), len(v)) for k, v in per.items()}
+
+
+def _pick(means, pred, what):
+    hits = [(k, v) for k, v in means.items() if pred(k)]
+    if len(hits) != 1:
+        raise SystemExit(f"expected one {what} kernel in the counter database, found {[k for k, _ in hits]}")
+    return hits[0]
+
+
+def write_traffic(fetch_db, write_db, command):
+    """Turn two rocprofv3 --pmc runs of `bench.py --calibration-copy` (one
+    with FETCH_SIZE, one with WRITE_SIZE) into HBM bytes per lm_head launch,
+    scaled by what the same counters read for the calibration copy, and store
+    them next to the kernel-source hash they were taken on."""
+    known = CALIB_MIB << 20
+    is_lm = lambda k: "gemv_kernel<1, 1," in k         # KIND = Q6_K, epilogue = argmax
+    is_cal = lambda k: CALIB_TAG in k
+    fm, wm = _counter_means(fetch_db, "FETCH_SIZE"), _counter_means(write_db, "WRITE_SIZE")
+    lm_name, (lm_f, n_f) = _pick(fm, is_lm, "lm_head")
+    _, (lm_w, n_w) = _pick(wm, is_lm, "lm_head")
+    cal_name, (cal_f, _) = _pick(fm, is_cal, "calibration")
+    _, (cal_w, _) = _pick(wm, is_cal, "calibration")
+    f_fac = known / (cal_f * 1024.0)
+    w_fac = known / (cal_w * 1024.0)
+    fetch_b = lm_f * 1024.0 * f_fac
+    write_b = lm_w * 1024.0 * w_fac
+    out = {
+        "kernel": lm_name, "dispatches": {"fetch": n_f, "write": n_w},
+        "fetch_size_kib_per_dispatch": round(lm_f, 1), "write_size_kib_per_dispatch": round(lm_w, 1),
+        "calibration": {"kernel": cal_name, "bytes_read": known, "bytes_written": known,
+                        "fetch_size_kib": round(cal_f, 1), "write_size_kib": round(cal_w, 1),
+                        "fetch_factor": round(f_fac, 4), "write_factor": round(w_fac, 4)},
+        "hbm_fetch_bytes_per_launch": int(round(fetch_b)), "hbm_write_bytes_per_launch": int(round(write_b)),
+        "bytes_per_launch": int(round(fetch_b + write_b)),
+        "algorithmic_bytes_per_launch": lm_head_algorithmic_bytes(),
+        "kernel_source_hash": kernel_source_hash(),
+        "command": command,
+    }
+    os.makedirs(os.path.dirname(PROFILE_TRAFFIC), exist_ok=True)
+    with open(PROFILE_TRAFFIC, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
 
 
 def cpu_baseline(host, budget_s=12.0):
@@ -326,7 +387,14 @@ def main():
     ap.add_argument("--no-breakdown", action="store_true")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="first run a plain 256 MiB device copy six times (counter calibration for rocprofv3)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
+                    help="no GPU work: summarise two rocprofv3 --pmc databases (FETCH_SIZE, WRITE_SIZE) of "
+                         "'bench.py --calibration-copy' into the lm_head traffic record under profiles/")
+    ap.add_argument("--traffic-command", default="", help="the profiling commands, stored with the record")
     args = ap.parse_args()
+    if args.traffic_from:
+        write_traffic(*args.traffic_from, args.traffic_command)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the path is a single-GPU kernel library); got --gpus {args.gpus}",
               file=sys.stderr)

@@ -1,0 +1,74 @@
+"""Host-side logic of bench.py (no GPU): the --gpus guard and the conversion
+of rocprofv3 counter databases into the lm_head traffic record."""
+import json
+import os
+import sqlite3
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=60)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def _db(path, counter, rows):
+    c = sqlite3.connect(path)
+    c.execute("create table counters_collection (kernel_name text, dispatch_id int, counter_name text, value real)")
+    c.executemany("insert into counters_collection values (?, ?, ?, ?)",
+                  [(k, d, counter, v) for k, d, v in rows])
+    c.commit()
+    c.close()
+
+
+LM = "void gemvq::gemv_kernel<1, 1, true, 2, true>(gemvq::GemvArgs)"
+CAL = "void at::native::vectorized_elementwise_kernel<4, at::native::neg_kernel_cuda(...)>"
+OTHER = "void gemvq::gemv_kernel<1, 0, true, 2, true>(gemvq::GemvArgs)"
+
+
+def test_traffic_record(tmp_path, monkeypatch):
+    known_kib = (bench.CALIB_MIB << 20) / 1024
+    # the fetch counter reads half the true bytes, split over two instances per dispatch
+    fetch_rows = [(CAL, d, known_kib / 4) for d in (1, 2) for _ in range(2)]
+    fetch_rows += [(LM, d, 50_000.0) for d in (3, 4) for _ in range(2)]
+    fetch_rows += [(OTHER, 5, 1.0)]
+    write_rows = [(CAL, 1, known_kib), (LM, 3, 10.0), (LM, 4, 30.0)]
+    fdb, wdb = str(tmp_path / "f.db"), str(tmp_path / "w.db")
+    _db(fdb, "FETCH_SIZE", fetch_rows)
+    _db(wdb, "WRITE_SIZE", write_rows)
+    out = tmp_path / "traffic.json"
+    monkeypatch.setattr(bench, "PROFILE_TRAFFIC", str(out))
+    bench.write_traffic(fdb, wdb, "cmd")
+    t = json.loads(out.read_text())
+    assert t["calibration"]["fetch_factor"] == pytest.approx(2.0)
+    assert t["calibration"]["write_factor"] == pytest.approx(1.0)
+    assert t["fetch_size_kib_per_dispatch"] == pytest.approx(100_000.0)
+    assert t["hbm_fetch_bytes_per_launch"] == 2 * 100_000 * 1024
+    assert t["hbm_write_bytes_per_launch"] == 20 * 1024
+    assert t["bytes_per_launch"] == 2 * 100_000 * 1024 + 20 * 1024
+    assert t["kernel_source_hash"] == bench.kernel_source_hash()
+    assert bench.traffic_entry(0) == t["bytes_per_launch"]
+
+
+def test_traffic_record_needs_one_lm_head_kernel(tmp_path, monkeypatch):
+    fdb, wdb = str(tmp_path / "f.db"), str(tmp_path / "w.db")
+    _db(fdb, "FETCH_SIZE", [(CAL, 1, 1.0)])
+    _db(wdb, "WRITE_SIZE", [(CAL, 1, 1.0)])
+    monkeypatch.setattr(bench, "PROFILE_TRAFFIC", str(tmp_path / "t.json"))
+    with pytest.raises(SystemExit):
+        bench.write_traffic(fdb, wdb, "cmd")
+
+
+def test_stale_traffic_record_is_ignored(tmp_path, monkeypatch):
+    p = tmp_path / "t.json"
+    p.write_text(json.dumps({"kernel_source_hash": "not-this-source", "bytes_per_launch": 123}))
+    monkeypatch.setattr(bench, "PROFILE_TRAFFIC", str(p))
+    assert bench.traffic_entry(0) is None
