@@ -20,7 +20,7 @@ import threading
 __all__ = [
     "GemvqError", "lib", "exported_names", "header_names",
     "q4k_gemv", "q6k_gemv", "q8_quantize", "q4k_q8_gemv", "swiglu_gemv",
-    "lm_head_argmax", "lm_head_argmax_ws_bytes", "q4k_q8_isums", "strerror", "tile_geometry",
+    "lm_head_argmax", "lm_head_argmax_timed", "lm_head_argmax_ws_bytes", "q4k_q8_isums", "strerror", "tile_geometry",
     "Q4K_BLOCK_BYTES", "Q6K_BLOCK_BYTES", "LIB_PATH", "HEADER_PATH",
 ]
 
@@ -52,6 +52,7 @@ _SIGS = {
     "q4k_q8_gemv": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _P]),
     "swiglu_gemv": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _P]),
     "lm_head_argmax": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_size_t, _I64, _I64, _P]),
+    "lm_head_argmax_timed": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_size_t, _I64, _I64, _P, _P, _P]),
     "gemvq_lm_head_argmax_ws_bytes": (ctypes.c_size_t, [_I64, _I64]),
     "gemvq_q4k_q8_isums": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P]),
     "gemvq_strerror": (ctypes.c_char_p, [ctypes.c_int]),
@@ -209,6 +210,15 @@ def lm_head_argmax_ws_bytes(N: int, K: int) -> int:
     return int(lib().gemvq_lm_head_argmax_ws_bytes(N, K))
 
 
+def _event_handle(ev) -> int:
+    """Raw hipEvent_t of a torch.cuda.Event created with enable_timing=True
+    (torch creates the handle at the first record, so record it once first)."""
+    h = int(ev.cuda_event)
+    if h == 0:
+        raise ValueError("event has no HIP handle yet: record it once before passing it")
+    return h
+
+
 def lm_head_argmax(W, x, N: int, K: int, workspace, out_idx=None, out_max=None, want_max: bool = False,
                    stream=None):
     """First index of the largest row value of W x (Q6_K W).  Returns the
@@ -216,6 +226,19 @@ def lm_head_argmax(W, x, N: int, K: int, workspace, out_idx=None, out_max=None, 
     want_max or out_max is given).  `workspace` is a uint8 device tensor of at
     least lm_head_argmax_ws_bytes(N, K) bytes, zero-filled before its first use
     (torch.zeros); every call leaves it zero again."""
+    return _lm_head(W, x, N, K, workspace, out_idx, out_max, want_max, stream, None)
+
+
+def lm_head_argmax_timed(W, x, N: int, K: int, workspace, start_event, stop_event, out_idx=None, out_max=None,
+                         want_max: bool = False, stream=None):
+    """lm_head_argmax that records the kernel's own start and end into two
+    torch.cuda.Event(enable_timing=True) objects (each recorded once before),
+    so start_event.elapsed_time(stop_event) is the kernel's duration."""
+    return _lm_head(W, x, N, K, workspace, out_idx, out_max, want_max, stream,
+                    (_event_handle(start_event), _event_handle(stop_event)))
+
+
+def _lm_head(W, x, N, K, workspace, out_idx, out_max, want_max, stream, events):
     torch = _torch()
     _weights(W, N, K, Q6K_BLOCK_BYTES)
     _dev_tensor(x, torch.float32, K, "x")
@@ -226,10 +249,12 @@ def lm_head_argmax(W, x, N: int, K: int, workspace, out_idx=None, out_max=None, 
         out_max = torch.empty(1, dtype=torch.float32, device=x.device)
     if out_max is not None:
         _dev_tensor(out_max, torch.float32, 1, "out_max")
-    st = lib().lm_head_argmax(W.data_ptr(), x.data_ptr(), out_idx.data_ptr(),
-                              out_max.data_ptr() if out_max is not None else None,
-                              workspace.data_ptr(), workspace.numel(), N, K, _stream(x, stream))
-    _check("lm_head_argmax", st)
+    args = (W.data_ptr(), x.data_ptr(), out_idx.data_ptr(), out_max.data_ptr() if out_max is not None else None,
+            workspace.data_ptr(), workspace.numel(), N, K, _stream(x, stream))
+    if events is None:
+        _check("lm_head_argmax", lib().lm_head_argmax(*args))
+    else:
+        _check("lm_head_argmax_timed", lib().lm_head_argmax_timed(*args, *events))
     return (out_idx, out_max) if out_max is not None else out_idx
 
 

@@ -163,8 +163,8 @@ int swiglu_gemv(const void *Wg, const void *Wu, const float *x, float *h, int64_
     return status_of(gemvq::launch_swiglu_gemv(Wg, Wu, x, h, N, K, cus, (hipStream_t)stream));
 }
 
-int lm_head_argmax(const void *W, const float *x, uint32_t *out_idx, float *out_max, void *workspace, size_t ws_bytes,
-                   int64_t N, int64_t K, void *stream)
+static int lm_head_argmax_impl(const void *W, const float *x, uint32_t *out_idx, float *out_max, void *workspace,
+                               size_t ws_bytes, int64_t N, int64_t K, void *stream, const gemvq::Timing &tm)
 {
     if (!W || !x || !out_idx || !workspace) return GEMVQ_ERR_NULL;
     size_t wb = 0;
@@ -183,7 +183,22 @@ int lm_head_argmax(const void *W, const float *x, uint32_t *out_idx, float *out_
     int cus = 0;
     if (int st = device_cus(&cus)) return st;
     return status_of(
-        gemvq::launch_lm_head_argmax(W, x, out_idx, out_max, workspace, N, K, cus, (hipStream_t)stream));
+        gemvq::launch_lm_head_argmax(W, x, out_idx, out_max, workspace, N, K, cus, (hipStream_t)stream, tm));
+}
+
+int lm_head_argmax(const void *W, const float *x, uint32_t *out_idx, float *out_max, void *workspace, size_t ws_bytes,
+                   int64_t N, int64_t K, void *stream)
+{
+    return lm_head_argmax_impl(W, x, out_idx, out_max, workspace, ws_bytes, N, K, stream, gemvq::Timing{});
+}
+
+int lm_head_argmax_timed(const void *W, const float *x, uint32_t *out_idx, float *out_max, void *workspace,
+                         size_t ws_bytes, int64_t N, int64_t K, void *stream, void *start_event, void *stop_event)
+{
+    gemvq::Timing tm;
+    tm.start = (hipEvent_t)start_event;
+    tm.stop = (hipEvent_t)stop_event;
+    return lm_head_argmax_impl(W, x, out_idx, out_max, workspace, ws_bytes, N, K, stream, tm);
 }
 
 int gemvq_q4k_q8_isums(const void *W, const int8_t *xq, int32_t *isums, int64_t N, int64_t K, void *stream)

@@ -10,6 +10,7 @@
 // wave or tile holds the row, so equal rows give bit-identical values (the
 // argmax tie rule relies on this) and q6k_gemv's outputs are exactly the values
 // lm_head_argmax compares.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -53,6 +54,26 @@ template <> struct XSlice<kSwiglu> { Q4KX v; };
 template <> struct XSlice<kQ6K> { Q6KX v; };
 template <> struct XSlice<kQ4KQ8> { Q8X v; };
 
+// Layout of the activation staged in LDS: 16 bytes of padding after every
+// 256 bytes.  A lane's slice is 64 consecutive bytes (Q8) or 64 consecutive
+// floats (Q4_K), and lanes read slices 64 or 256 bytes apart; unpadded, all
+// lanes of a read pass would hit the same four LDS banks (up to 16-way
+// conflicts).  The padding shifts consecutive lanes onto different banks.
+// Every 16-byte chunk, 16-float segment or 64-byte slice the kernels read
+// starts and ends inside one 256-byte span, so it stays contiguous.
+__device__ __forceinline__ uint32_t lds_pad(uint32_t byte_off) { return byte_off + ((byte_off >> 8) << 4); }
+
+// Address of activation element i: straight (global x) or in the padded LDS
+// layout.
+template <bool PADDED>
+__device__ __forceinline__ const float *x_at(const float *base, int i)
+{
+    if constexpr (PADDED)
+        return (const float *)((const unsigned char *)base + lds_pad(4u * (uint32_t)i));
+    else
+        return base + i;
+}
+
 __device__ __forceinline__ void load_x_f32(float *dst, const float *src, int n)
 {
 #pragma unroll
@@ -80,13 +101,14 @@ __device__ __forceinline__ float sum16(const float *v)
 }
 
 // Q4_K part c of block b: xl = x[256b + 64c + i], xh = x[256b + 64c + 32 + i].
+template <bool PADDED = false>
 __device__ __forceinline__ void load_x(Q4KX &xs, const float *xsrc, int b, int c)
 {
-    const float *p = xsrc + kQK * b + 64 * c;
+    const int o = kQK * b + 64 * c;
 #pragma unroll
     for (int i = 0; i < 32; i += 16) {
-        load_x_f32(xs.xl + i, p + i, 16);
-        load_x_f32(xs.xh + i, p + 32 + i, 16);
+        load_x_f32(xs.xl + i, x_at<PADDED>(xsrc, o + i), 16);
+        load_x_f32(xs.xh + i, x_at<PADDED>(xsrc, o + 32 + i), 16);
     }
 }
 
@@ -110,12 +132,13 @@ __device__ __forceinline__ void finish_x(Q4KX &xs, const float *sums, int b, int
 }
 
 // Q6_K part u of block b: xs[s][i] = x[256b + 128n + 32s + l0 + i].
+template <bool PADDED = false>
 __device__ __forceinline__ void load_x(Q6KX &xs, const float *xsrc, int b, int u)
 {
     const int n = u >> 1, l0 = 16 * (u & 1);
-    const float *p = xsrc + kQK * b + 128 * n + l0;
+    const int o = kQK * b + 128 * n + l0;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) load_x_f32(xs.xs[s], p + 32 * s, 16);
+    for (int s = 0; s < 4; ++s) load_x_f32(xs.xs[s], x_at<PADDED>(xsrc, o + 32 * s), 16);
 }
 
 __device__ __forceinline__ void finish_x(Q6KX &xs, const float *sums, int b, int u)
@@ -130,9 +153,11 @@ __device__ __forceinline__ void finish_x(Q6KX &xs, const float *sums, int b, int
 }
 
 // Q8 part c of block b: 32 int8 of sub-blocks 8b+2c and 8b+2c+1, their scales.
+template <bool PADDED = false>
 __device__ __forceinline__ void load_x(Q8X &xs, const int8_t *qsrc, const uint16_t *dsrc, int b, int c)
 {
-    const uint32_t *p = (const uint32_t *)(qsrc + kQK * b + 64 * c);
+    const uint32_t o = (uint32_t)(kQK * b + 64 * c);
+    const uint32_t *p = (const uint32_t *)(qsrc + (PADDED ? lds_pad(o) : o));
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
         xs.ql[k] = p[k];
@@ -364,23 +389,23 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_kernel(GemvArgs a)
 #pragma unroll
         for (int r = 0; r < kXRegs; ++r) {
             const int i = (tid + r * (int)blockDim.x) * step;
-            if (i < K) *(u32x4 *)(smem + (size_t)i * esz) = xr[r];
+            if (i < K) *(u32x4 *)(smem + lds_pad((uint32_t)(i * esz))) = xr[r];
         }
         for (int i = (tid + kXRegs * (int)blockDim.x) * step; i < K; i += (int)blockDim.x * step)
-            *(u32x4 *)(smem + (size_t)i * esz) = *(const u32x4 *)(src + (size_t)i * esz);
+            *(u32x4 *)(smem + lds_pad((uint32_t)(i * esz))) = *(const u32x4 *)(src + (size_t)i * esz);
         __syncthreads();
     }
     if constexpr (KIND == kQ4KQ8) {
-        if constexpr (XLDS) load_x(xs.v, (const int8_t *)smem, a.xd, xb, part);
+        if constexpr (XLDS) load_x<true>(xs.v, (const int8_t *)smem, a.xd, xb, part);
         finish_x(xs.v);
     } else {
         if constexpr (XLDS) {
             // K/16 sums of 16 consecutive activation values, once per workgroup
             const float *sx = (const float *)smem;
-            float *ssum = (float *)smem + K;
-            for (int g = tid; g < K / 16; g += blockDim.x) ssum[g] = sum16(sx + 16 * g);
+            float *ssum = (float *)(smem + lds_pad(4u * (uint32_t)K));
+            for (int g = tid; g < K / 16; g += blockDim.x) ssum[g] = sum16(x_at<true>(sx, 16 * g));
             __syncthreads();
-            load_x(xs.v, sx, xb, part);
+            load_x<true>(xs.v, sx, xb, part);
             finish_x(xs.v, (const float *)ssum, xb, part);
         } else {
             finish_x(xs.v, (const float *)nullptr, xb, part);
@@ -543,9 +568,10 @@ Plan make_plan(int64_t N, int64_t K, int kind)
     // Staging x through LDS pays when several rows of a tile read the same
     // slice; with one row per tile every element has a single reader.
     const size_t sums = (kind == kQ4KQ8) ? 0 : (size_t)(K / 16) * 4;
-    pl.x_in_lds = (pl.rows_tile > 1 && xbytes + sums <= 65536) ? 1 : 0;
+    const size_t xpadded = xbytes + xbytes / 16;   // 16 bytes of padding per 256 (lds_pad)
+    pl.x_in_lds = (pl.rows_tile > 1 && xpadded + sums <= 65536) ? 1 : 0;
     const size_t red = pl.wave_local ? 0 : (size_t)2 * outs * pl.rows_tile * pl.nb * 4;   // two buffers
-    pl.lds_bytes = (pl.x_in_lds ? xbytes + sums : 0);
+    pl.lds_bytes = (pl.x_in_lds ? xpadded + sums : 0);
     if (red > pl.lds_bytes) pl.lds_bytes = red;
     pl.grid = 0;   // set by the launcher from the occupancy
     return pl;
@@ -575,12 +601,11 @@ static int occupancy(const void *fn, int threads, size_t lds)
 // `min_tiles` tiles per workgroup: a workgroup's start-up (activation staging,
 // first-tile latency) costs several tile times, so short grids run faster
 // with fewer, longer-lived workgroups.
-static int grid_for(const Plan &pl, const void *fn, int cus, int64_t cap, int min_tiles)
+static int grid_for(const Plan &pl, const void *fn, int cus, int min_tiles)
 {
     int64_t g = (int64_t)cus * occupancy(fn, pl.threads, pl.lds_bytes);
     const int64_t by_tiles = (pl.tiles + min_tiles - 1) / min_tiles;
     if (g > by_tiles) g = by_tiles;
-    if (g > cap) g = cap;
     if (g < 1) g = 1;
     return (int)g;
 }
@@ -598,30 +623,42 @@ static GemvArgs base_args(const Plan &pl, int64_t N)
     return a;
 }
 
+// Launch on stream s; with a start or stop event the kernel's own start and
+// end are recorded into them (hipExtLaunchKernel), so their elapsed time is
+// the kernel's duration.
+template <typename Kern>
+static void launch_on(Kern k, const Plan &pl, const GemvArgs &a, hipStream_t s, const Timing &tm)
+{
+    if (tm.start || tm.stop)
+        hipExtLaunchKernelGGL(k, dim3(pl.grid), dim3(pl.threads), (uint32_t)pl.lds_bytes, s, tm.start, tm.stop, 0u, a);
+    else
+        hipLaunchKernelGGL(k, dim3(pl.grid), dim3(pl.threads), pl.lds_bytes, s, a);
+}
+
 template <int KIND, int EPI, bool WL, bool XLDS>
-static hipError_t launch_mode(Plan &pl, GemvArgs a, int cus, hipStream_t s, int64_t cap)
+static hipError_t launch_mode(Plan &pl, GemvArgs a, int cus, hipStream_t s, const Timing &tm)
 {
     // the occupancy of the deeper-pipelined kernel sizes the grid; if that
     // leaves at most one tile per workgroup the single-tile kernel runs
     const void *fn2 = (const void *)gemv_kernel<KIND, EPI, WL, 2, XLDS>;
-    pl.grid = grid_for(pl, fn2, cus, cap, KIND == kSwiglu ? 2 : 4);
+    pl.grid = grid_for(pl, fn2, cus, KIND == kSwiglu ? 2 : 4);
     a.tiles_q = (int)(pl.tiles / pl.grid);
     a.tiles_r = (int)(pl.tiles % pl.grid);
     if (a.tiles_q >= 2 || (a.tiles_q == 1 && a.tiles_r > 0))
-        hipLaunchKernelGGL((gemv_kernel<KIND, EPI, WL, 2, XLDS>), dim3(pl.grid), dim3(pl.threads), pl.lds_bytes, s, a);
+        launch_on(gemv_kernel<KIND, EPI, WL, 2, XLDS>, pl, a, s, tm);
     else
-        hipLaunchKernelGGL((gemv_kernel<KIND, EPI, WL, 1, XLDS>), dim3(pl.grid), dim3(pl.threads), pl.lds_bytes, s, a);
+        launch_on(gemv_kernel<KIND, EPI, WL, 1, XLDS>, pl, a, s, tm);
     return hipGetLastError();
 }
 
 template <int KIND, int EPI>
-static hipError_t launch(Plan &pl, const GemvArgs &a, int cus, hipStream_t s, int64_t cap = INT64_MAX)
+static hipError_t launch(Plan &pl, const GemvArgs &a, int cus, hipStream_t s, const Timing &tm = Timing{})
 {
     if (pl.wave_local)
-        return pl.x_in_lds ? launch_mode<KIND, EPI, true, true>(pl, a, cus, s, cap)
-                           : launch_mode<KIND, EPI, true, false>(pl, a, cus, s, cap);
-    return pl.x_in_lds ? launch_mode<KIND, EPI, false, true>(pl, a, cus, s, cap)
-                       : launch_mode<KIND, EPI, false, false>(pl, a, cus, s, cap);
+        return pl.x_in_lds ? launch_mode<KIND, EPI, true, true>(pl, a, cus, s, tm)
+                           : launch_mode<KIND, EPI, true, false>(pl, a, cus, s, tm);
+    return pl.x_in_lds ? launch_mode<KIND, EPI, false, true>(pl, a, cus, s, tm)
+                       : launch_mode<KIND, EPI, false, false>(pl, a, cus, s, tm);
 }
 
 hipError_t launch_q4k_gemv(const void *W, const float *x, float *y, int64_t N, int64_t K, int cus, hipStream_t s)
@@ -669,7 +706,7 @@ hipError_t launch_q4k_q8_gemv(const void *W, const int8_t *xq, const uint16_t *x
 }
 
 hipError_t launch_lm_head_argmax(const void *W, const float *x, uint32_t *out_idx, float *out_max, void *ws, int64_t N,
-                                 int64_t K, int cus, hipStream_t s)
+                                 int64_t K, int cus, hipStream_t s, const Timing &tm)
 {
     Plan pl = make_plan(N, K, kQ6K);
     GemvArgs a = base_args(pl, N);
@@ -678,7 +715,7 @@ hipError_t launch_lm_head_argmax(const void *W, const float *x, uint32_t *out_id
     a.ws = (uint8_t *)ws;
     a.out_idx = out_idx;
     a.out_max = out_max;
-    return launch<kQ6K, kArgmax>(pl, a, cus, s);
+    return launch<kQ6K, kArgmax>(pl, a, cus, s, tm);
 }
 
 hipError_t launch_q8_quantize(const float *x, int8_t *xq, uint16_t *xd, int64_t K, hipStream_t s)

@@ -34,6 +34,13 @@ struct Plan {
 
 Plan make_plan(int64_t N, int64_t K, int kind);
 
+// Optional device timestamps of one launch: the kernel's own start and end
+// are recorded into these caller-created events when they are not null.
+struct Timing {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+};
+
 hipError_t launch_q4k_gemv(const void *W, const float *x, float *y, int64_t N, int64_t K, int cus, hipStream_t s);
 hipError_t launch_q6k_gemv(const void *W, const float *x, float *y, int64_t N, int64_t K, int cus, hipStream_t s);
 hipError_t launch_swiglu_gemv(const void *Wg, const void *Wu, const float *x, float *h, int64_t N, int64_t K, int cus,
@@ -41,7 +48,7 @@ hipError_t launch_swiglu_gemv(const void *Wg, const void *Wu, const float *x, fl
 hipError_t launch_q4k_q8_gemv(const void *W, const int8_t *xq, const uint16_t *xd, float *y, int64_t N, int64_t K,
                               int cus, hipStream_t s);
 hipError_t launch_lm_head_argmax(const void *W, const float *x, uint32_t *out_idx, float *out_max, void *ws, int64_t N,
-                                 int64_t K, int cus, hipStream_t s);
+                                 int64_t K, int cus, hipStream_t s, const Timing &tm = Timing{});
 hipError_t launch_q8_quantize(const float *x, int8_t *xq, uint16_t *xd, int64_t K, hipStream_t s);
 hipError_t launch_q4k_q8_isums(const void *W, const int8_t *xq, int32_t *isums, int64_t N, int64_t K, hipStream_t s);
 

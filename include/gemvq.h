@@ -122,6 +122,20 @@ int swiglu_gemv(const void *Wg, const void *Wu, const float *x, float *h,
 int lm_head_argmax(const void *W, const float *x, uint32_t *out_idx, float *out_max,
                    void *workspace, size_t ws_bytes, int64_t N, int64_t K, void *stream);
 
+/*
+ * lm_head_argmax with device timestamps: the same work, checks and errors.
+ * start_event and stop_event are hipEvent_t handles (passed as void*) that
+ * the caller created with timing enabled, or NULL.  When given, the GEMV
+ * kernel's own start and end are recorded into them (hipExtLaunchKernel), so
+ * hipEventElapsedTime(start_event, stop_event) is the kernel's duration
+ * without the gaps around it: the per-launch time that a bandwidth figure
+ * needs (aprender PR #4332 times decode per token; this times the lm_head
+ * call itself).  The events stay owned by the caller.
+ */
+int lm_head_argmax_timed(const void *W, const float *x, uint32_t *out_idx, float *out_max,
+                         void *workspace, size_t ws_bytes, int64_t N, int64_t K, void *stream,
+                         void *start_event, void *stop_event);
+
 /* Workspace bytes lm_head_argmax needs for an N x K call (host-only, no HIP call). */
 size_t gemvq_lm_head_argmax_ws_bytes(int64_t N, int64_t K);
 

@@ -72,6 +72,7 @@ def test_null_pointers():
     _rejected(L.q4k_q8_gemv(A, B, None, D, 4, 256, None), gq.ERR_NULL)
     _rejected(L.swiglu_gemv(A, None, C, D, 4, 256, None), gq.ERR_NULL)
     _rejected(L.lm_head_argmax(A, B, C, None, None, 1 << 20, 4, 256, None), gq.ERR_NULL)
+    _rejected(L.lm_head_argmax_timed(A, B, C, None, None, 1 << 20, 4, 256, None, None, None), gq.ERR_NULL)
     _rejected(L.gemvq_q4k_q8_isums(A, B, None, 4, 256, None), gq.ERR_NULL)
 
 
@@ -84,6 +85,7 @@ def test_bad_shapes(N, K):
     _rejected(L.q4k_q8_gemv(A, B, C, D, N, K, None), gq.ERR_SHAPE)
     _rejected(L.swiglu_gemv(A, B, C, D, N, K, None), gq.ERR_SHAPE)
     _rejected(L.lm_head_argmax(A, B, C, D, E, 1 << 20, N, K, None), gq.ERR_SHAPE)
+    _rejected(L.lm_head_argmax_timed(A, B, C, D, E, 1 << 20, N, K, None, A, B), gq.ERR_SHAPE)
     _rejected(L.gemvq_q4k_q8_isums(A, B, C, N, K, None), gq.ERR_SHAPE)
 
 
@@ -105,6 +107,7 @@ def test_alignment():
     _rejected(L.swiglu_gemv(A, B + 8, C, D, 4, 256, None), gq.ERR_ALIGN)
     _rejected(L.lm_head_argmax(A, B, C, D, E + 16, 1 << 20, 4, 256, None), gq.ERR_ALIGN)   # workspace 256 B
     _rejected(L.lm_head_argmax(A, B, C + 1, D, E, 1 << 20, 4, 256, None), gq.ERR_ALIGN)
+    _rejected(L.lm_head_argmax_timed(A, B, C + 1, D, E, 1 << 20, 4, 256, None, None, None), gq.ERR_ALIGN)
     _rejected(L.gemvq_q4k_q8_isums(A, B, C + 2, 4, 256, None), gq.ERR_ALIGN)
 
 
@@ -113,6 +116,7 @@ def test_workspace_too_small():
     need = gq.lm_head_argmax_ws_bytes(4, 256)
     _rejected(L.lm_head_argmax(A, B, C, D, E, need - 1, 4, 256, None), gq.ERR_WORKSPACE)
     _rejected(L.lm_head_argmax(A, B, C, None, E, 0, 4, 256, None), gq.ERR_WORKSPACE)
+    _rejected(L.lm_head_argmax_timed(A, B, C, D, E, need - 1, 4, 256, None, A, B), gq.ERR_WORKSPACE)
 
 
 def test_aliasing():

@@ -208,6 +208,32 @@ def test_lm_head_argmax_c3_full(dev, c3_full):
     assert idx2 == idx
 
 
+def test_lm_head_argmax_timed(dev, c3_full):
+    """The timed entry point does the same work and records the kernel's own
+    start and end: its result equals lm_head_argmax's, the workspace is left
+    zero, and the elapsed time is positive and no longer than events recorded
+    around the call on the same stream."""
+    W, x, dW, dx = c3_full
+    N, K = synth.C3_LM_HEAD
+    ws = _ws(dev, N, K)
+    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    o0, o1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for e in (k0, k1):
+        e.record()          # creates the HIP handles
+    torch.cuda.synchronize()
+    ref, vref = gq().lm_head_argmax(dW, dx, N, K, ws, want_max=True)
+    o0.record()
+    idx, vmax = gq().lm_head_argmax_timed(dW, dx, N, K, ws, k0, k1, want_max=True)
+    o1.record()
+    torch.cuda.synchronize()
+    assert int(idx.item()) == int(ref.item())
+    assert float(vmax.item()) == float(vref.item())
+    assert int(torch.count_nonzero(ws).item()) == 0
+    t_kernel, t_outer = k0.elapsed_time(k1), o0.elapsed_time(o1)
+    print(f"lm_head kernel {t_kernel * 1e3:.2f} us, events around the call {t_outer * 1e3:.2f} us", flush=True)
+    assert 0.0 < t_kernel <= t_outer * 1.01 + 1e-3
+
+
 @pytest.mark.parametrize("seed", [1, 99, 199])
 def test_lm_head_argmax_c3_full_seeds(dev, seed):
     """Full-size seeds; seeds with s % 100 == 99 copy the max row over a later row."""
