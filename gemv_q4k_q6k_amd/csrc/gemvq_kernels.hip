@@ -482,6 +482,138 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_kernel(GemvArgs a)
     }
 }
 
+// ------------------------------------------------------ wave-unit kernel
+
+// Shapes whose rows fit inside one wave (4*K/256 lanes, a power of two up to
+// 64) run with one workgroup per CU, holding as many waves as the CU can
+// keep resident at this kernel's register use.  The matrix is cut into wave
+// units of 64/lanes_row rows; each workgroup owns a contiguous range of units
+// and its waves take them from an LDS counter.  Waves that the CU issues less
+// often (the arbiter favours older waves) then simply take fewer units, and
+// the CU finishes its range as a whole instead of waiting for its slowest
+// wave or workgroup.  The activation is staged in LDS once per CU.
+constexpr int kWaveMaxThreads = 768;
+
+template <int KIND, int EPI>
+__global__ __launch_bounds__(kWaveMaxThreads) void gemv_wave_kernel(GemvArgs a)
+{
+    constexpr int kPhase = 2;
+    extern __shared__ __align__(16) unsigned char smem[];
+    __shared__ uint32_t s_next;   // next unit to hand out, relative to the range
+    constexpr int BYTES = Traits<KIND>::kBytes;
+    constexpr int OUTS = Traits<KIND>::kOuts;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: unit bases stay scalar
+    const int waves = (int)(blockDim.x >> 6);
+    const int p = (int)__umulhi((uint32_t)lane, a.lanes_row_magic);   // row within the unit
+    const int rr = lane - p * a.lanes_row;
+    const int b = rr >> 2;
+    const int part = rr & 3;
+    const int K = a.nb * kQK;
+
+    // this workgroup's units [u_begin, u_end): a static split of all units
+    const int64_t units = a.tiles;
+    const int u_begin = (int)(units * blockIdx.x / gridDim.x);
+    const int u_end = (int)(units * (blockIdx.x + 1) / gridDim.x);
+    const int last_rows = (int)(a.N - (units - 1) * a.rows_tile);
+    const int64_t unit_stride = (int64_t)a.rows_tile * a.nb * BYTES;
+    const uint32_t lane_off = (uint32_t)((p * a.nb + b) * BYTES);
+
+    auto valid_unit = [&](int u) { return u < u_end && (u < units - 1 || p < last_rows); };
+    // unconditional loads, as in gemv_kernel: a unit past the range re-reads
+    // the unit `prev` this wave has just processed (still in its CU's cache),
+    // an idle lane the unit's first super-block
+    auto fetch = [&](RawSet<KIND> &rs, int u, int prev) {
+        const int uu = u < u_end ? u : prev;
+        const uint32_t off = valid_unit(u) ? lane_off : 0u;
+        const int64_t ub = (int64_t)uu * unit_stride;
+        if constexpr (KIND == kQ6K) {
+            q6k_load(rs.r[0], a.W + ub, off, part);
+        } else {
+            q4k_load(rs.r[0], a.W + ub, off, part);
+            if constexpr (KIND == kSwiglu) q4k_load(rs.r[1], a.W2 + ub, off, part);
+        }
+    };
+
+    // activation loads first, then the first two units of every wave (one or
+    // two 16-byte registers per thread cover x for any workgroup of 4+ waves;
+    // smaller workgroups load the rest below)
+    constexpr int kXRegs = KIND == kQ4KQ8 ? 1 : 2;
+    const int step = KIND == kQ4KQ8 ? 16 : 4;
+    const int esz = KIND == kQ4KQ8 ? 1 : 4;
+    const uint8_t *src = KIND == kQ4KQ8 ? (const uint8_t *)a.xq : (const uint8_t *)a.x;
+    u32x4 xr[kXRegs];
+#pragma unroll
+    for (int r = 0; r < kXRegs; ++r) {
+        const int i = (tid + r * (int)blockDim.x) * step;
+        if (i < K) xr[r] = *(const u32x4 *)(src + (size_t)i * esz);
+    }
+    int unit[kPhase];
+    RawSet<KIND> ring[kPhase];
+#pragma unroll
+    for (int d = 0; d < kPhase; ++d) {
+        unit[d] = u_begin + d * waves + wave;
+        fetch(ring[d], unit[d], u_end - 1);
+    }
+    if (tid == 0) s_next = (uint32_t)(kPhase * waves);
+#pragma unroll
+    for (int r = 0; r < kXRegs; ++r) {
+        const int i = (tid + r * (int)blockDim.x) * step;
+        if (i < K) *(u32x4 *)(smem + lds_pad((uint32_t)(i * esz))) = xr[r];
+    }
+    for (int i = (tid + kXRegs * (int)blockDim.x) * step; i < K; i += (int)blockDim.x * step)
+        *(u32x4 *)(smem + lds_pad((uint32_t)(i * esz))) = *(const u32x4 *)(src + (size_t)i * esz);
+    __syncthreads();
+    XSlice<KIND> xs;
+    if constexpr (KIND == kQ4KQ8) {
+        load_x<true>(xs.v, (const int8_t *)smem, a.xd, b, part);
+        finish_x(xs.v);
+    } else {
+        const float *sx = (const float *)smem;
+        float *ssum = (float *)(smem + lds_pad(4u * (uint32_t)K));
+        for (int g = tid; g < K / 16; g += blockDim.x) ssum[g] = sum16(x_at<true>(sx, 16 * g));
+        __syncthreads();
+        load_x<true>(xs.v, sx, b, part);
+        finish_x(xs.v, (const float *)ssum, b, part);
+    }
+
+    uint64_t best = 0;
+    // keep taking units until both ring slots come back past the range (the
+    // counter only grows, so once one claim is past it every later one is)
+    while (unit[0] < u_end || unit[1] < u_end) {
+#pragma unroll
+        for (int d = 0; d < kPhase; ++d) {
+            if (unit[d] < u_end) {   // wave-uniform
+                float ps[2];
+                dot_raw<KIND>(ring[d], xs, part, ps);
+                const bool v = valid_unit(unit[d]);
+                float r[2];
+#pragma unroll
+                for (int o = 0; o < OUTS; ++o) r[o] = group_sum(v ? ps[o] : 0.f, a.lanes_row);
+                if (rr == 0 && v) emit_row<KIND, EPI>(a, (int64_t)unit[d] * a.rows_tile + p, r, best);
+                uint32_t c = 0;
+                if (lane == 0) c = __hip_atomic_fetch_add(&s_next, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                const int done = unit[d];
+                unit[d] = u_begin + (int)__builtin_amdgcn_readfirstlane(c);
+                fetch(ring[d], unit[d], done);
+            }
+        }
+    }
+
+    if constexpr (EPI == kArgmax) {
+        // each wave's largest key reaches lane 0, then the workgroup's
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)best, off);
+            const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(best >> 32), off);
+            const uint64_t o = ((uint64_t)hi << 32) | lo;
+            best = o > best ? o : best;
+        }
+        argmax_finish(a, best, lane == 0 ? wave : -1, waves);
+    }
+}
+
 // --------------------------------------------------------- Q8 quantize
 
 // One 32-lane half-wave per 32-element block: amax by a lane-max tree (exact,
@@ -542,7 +674,17 @@ Plan make_plan(int64_t N, int64_t K, int kind)
     pl.lanes_row = kParts * pl.nb;
     pl.wave_local = (pl.lanes_row <= 64 && (pl.lanes_row & (pl.lanes_row - 1)) == 0) ? 1 : 0;
     if (pl.wave_local) {
-        pl.waves = 4;
+        // gemv_wave_kernel: units of one wave's rows; the launch decides how
+        // many waves a workgroup gets (at most kWaveMaxThreads / 64)
+        pl.waves = kWaveMaxThreads / 64;
+        pl.threads = pl.waves * 64;
+        pl.rows_tile = 64 / pl.lanes_row;
+        pl.tiles = (N + pl.rows_tile - 1) / pl.rows_tile;
+        const size_t xb = (kind == kQ4KQ8) ? (size_t)K : (size_t)K * 4;
+        pl.x_in_lds = 1;
+        pl.lds_bytes = xb + xb / 16 + ((kind == kQ4KQ8) ? 0 : (size_t)(K / 16) * 4);
+        pl.grid = 0;
+        return pl;
     } else {
         // 1, 2, 4 or 8 waves (a workgroup of another size leaves SIMDs unevenly
         // loaded and fewer workgroups fit on a CU); fewest idle lanes, ties to
@@ -651,12 +793,50 @@ static hipError_t launch_mode(Plan &pl, GemvArgs a, int cus, hipStream_t s, cons
     return hipGetLastError();
 }
 
+// Waves of gemv_wave_kernel<KIND, EPI> one workgroup can have while one such
+// workgroup still fits on a CU (registers, LDS), cached per LDS size.
+static int wave_kernel_waves(const void *fn, size_t lds)
+{
+    struct Entry { const void *fn; size_t lds; int waves; };
+    static std::mutex mu;
+    static Entry cache[32];
+    static int n = 0;
+    {
+        std::lock_guard<std::mutex> g(mu);
+        for (int i = 0; i < n; ++i)
+            if (cache[i].fn == fn && cache[i].lds == lds) return cache[i].waves;
+    }
+    int waves = 1;
+    for (int w = kWaveMaxThreads / 64; w >= 1; --w) {
+        int occ = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, 64 * w, lds) == hipSuccess && occ >= 1) {
+            waves = w;
+            break;
+        }
+    }
+    std::lock_guard<std::mutex> g(mu);
+    if (n < 32) cache[n++] = Entry{fn, lds, waves};
+    return waves;
+}
+
+template <int KIND, int EPI>
+static hipError_t launch_wave(Plan &pl, const GemvArgs &a, int cus, hipStream_t s, const Timing &tm)
+{
+    const void *fn = (const void *)gemv_wave_kernel<KIND, EPI>;
+    const int wmax = wave_kernel_waves(fn, pl.lds_bytes);
+    const int64_t grid = pl.tiles < cus ? pl.tiles : cus;
+    const int64_t per = (pl.tiles + grid - 1) / grid;   // units per workgroup
+    pl.grid = (int)grid;
+    pl.waves = (int)(per < wmax ? per : wmax);
+    pl.threads = 64 * pl.waves;
+    launch_on(gemv_wave_kernel<KIND, EPI>, pl, a, s, tm);
+    return hipGetLastError();
+}
+
 template <int KIND, int EPI>
 static hipError_t launch(Plan &pl, const GemvArgs &a, int cus, hipStream_t s, const Timing &tm = Timing{})
 {
-    if (pl.wave_local)
-        return pl.x_in_lds ? launch_mode<KIND, EPI, true, true>(pl, a, cus, s, tm)
-                           : launch_mode<KIND, EPI, true, false>(pl, a, cus, s, tm);
+    if (pl.wave_local) return launch_wave<KIND, EPI>(pl, a, cus, s, tm);
     return pl.x_in_lds ? launch_mode<KIND, EPI, false, true>(pl, a, cus, s, tm)
                        : launch_mode<KIND, EPI, false, false>(pl, a, cus, s, tm);
 }

@@ -17,7 +17,9 @@ W_BASE = 1 << 20          # any dword-aligned matrix address
 
 
 def lane_table(geo, nb):
-    tid = np.arange(64 * geo["waves"])
+    # rows that fit in a wave are processed in units of one wave's rows;
+    # otherwise a tile spans the workgroup's waves
+    tid = np.arange(64 if geo["wave_local"] else 64 * geo["waves"])
     lr = 4 * nb
     p = tid // lr
     rr = tid - p * lr
