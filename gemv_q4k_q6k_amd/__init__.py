@@ -94,10 +94,10 @@ KIND_Q4K, KIND_Q6K, KIND_Q4K_Q8, KIND_SWIGLU = range(4)
 
 def tile_geometry(kind: int, N: int, K: int) -> dict:
     """Launch geometry the library uses for an N x K matrix (host-only)."""
-    out = (ctypes.c_int64 * 6)()
+    out = (ctypes.c_int64 * 7)()
     _check("gemvq_tile_geometry", lib().gemvq_tile_geometry(kind, N, K, ctypes.cast(out, ctypes.c_void_p)))
     return {"waves": out[0], "rows_tile": out[1], "tiles": out[2], "wave_local": out[3],
-            "x_in_lds": out[4], "lds_bytes": out[5]}
+            "x_in_lds": out[4], "lds_bytes": out[5], "steps": out[6]}
 
 
 def strerror(status: int) -> str:

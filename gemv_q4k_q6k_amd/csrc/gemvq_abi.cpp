@@ -86,7 +86,7 @@ size_t gemvq_lm_head_argmax_ws_bytes(int64_t N, int64_t K)
     return gemvq::kArgmaxWsBytes;
 }
 
-int gemvq_tile_geometry(int kind, int64_t N, int64_t K, int64_t out[6])
+int gemvq_tile_geometry(int kind, int64_t N, int64_t K, int64_t out[7])
 {
     if (!out) return GEMVQ_ERR_NULL;
     if (kind < 0 || kind > 3) return GEMVQ_ERR_SHAPE;
@@ -99,6 +99,7 @@ int gemvq_tile_geometry(int kind, int64_t N, int64_t K, int64_t out[6])
     out[3] = pl.wave_local;
     out[4] = pl.x_in_lds;
     out[5] = (int64_t)pl.lds_bytes;
+    out[6] = pl.wave_local ? pl.steps : 1;
     return GEMVQ_OK;
 }
 

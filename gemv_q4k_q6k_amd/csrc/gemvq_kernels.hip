@@ -39,7 +39,7 @@ struct GemvArgs {
     int tiles;             // ceil(N / rows_tile)
     int tiles_q, tiles_r;  // tiles per workgroup: tiles_q, plus one for the first tiles_r workgroups
     int nb;                // super-blocks per row
-    int lanes_row;         // 4 * nb
+    int lanes_row;         // lanes per row: 4 * nb (64 for the two-step wave kernel)
     uint32_t lanes_row_magic;  // ceil(2^32 / lanes_row): tid / lanes_row == umulhi(tid, magic) for tid < 1024
     int rows_tile;         // rows per tile (P)
     int x_in_lds;          // stage the activation (and its 16-element sums) through LDS first
@@ -297,15 +297,14 @@ __device__ void argmax_finish(const GemvArgs &a, uint64_t best, int holder, int 
 
 // ------------------------------------------------------------------ kernel
 
-// WAVE_LOCAL: a row's 4*(K/256) lanes are an aligned power-of-two group inside
-// one wave (K/256 in {1,2,4,8,16}), so rows reduce with DPP only; otherwise
-// each super-block's quad sum goes through LDS and one thread per row adds the
-// K/256 block sums in order.
+// Tile kernel, for rows that do not fit an aligned power-of-two lane group of
+// one wave: a tile of rows spans the workgroup, each super-block's quad sum
+// goes through LDS and one thread per row adds the K/256 block sums in order.
 // PHASE: tiles in flight per lane (software pipeline depth); 1 for grids in
 // which workgroups own a single tile.  XLDS: the activation (and its
 // 16-element sums) is staged through LDS because several rows of a tile
 // share it; otherwise each lane reads its own slice.
-template <int KIND, int EPI, bool WAVE_LOCAL, int PHASE, bool XLDS>
+template <int KIND, int EPI, int PHASE, bool XLDS>
 __global__ __launch_bounds__(kMaxThreads) void gemv_kernel(GemvArgs a)
 {
     constexpr int kPhase = PHASE;
@@ -424,12 +423,7 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_kernel(GemvArgs a)
         const bool v = valid_tile(t);
 #pragma unroll
         for (int o = 0; o < OUTS; ++o) ps[o] = v ? ps[o] : 0.f;
-        if constexpr (WAVE_LOCAL) {
-            float r[2];
-#pragma unroll
-            for (int o = 0; o < OUTS; ++o) r[o] = group_sum(ps[o], a.lanes_row);
-            if (rr == 0 && v) emit_row<KIND, EPI>(a, (int64_t)t * a.rows_tile + p, r, best);
-        } else {
+        {
             float *rb = red + buf * red_stride;
 #pragma unroll
             for (int o = 0; o < OUTS; ++o) {
@@ -474,28 +468,32 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_kernel(GemvArgs a)
     }
 
     if constexpr (EPI == kArgmax) {
-        // row leaders (wave-local) or row-sum threads (LDS reduction) hold keys
-        if constexpr (WAVE_LOCAL)
-            argmax_finish(a, best, (rr == 0 && lane_on) ? p : -1, a.rows_tile);
-        else
-            argmax_finish(a, best, tid < a.rows_tile ? tid : -1, a.rows_tile);
+        // the row-sum threads hold the keys
+        argmax_finish(a, best, tid < a.rows_tile ? tid : -1, a.rows_tile);
     }
 }
 
 // ------------------------------------------------------ wave-unit kernel
 
-// Shapes whose rows fit inside one wave (4*K/256 lanes, a power of two up to
-// 64) run with one workgroup per CU, holding as many waves as the CU can
-// keep resident at this kernel's register use.  The matrix is cut into wave
-// units of 64/lanes_row rows; each workgroup owns a contiguous range of units
-// and its waves take them from an LDS counter.  Waves that the CU issues less
-// often (the arbiter favours older waves) then simply take fewer units, and
-// the CU finishes its range as a whole instead of waiting for its slowest
-// wave or workgroup.  The activation is staged in LDS once per CU.
-constexpr int kWaveMaxThreads = 768;
+// Shapes whose rows fit one wave run with one workgroup per CU, holding as
+// many waves as the CU can keep resident at this kernel's register use.  A
+// row fits one wave when its 4*K/256 lanes are a power of two up to 64
+// (STEPS = 1: a wave unit is 64/lanes_row rows), or when it is 32 super-blocks
+// wide (STEPS = 2: a unit is one row, and every lane takes one quarter
+// super-block in each half of the row).  The matrix is cut into units; each
+// workgroup owns a contiguous range of them and its waves take them from an
+// LDS counter.  Waves that the CU issues less often (the arbiter favours older
+// waves) then simply take fewer units, and the CU finishes its range as a
+// whole instead of waiting for its slowest wave or workgroup.  The activation
+// is staged in LDS once per CU.  A row's value is reduced the same way
+// wherever it sits (fixed lane layout, halves added in order), so equal rows
+// give equal bits.
+template <int KIND>
+constexpr int wave_max_threads() { return KIND == kQ4KQ8 ? 1024 : 768; }
+constexpr int kWaveMaxThreads = 1024;   // the largest of wave_max_threads
 
-template <int KIND, int EPI>
-__global__ __launch_bounds__(kWaveMaxThreads) void gemv_wave_kernel(GemvArgs a)
+template <int KIND, int EPI, int STEPS>
+__global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_wave_kernel(GemvArgs a)
 {
     constexpr int kPhase = 2;
     extern __shared__ __align__(16) unsigned char smem[];
@@ -506,7 +504,9 @@ __global__ __launch_bounds__(kWaveMaxThreads) void gemv_wave_kernel(GemvArgs a)
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: unit bases stay scalar
     const int waves = (int)(blockDim.x >> 6);
-    const int p = (int)__umulhi((uint32_t)lane, a.lanes_row_magic);   // row within the unit
+    // STEPS == 1: a.lanes_row lanes per row, rows side by side; STEPS == 2:
+    // one row, lanes_row == 64, block b + 16*s in step s
+    const int p = STEPS == 1 ? (int)__umulhi((uint32_t)lane, a.lanes_row_magic) : 0;   // row within the unit
     const int rr = lane - p * a.lanes_row;
     const int b = rr >> 2;
     const int part = rr & 3;
@@ -518,26 +518,29 @@ __global__ __launch_bounds__(kWaveMaxThreads) void gemv_wave_kernel(GemvArgs a)
     const int u_end = (int)(units * (blockIdx.x + 1) / gridDim.x);
     const int last_rows = (int)(a.N - (units - 1) * a.rows_tile);
     const int64_t unit_stride = (int64_t)a.rows_tile * a.nb * BYTES;
-    const uint32_t lane_off = (uint32_t)((p * a.nb + b) * BYTES);
 
     auto valid_unit = [&](int u) { return u < u_end && (u < units - 1 || p < last_rows); };
     // unconditional loads, as in gemv_kernel: a unit past the range re-reads
     // the unit `prev` this wave has just processed (still in its CU's cache),
     // an idle lane the unit's first super-block
-    auto fetch = [&](RawSet<KIND> &rs, int u, int prev) {
+    auto fetch = [&](RawSet<KIND> (&rs)[STEPS], int u, int prev) {
         const int uu = u < u_end ? u : prev;
-        const uint32_t off = valid_unit(u) ? lane_off : 0u;
+        const bool v = valid_unit(u);
         const int64_t ub = (int64_t)uu * unit_stride;
-        if constexpr (KIND == kQ6K) {
-            q6k_load(rs.r[0], a.W + ub, off, part);
-        } else {
-            q4k_load(rs.r[0], a.W + ub, off, part);
-            if constexpr (KIND == kSwiglu) q4k_load(rs.r[1], a.W2 + ub, off, part);
+#pragma unroll
+        for (int st = 0; st < STEPS; ++st) {
+            const uint32_t off = v ? (uint32_t)((p * a.nb + b + 16 * st) * BYTES) : 0u;
+            if constexpr (KIND == kQ6K) {
+                q6k_load(rs[st].r[0], a.W + ub, off, part);
+            } else {
+                q4k_load(rs[st].r[0], a.W + ub, off, part);
+                if constexpr (KIND == kSwiglu) q4k_load(rs[st].r[1], a.W2 + ub, off, part);
+            }
         }
     };
 
-    // activation loads first, then the first two units of every wave (one or
-    // two 16-byte registers per thread cover x for any workgroup of 4+ waves;
+    // activation loads first, then the first two units of every wave (a
+    // register or two per thread cover x for any workgroup of 4+ waves;
     // smaller workgroups load the rest below)
     constexpr int kXRegs = KIND == kQ4KQ8 ? 1 : 2;
     const int step = KIND == kQ4KQ8 ? 16 : 4;
@@ -550,7 +553,7 @@ __global__ __launch_bounds__(kWaveMaxThreads) void gemv_wave_kernel(GemvArgs a)
         if (i < K) xr[r] = *(const u32x4 *)(src + (size_t)i * esz);
     }
     int unit[kPhase];
-    RawSet<KIND> ring[kPhase];
+    RawSet<KIND> ring[kPhase][STEPS];
 #pragma unroll
     for (int d = 0; d < kPhase; ++d) {
         unit[d] = u_begin + d * waves + wave;
@@ -565,17 +568,23 @@ __global__ __launch_bounds__(kWaveMaxThreads) void gemv_wave_kernel(GemvArgs a)
     for (int i = (tid + kXRegs * (int)blockDim.x) * step; i < K; i += (int)blockDim.x * step)
         *(u32x4 *)(smem + lds_pad((uint32_t)(i * esz))) = *(const u32x4 *)(src + (size_t)i * esz);
     __syncthreads();
-    XSlice<KIND> xs;
+    XSlice<KIND> xs[STEPS];
     if constexpr (KIND == kQ4KQ8) {
-        load_x<true>(xs.v, (const int8_t *)smem, a.xd, b, part);
-        finish_x(xs.v);
+#pragma unroll
+        for (int st = 0; st < STEPS; ++st) {
+            load_x<true>(xs[st].v, (const int8_t *)smem, a.xd, b + 16 * st, part);
+            finish_x(xs[st].v);
+        }
     } else {
         const float *sx = (const float *)smem;
         float *ssum = (float *)(smem + lds_pad(4u * (uint32_t)K));
         for (int g = tid; g < K / 16; g += blockDim.x) ssum[g] = sum16(x_at<true>(sx, 16 * g));
         __syncthreads();
-        load_x<true>(xs.v, sx, b, part);
-        finish_x(xs.v, (const float *)ssum, b, part);
+#pragma unroll
+        for (int st = 0; st < STEPS; ++st) {
+            load_x<true>(xs[st].v, sx, b + 16 * st, part);
+            finish_x(xs[st].v, (const float *)ssum, b + 16 * st, part);
+        }
     }
 
     uint64_t best = 0;
@@ -585,8 +594,14 @@ __global__ __launch_bounds__(kWaveMaxThreads) void gemv_wave_kernel(GemvArgs a)
 #pragma unroll
         for (int d = 0; d < kPhase; ++d) {
             if (unit[d] < u_end) {   // wave-uniform
-                float ps[2];
-                dot_raw<KIND>(ring[d], xs, part, ps);
+                float ps[2] = {0.f, 0.f};
+#pragma unroll
+                for (int st = 0; st < STEPS; ++st) {
+                    float q[2];
+                    dot_raw<KIND>(ring[d][st], xs[st], part, q);
+#pragma unroll
+                    for (int o = 0; o < OUTS; ++o) ps[o] = st == 0 ? q[o] : ps[o] + q[o];
+                }
                 const bool v = valid_unit(unit[d]);
                 float r[2];
 #pragma unroll
@@ -672,11 +687,17 @@ Plan make_plan(int64_t N, int64_t K, int kind)
     Plan pl{};
     pl.nb = (int)(K / kQK);
     pl.lanes_row = kParts * pl.nb;
-    pl.wave_local = (pl.lanes_row <= 64 && (pl.lanes_row & (pl.lanes_row - 1)) == 0) ? 1 : 0;
+    const bool fits = pl.lanes_row <= 64 && (pl.lanes_row & (pl.lanes_row - 1)) == 0;
+    // two halves need the x slices of both in registers: only the int8 path
+    // has room for them without spilling
+    const bool halves = pl.nb == 32 && kind == kQ4KQ8;
+    pl.wave_local = (fits || halves) ? 1 : 0;
+    pl.steps = halves ? 2 : 1;
     if (pl.wave_local) {
         // gemv_wave_kernel: units of one wave's rows; the launch decides how
-        // many waves a workgroup gets (at most kWaveMaxThreads / 64)
-        pl.waves = kWaveMaxThreads / 64;
+        // many waves a workgroup gets
+        if (halves) pl.lanes_row = 64;   // lanes per row in each half
+        pl.waves = (kind == kQ4KQ8 ? 1024 : 768) / 64;
         pl.threads = pl.waves * 64;
         pl.rows_tile = 64 / pl.lanes_row;
         pl.tiles = (N + pl.rows_tile - 1) / pl.rows_tile;
@@ -685,23 +706,22 @@ Plan make_plan(int64_t N, int64_t K, int kind)
         pl.lds_bytes = xb + xb / 16 + ((kind == kQ4KQ8) ? 0 : (size_t)(K / 16) * 4);
         pl.grid = 0;
         return pl;
-    } else {
-        // 1, 2, 4 or 8 waves (a workgroup of another size leaves SIMDs unevenly
-        // loaded and fewer workgroups fit on a CU); fewest idle lanes, ties to
-        // fewer waves; at least one row per tile
-        int best_w = 0;
-        double best_u = -1.0;
-        for (int w = 1; w <= kMaxThreads / 64; w *= 2) {
-            const int rows = 64 * w / pl.lanes_row;
-            if (rows < 1) continue;
-            const double util = (double)(rows * pl.lanes_row) / (64.0 * w);
-            if (util > best_u + 1e-9) {
-                best_u = util;
-                best_w = w;
-            }
-        }
-        pl.waves = best_w;
     }
+    // tile kernel: 1, 2, 4 or 8 waves (a workgroup of another size leaves SIMDs
+    // unevenly loaded and fewer workgroups fit on a CU); fewest idle lanes,
+    // ties to fewer waves; at least one row per tile
+    int best_w = 0;
+    double best_u = -1.0;
+    for (int w = 1; w <= kMaxThreads / 64; w *= 2) {
+        const int rows = 64 * w / pl.lanes_row;
+        if (rows < 1) continue;
+        const double util = (double)(rows * pl.lanes_row) / (64.0 * w);
+        if (util > best_u + 1e-9) {
+            best_u = util;
+            best_w = w;
+        }
+    }
+    pl.waves = best_w;
     pl.threads = 64 * pl.waves;
     pl.rows_tile = pl.threads / pl.lanes_row;
     pl.tiles = (N + pl.rows_tile - 1) / pl.rows_tile;
@@ -712,7 +732,7 @@ Plan make_plan(int64_t N, int64_t K, int kind)
     const size_t sums = (kind == kQ4KQ8) ? 0 : (size_t)(K / 16) * 4;
     const size_t xpadded = xbytes + xbytes / 16;   // 16 bytes of padding per 256 (lds_pad)
     pl.x_in_lds = (pl.rows_tile > 1 && xpadded + sums <= 65536) ? 1 : 0;
-    const size_t red = pl.wave_local ? 0 : (size_t)2 * outs * pl.rows_tile * pl.nb * 4;   // two buffers
+    const size_t red = (size_t)2 * outs * pl.rows_tile * pl.nb * 4;   // two buffers
     pl.lds_bytes = (pl.x_in_lds ? xpadded + sums : 0);
     if (red > pl.lds_bytes) pl.lds_bytes = red;
     pl.grid = 0;   // set by the launcher from the occupancy
@@ -777,25 +797,25 @@ static void launch_on(Kern k, const Plan &pl, const GemvArgs &a, hipStream_t s, 
         hipLaunchKernelGGL(k, dim3(pl.grid), dim3(pl.threads), pl.lds_bytes, s, a);
 }
 
-template <int KIND, int EPI, bool WL, bool XLDS>
+template <int KIND, int EPI, bool XLDS>
 static hipError_t launch_mode(Plan &pl, GemvArgs a, int cus, hipStream_t s, const Timing &tm)
 {
     // the occupancy of the deeper-pipelined kernel sizes the grid; if that
     // leaves at most one tile per workgroup the single-tile kernel runs
-    const void *fn2 = (const void *)gemv_kernel<KIND, EPI, WL, 2, XLDS>;
+    const void *fn2 = (const void *)gemv_kernel<KIND, EPI, 2, XLDS>;
     pl.grid = grid_for(pl, fn2, cus, KIND == kSwiglu ? 2 : 4);
     a.tiles_q = (int)(pl.tiles / pl.grid);
     a.tiles_r = (int)(pl.tiles % pl.grid);
     if (a.tiles_q >= 2 || (a.tiles_q == 1 && a.tiles_r > 0))
-        launch_on(gemv_kernel<KIND, EPI, WL, 2, XLDS>, pl, a, s, tm);
+        launch_on(gemv_kernel<KIND, EPI, 2, XLDS>, pl, a, s, tm);
     else
-        launch_on(gemv_kernel<KIND, EPI, WL, 1, XLDS>, pl, a, s, tm);
+        launch_on(gemv_kernel<KIND, EPI, 1, XLDS>, pl, a, s, tm);
     return hipGetLastError();
 }
 
 // Waves of gemv_wave_kernel<KIND, EPI> one workgroup can have while one such
 // workgroup still fits on a CU (registers, LDS), cached per LDS size.
-static int wave_kernel_waves(const void *fn, size_t lds)
+static int wave_kernel_waves(const void *fn, size_t lds, int max_waves)
 {
     struct Entry { const void *fn; size_t lds; int waves; };
     static std::mutex mu;
@@ -807,7 +827,7 @@ static int wave_kernel_waves(const void *fn, size_t lds)
             if (cache[i].fn == fn && cache[i].lds == lds) return cache[i].waves;
     }
     int waves = 1;
-    for (int w = kWaveMaxThreads / 64; w >= 1; --w) {
+    for (int w = max_waves; w >= 1; --w) {
         int occ = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, 64 * w, lds) == hipSuccess && occ >= 1) {
             waves = w;
@@ -819,26 +839,29 @@ static int wave_kernel_waves(const void *fn, size_t lds)
     return waves;
 }
 
-template <int KIND, int EPI>
+template <int KIND, int EPI, int STEPS>
 static hipError_t launch_wave(Plan &pl, const GemvArgs &a, int cus, hipStream_t s, const Timing &tm)
 {
-    const void *fn = (const void *)gemv_wave_kernel<KIND, EPI>;
-    const int wmax = wave_kernel_waves(fn, pl.lds_bytes);
+    const void *fn = (const void *)gemv_wave_kernel<KIND, EPI, STEPS>;
+    const int wmax = wave_kernel_waves(fn, pl.lds_bytes, wave_max_threads<KIND>() / 64);
     const int64_t grid = pl.tiles < cus ? pl.tiles : cus;
     const int64_t per = (pl.tiles + grid - 1) / grid;   // units per workgroup
     pl.grid = (int)grid;
     pl.waves = (int)(per < wmax ? per : wmax);
     pl.threads = 64 * pl.waves;
-    launch_on(gemv_wave_kernel<KIND, EPI>, pl, a, s, tm);
+    launch_on(gemv_wave_kernel<KIND, EPI, STEPS>, pl, a, s, tm);
     return hipGetLastError();
 }
 
 template <int KIND, int EPI>
 static hipError_t launch(Plan &pl, const GemvArgs &a, int cus, hipStream_t s, const Timing &tm = Timing{})
 {
-    if (pl.wave_local) return launch_wave<KIND, EPI>(pl, a, cus, s, tm);
-    return pl.x_in_lds ? launch_mode<KIND, EPI, false, true>(pl, a, cus, s, tm)
-                       : launch_mode<KIND, EPI, false, false>(pl, a, cus, s, tm);
+    if (pl.wave_local) {
+        if constexpr (KIND == kQ4KQ8)
+            if (pl.steps == 2) return launch_wave<KIND, EPI, 2>(pl, a, cus, s, tm);
+        return launch_wave<KIND, EPI, 1>(pl, a, cus, s, tm);
+    }
+    return pl.x_in_lds ? launch_mode<KIND, EPI, true>(pl, a, cus, s, tm) : launch_mode<KIND, EPI, false>(pl, a, cus, s, tm);
 }
 
 hipError_t launch_q4k_gemv(const void *W, const float *x, float *y, int64_t N, int64_t K, int cus, hipStream_t s)

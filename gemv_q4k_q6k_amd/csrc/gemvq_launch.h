@@ -22,7 +22,8 @@ constexpr size_t kArgmaxWsBytes = 256;
 struct Plan {
     int nb;          // super-blocks per row
     int lanes_row;   // lanes per row (4 per super-block)
-    int wave_local;  // rows reduce inside one wave
+    int wave_local;  // rows reduce inside one wave (gemv_wave_kernel)
+    int steps;       // wave kernel: 1, or 2 when a row is two 16-super-block halves
     int waves;       // waves per workgroup
     int threads;     // 64 * waves
     int rows_tile;   // rows per tile

@@ -154,13 +154,16 @@ int gemvq_q4k_q8_isums(const void *W, const int8_t *xq, int32_t *isums,
  * lm_head_argmax), 2 = Q4_K x Q8 (q4k_q8_gemv), 3 = SwiGLU (swiglu_gemv).
  * out[0] = waves per workgroup, out[1] = rows per tile, out[2] = tiles,
  * out[3] = 1 if a row's partial sums reduce inside one wave, out[4] = 1 if the
- * activation is staged through LDS, out[5] = dynamic LDS bytes.  When out[3]
- * is 1 a tile is one wave's rows (64 / (4*K/256) rows), taken by the waves of
+ * activation is staged through LDS, out[5] = dynamic LDS bytes, out[6] =
+ * steps.  When out[3] is 1 a tile is one wave's rows, taken by the waves of
  * one workgroup per CU, and out[0] is the most waves such a workgroup has (the
- * launch uses as many as fit on a CU).
+ * launch uses as many as fit on a CU): with out[6] = 1 a tile is
+ * 64 / (4*K/256) rows side by side; with out[6] = 2 (Q4_K x Q8 at
+ * K = 8192) it is one row whose lane l takes quarter l%4 of super-blocks
+ * l/4 and 16 + l/4.
  * Returns GEMVQ_ERR_SHAPE for shapes the GEMV entry points reject.
  */
-int gemvq_tile_geometry(int kind, int64_t N, int64_t K, int64_t out[6]);
+int gemvq_tile_geometry(int kind, int64_t N, int64_t K, int64_t out[7]);
 
 /* Static description of a status code (never NULL). */
 const char *gemvq_strerror(int status);

@@ -65,17 +65,24 @@ def q4k_windows(kind, N, K):
     P, tiles = geo["rows_tile"], geo["tiles"]
     stride = P * nb * 144
     last_rows = N - (tiles - 1) * P
-    p, b, c, on = lane_table(geo, nb)
-    lane_off = (p * nb + b) * 144
+    if geo["steps"] == 2:
+        # one row per tile; lane l takes block l//4, then block 16 + l//4
+        lanes = np.arange(64)
+        p, b, c, on = np.zeros(64, int), lanes >> 2, lanes & 3, np.ones(64, bool)
+        steps = [0, 16]
+    else:
+        p, b, c, on = lane_table(geo, nb)
+        steps = [0]
     lo, hi = None, None
     for t in range(tiles):
         tile = W_BASE + t * stride
         valid = on & ((t < tiles - 1) | (p < last_rows))
-        off = np.where(valid, lane_off, 0)
-        l_ = tile + off.min()
-        h_ = tile + max((off + 16).max(), (off + 32 * c + 48).max())
-        lo = l_ if lo is None else min(lo, l_)
-        hi = h_ if hi is None else max(hi, h_)
+        for s16 in steps:
+            off = np.where(valid, (p * nb + b + s16) * 144, 0)
+            l_ = tile + off.min()
+            h_ = tile + max((off + 16).max(), (off + 32 * c + 48).max())
+            lo = l_ if lo is None else min(lo, l_)
+            hi = h_ if hi is None else max(hi, h_)
     return lo, hi, W_BASE + N * nb * 144
 
 
@@ -98,7 +105,7 @@ def test_q6k_loads_in_bounds_large(N, K):
 
 
 @pytest.mark.parametrize("kind", [gq.KIND_Q4K, gq.KIND_Q4K_Q8, gq.KIND_SWIGLU])
-@pytest.mark.parametrize("N,K", [(1, 256), (5, 768), (100, 2560), (257, 9728), (77, 8192), (3, 32768)])
+@pytest.mark.parametrize("N,K", [(1, 256), (5, 768), (100, 2560), (257, 9728), (77, 8192), (1, 8192), (3, 32768)])
 def test_q4k_loads_in_bounds(kind, N, K):
     lo, hi, end = q4k_windows(kind, N, K)
     assert W_BASE <= lo and hi <= end
@@ -109,3 +116,13 @@ def test_geometry_rejects_bad_shapes():
         gq.tile_geometry(gq.KIND_Q6K, 0, 1024)
     with pytest.raises(gq.GemvqError):
         gq.tile_geometry(gq.KIND_Q4K, 10, 300)
+
+
+def test_two_step_rows_cover_every_block_once():
+    """In a two-step (K = 8192) row every (super-block, quarter) pair is taken
+    by exactly one lane and step."""
+    geo = gq.tile_geometry(gq.KIND_Q4K_Q8, 28_672, 8192)
+    assert geo["wave_local"] == 1 and geo["steps"] == 2 and geo["rows_tile"] == 1 and geo["tiles"] == 28_672
+    lanes = np.arange(64)
+    pairs = {(int(b) + s16, int(c)) for s16 in (0, 16) for b, c in zip(lanes >> 2, lanes & 3)}
+    assert pairs == {(b, c) for b in range(32) for c in range(4)}
