@@ -25,6 +25,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -328,7 +329,7 @@ def write_traffic(fetch_db, write_db, command):
     scaled by what the same counters read for the calibration copy, and store
     them next to the kernel-source hash they were taken on."""
     known = CALIB_MIB << 20
-    is_lm = lambda k: "gemv_kernel<1, 1," in k         # KIND = Q6_K, epilogue = argmax
+    is_lm = lambda k: re.search(r"gemv_(wave_)?kernel<1, 1,", k) is not None   # Q6_K rows, argmax epilogue
     is_cal = lambda k: CALIB_TAG in k
     fm, wm = _counter_means(fetch_db, "FETCH_SIZE"), _counter_means(write_db, "WRITE_SIZE")
     lm_name, (lm_f, n_f) = _pick(fm, is_lm, "lm_head")

@@ -29,7 +29,7 @@ def _db(path, counter, rows):
     c.close()
 
 
-LM = "void gemvq::gemv_kernel<1, 1, true, 2, true>(gemvq::GemvArgs)"
+LM = "void gemvq::gemv_wave_kernel<1, 1, 1>(gemvq::GemvArgs)"
 CAL = "void at::native::vectorized_elementwise_kernel<4, at::native::neg_kernel_cuda(...)>"
 OTHER = "void gemvq::gemv_kernel<1, 0, true, 2, true>(gemvq::GemvArgs)"
 
