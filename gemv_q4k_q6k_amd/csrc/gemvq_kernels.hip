@@ -43,6 +43,7 @@ struct GemvArgs {
     uint32_t lanes_row_magic;  // ceil(2^32 / lanes_row): tid / lanes_row == umulhi(tid, magic) for tid < 1024
     int rows_tile;         // rows per tile (P)
     int x_in_lds;          // stage the activation (and its 16-element sums) through LDS first
+    int steps;             // row-stream kernel: 16-super-block steps per row
 };
 
 // ------------------------------------------------------- activation setup
@@ -489,7 +490,7 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_kernel(GemvArgs a)
 // wherever it sits (fixed lane layout, halves added in order), so equal rows
 // give equal bits.
 template <int KIND>
-constexpr int wave_max_threads() { return KIND == kQ4KQ8 ? 1024 : 768; }
+constexpr int wave_max_threads() { return (KIND == kQ4KQ8 || KIND == kQ4K) ? 1024 : 768; }
 constexpr int kWaveMaxThreads = 1024;   // the largest of wave_max_threads
 
 template <int KIND, int EPI, int STEPS>
@@ -629,6 +630,183 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_wave_kernel(Gem
     }
 }
 
+// ---------------------------------------------------- row-stream kernel
+
+// Every other shape (K/256 not a power of two up to 16, or more than 16
+// super-blocks): a wave takes whole rows and walks each one in steps of 16
+// super-blocks, lane l taking quarter l%4 of super-block l/4 of the step
+// (lanes past the row's last super-block idle).  Rows of up to 16 super-blocks
+// are one step; a power-of-two group of lanes holds each, so a wave unit is
+// 64/group rows.  Longer rows are one row per unit and S = ceil(K/4096) steps.
+// As in the wave-unit kernel there is one workgroup per CU, its waves take
+// units from an LDS counter, and the activation is staged in LDS once; the
+// slice of a step is re-read from LDS when a row has several steps.  Each wave
+// runs a pipeline of (unit, step) pairs, two in flight; a row's step sums are
+// added in step order and reduced over its lane group, the same way for every
+// row.
+template <int KIND, int EPI>
+__global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_rows_kernel(GemvArgs a)
+{
+    constexpr int kPhase = 2;
+    extern __shared__ __align__(16) unsigned char smem[];
+    __shared__ uint32_t s_next;   // next unit to hand out, relative to the range
+    constexpr int BYTES = Traits<KIND>::kBytes;
+    constexpr int OUTS = Traits<KIND>::kOuts;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int waves = (int)(blockDim.x >> 6);
+    const int group = a.lanes_row;                                      // lanes per row (power of two)
+    const int p = (int)__umulhi((uint32_t)lane, a.lanes_row_magic);    // row within the unit
+    const int rr = lane - p * group;
+    const int b = rr >> 2;
+    const int part = rr & 3;
+    const int K = a.nb * kQK;
+    const int S = a.steps;
+
+    const int64_t units = a.tiles;
+    const int u_begin = (int)(units * blockIdx.x / gridDim.x);
+    const int u_end = (int)(units * (blockIdx.x + 1) / gridDim.x);
+    const int last_rows = (int)(a.N - (units - 1) * a.rows_tile);
+    const int64_t unit_stride = (int64_t)a.rows_tile * a.nb * BYTES;
+
+    // super-block of this lane in step s, or -1 past the row's end
+    auto block_of = [&](int st) { const int c = b + 16 * st; return c < a.nb ? c : -1; };
+    auto valid_row = [&](int u) { return u < u_end && (u < units - 1 || p < last_rows); };
+    // unconditional loads: past the range the unit `prev` is re-read (still
+    // cached), an idle lane reads the unit's first super-block
+    auto fetch = [&](RawSet<KIND> &rs, int u, int st, int prev) {
+        const int uu = u < u_end ? u : prev;
+        const int c = block_of(st);
+        const uint32_t off = (valid_row(u) && c >= 0) ? (uint32_t)((p * a.nb + c) * BYTES) : 0u;
+        const int64_t ub = (int64_t)uu * unit_stride;
+        if constexpr (KIND == kQ6K) {
+            q6k_load(rs.r[0], a.W + ub, off, part);
+        } else {
+            q4k_load(rs.r[0], a.W + ub, off, part);
+            if constexpr (KIND == kSwiglu) q4k_load(rs.r[1], a.W2 + ub, off, part);
+        }
+    };
+
+    // activation loads first
+    constexpr int kXRegs = KIND == kQ4KQ8 ? 1 : 2;
+    const int xstep = KIND == kQ4KQ8 ? 16 : 4;
+    const int esz = KIND == kQ4KQ8 ? 1 : 4;
+    const uint8_t *src = KIND == kQ4KQ8 ? (const uint8_t *)a.xq : (const uint8_t *)a.x;
+    u32x4 xr[kXRegs];
+#pragma unroll
+    for (int r = 0; r < kXRegs; ++r) {
+        const int i = (tid + r * (int)blockDim.x) * xstep;
+        if (i < K) xr[r] = *(const u32x4 *)(src + (size_t)i * esz);
+    }
+
+    // the fetch cursor walks (unit, step) pairs: the first two units of the
+    // wave are fixed, later ones come from the counter when their first step
+    // is fetched
+    int fu = u_begin + wave, fs = 0;
+    int next_fixed = u_begin + waves + wave;   // second fixed unit, then -1
+    int ring_u[kPhase], ring_s[kPhase];
+    RawSet<KIND> ring[kPhase];
+    auto advance = [&]() {
+        if (++fs == S) {
+            fs = 0;
+            if (next_fixed >= 0) {
+                fu = next_fixed;
+                next_fixed = -1;
+            } else {
+                uint32_t c = 0;
+                if (lane == 0) c = __hip_atomic_fetch_add(&s_next, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                fu = u_begin + (int)__builtin_amdgcn_readfirstlane(c);
+            }
+        }
+    };
+    if (tid == 0) s_next = (uint32_t)(2 * waves);
+    __syncthreads();   // the counter is set before any wave claims
+#pragma unroll
+    for (int d = 0; d < kPhase; ++d) {
+        ring_u[d] = fu;
+        ring_s[d] = fs;
+        fetch(ring[d], fu, fs, u_end - 1);
+        advance();
+    }
+
+#pragma unroll
+    for (int r = 0; r < kXRegs; ++r) {
+        const int i = (tid + r * (int)blockDim.x) * xstep;
+        if (i < K) *(u32x4 *)(smem + lds_pad((uint32_t)(i * esz))) = xr[r];
+    }
+    for (int i = (tid + kXRegs * (int)blockDim.x) * xstep; i < K; i += (int)blockDim.x * xstep)
+        *(u32x4 *)(smem + lds_pad((uint32_t)(i * esz))) = *(const u32x4 *)(src + (size_t)i * esz);
+    __syncthreads();
+    const float *sx = (const float *)smem;
+    const float *ssum = (const float *)(smem + lds_pad(4u * (uint32_t)K));
+    if constexpr (KIND != kQ4KQ8) {
+        float *w = (float *)ssum;
+        for (int g = tid; g < K / 16; g += blockDim.x) w[g] = sum16(x_at<true>(sx, 16 * g));
+        __syncthreads();
+    }
+    XSlice<KIND> xs;
+    auto slice = [&](int st) {
+        const int c = block_of(st);
+        const int cb = c >= 0 ? c : 0;   // idle lanes read any valid slice
+        if constexpr (KIND == kQ4KQ8) {
+            load_x<true>(xs.v, (const int8_t *)smem, a.xd, cb, part);
+            finish_x(xs.v);
+        } else {
+            load_x<true>(xs.v, sx, cb, part);
+            finish_x(xs.v, ssum, cb, part);
+        }
+    };
+    if (S == 1) slice(0);
+
+    uint64_t best = 0;
+    float acc[2] = {0.f, 0.f};
+    bool done = false;
+    while (!done) {
+#pragma unroll
+        for (int d = 0; d < kPhase; ++d) {
+            if (!done) {
+                const int u = ring_u[d], st = ring_s[d];
+                if (u >= u_end) {   // wave-uniform; every later pair is past the range too
+                    done = true;
+                } else {
+                    if (S > 1) slice(st);
+                    float q[2];
+                    dot_raw<KIND>(ring[d], xs, part, q);
+                    const bool lv = block_of(st) >= 0;
+#pragma unroll
+                    for (int o = 0; o < OUTS; ++o) {
+                        const float t = lv ? q[o] : 0.f;
+                        acc[o] = st == 0 ? t : acc[o] + t;
+                    }
+                    if (st == S - 1) {
+                        const bool v = valid_row(u);
+                        float r[2];
+#pragma unroll
+                        for (int o = 0; o < OUTS; ++o) r[o] = group_sum(acc[o], group);
+                        if (rr == 0 && v) emit_row<KIND, EPI>(a, (int64_t)u * a.rows_tile + p, r, best);
+                    }
+                    ring_u[d] = fu;
+                    ring_s[d] = fs;
+                    fetch(ring[d], fu, fs, u);
+                    advance();
+                }
+            }
+        }
+    }
+
+    if constexpr (EPI == kArgmax) {
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)best, off);
+            const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(best >> 32), off);
+            const uint64_t o = ((uint64_t)hi << 32) | lo;
+            best = o > best ? o : best;
+        }
+        argmax_finish(a, best, lane == 0 ? wave : -1, waves);
+    }
+}
+
 // --------------------------------------------------------- Q8 quantize
 
 // One 32-lane half-wave per 32-element block: amax by a lane-max tree (exact,
@@ -682,31 +860,58 @@ __global__ __launch_bounds__(256) void q4k_q8_isums_kernel(const uint8_t *__rest
 
 // ------------------------------------------------------------ launch plan
 
-Plan make_plan(int64_t N, int64_t K, int kind)
+// Plan of a wave-unit or row-stream launch (every row reduced inside one
+// wave), or false when the shape goes to the tile kernel.
+static bool plan_in_wave(Plan &pl, int64_t N, int64_t K, int kind)
 {
-    Plan pl{};
     pl.nb = (int)(K / kQK);
     pl.lanes_row = kParts * pl.nb;
     const bool fits = pl.lanes_row <= 64 && (pl.lanes_row & (pl.lanes_row - 1)) == 0;
     // two halves need the x slices of both in registers: only the int8 path
     // has room for them without spilling
     const bool halves = pl.nb == 32 && kind == kQ4KQ8;
-    pl.wave_local = (fits || halves) ? 1 : 0;
-    pl.steps = halves ? 2 : 1;
-    if (pl.wave_local) {
-        // gemv_wave_kernel: units of one wave's rows; the launch decides how
-        // many waves a workgroup gets
-        if (halves) pl.lanes_row = 64;   // lanes per row in each half
-        pl.waves = (kind == kQ4KQ8 ? 1024 : 768) / 64;
-        pl.threads = pl.waves * 64;
-        pl.rows_tile = 64 / pl.lanes_row;
-        pl.tiles = (N + pl.rows_tile - 1) / pl.rows_tile;
-        const size_t xb = (kind == kQ4KQ8) ? (size_t)K : (size_t)K * 4;
-        pl.x_in_lds = 1;
-        pl.lds_bytes = xb + xb / 16 + ((kind == kQ4KQ8) ? 0 : (size_t)(K / 16) * 4);
-        pl.grid = 0;
-        return pl;
+    // The row-stream kernel wins (measured) for f32 Q4_K rows of two halves,
+    // and for one-step rows of a single matrix when each CU gets a couple of
+    // dozen rows at most; with more rows per CU, longer rows or the SwiGLU
+    // pair, the tile kernel's shorter start-up wins.
+    const bool stream = (kind == kQ4K && pl.nb == 32) || (pl.nb < 16 && kind != kSwiglu && N <= 6144);
+    if (!fits && !halves && !stream) return false;
+    // gemv_wave_kernel when the row's lanes are a power-of-two group (or two
+    // halves), gemv_rows_kernel (16-super-block steps) otherwise
+    pl.wave_local = 1;
+    pl.rows_kernel = (fits || halves) ? 0 : 1;
+    if (fits) {
+        pl.steps = 1;
+    } else if (halves) {
+        pl.steps = 2;
+        pl.lanes_row = 64;
+    } else {
+        pl.steps = (pl.nb + 15) / 16;
+        int g = 4;
+        while (g < 4 * pl.nb && g < 64) g *= 2;
+        pl.lanes_row = g;   // lanes per row: a power of two holding min(nb, 16) super-blocks
     }
+    pl.waves = (kind == kQ4KQ8 || (kind == kQ4K && pl.steps == 2) ? 1024 : 768) / 64;   // the most; the launch decides
+    pl.threads = pl.waves * 64;
+    pl.rows_tile = 64 / pl.lanes_row;
+    pl.tiles = (N + pl.rows_tile - 1) / pl.rows_tile;
+    const size_t xb = (kind == kQ4KQ8) ? (size_t)K : (size_t)K * 4;
+    pl.x_in_lds = 1;
+    pl.lds_bytes = xb + xb / 16 + ((kind == kQ4KQ8) ? 0 : (size_t)(K / 16) * 4);
+    pl.grid = 0;
+    return pl.lds_bytes <= 65536;   // larger x (f32, K > ~15000) goes to the tile kernel
+}
+
+Plan make_plan(int64_t N, int64_t K, int kind)
+{
+    Plan pl{};
+    if (plan_in_wave(pl, N, K, kind)) return pl;
+    pl = Plan{};
+    pl.nb = (int)(K / kQK);
+    pl.wave_local = 0;
+    pl.rows_kernel = 0;
+    pl.steps = 1;
+    pl.lanes_row = kParts * pl.nb;
     // tile kernel: 1, 2, 4 or 8 waves (a workgroup of another size leaves SIMDs
     // unevenly loaded and fewer workgroups fit on a CU); fewest idle lanes,
     // ties to fewer waves; at least one row per tile
@@ -782,6 +987,7 @@ static GemvArgs base_args(const Plan &pl, int64_t N)
     a.lanes_row_magic = (uint32_t)((((uint64_t)1 << 32) + (uint64_t)pl.lanes_row - 1) / (uint64_t)pl.lanes_row);
     a.rows_tile = pl.rows_tile;
     a.x_in_lds = pl.x_in_lds;
+    a.steps = pl.steps;
     return a;
 }
 
@@ -839,24 +1045,33 @@ static int wave_kernel_waves(const void *fn, size_t lds, int max_waves)
     return waves;
 }
 
-template <int KIND, int EPI, int STEPS>
-static hipError_t launch_wave(Plan &pl, const GemvArgs &a, int cus, hipStream_t s, const Timing &tm)
+// One workgroup per CU (at most one per unit), each with as many waves as fit
+// on a CU next to nothing else, but no more waves than it has units.
+template <typename Kern>
+static hipError_t launch_per_cu(Kern k, int max_waves, Plan &pl, const GemvArgs &a, int cus, hipStream_t s,
+                                const Timing &tm)
 {
-    const void *fn = (const void *)gemv_wave_kernel<KIND, EPI, STEPS>;
-    const int wmax = wave_kernel_waves(fn, pl.lds_bytes, wave_max_threads<KIND>() / 64);
+    const int wmax = wave_kernel_waves((const void *)k, pl.lds_bytes, max_waves);
     const int64_t grid = pl.tiles < cus ? pl.tiles : cus;
     const int64_t per = (pl.tiles + grid - 1) / grid;   // units per workgroup
     pl.grid = (int)grid;
     pl.waves = (int)(per < wmax ? per : wmax);
     pl.threads = 64 * pl.waves;
-    launch_on(gemv_wave_kernel<KIND, EPI, STEPS>, pl, a, s, tm);
+    launch_on(k, pl, a, s, tm);
     return hipGetLastError();
+}
+
+template <int KIND, int EPI, int STEPS>
+static hipError_t launch_wave(Plan &pl, const GemvArgs &a, int cus, hipStream_t s, const Timing &tm)
+{
+    return launch_per_cu(gemv_wave_kernel<KIND, EPI, STEPS>, wave_max_threads<KIND>() / 64, pl, a, cus, s, tm);
 }
 
 template <int KIND, int EPI>
 static hipError_t launch(Plan &pl, const GemvArgs &a, int cus, hipStream_t s, const Timing &tm = Timing{})
 {
     if (pl.wave_local) {
+        if (pl.rows_kernel) return launch_per_cu(gemv_rows_kernel<KIND, EPI>, pl.waves, pl, a, cus, s, tm);
         if constexpr (KIND == kQ4KQ8)
             if (pl.steps == 2) return launch_wave<KIND, EPI, 2>(pl, a, cus, s, tm);
         return launch_wave<KIND, EPI, 1>(pl, a, cus, s, tm);

@@ -23,7 +23,8 @@ struct Plan {
     int nb;          // super-blocks per row
     int lanes_row;   // lanes per row (4 per super-block)
     int wave_local;  // rows reduce inside one wave (gemv_wave_kernel)
-    int steps;       // wave kernel: 1, or 2 when a row is two 16-super-block halves
+    int steps;       // 16-super-block steps per row (wave and row-stream kernels)
+    int rows_kernel; // 1: gemv_rows_kernel, 0: gemv_wave_kernel (when wave_local)
     int waves;       // waves per workgroup
     int threads;     // 64 * waves
     int rows_tile;   // rows per tile
