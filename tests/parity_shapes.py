@@ -1,0 +1,38 @@
+"""Shapes of the small GPU parity cases, and the kernel path each one takes.
+
+Shared by the GPU parity tests and a CPU test that checks every kernel path
+of the library (as reported by its launch geometry) is exercised by at least
+one parity case of every kind that can take it.
+"""
+import gemv_q4k_q6k_amd as gq
+
+SMALL_Q4K = [(1, 256), (5, 256), (1000, 1024), (333, 2560), (77, 8192), (129, 9728), (17, 4352),
+             (3, 32768), (70, 512), (130, 2048), (31, 4096), (9, 768), (6000, 2560), (5, 12288)]
+SMALL_Q6K = [(1, 256), (4, 256), (100, 768), (1000, 1024), (257, 9728), (33, 1280), (21, 2560),
+             (3, 32768), (65, 2048), (5, 16384)]
+SMALL_SWIGLU = [(1, 256), (100, 1024), (333, 2560), (50, 8192), (7, 16384)]
+SMALL_Q8 = [(1, 256), (1000, 1024), (333, 2560), (77, 8192), (50, 9728), (3, 32768)]
+
+
+def kernel_path(kind, N, K):
+    """'wave1', 'wave2' (wave-unit kernel), 'rows<S>' (row-stream kernel, S
+    steps), 'tile-lds' or 'tile' (tile kernel with or without x in LDS)."""
+    g = gq.tile_geometry(kind, N, K)
+    if not g["wave_local"]:
+        return "tile-lds" if g["x_in_lds"] else "tile"
+    nb = K // 256
+    group = 64 // g["rows_tile"]
+    if kind == gq.KIND_Q4K_Q8 and g["steps"] == 2:
+        return "wave2"
+    if g["steps"] == 1 and group == 4 * nb:
+        return "wave1"
+    return f"rows{g['steps']}"
+
+
+REQUIRED_PATHS = {
+    gq.KIND_Q4K: {"wave1", "rows1", "rows2", "tile-lds", "tile"},
+    gq.KIND_Q6K: {"wave1", "rows1", "tile-lds", "tile"},
+    gq.KIND_SWIGLU: {"wave1", "tile-lds", "tile"},
+    gq.KIND_Q4K_Q8: {"wave1", "wave2", "rows1", "tile-lds", "tile"},
+}
+CASES = {gq.KIND_Q4K: SMALL_Q4K, gq.KIND_Q6K: SMALL_Q6K, gq.KIND_SWIGLU: SMALL_SWIGLU, gq.KIND_Q4K_Q8: SMALL_Q8}

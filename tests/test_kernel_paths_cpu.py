@@ -1,0 +1,28 @@
+"""Every kernel path the library can launch is taken by at least one small
+GPU parity case of each kind that can use it (decided from the library's own
+launch geometry, no GPU needed)."""
+import pytest
+
+import gemv_q4k_q6k_amd as gq
+import parity_shapes as ps
+
+
+@pytest.mark.parametrize("kind", sorted(ps.CASES))
+def test_parity_cases_cover_every_path(kind):
+    got = {ps.kernel_path(kind, N, K) for N, K in ps.CASES[kind]}
+    assert ps.REQUIRED_PATHS[kind] <= got, ps.REQUIRED_PATHS[kind] - got
+
+
+@pytest.mark.parametrize("kind,N,K,path", [
+    (gq.KIND_Q6K, 248_320, 1024, "wave1"),      # lm_head
+    (gq.KIND_Q4K, 4096, 2560, "rows1"),
+    (gq.KIND_Q4K, 9728, 2560, "tile-lds"),
+    (gq.KIND_Q4K, 2560, 9728, "tile-lds"),
+    (gq.KIND_SWIGLU, 9728, 2560, "tile-lds"),
+    (gq.KIND_Q6K, 2560, 9728, "tile-lds"),
+    (gq.KIND_Q4K_Q8, 28_672, 8192, "wave2"),
+    (gq.KIND_Q4K, 28_672, 8192, "rows2"),
+])
+def test_workload_paths(kind, N, K, path):
+    """The benchmarked workloads run the kernels their parity tests cover."""
+    assert ps.kernel_path(kind, N, K) == path

@@ -70,10 +70,7 @@ def q6k_abs_rows(W, x, N, K):
     return np.abs(Wf) @ np.abs(x.astype(np.float64))
 
 
-SMALL_Q4K = [(1, 256), (5, 256), (1000, 1024), (333, 2560), (77, 8192), (129, 9728), (17, 4352),
-             (3, 32768), (70, 512), (130, 2048), (31, 4096), (9, 768)]
-SMALL_Q6K = [(1, 256), (4, 256), (100, 768), (1000, 1024), (257, 9728), (33, 1280), (21, 2560),
-             (3, 32768), (65, 2048)]
+from parity_shapes import SMALL_Q4K, SMALL_Q6K, SMALL_SWIGLU, SMALL_Q8  # noqa: E402
 
 
 @pytest.mark.parametrize("N,K", SMALL_Q4K)
@@ -333,7 +330,7 @@ def test_lm_head_nan_and_inf_rows(dev):
 
 # ------------------------------------------------------------------ SwiGLU
 def test_swiglu_small(dev):
-    for N, K in [(1, 256), (100, 1024), (333, 2560), (50, 8192)]:
+    for N, K in SMALL_SWIGLU:
         r = synth.rng_for(3000 + N)
         Wg, Wu = synth.q4k_weights(r, N, K), synth.q4k_weights(r, N, K)
         x = synth.activation(r, K)
@@ -388,7 +385,7 @@ def test_q8_quantize_exact(dev):
 
 
 def test_q4k_q8_isums_exact(dev):
-    for N, K in [(1, 256), (37, 1024), (300, 2560), (64, 8192)]:
+    for N, K in [(1, 256), (37, 1024), (300, 2560), (64, 8192), (5, 9728)]:
         r = synth.rng_for(4000 + N)
         W = synth.q4k_weights(r, N, K)
         x = synth.activation_outliers(r, K)
@@ -398,7 +395,7 @@ def test_q4k_q8_isums_exact(dev):
 
 
 def test_q4k_q8_gemv_small(dev):
-    for N, K in [(1, 256), (1000, 1024), (333, 2560), (77, 8192), (50, 9728)]:
+    for N, K in SMALL_Q8:
         r = synth.rng_for(5000 + N)
         W = synth.q4k_weights(r, N, K)
         x = synth.activation_outliers(r, K)
@@ -426,3 +423,12 @@ def test_q4k_q8_c5_full(dev):
     check_f32("C5 f32 path", yf, yhat)
     cos = float(np.dot(y8hat, yhat) / np.linalg.norm(y8hat) / np.linalg.norm(yhat))
     print(f"C5: q8 path vs exact activation: cosine={cos:.6f} rel_err_inf={rel_err(y8hat, yhat):.3e}")
+
+
+def test_q4k_f32_c5_shape_full(dev):
+    """The f32 Q4_K GEMV at the 70B-class FFN shape (28,672 x 8192, rows of
+    two 16-super-block halves), against the f64 oracle on the exact x."""
+    W, x = synth.c5_inputs(0)
+    N, K = synth.C5_Q8
+    y = gq().q4k_gemv(up(W, dev), up(x, dev), N, K).cpu().numpy()
+    check_f32("C5 f32 q4k", y, oracle.q4k_gemv(W, x, N, K))
