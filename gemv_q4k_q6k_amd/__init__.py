@@ -225,7 +225,8 @@ def lm_head_argmax(W, x, N: int, K: int, workspace, out_idx=None, out_max=None, 
     int32[1] device tensor holding the index (and the float32[1] maximum if
     want_max or out_max is given).  `workspace` is a uint8 device tensor of at
     least lm_head_argmax_ws_bytes(N, K) bytes, zero-filled before its first use
-    (torch.zeros); every call leaves it zero again."""
+    (torch.zeros); every call leaves its counters (the first 4096 bytes) zero
+    again."""
     return _lm_head(W, x, N, K, workspace, out_idx, out_max, want_max, stream, None)
 
 

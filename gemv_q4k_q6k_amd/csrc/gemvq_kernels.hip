@@ -258,41 +258,77 @@ __device__ __forceinline__ void emit_row(const GemvArgs &a, int64_t row, const f
     }
 }
 
-// Workspace of lm_head_argmax: [0,8) the running best key, [8,12) the count of
-// finished workgroups.  Both are zero between calls.
-__device__ __forceinline__ uint64_t *ws_key(uint8_t *ws) { return (uint64_t *)ws; }
-__device__ __forceinline__ uint32_t *ws_done(uint8_t *ws) { return (uint32_t *)(ws + 8); }
+// Workspace of lm_head_argmax (all offsets in bytes; every counter sits on a
+// 128-byte line of its own, so the atomics of different groups never meet):
+//   [0, 4)                     top counter: groups that have finished
+//   [128*(1+r), +4), r < 16    group counter r: finished workgroups g with g % 16 == r
+//   [kArgmaxSlot0 + 128*g, +8) workgroup g's best key (written every call)
+// The counters are zero between calls; the keys need no initial value.
+__device__ __forceinline__ uint32_t *ws_top(uint8_t *ws) { return (uint32_t *)ws; }
+__device__ __forceinline__ uint32_t *ws_group(uint8_t *ws, int r) { return (uint32_t *)(ws + 128 * (1 + r)); }
+__device__ __forceinline__ uint64_t *ws_slot(uint8_t *ws, int g) { return (uint64_t *)(ws + kArgmaxSlot0 + 128 * (size_t)g); }
 
-// Grid-level argmax without fences: the threads' running keys are gathered
-// through LDS (one barrier) and thread 0 folds the workgroup's best into one
-// 64-bit atomic max, waits for that atomic to complete, then counts the
-// workgroup done with an atomic add; the workgroup that counts last reads the
-// key with an atomic exchange (which also clears it for the next call), writes
-// the 4-byte result and clears the counter.  Atomics are coherent at device
-// scope across all XCDs, so no cache writeback or invalidation is needed.
+// Grid-level argmax without fences and without a hot spot: the threads'
+// running keys meet in LDS (one barrier); thread 0 publishes the workgroup's
+// best key in its own slot with a returning atomic exchange (so it has been
+// performed at device scope before the count below), then counts the
+// workgroup done in its group's counter.  The last workgroup of a group clears
+// that counter and counts the group done in the top counter; the last group's
+// last workgroup reads every slot (device-scope atomic loads), writes the
+// 4-byte result and clears the top counter.  Device-scope atomics are coherent
+// across all XCDs, so no cache writeback or invalidation is needed, and with
+// at most 16 workgroups per counter the atomics barely queue.
 // `holders` threads (0..holders-1) carry running keys.
 __device__ void argmax_finish(const GemvArgs &a, uint64_t best, int holder, int holders)
 {
     __shared__ uint64_t s_key[kMaxThreads];
     if (holder >= 0) s_key[holder] = best;
     __syncthreads();
+    if (threadIdx.x >= 64) return;   // wave 0 finishes
+    const int G = (int)gridDim.x, g = (int)blockIdx.x;
+    const int groups = G < kArgmaxGroups ? G : kArgmaxGroups;
+    uint32_t last = 0;
     if (threadIdx.x == 0) {
         uint64_t k = 0;
         for (int h = 0; h < holders; ++h) k = s_key[h] > k ? s_key[h] : k;
-        if (k) {
-            // a returning atomic: consuming its result makes the wave wait until
-            // the max has been performed before it counts itself done
-            const uint64_t old = __hip_atomic_fetch_max(ws_key(a.ws), k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            asm volatile("" ::"v"(old));
+        const uint64_t old = __hip_atomic_exchange(ws_slot(a.ws, g), k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        asm volatile("" ::"v"(old));   // consumed: the exchange is performed before the count
+        const int r = g % groups;
+        const int members = (G - r + groups - 1) / groups;   // workgroups g' < G with g' % groups == r
+        const uint32_t prev = __hip_atomic_fetch_add(ws_group(a.ws, r), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (prev == (uint32_t)members - 1) {
+            __hip_atomic_store(ws_group(a.ws, r), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const uint32_t t = __hip_atomic_fetch_add(ws_top(a.ws), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            last = (t == (uint32_t)groups - 1) ? 1u : 0u;
         }
-        const uint32_t prev = __hip_atomic_fetch_add(ws_done(a.ws), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (prev == gridDim.x - 1) {
-            const uint64_t g = __hip_atomic_exchange(ws_key(a.ws), (uint64_t)0, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT);
-            a.out_idx[0] = g ? argmax_key_index(g) : 0u;
-            if (a.out_max) a.out_max[0] = g ? argmax_key_value(g) : __builtin_nanf("");
-            __hip_atomic_store(ws_done(a.ws), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
+    }
+    last = (uint32_t)__shfl((int)last, 0);
+    if (!last) return;
+    // every slot of the workspace is read unconditionally (no branch, so all
+    // loads are in flight together); slots of workgroups past the grid hold
+    // stale keys and are masked out
+    constexpr int kPerLane = kArgmaxMaxGrid / 64;
+    uint64_t v[kPerLane];
+#pragma unroll
+    for (int j = 0; j < kPerLane; ++j)
+        v[j] = __hip_atomic_load(ws_slot(a.ws, (int)threadIdx.x + 64 * j), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint64_t k = 0;
+#pragma unroll
+    for (int j = 0; j < kPerLane; ++j) {
+        const uint64_t w = ((int)threadIdx.x + 64 * j < G) ? v[j] : 0ull;
+        k = w > k ? w : k;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)k, off);
+        const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(k >> 32), off);
+        const uint64_t o = ((uint64_t)hi << 32) | lo;
+        k = o > k ? o : k;
+    }
+    if (threadIdx.x == 0) {
+        a.out_idx[0] = k ? argmax_key_index(k) : 0u;
+        if (a.out_max) a.out_max[0] = k ? argmax_key_value(k) : __builtin_nanf("");
+        __hip_atomic_store(ws_top(a.ws), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -513,15 +549,24 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_wave_kernel(Gem
     const int part = rr & 3;
     const int K = a.nb * kQK;
 
-    // this workgroup's units [u_begin, u_end): a static split of all units
+    // this workgroup's units: chunks of `waves` consecutive units, dealt to
+    // the workgroups in turn (chunk c belongs to workgroup c % grid).  Its
+    // waves take the workgroup's units in order through the LDS counter, so
+    // at any moment the whole grid reads one window of the matrix, the access
+    // pattern the HBM serves fastest.  umap(v) is the workgroup's v-th unit,
+    // or `units` once past the end (it grows with v).
     const int64_t units = a.tiles;
-    const int u_begin = (int)(units * blockIdx.x / gridDim.x);
-    const int u_end = (int)(units * (blockIdx.x + 1) / gridDim.x);
+    const int u_end = (int)units;
     const int last_rows = (int)(a.N - (units - 1) * a.rows_tile);
     const int64_t unit_stride = (int64_t)a.rows_tile * a.nb * BYTES;
+    auto umap = [&](int v) {
+        const int c = v / waves;
+        const int64_t u = ((int64_t)c * gridDim.x + blockIdx.x) * waves + (v - c * waves);
+        return (int)(u < units ? u : units);
+    };
 
     auto valid_unit = [&](int u) { return u < u_end && (u < units - 1 || p < last_rows); };
-    // unconditional loads, as in gemv_kernel: a unit past the range re-reads
+    // unconditional loads, as in gemv_kernel: a unit past the end re-reads
     // the unit `prev` this wave has just processed (still in its CU's cache),
     // an idle lane the unit's first super-block
     auto fetch = [&](RawSet<KIND> (&rs)[STEPS], int u, int prev) {
@@ -557,7 +602,7 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_wave_kernel(Gem
     RawSet<KIND> ring[kPhase][STEPS];
 #pragma unroll
     for (int d = 0; d < kPhase; ++d) {
-        unit[d] = u_begin + d * waves + wave;
+        unit[d] = umap(d * waves + wave);
         fetch(ring[d], unit[d], u_end - 1);
     }
     if (tid == 0) s_next = (uint32_t)(kPhase * waves);
@@ -589,9 +634,15 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_wave_kernel(Gem
     }
 
     uint64_t best = 0;
-    // keep taking units until both ring slots come back past the range (the
+    // keep taking units until every ring slot comes back past the range (the
     // counter only grows, so once one claim is past it every later one is)
-    while (unit[0] < u_end || unit[1] < u_end) {
+    auto active = [&]() {
+        bool any = false;
+#pragma unroll
+        for (int d = 0; d < kPhase; ++d) any = any || unit[d] < u_end;
+        return any;
+    };
+    while (active()) {
 #pragma unroll
         for (int d = 0; d < kPhase; ++d) {
             if (unit[d] < u_end) {   // wave-uniform
@@ -611,7 +662,7 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_wave_kernel(Gem
                 uint32_t c = 0;
                 if (lane == 0) c = __hip_atomic_fetch_add(&s_next, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
                 const int done = unit[d];
-                unit[d] = u_begin + (int)__builtin_amdgcn_readfirstlane(c);
+                unit[d] = umap((int)__builtin_amdgcn_readfirstlane(c));
                 fetch(ring[d], unit[d], done);
             }
         }
@@ -1010,6 +1061,7 @@ static hipError_t launch_mode(Plan &pl, GemvArgs a, int cus, hipStream_t s, cons
     // leaves at most one tile per workgroup the single-tile kernel runs
     const void *fn2 = (const void *)gemv_kernel<KIND, EPI, 2, XLDS>;
     pl.grid = grid_for(pl, fn2, cus, KIND == kSwiglu ? 2 : 4);
+    if (EPI == kArgmax && pl.grid > kArgmaxMaxGrid) pl.grid = kArgmaxMaxGrid;   // one workspace slot each
     a.tiles_q = (int)(pl.tiles / pl.grid);
     a.tiles_r = (int)(pl.tiles % pl.grid);
     if (a.tiles_q >= 2 || (a.tiles_q == 1 && a.tiles_r > 0))
@@ -1052,7 +1104,8 @@ static hipError_t launch_per_cu(Kern k, int max_waves, Plan &pl, const GemvArgs 
                                 const Timing &tm)
 {
     const int wmax = wave_kernel_waves((const void *)k, pl.lds_bytes, max_waves);
-    const int64_t grid = pl.tiles < cus ? pl.tiles : cus;
+    int64_t grid = pl.tiles < cus ? pl.tiles : cus;
+    if (grid > kArgmaxMaxGrid) grid = kArgmaxMaxGrid;   // argmax: one workspace slot per workgroup
     const int64_t per = (pl.tiles + grid - 1) / grid;   // units per workgroup
     pl.grid = (int)grid;
     pl.waves = (int)(per < wmax ? per : wmax);

@@ -13,9 +13,13 @@ namespace gemvq {
 constexpr int kMaxThreads = 512;
 constexpr int64_t kMaxK = 32768;
 
-// lm_head_argmax workspace: a 64-bit running best key and a 32-bit counter
-// (padded to 256 bytes).
-constexpr size_t kArgmaxWsBytes = 256;
+// lm_head_argmax workspace: counters in the first kArgmaxSlot0 bytes (zero
+// between calls), then one 128-byte slot per workgroup for its best key; the
+// argmax launches use at most kArgmaxMaxGrid workgroups.
+constexpr int kArgmaxGroups = 16;
+constexpr size_t kArgmaxSlot0 = 4096;
+constexpr int kArgmaxMaxGrid = 1024;
+constexpr size_t kArgmaxWsBytes = kArgmaxSlot0 + 128 * (size_t)kArgmaxMaxGrid;
 
 // Launch geometry of the GEMV kernel template (pure function of N, K, the
 // CU count and the kernel kind).

@@ -199,8 +199,8 @@ def test_lm_head_argmax_c3_full(dev, c3_full):
     ws = _ws(dev, N, K)
     idx, ihat = _argmax_case(dev, W, x, dW, dx, N, K, ws)
     print(f"C3 seed 0: idx={idx} oracle={ihat} gap={oracle.top2_gap(oracle.q6k_gemv(W, x, N, K)):.4f}")
-    # every call leaves the workspace zero, and a second call on it agrees
-    assert int(torch.count_nonzero(ws).item()) == 0
+    # every call leaves the workspace counters zero, and a second call on it agrees
+    assert int(torch.count_nonzero(ws[:4096]).item()) == 0
     idx2 = int(gq().lm_head_argmax(dW, dx, N, K, ws).item())
     assert idx2 == idx
 
@@ -225,7 +225,7 @@ def test_lm_head_argmax_timed(dev, c3_full):
     torch.cuda.synchronize()
     assert int(idx.item()) == int(ref.item())
     assert float(vmax.item()) == float(vref.item())
-    assert int(torch.count_nonzero(ws).item()) == 0
+    assert int(torch.count_nonzero(ws[:4096]).item()) == 0
     t_kernel, t_outer = k0.elapsed_time(k1), o0.elapsed_time(o1)
     print(f"lm_head kernel {t_kernel * 1e3:.2f} us, events around the call {t_outer * 1e3:.2f} us", flush=True)
     assert 0.0 < t_kernel <= t_outer * 1.01 + 1e-3
