@@ -517,10 +517,10 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_kernel(GemvArgs a)
 // row fits one wave when its 4*K/256 lanes are a power of two up to 64
 // (STEPS = 1: a wave unit is 64/lanes_row rows), or when it is 32 super-blocks
 // wide (STEPS = 2: a unit is one row, and every lane takes one quarter
-// super-block in each half of the row).  The matrix is cut into units; each
-// workgroup owns a contiguous range of them and its waves take them from an
-// LDS counter.  Waves that the CU issues less often (the arbiter favours older
-// waves) then simply take fewer units, and the CU finishes its range as a
+// super-block in each half of the row).  The matrix is cut into units, dealt
+// to the workgroups in turn; a workgroup's waves take its units from an LDS
+// counter.  Waves that the CU issues less often (the arbiter favours older
+// waves) then simply take fewer units, and the CU finishes its share as a
 // whole instead of waiting for its slowest wave or workgroup.  The activation
 // is staged in LDS once per CU.  A row's value is reduced the same way
 // wherever it sits (fixed lane layout, halves added in order), so equal rows
@@ -549,19 +549,18 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_wave_kernel(Gem
     const int part = rr & 3;
     const int K = a.nb * kQK;
 
-    // this workgroup's units: chunks of `waves` consecutive units, dealt to
-    // the workgroups in turn (chunk c belongs to workgroup c % grid).  Its
-    // waves take the workgroup's units in order through the LDS counter, so
-    // at any moment the whole grid reads one window of the matrix, the access
-    // pattern the HBM serves fastest.  umap(v) is the workgroup's v-th unit,
-    // or `units` once past the end (it grows with v).
+    // this workgroup's units: units are dealt to the workgroups in turn
+    // (unit u belongs to workgroup u % grid), and its waves take them in order
+    // through the LDS counter, so at any moment the whole grid reads one
+    // window of the matrix, the access pattern the HBM serves fastest.
+    // umap(v) is the workgroup's v-th unit, or `units` once past the end (it
+    // grows with v).
     const int64_t units = a.tiles;
     const int u_end = (int)units;
     const int last_rows = (int)(a.N - (units - 1) * a.rows_tile);
     const int64_t unit_stride = (int64_t)a.rows_tile * a.nb * BYTES;
     auto umap = [&](int v) {
-        const int c = v / waves;
-        const int64_t u = ((int64_t)c * gridDim.x + blockIdx.x) * waves + (v - c * waves);
+        const int64_t u = (int64_t)v * gridDim.x + blockIdx.x;
         return (int)(u < units ? u : units);
     };
 
@@ -715,11 +714,15 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_rows_kernel(Gem
     const int K = a.nb * kQK;
     const int S = a.steps;
 
+    // units dealt to the workgroups in turn, as in the wave-unit kernel
     const int64_t units = a.tiles;
-    const int u_begin = (int)(units * blockIdx.x / gridDim.x);
-    const int u_end = (int)(units * (blockIdx.x + 1) / gridDim.x);
+    const int u_end = (int)units;
     const int last_rows = (int)(a.N - (units - 1) * a.rows_tile);
     const int64_t unit_stride = (int64_t)a.rows_tile * a.nb * BYTES;
+    auto umap = [&](int v) {
+        const int64_t u = (int64_t)v * gridDim.x + blockIdx.x;
+        return (int)(u < units ? u : units);
+    };
 
     // super-block of this lane in step s, or -1 past the row's end
     auto block_of = [&](int st) { const int c = b + 16 * st; return c < a.nb ? c : -1; };
@@ -754,8 +757,8 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_rows_kernel(Gem
     // the fetch cursor walks (unit, step) pairs: the first two units of the
     // wave are fixed, later ones come from the counter when their first step
     // is fetched
-    int fu = u_begin + wave, fs = 0;
-    int next_fixed = u_begin + waves + wave;   // second fixed unit, then -1
+    int fu = umap(wave), fs = 0;
+    int next_fixed = umap(waves + wave);   // second fixed unit, then -1
     int ring_u[kPhase], ring_s[kPhase];
     RawSet<KIND> ring[kPhase];
     auto advance = [&]() {
@@ -767,7 +770,7 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_rows_kernel(Gem
             } else {
                 uint32_t c = 0;
                 if (lane == 0) c = __hip_atomic_fetch_add(&s_next, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-                fu = u_begin + (int)__builtin_amdgcn_readfirstlane(c);
+                fu = umap((int)__builtin_amdgcn_readfirstlane(c));
             }
         }
     };
