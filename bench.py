@@ -211,7 +211,7 @@ def self_check(gq, sets, v):
 def breakdown(gq, sets, v, reps=24):
     """Per-call device time of each kernel, not part of `value`: `reps`
     launches are captured in a HIP graph and replayed between two HIP events
-    (no host launch overhead in the measurement).  Each kernel rotates through
+    (no host launch overhead in the measurement; median of 7 trials).  Each kernel rotates through
     enough device-side copies of its weights (>= 640 MB in total) that the
     256 MB Infinity Cache cannot serve a repeat.  rocprofv3 kernel traces are
     the cross-check."""
@@ -237,14 +237,16 @@ def breakdown(gq, sets, v, reps=24):
                 fn(ws[r % len(ws)])
         g.replay()
         torch.cuda.synchronize()
-        st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        n_rep = 5
-        st.record()
-        for _ in range(n_rep):
-            g.replay()
-        en.record()
-        torch.cuda.synchronize()
-        us = st.elapsed_time(en) * 1000.0 / (reps * n_rep)
+        trials = []
+        for _ in range(7):   # the median of 7 trials of 3 replays each
+            st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            st.record()
+            for _ in range(3):
+                g.replay()
+            en.record()
+            torch.cuda.synchronize()
+            trials.append(st.elapsed_time(en) * 1000.0 / (reps * 3))
+        us = float(np.median(trials))
         out[name] = {"us": round(us, 2), "GBps": round(nbytes / us / 1e3, 1),
                      "frac_hbm_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4), "weight_copies": len(ws)}
         del g

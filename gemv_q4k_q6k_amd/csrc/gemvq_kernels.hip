@@ -44,6 +44,7 @@ struct GemvArgs {
     int rows_tile;         // rows per tile (P)
     int x_in_lds;          // stage the activation (and its 16-element sums) through LDS first
     int steps;             // row-stream kernel: 16-super-block steps per row
+    int chunk_shift;       // wave/row-stream kernels: units are dealt in chunks of 1 << chunk_shift
 };
 
 // ------------------------------------------------------- activation setup
@@ -549,18 +550,20 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_wave_kernel(Gem
     const int part = rr & 3;
     const int K = a.nb * kQK;
 
-    // this workgroup's units: units are dealt to the workgroups in turn
-    // (unit u belongs to workgroup u % grid), and its waves take them in order
-    // through the LDS counter, so at any moment the whole grid reads one
-    // window of the matrix, the access pattern the HBM serves fastest.
-    // umap(v) is the workgroup's v-th unit, or `units` once past the end (it
-    // grows with v).
+    // this workgroup's units: units are dealt to the workgroups in turn, in
+    // chunks of 1 << chunk_shift units (the fewest whose bytes fill whole
+    // 128-byte lines, so no line is fetched by two CUs), and its waves take
+    // them in order through the LDS counter.  At any moment the whole grid
+    // reads one window of the matrix, the access pattern the HBM serves
+    // fastest.  umap(v) is the workgroup's v-th unit, or `units` once past
+    // the end (it grows with v).
     const int64_t units = a.tiles;
     const int u_end = (int)units;
     const int last_rows = (int)(a.N - (units - 1) * a.rows_tile);
     const int64_t unit_stride = (int64_t)a.rows_tile * a.nb * BYTES;
     auto umap = [&](int v) {
-        const int64_t u = (int64_t)v * gridDim.x + blockIdx.x;
+        const int sh = a.chunk_shift;
+        const int64_t u = ((((int64_t)(v >> sh)) * gridDim.x + blockIdx.x) << sh) | (v & ((1 << sh) - 1));
         return (int)(u < units ? u : units);
     };
 
@@ -720,7 +723,8 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_rows_kernel(Gem
     const int last_rows = (int)(a.N - (units - 1) * a.rows_tile);
     const int64_t unit_stride = (int64_t)a.rows_tile * a.nb * BYTES;
     auto umap = [&](int v) {
-        const int64_t u = (int64_t)v * gridDim.x + blockIdx.x;
+        const int sh = a.chunk_shift;
+        const int64_t u = ((((int64_t)(v >> sh)) * gridDim.x + blockIdx.x) << sh) | (v & ((1 << sh) - 1));
         return (int)(u < units ? u : units);
     };
 
@@ -949,6 +953,10 @@ static bool plan_in_wave(Plan &pl, int64_t N, int64_t K, int kind)
     pl.threads = pl.waves * 64;
     pl.rows_tile = 64 / pl.lanes_row;
     pl.tiles = (N + pl.rows_tile - 1) / pl.rows_tile;
+    // chunk of units whose bytes are a whole number of 128-byte lines
+    const int64_t unit_bytes = (int64_t)pl.rows_tile * pl.nb * (kind == kQ6K ? 210 : 144);
+    pl.chunk_shift = 0;
+    while (((unit_bytes << pl.chunk_shift) & 127) != 0) ++pl.chunk_shift;
     const size_t xb = (kind == kQ4KQ8) ? (size_t)K : (size_t)K * 4;
     pl.x_in_lds = 1;
     pl.lds_bytes = xb + xb / 16 + ((kind == kQ4KQ8) ? 0 : (size_t)(K / 16) * 4);
@@ -1042,6 +1050,7 @@ static GemvArgs base_args(const Plan &pl, int64_t N)
     a.rows_tile = pl.rows_tile;
     a.x_in_lds = pl.x_in_lds;
     a.steps = pl.steps;
+    a.chunk_shift = pl.chunk_shift;
     return a;
 }
 

@@ -29,6 +29,7 @@ struct Plan {
     int wave_local;  // rows reduce inside one wave (gemv_wave_kernel)
     int steps;       // 16-super-block steps per row (wave and row-stream kernels)
     int rows_kernel; // 1: gemv_rows_kernel, 0: gemv_wave_kernel (when wave_local)
+    int chunk_shift; // wave/row-stream kernels: units dealt in chunks of 1 << chunk_shift
     int waves;       // waves per workgroup
     int threads;     // 64 * waves
     int rows_tile;   // rows per tile
