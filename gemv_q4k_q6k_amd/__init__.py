@@ -20,7 +20,7 @@ import threading
 __all__ = [
     "GemvqError", "lib", "exported_names", "header_names",
     "q4k_gemv", "q6k_gemv", "q8_quantize", "q4k_q8_gemv", "swiglu_gemv",
-    "lm_head_argmax", "lm_head_argmax_timed", "lm_head_argmax_ws_bytes", "q4k_q8_isums", "strerror", "tile_geometry",
+    "lm_head_argmax", "lm_head_argmax_timed", "lm_head_argmax_masked", "lm_head_argmax_ws_bytes", "q4k_q8_isums", "strerror", "tile_geometry",
     "Q4K_BLOCK_BYTES", "Q6K_BLOCK_BYTES", "LIB_PATH", "HEADER_PATH",
 ]
 
@@ -53,6 +53,7 @@ _SIGS = {
     "swiglu_gemv": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _P]),
     "lm_head_argmax": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_size_t, _I64, _I64, _P]),
     "lm_head_argmax_timed": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_size_t, _I64, _I64, _P, _P, _P]),
+    "lm_head_argmax_masked": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_size_t, _I64, _I64, _P]),
     "gemvq_lm_head_argmax_ws_bytes": (ctypes.c_size_t, [_I64, _I64]),
     "gemvq_q4k_q8_isums": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P]),
     "gemvq_strerror": (ctypes.c_char_p, [ctypes.c_int]),
@@ -239,7 +240,20 @@ def lm_head_argmax_timed(W, x, N: int, K: int, workspace, start_event, stop_even
                     (_event_handle(start_event), _event_handle(stop_event)))
 
 
-def _lm_head(W, x, N, K, workspace, out_idx, out_max, want_max, stream, events):
+def lm_head_argmax_masked(W, x, mask, N: int, K: int, workspace, out_idx=None, out_max=None,
+                          want_max: bool = False, stream=None):
+    """lm_head_argmax over the rows the mask allows.  `mask` is an int32 (or
+    uint32) device tensor of ceil(N/32) words; bit i % 32 of word i // 32 set
+    bans row i."""
+    torch = _torch()
+    words = (N + 31) // 32
+    if (not isinstance(mask, torch.Tensor) or mask.device.type != "cuda" or mask.dtype not in (torch.int32, torch.uint32)
+            or mask.numel() < words or not mask.is_contiguous()):
+        raise TypeError(f"mask: expected a contiguous int32/uint32 device tensor of at least {words} words")
+    return _lm_head(W, x, N, K, workspace, out_idx, out_max, want_max, stream, None, mask)
+
+
+def _lm_head(W, x, N, K, workspace, out_idx, out_max, want_max, stream, events, mask=None):
     torch = _torch()
     _weights(W, N, K, Q6K_BLOCK_BYTES)
     _dev_tensor(x, torch.float32, K, "x")
@@ -252,7 +266,9 @@ def _lm_head(W, x, N, K, workspace, out_idx, out_max, want_max, stream, events):
         _dev_tensor(out_max, torch.float32, 1, "out_max")
     args = (W.data_ptr(), x.data_ptr(), out_idx.data_ptr(), out_max.data_ptr() if out_max is not None else None,
             workspace.data_ptr(), workspace.numel(), N, K, _stream(x, stream))
-    if events is None:
+    if mask is not None:
+        _check("lm_head_argmax_masked", lib().lm_head_argmax_masked(args[0], args[1], mask.data_ptr(), *args[2:]))
+    elif events is None:
         _check("lm_head_argmax", lib().lm_head_argmax(*args))
     else:
         _check("lm_head_argmax_timed", lib().lm_head_argmax_timed(*args, *events))

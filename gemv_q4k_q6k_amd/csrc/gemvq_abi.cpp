@@ -164,33 +164,39 @@ int swiglu_gemv(const void *Wg, const void *Wu, const float *x, float *h, int64_
     return status_of(gemvq::launch_swiglu_gemv(Wg, Wu, x, h, N, K, cus, (hipStream_t)stream));
 }
 
-static int lm_head_argmax_impl(const void *W, const float *x, uint32_t *out_idx, float *out_max, void *workspace,
-                               size_t ws_bytes, int64_t N, int64_t K, void *stream, const gemvq::Timing &tm)
+static int lm_head_argmax_impl(const void *W, const float *x, const uint32_t *mask, uint32_t *out_idx, float *out_max,
+                               void *workspace, size_t ws_bytes, int64_t N, int64_t K, void *stream,
+                               const gemvq::Timing &tm)
 {
     if (!W || !x || !out_idx || !workspace) return GEMVQ_ERR_NULL;
     size_t wb = 0;
     if (int st = check_shape(N, K, 210, &wb)) return st;
     if (!aligned(W, 4) || !aligned(x, 16) || !aligned(out_idx, 4) || (out_max && !aligned(out_max, 4)) ||
-        !aligned(workspace, 256))
+        !aligned(workspace, 256) || (mask && !aligned(mask, 4)))
         return GEMVQ_ERR_ALIGN;
     if (ws_bytes < gemvq::kArgmaxWsBytes) return GEMVQ_ERR_WORKSPACE;
     const size_t nx = (size_t)K * 4;
-    if (overlap(out_idx, 4, W, wb) || overlap(out_idx, 4, x, nx) || overlap(out_idx, 4, workspace, ws_bytes))
+    const size_t nm = mask ? (size_t)((N + 31) / 32) * 4 : 0;
+    if (overlap(out_idx, 4, W, wb) || overlap(out_idx, 4, x, nx) || overlap(out_idx, 4, workspace, ws_bytes) ||
+        overlap(out_idx, 4, mask, nm))
         return GEMVQ_ERR_ALIAS;
     if (out_max && (overlap(out_max, 4, W, wb) || overlap(out_max, 4, x, nx) ||
-                    overlap(out_max, 4, workspace, ws_bytes) || overlap(out_max, 4, out_idx, 4)))
+                    overlap(out_max, 4, workspace, ws_bytes) || overlap(out_max, 4, out_idx, 4) ||
+                    overlap(out_max, 4, mask, nm)))
         return GEMVQ_ERR_ALIAS;
-    if (overlap(workspace, ws_bytes, W, wb) || overlap(workspace, ws_bytes, x, nx)) return GEMVQ_ERR_ALIAS;
+    if (overlap(workspace, ws_bytes, W, wb) || overlap(workspace, ws_bytes, x, nx) ||
+        overlap(workspace, ws_bytes, mask, nm))
+        return GEMVQ_ERR_ALIAS;
     int cus = 0;
     if (int st = device_cus(&cus)) return st;
-    return status_of(
-        gemvq::launch_lm_head_argmax(W, x, out_idx, out_max, workspace, N, K, cus, (hipStream_t)stream, tm));
+    return status_of(gemvq::launch_lm_head_argmax(W, x, mask, out_idx, out_max, workspace, N, K, cus,
+                                                  (hipStream_t)stream, tm));
 }
 
 int lm_head_argmax(const void *W, const float *x, uint32_t *out_idx, float *out_max, void *workspace, size_t ws_bytes,
                    int64_t N, int64_t K, void *stream)
 {
-    return lm_head_argmax_impl(W, x, out_idx, out_max, workspace, ws_bytes, N, K, stream, gemvq::Timing{});
+    return lm_head_argmax_impl(W, x, nullptr, out_idx, out_max, workspace, ws_bytes, N, K, stream, gemvq::Timing{});
 }
 
 int lm_head_argmax_timed(const void *W, const float *x, uint32_t *out_idx, float *out_max, void *workspace,
@@ -199,7 +205,14 @@ int lm_head_argmax_timed(const void *W, const float *x, uint32_t *out_idx, float
     gemvq::Timing tm;
     tm.start = (hipEvent_t)start_event;
     tm.stop = (hipEvent_t)stop_event;
-    return lm_head_argmax_impl(W, x, out_idx, out_max, workspace, ws_bytes, N, K, stream, tm);
+    return lm_head_argmax_impl(W, x, nullptr, out_idx, out_max, workspace, ws_bytes, N, K, stream, tm);
+}
+
+int lm_head_argmax_masked(const void *W, const float *x, const uint32_t *mask, uint32_t *out_idx, float *out_max,
+                          void *workspace, size_t ws_bytes, int64_t N, int64_t K, void *stream)
+{
+    if (!mask) return GEMVQ_ERR_NULL;
+    return lm_head_argmax_impl(W, x, mask, out_idx, out_max, workspace, ws_bytes, N, K, stream, gemvq::Timing{});
 }
 
 int gemvq_q4k_q8_isums(const void *W, const int8_t *xq, int32_t *isums, int64_t N, int64_t K, void *stream)

@@ -22,7 +22,8 @@
 namespace gemvq {
 
 enum Kind : int { kQ4K = 0, kQ6K = 1, kQ4KQ8 = 2, kSwiglu = 3 };
-enum Epi : int { kStore = 0, kArgmax = 1 };
+enum Epi : int { kStore = 0, kArgmax = 1, kArgmaxMasked = 2 };
+constexpr bool is_argmax(int epi) { return epi != kStore; }
 
 
 struct GemvArgs {
@@ -35,6 +36,7 @@ struct GemvArgs {
     uint32_t *out_idx;     // argmax result
     float *out_max;        // argmax value or nullptr
     uint8_t *ws;           // argmax workspace
+    const uint32_t *mask;  // masked argmax: bit (i & 31) of word i >> 5 set = row i banned
     int64_t N;
     int tiles;             // ceil(N / rows_tile)
     int tiles_q, tiles_r;  // tiles per workgroup: tiles_q, plus one for the first tiles_r workgroups
@@ -244,12 +246,15 @@ __device__ __forceinline__ void dot_raw(const RawSet<KIND> &rs, const XSlice<KIN
 // ---------------------------------------------------------------- epilogue
 
 // Running argmax of a thread: the largest key (argmax_key) of the rows it has
-// emitted; NaN rows are skipped, 0 means none.
+// emitted; NaN rows are skipped, and so are banned rows of a masked argmax
+// (`mword` is the mask word holding the row's bit), 0 means none.
 template <int KIND, int EPI>
-__device__ __forceinline__ void emit_row(const GemvArgs &a, int64_t row, const float (&v)[2], uint64_t &best)
+__device__ __forceinline__ void emit_row(const GemvArgs &a, int64_t row, const float (&v)[2], uint64_t &best,
+                                         uint32_t mword = 0)
 {
-    if constexpr (EPI == kArgmax) {
-        const uint64_t k = (v[0] != v[0]) ? 0ull : argmax_key(v[0], (uint32_t)row);
+    if constexpr (is_argmax(EPI)) {
+        const bool banned = EPI == kArgmaxMasked && ((mword >> (row & 31)) & 1u);
+        const uint64_t k = (v[0] != v[0] || banned) ? 0ull : argmax_key(v[0], (uint32_t)row);
         best = k > best ? k : best;
     } else if constexpr (KIND == kSwiglu) {
         const float g = v[0], u = v[1];
@@ -486,7 +491,9 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_kernel(GemvArgs a)
                         for (; c < a.nb; ++c) acc += src[c];
                         r[o] = acc;
                     }
-                    emit_row<KIND, EPI>(a, row, r, best);
+                    uint32_t mw = 0;
+                    if constexpr (EPI == kArgmaxMasked) mw = a.mask[row >> 5];
+                    emit_row<KIND, EPI>(a, row, r, best, mw);
                 }
             }
             buf ^= 1;   // the next tile writes the other half; one barrier per tile suffices
@@ -505,7 +512,7 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_kernel(GemvArgs a)
         }
     }
 
-    if constexpr (EPI == kArgmax) {
+    if constexpr (is_argmax(EPI)) {
         // the row-sum threads hold the keys
         argmax_finish(a, best, tid < a.rows_tile ? tid : -1, a.rows_tile);
     }
@@ -602,10 +609,23 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_wave_kernel(Gem
     }
     int unit[kPhase];
     RawSet<KIND> ring[kPhase][STEPS];
+    // masked argmax: each unit's mask word is loaded with its weights (the
+    // word of the lane's row, clamped to the last row)
+    uint32_t mword[kPhase];
+    auto fetch_mask = [&](int d, int u, int prev) {
+        if constexpr (EPI == kArgmaxMasked) {
+            int64_t row = (int64_t)(u < u_end ? u : prev) * a.rows_tile + p;
+            row = row < a.N ? row : a.N - 1;
+            mword[d] = a.mask[row >> 5];
+        } else {
+            mword[d] = 0;
+        }
+    };
 #pragma unroll
     for (int d = 0; d < kPhase; ++d) {
         unit[d] = umap(d * waves + wave);
         fetch(ring[d], unit[d], u_end - 1);
+        fetch_mask(d, unit[d], u_end - 1);
     }
     if (tid == 0) s_next = (uint32_t)(kPhase * waves);
 #pragma unroll
@@ -660,17 +680,18 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_wave_kernel(Gem
                 float r[2];
 #pragma unroll
                 for (int o = 0; o < OUTS; ++o) r[o] = group_sum(v ? ps[o] : 0.f, a.lanes_row);
-                if (rr == 0 && v) emit_row<KIND, EPI>(a, (int64_t)unit[d] * a.rows_tile + p, r, best);
+                if (rr == 0 && v) emit_row<KIND, EPI>(a, (int64_t)unit[d] * a.rows_tile + p, r, best, mword[d]);
                 uint32_t c = 0;
                 if (lane == 0) c = __hip_atomic_fetch_add(&s_next, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
                 const int done = unit[d];
                 unit[d] = umap((int)__builtin_amdgcn_readfirstlane(c));
                 fetch(ring[d], unit[d], done);
+                fetch_mask(d, unit[d], done);
             }
         }
     }
 
-    if constexpr (EPI == kArgmax) {
+    if constexpr (is_argmax(EPI)) {
         // each wave's largest key reaches lane 0, then the workgroup's
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) {
@@ -842,7 +863,12 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_rows_kernel(Gem
                         float r[2];
 #pragma unroll
                         for (int o = 0; o < OUTS; ++o) r[o] = group_sum(acc[o], group);
-                        if (rr == 0 && v) emit_row<KIND, EPI>(a, (int64_t)u * a.rows_tile + p, r, best);
+                        if (rr == 0 && v) {
+                            const int64_t row = (int64_t)u * a.rows_tile + p;
+                            uint32_t mw = 0;
+                            if constexpr (EPI == kArgmaxMasked) mw = a.mask[row >> 5];
+                            emit_row<KIND, EPI>(a, row, r, best, mw);
+                        }
                     }
                     ring_u[d] = fu;
                     ring_s[d] = fs;
@@ -853,7 +879,7 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_rows_kernel(Gem
         }
     }
 
-    if constexpr (EPI == kArgmax) {
+    if constexpr (is_argmax(EPI)) {
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) {
             const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)best, off);
@@ -1073,7 +1099,7 @@ static hipError_t launch_mode(Plan &pl, GemvArgs a, int cus, hipStream_t s, cons
     // leaves at most one tile per workgroup the single-tile kernel runs
     const void *fn2 = (const void *)gemv_kernel<KIND, EPI, 2, XLDS>;
     pl.grid = grid_for(pl, fn2, cus, KIND == kSwiglu ? 2 : 4);
-    if (EPI == kArgmax && pl.grid > kArgmaxMaxGrid) pl.grid = kArgmaxMaxGrid;   // one workspace slot each
+    if (is_argmax(EPI) && pl.grid > kArgmaxMaxGrid) pl.grid = kArgmaxMaxGrid;   // one workspace slot each
     a.tiles_q = (int)(pl.tiles / pl.grid);
     a.tiles_r = (int)(pl.tiles % pl.grid);
     if (a.tiles_q >= 2 || (a.tiles_q == 1 && a.tiles_r > 0))
@@ -1188,8 +1214,9 @@ hipError_t launch_q4k_q8_gemv(const void *W, const int8_t *xq, const uint16_t *x
     return launch<kQ4KQ8, kStore>(pl, a, cus, s);
 }
 
-hipError_t launch_lm_head_argmax(const void *W, const float *x, uint32_t *out_idx, float *out_max, void *ws, int64_t N,
-                                 int64_t K, int cus, hipStream_t s, const Timing &tm)
+hipError_t launch_lm_head_argmax(const void *W, const float *x, const uint32_t *mask, uint32_t *out_idx,
+                                 float *out_max, void *ws, int64_t N, int64_t K, int cus, hipStream_t s,
+                                 const Timing &tm)
 {
     Plan pl = make_plan(N, K, kQ6K);
     GemvArgs a = base_args(pl, N);
@@ -1198,6 +1225,8 @@ hipError_t launch_lm_head_argmax(const void *W, const float *x, uint32_t *out_id
     a.ws = (uint8_t *)ws;
     a.out_idx = out_idx;
     a.out_max = out_max;
+    a.mask = mask;
+    if (mask) return launch<kQ6K, kArgmaxMasked>(pl, a, cus, s, tm);
     return launch<kQ6K, kArgmax>(pl, a, cus, s, tm);
 }
 

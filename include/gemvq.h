@@ -138,6 +138,21 @@ int lm_head_argmax_timed(const void *W, const float *x, uint32_t *out_idx, float
                          void *workspace, size_t ws_bytes, int64_t N, int64_t K, void *stream,
                          void *start_event, void *stop_event);
 
+/*
+ * lm_head_argmax over the rows a mask allows: rows whose bit is set in `mask`
+ * are banned and never win, exactly as if their value were NaN (memra-engine
+ * decode.rs `decode_step_dc_cap_masked`: a grammar mask bans tokens before
+ * the argmax reads the row, and the masked device argmax equals the masked
+ * host argmax).  The result is the first index of the largest value among the
+ * allowed, non-NaN rows; if there is none, 0 (out_max NaN).
+ *   mask: uint32[ceil(N/32)], device memory, 4-B aligned; bit (i % 32) of
+ *   word i / 32 bans row i; bits past N are ignored.  Other arguments,
+ *   workspace rules and errors as lm_head_argmax; mask NULL is GEMVQ_ERR_NULL.
+ */
+int lm_head_argmax_masked(const void *W, const float *x, const uint32_t *mask, uint32_t *out_idx,
+                          float *out_max, void *workspace, size_t ws_bytes, int64_t N, int64_t K,
+                          void *stream);
+
 /* Workspace bytes lm_head_argmax needs for an N x K call (host-only, no HIP call). */
 size_t gemvq_lm_head_argmax_ws_bytes(int64_t N, int64_t K);
 

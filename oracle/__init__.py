@@ -67,6 +67,8 @@ def _load():
             "orc_q4k_q8_gemv": (None, [P, P, P, P, I64, I64]),
             "orc_argmax_first_f64": (I64, [P, I64]),
             "orc_argmax_first_f32": (I64, [P, I64]),
+            "orc_argmax_first_masked_f64": (I64, [P, P, I64]),
+            "orc_argmax_first_masked_f32": (I64, [P, P, I64]),
             "orc_num_threads": (ctypes.c_int, []),
             "orc_set_num_threads": (None, [ctypes.c_int]),
         }
@@ -203,6 +205,19 @@ def argmax_first(v) -> int:
         return int(_load().orc_argmax_first_f32(_ptr(v), v.size))
     v = _vec(v, np.float64)
     return int(_load().orc_argmax_first_f64(_ptr(v), v.size))
+
+
+def argmax_first_masked(v, mask_words) -> int:
+    """First index of the maximum over non-NaN rows the mask allows (bit
+    i % 32 of word i // 32 set bans row i); 0 if none is left."""
+    v = np.asarray(v)
+    m = np.ascontiguousarray(np.asarray(mask_words).view(np.uint32))
+    assert m.size * 32 >= v.size
+    if v.dtype == np.float32:
+        v = np.ascontiguousarray(v)
+        return int(_load().orc_argmax_first_masked_f32(_ptr(v), _ptr(m), v.size))
+    v = _vec(v, np.float64)
+    return int(_load().orc_argmax_first_masked_f64(_ptr(v), _ptr(m), v.size))
 
 
 def top2_gap(v) -> float:

@@ -361,6 +361,39 @@ int64_t orc_argmax_first_f32(const float *v, int64_t n)
     return best < 0 ? 0 : best;
 }
 
+/* Masked argmax (memra-engine decode.rs, `decode_step_dc_cap_masked`: a
+ * grammar mask bans tokens before the argmax reads the row).  Row i is banned
+ * when bit (i % 32) of mask[i / 32] is set; banned and NaN rows are skipped;
+ * the first index of the largest remaining value wins; none left gives 0. */
+static int orc_banned(const uint32_t *mask, int64_t i)
+{
+    return (int)((mask[i / 32] >> (i % 32)) & 1u);
+}
+
+int64_t orc_argmax_first_masked_f64(const double *v, const uint32_t *mask, int64_t n)
+{
+    int64_t best = -1;
+    for (int64_t i = 0; i < n; ++i) {
+        if (isnan(v[i]) || orc_banned(mask, i))
+            continue;
+        if (best < 0 || v[i] > v[best])
+            best = i;
+    }
+    return best < 0 ? 0 : best;
+}
+
+int64_t orc_argmax_first_masked_f32(const float *v, const uint32_t *mask, int64_t n)
+{
+    int64_t best = -1;
+    for (int64_t i = 0; i < n; ++i) {
+        if (isnan(v[i]) || orc_banned(mask, i))
+            continue;
+        if (best < 0 || v[i] > v[best])
+            best = i;
+    }
+    return best < 0 ? 0 : best;
+}
+
 /* Number of OpenMP threads a parallel region uses (1 without OpenMP). */
 int orc_num_threads(void)
 {

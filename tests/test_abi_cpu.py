@@ -74,6 +74,7 @@ def test_null_pointers():
     _rejected(L.lm_head_argmax(A, B, C, None, None, 1 << 20, 4, 256, None), gq.ERR_NULL)
     _rejected(L.lm_head_argmax_timed(A, B, C, None, None, 1 << 20, 4, 256, None, None, None), gq.ERR_NULL)
     _rejected(L.gemvq_q4k_q8_isums(A, B, None, 4, 256, None), gq.ERR_NULL)
+    _rejected(L.lm_head_argmax_masked(A, B, None, C, D, E, 1 << 20, 4, 256, None), gq.ERR_NULL)
 
 
 @pytest.mark.parametrize("N,K", [(0, 256), (-1, 256), (4, 0), (4, 255), (4, 300), (4, 128),
@@ -109,6 +110,7 @@ def test_alignment():
     _rejected(L.lm_head_argmax(A, B, C + 1, D, E, 1 << 20, 4, 256, None), gq.ERR_ALIGN)
     _rejected(L.lm_head_argmax_timed(A, B, C + 1, D, E, 1 << 20, 4, 256, None, None, None), gq.ERR_ALIGN)
     _rejected(L.gemvq_q4k_q8_isums(A, B, C + 2, 4, 256, None), gq.ERR_ALIGN)
+    _rejected(L.lm_head_argmax_masked(A, B, C + 2, D, None, E, 1 << 20, 4, 256, None), gq.ERR_ALIGN)
 
 
 def test_workspace_too_small():
@@ -135,6 +137,8 @@ def test_aliasing():
     _rejected(L.lm_head_argmax(A, B, E + 8, None, E, ws, N, K, None), gq.ERR_ALIAS)   # idx inside ws
     _rejected(L.lm_head_argmax(A, B, C, C, E, ws, N, K, None), gq.ERR_ALIAS)          # max == idx
     _rejected(L.lm_head_argmax(A, B, C, None, A + 256, ws, N, K, None), gq.ERR_ALIAS)  # ws inside W
+    _rejected(L.lm_head_argmax_masked(A, B, C, C, None, E, ws, N, K, None), gq.ERR_ALIAS)   # idx over the mask
+    _rejected(L.lm_head_argmax_masked(A, B, E + 64, C, None, E, ws, N, K, None), gq.ERR_ALIAS)  # mask inside ws
     _rejected(L.gemvq_q4k_q8_isums(A, B, B, N, K, None), gq.ERR_ALIAS)
 
 

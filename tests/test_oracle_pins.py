@@ -354,3 +354,39 @@ def test_argmax_edges():
 def test_top2_gap():
     assert oracle.top2_gap(np.array([1.0, 5.0, 3.0])) == 2.0
     assert oracle.top2_gap(np.array([5.0, 1.0, 5.0])) == 0.0
+
+
+# ------------------------------------------------------------ masked argmax
+def _np_masked_first_max(v, words, n):
+    banned = np.unpackbits(np.asarray(words, np.uint32).view(np.uint8), bitorder="little")[:n].astype(bool)
+    allowed = ~banned & ~np.isnan(v)
+    if not allowed.any():
+        return 0
+    m = v[allowed].max()
+    return int(np.flatnonzero(allowed & (v == m))[0])
+
+
+def test_masked_argmax_vs_numpy():
+    rng = np.random.default_rng(21)
+    for n in (1, 31, 32, 33, 1000, 4097):
+        for density in (0.0, 0.3, 0.9, 1.0):
+            v = rng.standard_normal(n)
+            v[rng.random(n) < 0.05] = np.nan
+            if n > 10:
+                v[n // 3] = v[2 * n // 3] = 10.0          # a tie
+            bits = rng.random(n) < density
+            words = np.packbits(np.concatenate([bits, np.zeros((-n) % 32, bool)]), bitorder="little").view(np.uint32)
+            for dtype in (np.float64, np.float32):
+                vv = v.astype(dtype)
+                assert oracle.argmax_first_masked(vv, words) == _np_masked_first_max(vv, words, n), (n, density)
+
+
+def test_masked_argmax_edges():
+    v = np.array([1.0, 7.0, 7.0, 3.0, np.nan, 7.5])
+    none = np.zeros(1, np.uint32)
+    assert oracle.argmax_first_masked(v, none) == oracle.argmax_first(v) == 5
+    assert oracle.argmax_first_masked(v, np.array([1 << 5], np.uint32)) == 1       # best banned: first of the tie
+    assert oracle.argmax_first_masked(v, np.array([(1 << 5) | (1 << 1)], np.uint32)) == 2
+    assert oracle.argmax_first_masked(v, np.array([0x3F], np.uint32)) == 0          # everything banned
+    assert oracle.argmax_first_masked(v, np.array([0xFFFFFFFF], np.uint32)) == 0    # bits past n ignored
+    assert oracle.argmax_first_masked(v, np.array([0x2F], np.uint32)) == 0          # only NaN left -> 0

@@ -432,3 +432,84 @@ def test_q4k_f32_c5_shape_full(dev):
     N, K = synth.C5_Q8
     y = gq().q4k_gemv(up(W, dev), up(x, dev), N, K).cpu().numpy()
     check_f32("C5 f32 q4k", y, oracle.q4k_gemv(W, x, N, K))
+
+
+# ------------------------------------------------------------ masked argmax
+def _mask_words(bits):
+    n = bits.size
+    return np.packbits(np.concatenate([bits, np.zeros((-n) % 32, bool)]), bitorder="little").view(np.uint32)
+
+
+def _masked_case(dev, W, x, N, K, bits, ws):
+    words = _mask_words(bits)
+    dmask = torch.from_numpy(words.view(np.int32)).to(dev)
+    idx, vmax = gq().lm_head_argmax_masked(up(W, dev), up(x, dev), dmask, N, K, ws, want_max=True)
+    idx = int(idx.item())
+    logits = gq().q6k_gemv(up(W, dev), up(x, dev), N, K).cpu().numpy()
+    # self-consistency with the library's own logits, masked on the host
+    assert idx == oracle.argmax_first_masked(logits, words), (idx, oracle.argmax_first_masked(logits, words))
+    yhat = oracle.q6k_gemv(W, x, N, K)
+    ihat = oracle.argmax_first_masked(yhat, words)
+    allowed = ~bits
+    if allowed.any():
+        vals = np.sort(yhat[allowed])[::-1]
+        if vals.size < 2 or vals[0] - vals[1] > 1e-3:
+            assert idx == ihat, (idx, ihat)
+        assert float(vmax.item()) == float(logits[idx])
+    else:
+        assert idx == 0 and np.isnan(float(vmax.item()))
+    return idx, ihat
+
+
+@pytest.mark.parametrize("N,K", [(20_000, 1024), (5000, 2560), (3000, 9728)])
+def test_lm_head_argmax_masked(dev, N, K):
+    """Banned rows never win, on every kernel path (one-wave units, row-stream,
+    tiles); the best allowed row wins at its first index."""
+    r = synth.rng_for(777 + N)
+    W = synth.q6k_weights(r, N, K)
+    x = synth.activation(r, K)
+    ws = _ws(dev, N, K)
+    yhat = oracle.q6k_gemv(W, x, N, K)
+    top = oracle.argmax_first(yhat)
+    rng = np.random.default_rng(N)
+    cases = [np.zeros(N, bool), rng.random(N) < 0.5, rng.random(N) < 0.999, np.ones(N, bool)]
+    only_top_banned = np.zeros(N, bool)
+    only_top_banned[top] = True
+    cases.append(only_top_banned)
+    for bits in cases:
+        idx, ihat = _masked_case(dev, W, x, N, K, bits, ws)
+        if bits[top]:
+            assert idx != top
+    assert int(torch.count_nonzero(ws[:4096]).item()) == 0
+
+
+def test_lm_head_argmax_masked_ties(dev):
+    """Three copies of the best row; banning the first copy makes the second
+    win, banning the first two the third."""
+    N, K = 9000, 1024
+    W, x = synth.c3_inputs(31, N=N)
+    yhat = oracle.q6k_gemv(W, x, N, K)
+    top = oracle.argmax_first(yhat)
+    pos = sorted({top, (top + 1234) % N, (top + 4321) % N})
+    Wt = W.copy()
+    for p_ in pos:
+        Wt[p_] = W[top]
+    ws = _ws(dev, N, K)
+    bits = np.zeros(N, bool)
+    idx, _ = _masked_case(dev, Wt, x, N, K, bits, ws)
+    assert idx == pos[0]
+    bits[pos[0]] = True
+    idx, _ = _masked_case(dev, Wt, x, N, K, bits, ws)
+    assert idx == pos[1]
+    bits[pos[1]] = True
+    idx, _ = _masked_case(dev, Wt, x, N, K, bits, ws)
+    assert idx == pos[2]
+
+
+def test_lm_head_argmax_masked_c3_full(dev, c3_full):
+    W, x, dW, dx = c3_full
+    N, K = synth.C3_LM_HEAD
+    rng = np.random.default_rng(5)
+    bits = rng.random(N) < 0.7
+    ws = _ws(dev, N, K)
+    _masked_case(dev, W, x, N, K, bits, ws)
