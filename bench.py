@@ -168,6 +168,33 @@ def run_step(gq, s, v):
     gq.q4k_q8_gemv(s["c5W"], v["xq"], v["xd"], N, K, y=v["c5y"])
 
 
+def graph_step_ms(gq, sets, v, steps):
+    """ms per step when each step is one replay of a HIP graph holding the
+    whole step (one graph per weight copy, replayed alternately): the same
+    kernels without per-launch host work."""
+    import torch
+    graphs = []
+    for s in sets:
+        run_step(gq, s, v)   # warm-up outside capture
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run_step(gq, s, v)
+        graphs.append(g)
+    for k in range(4):
+        graphs[k % 2].replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for k in range(steps):
+        graphs[k % 2].replay()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    del graphs
+    return ms
+
+
 def sync_rate(prepared, v, n=400):
     """lm_head calls per second when every call is followed by the 4-byte
     download of the token id and a host sync (a greedy decode loop's
@@ -468,6 +495,7 @@ def main():
 
     wb = weight_bytes()
     step_bytes = sum(wb.values())
+    gms = graph_step_ms(gq, sets, v, args.steps)
     value = step_bytes / (ms_step * 1e-3) / 1e9
     alg = lm_head_algorithmic_bytes()
     achieved = alg / (lm_us * 1e-6) / 1e9
@@ -486,6 +514,8 @@ def main():
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "lm_head_argmax_calls_per_s": round(1e6 / lm_us, 1),
         "lm_head_argmax_sync_calls_per_s": round(sync_rate(prepared, v), 1),
+        "graph_ms_per_step": round(gms, 4),
+        "graph_value": round(step_bytes / (gms * 1e-3) / 1e9, 1),
         "self_check_ok": parity_ok,
         "wall_s": round(wall, 3),
         "roofline": roofline,
