@@ -309,6 +309,24 @@ def breakdown(gq, sets, v, reps=24):
     timeit("q4k_gemv_28672x8192", lambda w: gq.q4k_gemv(w[0], v["c5x"], N, K, y=v["c5y"]), ws,
            N * K // 256 * 144 + 4 * (N + K))
     del ws
+    # the fused q/k/v projection of a 4B-class attention block (one launch for
+    # three Q4_K matrices sharing x) against three separate launches
+    K = 2560
+    qkv = (4096, 1024, 1024)
+    r = synth.rng_for(77)
+    mats = [torch.from_numpy(synth.q4k_weights(r, n, K)).to(dev) for n in qkv]
+    xq = torch.from_numpy(synth.activation(r, K)).to(dev)
+    ys = [torch.empty(n, dtype=torch.float32, device=dev) for n in qkv]
+    nbytes = sum(n * K // 256 * 144 for n in qkv) + 4 * (K + sum(qkv))
+    sets_ = list(zip(*[copies(m) for m in mats]))
+    timeit("q4k_gemv_multi_qkv_4096+1024+1024x2560",
+           lambda w: gq.q4k_gemv_multi(list(w), list(qkv), xq, K, ys=ys), sets_, nbytes)
+
+    def three(w):
+        for m, n, y in zip(w, qkv, ys):
+            gq.q4k_gemv(m, xq, n, K, y=y)
+    timeit("q4k_gemv_x3_separate_4096+1024+1024x2560", three, sets_, nbytes)
+    del sets_, mats
     torch.cuda.empty_cache()
     return out
 

@@ -19,7 +19,7 @@ import threading
 
 __all__ = [
     "GemvqError", "lib", "exported_names", "header_names",
-    "q4k_gemv", "q6k_gemv", "q8_quantize", "q4k_q8_gemv", "swiglu_gemv",
+    "q4k_gemv", "q4k_gemv_multi", "q6k_gemv", "q8_quantize", "q4k_q8_gemv", "swiglu_gemv",
     "lm_head_argmax", "lm_head_argmax_timed", "lm_head_argmax_masked", "lm_head_argmax_ws_bytes", "q4k_q8_isums", "strerror", "tile_geometry",
     "Q4K_BLOCK_BYTES", "Q6K_BLOCK_BYTES", "LIB_PATH", "HEADER_PATH",
 ]
@@ -47,6 +47,7 @@ _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
 _SIGS = {
     "q4k_gemv": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P]),
+    "q4k_gemv_multi": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int, _P, _I64, _P]),
     "q6k_gemv": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P]),
     "q8_quantize": (ctypes.c_int, [_P, _P, _P, _I64, _P]),
     "q4k_q8_gemv": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _P]),
@@ -160,6 +161,36 @@ def q4k_gemv(W, x, N: int, K: int, y=None, stream=None):
     y = _out(y, x.device, torch.float32, N, "y")
     _check("q4k_gemv", lib().q4k_gemv(W.data_ptr(), x.data_ptr(), y.data_ptr(), N, K, _stream(x, stream)))
     return y
+
+
+def q4k_gemv_multi(Ws, Ns, x, K: int, ys=None, residuals=None, stream=None):
+    """y_i = W_i x (+ residuals[i]) for up to 4 Q4_K matrices of the same K in
+    one launch.  Returns the list of float32 outputs (ys if given).  A
+    residual may be its own output (in-place add)."""
+    torch = _torch()
+    count = len(Ws)
+    if count != len(Ns):
+        raise ValueError("Ws and Ns differ in length")
+    _dev_tensor(x, torch.float32, K, "x")
+    for W, N in zip(Ws, Ns):
+        _weights(W, N, K, Q4K_BLOCK_BYTES)
+    if ys is None:
+        ys = [None] * count
+    ys = [_out(y, x.device, torch.float32, N, f"y[{i}]") for i, (y, N) in enumerate(zip(ys, Ns))]
+    if residuals is not None:
+        for i, (r, N) in enumerate(zip(residuals, Ns)):
+            if r is not None:
+                _dev_tensor(r, torch.float32, N, f"residual[{i}]")
+    P = ctypes.c_void_p * count
+    w_arr = P(*[W.data_ptr() for W in Ws])
+    y_arr = P(*[y.data_ptr() for y in ys])
+    n_arr = (ctypes.c_int64 * count)(*Ns)
+    r_arr = None if residuals is None else P(*[r.data_ptr() if r is not None else None for r in residuals])
+    _check("q4k_gemv_multi", lib().q4k_gemv_multi(ctypes.cast(w_arr, ctypes.c_void_p), ctypes.cast(n_arr, ctypes.c_void_p),
+                                                  ctypes.cast(y_arr, ctypes.c_void_p),
+                                                  ctypes.cast(r_arr, ctypes.c_void_p) if r_arr is not None else None,
+                                                  count, x.data_ptr(), K, _stream(x, stream)))
+    return ys
 
 
 def q6k_gemv(W, x, N: int, K: int, y=None, stream=None):

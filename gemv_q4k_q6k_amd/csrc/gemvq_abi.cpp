@@ -103,6 +103,41 @@ int gemvq_tile_geometry(int kind, int64_t N, int64_t K, int64_t out[7])
     return GEMVQ_OK;
 }
 
+int q4k_gemv_multi(const void *const *W, const int64_t *N, float *const *y, const float *const *residual, int count,
+                   const float *x, int64_t K, void *stream)
+{
+    if (!W || !N || !y || !x) return GEMVQ_ERR_NULL;
+    if (count < 1 || count > gemvq::kMaxMulti) return GEMVQ_ERR_SHAPE;
+    size_t wb[gemvq::kMaxMulti] = {0};
+    int64_t total = 0;
+    for (int i = 0; i < count; ++i) {
+        if (!W[i] || !y[i]) return GEMVQ_ERR_NULL;
+        if (int st = check_shape(N[i], K, 144, &wb[i])) return st;
+        total += N[i];
+    }
+    if (K > gemvq::kMaxMultiK || total > kMaxN) return GEMVQ_ERR_SHAPE;
+    if (!aligned(x, 16)) return GEMVQ_ERR_ALIGN;
+    for (int i = 0; i < count; ++i) {
+        if (!aligned(W[i], 16) || !aligned(y[i], 4)) return GEMVQ_ERR_ALIGN;
+        if (residual && residual[i] && !aligned(residual[i], 4)) return GEMVQ_ERR_ALIGN;
+    }
+    const size_t nx = (size_t)K * 4;
+    for (int i = 0; i < count; ++i) {
+        const size_t ny = (size_t)N[i] * 4;
+        if (overlap(y[i], ny, x, nx)) return GEMVQ_ERR_ALIAS;
+        for (int j = 0; j < count; ++j) {
+            if (overlap(y[i], ny, W[j], wb[j])) return GEMVQ_ERR_ALIAS;
+            if (j != i && overlap(y[i], ny, y[j], (size_t)N[j] * 4)) return GEMVQ_ERR_ALIAS;
+            // a residual may be its own output exactly (in-place add), nothing else
+            const float *r = residual ? residual[j] : nullptr;
+            if (r && overlap(y[i], ny, r, (size_t)N[j] * 4) && !(j == i && r == y[i])) return GEMVQ_ERR_ALIAS;
+        }
+    }
+    int cus = 0;
+    if (int st = device_cus(&cus)) return st;
+    return status_of(gemvq::launch_q4k_gemv_multi(W, N, y, residual, count, x, K, cus, (hipStream_t)stream));
+}
+
 int q4k_gemv(const void *W, const float *x, float *y, int64_t N, int64_t K, void *stream)
 {
     if (!W || !x || !y) return GEMVQ_ERR_NULL;

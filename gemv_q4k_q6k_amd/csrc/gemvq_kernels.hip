@@ -47,6 +47,13 @@ struct GemvArgs {
     int x_in_lds;          // stage the activation (and its 16-element sums) through LDS first
     int steps;             // row-stream kernel: 16-super-block steps per row
     int chunk_shift;       // wave/row-stream kernels: units are dealt in chunks of 1 << chunk_shift
+    // multi-output launches (gemv_rows_kernel<..., MULTI = 1>): up to kMaxMulti
+    // matrices of the same K; units [ustart[m], ustart[m+1]) belong to matrix m
+    const uint8_t *Wm[kMaxMulti];
+    float *ym[kMaxMulti];
+    const float *rm[kMaxMulti];   // residual added to y, or nullptr
+    int64_t Nm[kMaxMulti];
+    int ustart[kMaxMulti + 1];
 };
 
 // ------------------------------------------------------- activation setup
@@ -718,7 +725,7 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_wave_kernel(Gem
 // runs a pipeline of (unit, step) pairs, two in flight; a row's step sums are
 // added in step order and reduced over its lane group, the same way for every
 // row.
-template <int KIND, int EPI>
+template <int KIND, int EPI, int MULTI>
 __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_rows_kernel(GemvArgs a)
 {
     constexpr int kPhase = 2;
@@ -751,20 +758,56 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_rows_kernel(Gem
 
     // super-block of this lane in step s, or -1 past the row's end
     auto block_of = [&](int st) { const int c = b + 16 * st; return c < a.nb ? c : -1; };
-    auto valid_row = [&](int u) { return u < u_end && (u < units - 1 || p < last_rows); };
+    // multi-output: the matrix of unit u (wave-uniform) and the unit's index in it
+    auto mat_of = [&](int u) {
+        int m = 0;
+        if constexpr (MULTI) {
+#pragma unroll
+            for (int j = 1; j < kMaxMulti; ++j) m += u >= a.ustart[j] ? 1 : 0;
+        }
+        return m;
+    };
+    auto valid_row = [&](int u) {
+        if constexpr (MULTI) {
+            const int m = mat_of(u);
+            return u < u_end && (int64_t)(u - a.ustart[m]) * a.rows_tile + p < a.Nm[m];
+        } else {
+            return u < u_end && (u < units - 1 || p < last_rows);
+        }
+    };
     // unconditional loads: past the range the unit `prev` is re-read (still
     // cached), an idle lane reads the unit's first super-block
     auto fetch = [&](RawSet<KIND> &rs, int u, int st, int prev) {
         const int uu = u < u_end ? u : prev;
         const int c = block_of(st);
         const uint32_t off = (valid_row(u) && c >= 0) ? (uint32_t)((p * a.nb + c) * BYTES) : 0u;
-        const int64_t ub = (int64_t)uu * unit_stride;
+        const uint8_t *Wb = a.W;
+        int64_t ub = (int64_t)uu * unit_stride;
+        if constexpr (MULTI) {
+            const int m = mat_of(uu);
+            Wb = a.Wm[m];
+            ub = (int64_t)(uu - a.ustart[m]) * unit_stride;
+        }
         if constexpr (KIND == kQ6K) {
-            q6k_load(rs.r[0], a.W + ub, off, part);
+            q6k_load(rs.r[0], Wb + ub, off, part);
         } else {
-            q4k_load(rs.r[0], a.W + ub, off, part);
+            q4k_load(rs.r[0], Wb + ub, off, part);
             if constexpr (KIND == kSwiglu) q4k_load(rs.r[1], a.W2 + ub, off, part);
         }
+    };
+    // multi-output residual of the lane's row in unit u (loaded with the unit's
+    // first step; a launch without residual re-reads y, which is discarded)
+    auto fetch_res = [&](int u, int prev) {
+        float r = 0.f;
+        if constexpr (MULTI) {
+            const int uu = u < u_end ? u : prev;
+            const int m = mat_of(uu);
+            int64_t row = (int64_t)(uu - a.ustart[m]) * a.rows_tile + p;
+            row = row < a.Nm[m] ? row : a.Nm[m] - 1;
+            const float *src = a.rm[m] ? a.rm[m] : a.ym[m];
+            r = src[row];
+        }
+        return r;
     };
 
     // activation loads first
@@ -786,6 +829,7 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_rows_kernel(Gem
     int next_fixed = umap(waves + wave);   // second fixed unit, then -1
     int ring_u[kPhase], ring_s[kPhase];
     RawSet<KIND> ring[kPhase];
+    float ring_r[kPhase];   // multi-output: residual of the lane's row
     auto advance = [&]() {
         if (++fs == S) {
             fs = 0;
@@ -806,6 +850,7 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_rows_kernel(Gem
         ring_u[d] = fu;
         ring_s[d] = fs;
         fetch(ring[d], fu, fs, u_end - 1);
+        ring_r[d] = fetch_res(fu, u_end - 1);
         advance();
     }
 
@@ -864,15 +909,22 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_rows_kernel(Gem
 #pragma unroll
                         for (int o = 0; o < OUTS; ++o) r[o] = group_sum(acc[o], group);
                         if (rr == 0 && v) {
-                            const int64_t row = (int64_t)u * a.rows_tile + p;
-                            uint32_t mw = 0;
-                            if constexpr (EPI == kArgmaxMasked) mw = a.mask[row >> 5];
-                            emit_row<KIND, EPI>(a, row, r, best, mw);
+                            if constexpr (MULTI) {
+                                const int m = mat_of(u);
+                                const int64_t row = (int64_t)(u - a.ustart[m]) * a.rows_tile + p;
+                                a.ym[m][row] = a.rm[m] ? r[0] + ring_r[d] : r[0];
+                            } else {
+                                const int64_t row = (int64_t)u * a.rows_tile + p;
+                                uint32_t mw = 0;
+                                if constexpr (EPI == kArgmaxMasked) mw = a.mask[row >> 5];
+                                emit_row<KIND, EPI>(a, row, r, best, mw);
+                            }
                         }
                     }
                     ring_u[d] = fu;
                     ring_s[d] = fs;
                     fetch(ring[d], fu, fs, u);
+                    ring_r[d] = fetch_res(fu, u);
                     advance();
                 }
             }
@@ -946,6 +998,40 @@ __global__ __launch_bounds__(256) void q4k_q8_isums_kernel(const uint8_t *__rest
 
 // Plan of a wave-unit or row-stream launch (every row reduced inside one
 // wave), or false when the shape goes to the tile kernel.
+// Shared tail of a wave-unit or row-stream plan (steps and lanes_row set).
+static bool finish_wave_plan(Plan &pl, int64_t N, int64_t K, int kind)
+{
+    pl.wave_local = 1;
+    pl.waves = (kind == kQ4KQ8 || (kind == kQ4K && pl.steps == 2) ? 1024 : 768) / 64;   // the most; the launch decides
+    pl.threads = pl.waves * 64;
+    pl.rows_tile = 64 / pl.lanes_row;
+    pl.tiles = (N + pl.rows_tile - 1) / pl.rows_tile;
+    // chunk of units whose bytes are a whole number of 128-byte lines
+    const int64_t unit_bytes = (int64_t)pl.rows_tile * pl.nb * (kind == kQ6K ? 210 : 144);
+    pl.chunk_shift = 0;
+    while (((unit_bytes << pl.chunk_shift) & 127) != 0) ++pl.chunk_shift;
+    const size_t xb = (kind == kQ4KQ8) ? (size_t)K : (size_t)K * 4;
+    pl.x_in_lds = 1;
+    pl.lds_bytes = xb + xb / 16 + ((kind == kQ4KQ8) ? 0 : (size_t)(K / 16) * 4);
+    pl.grid = 0;
+    return pl.lds_bytes <= 65536;   // larger x (f32, K > ~15000) goes to the tile kernel
+}
+
+// Row-stream plan: rows walked in steps of 16 super-blocks, each row inside a
+// power-of-two lane group of one wave.
+static bool plan_rows(Plan &pl, int64_t N, int64_t K, int kind)
+{
+    pl.nb = (int)(K / kQK);
+    pl.rows_kernel = 1;
+    pl.steps = (pl.nb + 15) / 16;
+    int g = 4;
+    while (g < 4 * pl.nb && g < 64) g *= 2;
+    pl.lanes_row = g;   // lanes per row: a power of two holding min(nb, 16) super-blocks
+    return finish_wave_plan(pl, N, K, kind);
+}
+
+// Plan of a wave-unit or row-stream launch (every row reduced inside one
+// wave), or false when the shape goes to the tile kernel.
 static bool plan_in_wave(Plan &pl, int64_t N, int64_t K, int kind)
 {
     pl.nb = (int)(K / kQK);
@@ -960,34 +1046,16 @@ static bool plan_in_wave(Plan &pl, int64_t N, int64_t K, int kind)
     // pair, the tile kernel's shorter start-up wins.
     const bool stream = (kind == kQ4K && pl.nb == 32) || (pl.nb < 16 && kind != kSwiglu && N <= 6144);
     if (!fits && !halves && !stream) return false;
-    // gemv_wave_kernel when the row's lanes are a power-of-two group (or two
-    // halves), gemv_rows_kernel (16-super-block steps) otherwise
-    pl.wave_local = 1;
-    pl.rows_kernel = (fits || halves) ? 0 : 1;
+    if (!fits && !halves) return plan_rows(pl, N, K, kind);
+    // gemv_wave_kernel: the row's lanes are a power-of-two group (or two halves)
+    pl.rows_kernel = 0;
     if (fits) {
         pl.steps = 1;
-    } else if (halves) {
+    } else {
         pl.steps = 2;
         pl.lanes_row = 64;
-    } else {
-        pl.steps = (pl.nb + 15) / 16;
-        int g = 4;
-        while (g < 4 * pl.nb && g < 64) g *= 2;
-        pl.lanes_row = g;   // lanes per row: a power of two holding min(nb, 16) super-blocks
     }
-    pl.waves = (kind == kQ4KQ8 || (kind == kQ4K && pl.steps == 2) ? 1024 : 768) / 64;   // the most; the launch decides
-    pl.threads = pl.waves * 64;
-    pl.rows_tile = 64 / pl.lanes_row;
-    pl.tiles = (N + pl.rows_tile - 1) / pl.rows_tile;
-    // chunk of units whose bytes are a whole number of 128-byte lines
-    const int64_t unit_bytes = (int64_t)pl.rows_tile * pl.nb * (kind == kQ6K ? 210 : 144);
-    pl.chunk_shift = 0;
-    while (((unit_bytes << pl.chunk_shift) & 127) != 0) ++pl.chunk_shift;
-    const size_t xb = (kind == kQ4KQ8) ? (size_t)K : (size_t)K * 4;
-    pl.x_in_lds = 1;
-    pl.lds_bytes = xb + xb / 16 + ((kind == kQ4KQ8) ? 0 : (size_t)(K / 16) * 4);
-    pl.grid = 0;
-    return pl.lds_bytes <= 65536;   // larger x (f32, K > ~15000) goes to the tile kernel
+    return finish_wave_plan(pl, N, K, kind);
 }
 
 Plan make_plan(int64_t N, int64_t K, int kind)
@@ -1162,7 +1230,7 @@ template <int KIND, int EPI>
 static hipError_t launch(Plan &pl, const GemvArgs &a, int cus, hipStream_t s, const Timing &tm = Timing{})
 {
     if (pl.wave_local) {
-        if (pl.rows_kernel) return launch_per_cu(gemv_rows_kernel<KIND, EPI>, pl.waves, pl, a, cus, s, tm);
+        if (pl.rows_kernel) return launch_per_cu(gemv_rows_kernel<KIND, EPI, 0>, pl.waves, pl, a, cus, s, tm);
         if constexpr (KIND == kQ4KQ8)
             if (pl.steps == 2) return launch_wave<KIND, EPI, 2>(pl, a, cus, s, tm);
         return launch_wave<KIND, EPI, 1>(pl, a, cus, s, tm);
@@ -1228,6 +1296,41 @@ hipError_t launch_lm_head_argmax(const void *W, const float *x, const uint32_t *
     a.mask = mask;
     if (mask) return launch<kQ6K, kArgmaxMasked>(pl, a, cus, s, tm);
     return launch<kQ6K, kArgmax>(pl, a, cus, s, tm);
+}
+
+hipError_t launch_q4k_gemv_multi(const void *const *W, const int64_t *N, float *const *y, const float *const *r,
+                                 int count, const float *x, int64_t K, int cus, hipStream_t s)
+{
+    // one row-stream plan for the stacked matrices (every row inside one wave)
+    int64_t total = 0;
+    for (int m = 0; m < count; ++m) total += N[m];
+    Plan pl{};
+    plan_rows(pl, total, K, kQ4K);
+    GemvArgs a = base_args(pl, total);
+    a.x = x;
+    int64_t u = 0;
+    for (int m = 0; m < kMaxMulti; ++m) {
+        a.ustart[m] = (int)u;
+        if (m < count) {
+            a.Wm[m] = (const uint8_t *)W[m];
+            a.ym[m] = y[m];
+            a.rm[m] = r ? r[m] : nullptr;
+            a.Nm[m] = N[m];
+            u += (N[m] + pl.rows_tile - 1) / pl.rows_tile;
+        } else {
+            a.Wm[m] = nullptr;
+            a.ym[m] = nullptr;
+            a.rm[m] = nullptr;
+            a.Nm[m] = 0;
+        }
+    }
+    for (int m = count; m < kMaxMulti; ++m) a.ustart[m] = INT32_MAX;
+    a.ustart[kMaxMulti] = INT32_MAX;
+    pl.tiles = u;
+    a.tiles = (int)u;
+    a.W = a.Wm[0];
+    a.y = a.ym[0];
+    return launch_per_cu(gemv_rows_kernel<kQ4K, kStore, 1>, pl.waves, pl, a, cus, s, Timing{});
 }
 
 hipError_t launch_q8_quantize(const float *x, int8_t *xq, uint16_t *xd, int64_t K, hipStream_t s)

@@ -21,6 +21,10 @@ constexpr size_t kArgmaxSlot0 = 4096;
 constexpr int kArgmaxMaxGrid = 1024;
 constexpr size_t kArgmaxWsBytes = kArgmaxSlot0 + 128 * (size_t)kArgmaxMaxGrid;
 
+// Matrices one multi-output GEMV launch can take; x (f32) must fit in LDS.
+constexpr int kMaxMulti = 4;
+constexpr int64_t kMaxMultiK = 14336;   // 4.5 K bytes of LDS (padded x and its sums) <= 64 KiB
+
 // Launch geometry of the GEMV kernel template (pure function of N, K, the
 // CU count and the kernel kind).
 struct Plan {
@@ -58,6 +62,8 @@ hipError_t launch_q4k_q8_gemv(const void *W, const int8_t *xq, const uint16_t *x
 hipError_t launch_lm_head_argmax(const void *W, const float *x, const uint32_t *mask, uint32_t *out_idx,
                                  float *out_max, void *ws, int64_t N, int64_t K, int cus, hipStream_t s,
                                  const Timing &tm = Timing{});
+hipError_t launch_q4k_gemv_multi(const void *const *W, const int64_t *N, float *const *y, const float *const *r,
+                                 int count, const float *x, int64_t K, int cus, hipStream_t s);
 hipError_t launch_q8_quantize(const float *x, int8_t *xq, uint16_t *xd, int64_t K, hipStream_t s);
 hipError_t launch_q4k_q8_isums(const void *W, const int8_t *xq, int32_t *isums, int64_t N, int64_t K, hipStream_t s);
 

@@ -59,6 +59,25 @@ extern "C" {
 int q4k_gemv(const void *W, const float *x, float *y, int64_t N, int64_t K, void *stream);
 
 /*
+ * Several Q4_K matrices of the same K against one x in a single launch, with
+ * an optional residual added to each output: y_i = W_i x (+ residual_i)
+ * (memra-engine decode.rs: the q, k and v projections share their input and
+ * run as one launch, split by block offset, and the small beta/alpha pair
+ * likewise, so launch-latency-sized GEMVs stop paying a launch each;
+ * qualiaDB resident_decode.rs: the output projection adds the residual in the
+ * GEMV's epilogue, `coop_gemv_residual`).  One pass streams all matrices,
+ * every row reduced inside one wave.
+ *   W, N, y: host arrays of `count` (1..4) device pointers / row counts;
+ *   W[i]: Q4_K N[i] x K; y[i]: float[N[i]] (written).
+ *   residual: NULL, or a host array of `count` device pointers, each NULL or
+ *   float[N[i]]; residual[i] may equal y[i] (in-place add), no other overlap.
+ *   x: float[K], 256 <= K <= 14336 (x and its sums are staged in LDS).
+ * Errors as q4k_gemv; count outside 1..4 or a larger K is GEMVQ_ERR_SHAPE.
+ */
+int q4k_gemv_multi(const void *const *W, const int64_t *N, float *const *y, const float *const *residual,
+                   int count, const float *x, int64_t K, void *stream);
+
+/*
  * Same over a Q6_K matrix (210-byte blocks): the ffn_down projection and the
  * unfused lm_head (aprender-serve forward_qwen35_cuda.rs, the lm_head
  * `gemv_dispatch` at the end of `forward_single`).

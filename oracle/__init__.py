@@ -197,6 +197,18 @@ def q4k_q8_gemv(W, xq, xd, N: int, K: int) -> np.ndarray:
 
 
 # ------------------------------------------------------------------- argmax
+def q4k_gemv_multi(Ws, Ns, x, K, residuals=None):
+    """y_i = W_i x (+ residual_i) for each matrix, each a plain q4k_gemv in
+    f64 plus the f32 residual widened to f64."""
+    out = []
+    for i, (W, N) in enumerate(zip(Ws, Ns)):
+        y = q4k_gemv(W, x, N, K)
+        if residuals is not None and residuals[i] is not None:
+            y = y + np.asarray(residuals[i], np.float64)
+        out.append(y)
+    return out
+
+
 def argmax_first(v) -> int:
     """First index of the maximum over non-NaN values; 0 if all are NaN."""
     v = np.asarray(v)

@@ -4,6 +4,7 @@ documented status before any HIP call.
 
 Pointers here are fake integers; every call below is built to be rejected by
 the host-side checks, so nothing is ever dereferenced or launched."""
+import ctypes
 import glob
 import os
 
@@ -148,3 +149,28 @@ def test_binding_rejects_host_tensors():
     x = torch.zeros(256, dtype=torch.float32)
     with pytest.raises(ValueError):
         gq.q4k_gemv(W, x, 1, 256)
+
+
+def _arr(ctype, vals):
+    return ctypes.cast((ctype * len(vals))(*vals), ctypes.c_void_p)
+
+
+def test_multi_rejections():
+    L = gq.lib()
+    P, I = ctypes.c_void_p, ctypes.c_int64
+    W3 = _arr(P, [A, A + (1 << 24), A + (2 << 24)])
+    Y3 = _arr(P, [C, C + (1 << 20), C + (2 << 20)])
+    N3 = _arr(I, [64, 32, 32])
+    _rejected(L.q4k_gemv_multi(None, N3, Y3, None, 3, B, 2560, None), gq.ERR_NULL)
+    _rejected(L.q4k_gemv_multi(W3, N3, Y3, None, 3, None, 2560, None), gq.ERR_NULL)
+    _rejected(L.q4k_gemv_multi(_arr(P, [A, None, A]), N3, Y3, None, 3, B, 2560, None), gq.ERR_NULL)
+    _rejected(L.q4k_gemv_multi(W3, N3, Y3, None, 0, B, 2560, None), gq.ERR_SHAPE)
+    _rejected(L.q4k_gemv_multi(W3, N3, Y3, None, 5, B, 2560, None), gq.ERR_SHAPE)
+    _rejected(L.q4k_gemv_multi(W3, _arr(I, [64, 0, 32]), Y3, None, 3, B, 2560, None), gq.ERR_SHAPE)
+    _rejected(L.q4k_gemv_multi(W3, N3, Y3, None, 3, B, 14336 + 256, None), gq.ERR_SHAPE)   # x too big for LDS
+    _rejected(L.q4k_gemv_multi(W3, N3, Y3, None, 3, B + 4, 2560, None), gq.ERR_ALIGN)
+    _rejected(L.q4k_gemv_multi(W3, N3, _arr(P, [C, C + 2, C + 4096]), None, 3, B, 2560, None), gq.ERR_ALIGN)
+    _rejected(L.q4k_gemv_multi(W3, N3, _arr(P, [C, C + 128, C + 4096]), None, 3, B, 2560, None), gq.ERR_ALIAS)  # y0/y1
+    _rejected(L.q4k_gemv_multi(W3, N3, _arr(P, [A + 64, C + 4096, C + 8192]), None, 3, B, 2560, None), gq.ERR_ALIAS)
+    R3 = _arr(P, [None, C, None])      # residual of matrix 1 overlaps y[0]
+    _rejected(L.q4k_gemv_multi(W3, N3, Y3, R3, 3, B, 2560, None), gq.ERR_ALIAS)

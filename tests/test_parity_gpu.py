@@ -513,3 +513,51 @@ def test_lm_head_argmax_masked_c3_full(dev, c3_full):
     bits = rng.random(N) < 0.7
     ws = _ws(dev, N, K)
     _masked_case(dev, W, x, N, K, bits, ws)
+
+
+# ---------------------------------------------------- multi-output GEMV
+@pytest.mark.parametrize("Ns,K,res", [
+    ((4096, 1024, 1024), 2560, "none"),      # q, k, v of a 4B-class attention block
+    ((4096, 1024, 1024), 2560, "some"),
+    ((2560,), 9728, "inplace"),              # down projection plus the residual, in place
+    ((32, 32), 1024, "none"),                # a tiny pair (beta/alpha-sized)
+    ((777, 1, 3, 300), 8192, "some"),        # ragged, four matrices, two-step rows
+    ((5, 7), 256, "inplace"),
+    ((100, 200), 14336, "some"),             # the largest K
+])
+def test_q4k_gemv_multi(dev, Ns, K, res):
+    r = synth.rng_for(sum(Ns) + K)
+    Ws = [synth.q4k_weights(r, N, K) for N in Ns]
+    x = synth.activation(r, K)
+    rs = [synth.activation(r, N) for N in Ns]
+    dx = up(x, dev)
+    if res == "none":
+        resid, dres = None, None
+        ys = None
+    elif res == "some":
+        resid = [rs[i] if i % 2 == 0 else None for i in range(len(Ns))]
+        dres = [up(v, dev) if v is not None else None for v in resid]
+        ys = None
+    else:   # in place: y starts as the residual
+        resid = rs
+        ys = [up(v, dev) for v in rs]
+        dres = ys
+    out = gq().q4k_gemv_multi([up(W, dev) for W in Ws], list(Ns), dx, K, ys=ys, residuals=dres)
+    want = oracle.q4k_gemv_multi(Ws, Ns, x, K, resid)
+    for i, (y, yhat) in enumerate(zip(out, want)):
+        check_f32(f"multi {Ns} K={K} {res} [{i}]", y.cpu().numpy(), yhat)
+
+
+def test_q4k_gemv_multi_matches_single_rows(dev):
+    """For shapes whose single GEMV is also reduced inside one wave, each
+    output is bit-identical to that tensor's own q4k_gemv."""
+    import parity_shapes as ps
+    K = 2560
+    Ns = (4096, 1024, 1024)
+    r = synth.rng_for(9)
+    Ws = [up(synth.q4k_weights(r, N, K), dev) for N in Ns]
+    dx = up(synth.activation(r, K), dev)
+    out = gq().q4k_gemv_multi(Ws, list(Ns), dx, K)
+    for W, N, y in zip(Ws, Ns, out):
+        assert ps.kernel_path(gq().KIND_Q4K, N, K) == "rows1"
+        assert torch.equal(y, gq().q4k_gemv(W, dx, N, K))
