@@ -4,10 +4,11 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package.  The product (``gemv_q4k_q6k_amd`` and
 its HIP library) never does, and the two share no code.
 
-The arithmetic lives in ``oracle.c`` (plain C, f64 accumulation, exact
-super-block decoding; see that file's header for the block formats and the
-readings they rest on).  This module only builds it with gcc, loads it with
-ctypes and converts numpy arrays.  Every function is pinned by
+The GEMV and quantizer arithmetic lives in ``oracle.c`` (plain C, f64
+accumulation, exact super-block decoding; see that file's header for the
+block formats and the readings they rest on); this module builds it with gcc,
+loads it with ctypes and converts numpy arrays.  The RMS norms are plain
+numpy in f64 here.  Every function is pinned by
 ``tests/test_oracle_pins.py`` against closed forms, hand-packed blocks,
 library routines (numpy float16, numpy matmul, numpy nanargmax) and brute
 force.
@@ -15,6 +16,7 @@ force.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 import subprocess
 import threading
@@ -65,6 +67,8 @@ def _load():
             "orc_q8_quantize": (None, [P, P, P, I64]),
             "orc_q4k_q8_isums": (None, [P, P, P, I64, I64]),
             "orc_q4k_q8_gemv": (None, [P, P, P, P, I64, I64]),
+            "orc_q6k_q8_isums": (None, [P, P, P, I64, I64]),
+            "orc_q6k_q8_gemv": (None, [P, P, P, P, I64, I64]),
             "orc_argmax_first_f64": (I64, [P, I64]),
             "orc_argmax_first_f32": (I64, [P, I64]),
             "orc_argmax_first_masked_f64": (I64, [P, P, I64]),
@@ -194,6 +198,75 @@ def q4k_q8_gemv(W, xq, xd, N: int, K: int) -> np.ndarray:
     y = np.empty(N, np.float64)
     _load().orc_q4k_q8_gemv(_ptr(W), _ptr(xq), _ptr(xd), _ptr(y), N, K)
     return y
+
+
+def q6k_q8_isums(W, xq, N: int, K: int) -> np.ndarray:
+    """Exact integer sums of the Q6_K x Q8 path, int32[N, K/16]: one per
+    16-element group (the Q6_K scale granularity), quants offset by -32."""
+    W = _blocks(W, N, K, Q6K_BLOCK_BYTES)
+    xq = _vec(xq, np.int8)
+    out = np.empty((N, K // 16), np.int32)
+    _load().orc_q6k_q8_isums(_ptr(W), _ptr(xq), _ptr(out), N, K)
+    return out
+
+
+def q6k_q8_gemv(W, xq, xd, N: int, K: int) -> np.ndarray:
+    """y = W * xdq over Q6_K rows (xdq the dequantized Q8 activation), f64."""
+    W = _blocks(W, N, K, Q6K_BLOCK_BYTES)
+    xq = _vec(xq, np.int8)
+    xd = _vec(xd, np.uint16)
+    y = np.empty(N, np.float64)
+    _load().orc_q6k_q8_gemv(_ptr(W), _ptr(xq), _ptr(xd), _ptr(y), N, K)
+    return y
+
+
+# ------------------------------------------------ norms and Q8 emission
+# memra-engine decode.rs names the producers that emit a quantized activation
+# directly: `rms_norm_q8_1` (norm, then quantize), `add_rms_norm_q8_1`
+# (residual add, norm, quantize; the sum is also returned as the new
+# residual) and `silu_mul_scaled_q8_1` (the SwiGLU product, then quantize),
+# each stated to equal the unfused sequence.  The pages name the norm and its
+# eps (`cfg.rms_eps`) without writing it out; the reading here is the usual
+# RMS norm, y_i = w_i * x_i / sqrt(mean_j x_j^2 + eps).
+
+
+def rms_norm(x, w, eps: float) -> np.ndarray:
+    """y = w * x / sqrt(mean(x^2) + eps) in f64 from f32 x, w and eps."""
+    x = _vec(x, np.float32).astype(np.float64)
+    w = _vec(w, np.float32).astype(np.float64)
+    if x.shape != w.shape or x.size == 0:
+        raise ValueError("x and w must be non-empty and of one length")
+    e = float(np.float32(eps))
+    ms = float(np.sum(x * x)) / x.size
+    return w * (x / math.sqrt(ms + e))
+
+
+def add_rms_norm(x, r, w, eps: float):
+    """(res, y): res = x + r rounded once to f32 (the residual stream keeps
+    f32), y = rms_norm(res, w, eps) in f64."""
+    res = (_vec(x, np.float32) + _vec(r, np.float32)).astype(np.float32)
+    return res, rms_norm(res, w, eps)
+
+
+def rms_norm_q8(x, w, eps: float, r=None):
+    """(res or None, y, q, d): the norm (after the residual add when r is
+    given), then the Q8 quantization of y as an f32 vector.  The quantizer
+    takes its decisions on f32 values, as q8_quantize does."""
+    res = None
+    if r is None:
+        y = rms_norm(x, w, eps)
+    else:
+        res, y = add_rms_norm(x, r, w, eps)
+    q, d = q8_quantize(y.astype(np.float32))
+    return res, y, q, d
+
+
+def swiglu_q8(Wg, Wu, x, N: int, K: int):
+    """(h, q, d): the SwiGLU product h (f64), then the Q8 quantization of h as
+    an f32 vector (N a multiple of 32)."""
+    h, _, _ = swiglu(Wg, Wu, x, N, K)
+    q, d = q8_quantize(h.astype(np.float32))
+    return h, q, d
 
 
 # ------------------------------------------------------------------- argmax

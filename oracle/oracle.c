@@ -330,6 +330,54 @@ void orc_q4k_q8_gemv(const uint8_t *W, const int8_t *xq, const uint16_t *xd, dou
     }
 }
 
+/* ------------------------------------------------------- Q6_K x Q8 path */
+
+/* Integer part of the Q6_K int8-dot path (the Q6_K x Q8 ffn_down of the
+ * memra-engine decode.rs q8_1 fast path, `ffn_swiglu_decode`: the SwiGLU
+ * epilogue emits a quantized activation that ffn_down consumes through
+ * `matmul_pre`), exact: for row n and 16-element group g, the granularity
+ * of the Q6_K scales, isum[n][g] = sum_i (q6[n][16g+i] - 32) * q8[16g+i]. */
+void orc_q6k_q8_isums(const uint8_t *W, const int8_t *xq, int32_t *isums, int64_t N, int64_t K)
+{
+    int64_t nb = K / QK;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        double d;
+        int sc[16], q[256];
+        for (int64_t b = 0; b < nb; ++b) {
+            orc_q6k_fields(W + (n * nb + b) * Q6K_BLOCK_BYTES, &d, sc, q);
+            for (int g = 0; g < 16; ++g) {
+                int32_t s = 0;
+                for (int i = 0; i < 16; ++i)
+                    s += (q[16 * g + i] - 32) * (int32_t)xq[b * QK + 16 * g + i];
+                isums[n * (K / 16) + b * 16 + g] = s;
+            }
+        }
+    }
+}
+
+/* y = W * xdq over Q6_K rows, xdq the dequantized Q8 activation
+ * (fp16(d8[k/32]) * q8[k]); f64 weights, f64 accumulation. */
+void orc_q6k_q8_gemv(const uint8_t *W, const int8_t *xq, const uint16_t *xd, double *y,
+                     int64_t N, int64_t K)
+{
+    int64_t nb = K / QK;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        double w[256];
+        double acc = 0.0;
+        for (int64_t b = 0; b < nb; ++b) {
+            orc_q6k_block(W + (n * nb + b) * Q6K_BLOCK_BYTES, w);
+            for (int i = 0; i < 256; ++i) {
+                int64_t k = b * QK + i;
+                double xk = orc_fp16_to_f64(xd[k / 32]) * (double)xq[k];
+                acc += w[i] * xk;
+            }
+        }
+        y[n] = acc;
+    }
+}
+
 /* ------------------------------------------------------------- argmax */
 
 /* First index of the maximum over the non-NaN values; 0 when every value is

@@ -390,3 +390,149 @@ def test_masked_argmax_edges():
     assert oracle.argmax_first_masked(v, np.array([0x3F], np.uint32)) == 0          # everything banned
     assert oracle.argmax_first_masked(v, np.array([0xFFFFFFFF], np.uint32)) == 0    # bits past n ignored
     assert oracle.argmax_first_masked(v, np.array([0x2F], np.uint32)) == 0          # only NaN left -> 0
+
+
+# ------------------------------------------------------------------ Q6_K x Q8
+def test_q6k_q8_vs_numpy():
+    """Integer sums against the test-side encoder's raw quants, and the GEMV
+    against numpy matmul over the dequantized activation."""
+    rng = np.random.default_rng(21)
+    N, K = 5, 1024
+    fields = random_q6k_fields(rng, N * K // 256)
+    W, Wf = q6k_matrix_from_fields(fields, N, K)
+    x = (rng.standard_normal(K) * 2).astype(np.float32)
+    q, d = oracle.q8_quantize(x)
+    qraw = fields[2].reshape(N, K).astype(np.int64) - 32
+    isum_ref = (qraw * q.astype(np.int64)).reshape(N, K // 16, 16).sum(axis=2)
+    assert np.array_equal(oracle.q6k_q8_isums(W, q, N, K), isum_ref)
+    xdq = np.repeat(d.view(np.float16).astype(np.float64), 32) * q
+    y = oracle.q6k_q8_gemv(W, q, d, N, K)
+    assert np.allclose(y, Wf @ xdq, rtol=1e-13, atol=1e-12)
+    # the same GEMV through the f64-activation Q6_K path
+    assert np.allclose(y, oracle.q6k_gemv_f64x(W, xdq, N, K), rtol=1e-14, atol=1e-12)
+
+
+def test_q6k_q8_isums_offset_closed_form():
+    """All quants 0 give -32 * (group sum of q8), all quants 63 give
+    31 * (group sum): catches a missing or doubled -32 offset and a wrong
+    group index (every group has a distinct activation sum)."""
+    sc = [1] * 16
+    xq = np.array([(g + 1) * (1 if i % 2 else 2) for g in range(16) for i in range(16)], np.int8)
+    gsum = xq.astype(np.int64).reshape(16, 16).sum(axis=1)
+    for v, mult in ((0, -32), (63, 31), (32, 0)):
+        blk = pack_q6k(f16_bits(1.0), sc, [v] * 256)
+        assert list(oracle.q6k_q8_isums(blk, xq, 1, 256)[0]) == list(mult * gsum)
+
+
+def test_q6k_q8_worked_block(golden_dir):
+    """A constant activation quantizes to 127 with scale fp16(1/127), so the
+    Q6_K x Q8 dot of the worked block is its weight sum times 127 * that
+    scale."""
+    g = _golden(golden_dir, "q6k_worked_block.json")
+    blk = np.frombuffer(bytes.fromhex(g["bytes_hex"]), np.uint8)
+    q, d = oracle.q8_quantize(np.ones(256, np.float32))
+    assert np.all(q == 127) and np.all(d == f16_bits(1.0 / 127.0))
+    scale = float(np.array([d[0]], np.uint16).view(np.float16)[0])
+    y = oracle.q6k_q8_gemv(blk, q, d, 1, 256)[0]
+    assert y == pytest.approx(g["sum_all_ones"] * 127 * scale, rel=1e-15)
+
+
+# ------------------------------------------------------------------ RMS norm
+def test_rms_norm_vs_torch():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(22)
+    for K, eps in ((32, 1e-6), (1000, 1e-5), (8192, 0.0), (4096, 0.5)):
+        x = (rng.standard_normal(K) * rng.uniform(0.01, 50)).astype(np.float32)
+        w = rng.uniform(-2, 2, K).astype(np.float32)
+        y = oracle.rms_norm(x, w, eps)
+        ref = torch.nn.functional.rms_norm(torch.from_numpy(x.astype(np.float64)), (K,),
+                                           torch.from_numpy(w.astype(np.float64)),
+                                           float(np.float32(eps))).numpy()
+        assert np.allclose(y, ref, rtol=1e-13, atol=0)
+
+
+def test_rms_norm_closed_forms():
+    K = 64
+    ones = np.ones(K, np.float32)
+    # constant vector: y = w * c / sqrt(c^2 + eps)
+    for c, eps in ((3.0, 0.0), (0.5, 0.25), (-2.0, 1e-6)):
+        y = oracle.rms_norm(np.full(K, c, np.float32), ones, eps)
+        e = float(np.float32(eps))
+        assert np.allclose(y, c / math.sqrt(c * c + e), rtol=1e-15)
+    # eps = 0: unit root mean square, invariant under positive scaling, odd
+    rng = np.random.default_rng(23)
+    x = rng.standard_normal(K).astype(np.float32)
+    y = oracle.rms_norm(x, ones, 0.0)
+    assert math.sqrt(float(np.mean(y * y))) == pytest.approx(1.0, rel=1e-14)
+    assert np.allclose(oracle.rms_norm(4 * x, ones, 0.0), y, rtol=1e-14)
+    assert np.array_equal(oracle.rms_norm(-x, ones, 0.0), -y)
+    # the weight multiplies elementwise (a one-hot weight keeps one element)
+    w = np.zeros(K, np.float32)
+    w[5] = 2.0
+    yw = oracle.rms_norm(x, w, 0.0)
+    assert yw[5] == pytest.approx(2 * y[5], rel=1e-15) and np.count_nonzero(yw) == 1
+    # one-hot x: the only nonzero element becomes sqrt(K) (eps = 0)
+    e1 = np.zeros(K, np.float32)
+    e1[7] = 5.0
+    assert oracle.rms_norm(e1, ones, 0.0)[7] == pytest.approx(math.sqrt(K), rel=1e-15)
+
+
+def test_add_rms_norm():
+    rng = np.random.default_rng(24)
+    K = 512
+    x = rng.standard_normal(K).astype(np.float32)
+    r = rng.standard_normal(K).astype(np.float32)
+    w = rng.uniform(0.5, 1.5, K).astype(np.float32)
+    res, y = oracle.add_rms_norm(x, r, w, 1e-6)
+    assert res.dtype == np.float32 and np.array_equal(res, x + r)   # one f32 rounding per element
+    assert np.array_equal(y, oracle.rms_norm(x + r, w, 1e-6))
+    # adding zero is the plain norm
+    res0, y0 = oracle.add_rms_norm(x, np.zeros(K, np.float32), w, 1e-6)
+    assert np.array_equal(res0, x) and np.array_equal(y0, oracle.rms_norm(x, w, 1e-6))
+
+
+def test_rms_norm_q8_closed_forms():
+    K = 256
+    ones = np.ones(K, np.float32)
+    # constant positive input, eps = 0: y = 1 everywhere -> q = 127, d = fp16(1/127)
+    _, y, q, d = oracle.rms_norm_q8(np.full(K, 0.75, np.float32), ones, 0.0)
+    assert np.all(y == 1.0) and np.all(q == 127) and np.all(d == f16_bits(1.0 / 127.0))
+    # alternating signs: +-127
+    alt = np.where(np.arange(K) % 2 == 0, 2.0, -2.0).astype(np.float32)
+    _, y, q, d = oracle.rms_norm_q8(alt, ones, 0.0)
+    assert np.array_equal(q, np.where(np.arange(K) % 2 == 0, 127, -127).astype(np.int8))
+    # with a residual, the returned residual is the f32 sum and the codes are
+    # those of the norm of that sum
+    rng = np.random.default_rng(25)
+    x = rng.standard_normal(K).astype(np.float32)
+    r = rng.standard_normal(K).astype(np.float32)
+    w = rng.uniform(0.5, 1.5, K).astype(np.float32)
+    res, y, q, d = oracle.rms_norm_q8(x, w, 1e-5, r)
+    assert np.array_equal(res, x + r)
+    qq, dd = oracle.q8_quantize(oracle.rms_norm(x + r, w, 1e-5).astype(np.float32))
+    assert np.array_equal(q, qq) and np.array_equal(d, dd)
+    # dequantized codes stay within half a step of the normalized value
+    step = np.repeat(d.view(np.float16).astype(np.float64), 32)
+    # (codes are decided with the f32 scale; the stored fp16 scale is within
+    # 2^-11 of it, which moves a code of at most 127 by 127 * 2^-11 steps)
+    assert np.all(np.abs(q * step - y) <= (0.5 + 127 * 2.0 ** -11) * step * (1 + 1e-6))
+
+
+def test_swiglu_q8_properties():
+    """The quantized SwiGLU output: h is the plain SwiGLU, codes lie within
+    half a step (plus the fp16 scale's rounding) of h, and the largest code
+    of every nonzero block is +-127."""
+    rng = np.random.default_rng(26)
+    N, K = 64, 512
+    Wg, _ = q4k_matrix_from_fields(random_q4k_fields(rng, N * K // 256), N, K)
+    Wu, _ = q4k_matrix_from_fields(random_q4k_fields(rng, N * K // 256), N, K)
+    Wg[40] = Wg[3]
+    Wu[40] = Wu[3]
+    x = rng.standard_normal(K).astype(np.float32)
+    h, q, d = oracle.swiglu_q8(Wg, Wu, x, N, K)
+    assert np.array_equal(h, oracle.swiglu(Wg, Wu, x, N, K)[0])
+    step = np.repeat(d.view(np.float16).astype(np.float64), 32)
+    assert np.all(np.abs(q * step - h) <= (0.5 + 127 * 2.0 ** -11) * step * (1 + 1e-6))
+    assert np.all(np.abs(q.astype(np.int64)).reshape(-1, 32).max(axis=1) == 127)
+    # rows 3 and 40 are equal by construction and sit in different blocks
+    assert h[3] == h[40]
