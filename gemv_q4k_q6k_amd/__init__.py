@@ -21,6 +21,7 @@ __all__ = [
     "GemvqError", "lib", "exported_names", "header_names",
     "q4k_gemv", "q4k_gemv_multi", "q6k_gemv", "q8_quantize", "q4k_q8_gemv", "swiglu_gemv",
     "lm_head_argmax", "lm_head_argmax_timed", "lm_head_argmax_masked", "lm_head_argmax_ws_bytes", "q4k_q8_isums", "strerror", "tile_geometry",
+    "q6k_q8_gemv", "q6k_q8_isums",
     "Q4K_BLOCK_BYTES", "Q6K_BLOCK_BYTES", "LIB_PATH", "HEADER_PATH",
 ]
 
@@ -52,6 +53,8 @@ _SIGS = {
     "q8_quantize": (ctypes.c_int, [_P, _P, _P, _I64, _P]),
     "q4k_q8_gemv": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _P]),
     "swiglu_gemv": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _P]),
+    "q6k_q8_gemv": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _P]),
+    "gemvq_q6k_q8_isums": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P]),
     "lm_head_argmax": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_size_t, _I64, _I64, _P]),
     "lm_head_argmax_timed": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_size_t, _I64, _I64, _P, _P, _P]),
     "lm_head_argmax_masked": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_size_t, _I64, _I64, _P]),
@@ -91,7 +94,7 @@ def exported_names() -> list[str]:
     return sorted(_SIGS)
 
 
-KIND_Q4K, KIND_Q6K, KIND_Q4K_Q8, KIND_SWIGLU = range(4)
+KIND_Q4K, KIND_Q6K, KIND_Q4K_Q8, KIND_SWIGLU, KIND_Q6K_Q8 = range(5)
 
 
 def tile_geometry(kind: int, N: int, K: int) -> dict:
@@ -226,6 +229,19 @@ def q4k_q8_gemv(W, xq, xd, N: int, K: int, y=None, stream=None):
     return y
 
 
+def q6k_q8_gemv(W, xq, xd, N: int, K: int, y=None, stream=None):
+    """y = W (dequantized Q8 x) for a Q6_K matrix W, exact int8 dots per
+    16-element group; xq int8[K], xd int16[K/32]."""
+    torch = _torch()
+    _weights(W, N, K, Q6K_BLOCK_BYTES)
+    _dev_tensor(xq, torch.int8, K, "xq")
+    _dev_tensor(xd, torch.int16, K // 32, "xd")
+    y = _out(y, xq.device, torch.float32, N, "y")
+    _check("q6k_q8_gemv", lib().q6k_q8_gemv(W.data_ptr(), xq.data_ptr(), xd.data_ptr(), y.data_ptr(), N, K,
+                                            _stream(xq, stream)))
+    return y
+
+
 def swiglu_gemv(Wg, Wu, x, N: int, K: int, h=None, stream=None):
     """h = silu(Wg x) * (Wu x), Wg and Wu Q4_K N x K."""
     torch = _torch()
@@ -315,3 +331,15 @@ def q4k_q8_isums(W, xq, N: int, K: int, out=None, stream=None):
     _check("gemvq_q4k_q8_isums", lib().gemvq_q4k_q8_isums(W.data_ptr(), xq.data_ptr(), out.data_ptr(), N, K,
                                                           _stream(xq, stream)))
     return out.view(N, K // 32)
+
+
+def q6k_q8_isums(W, xq, N: int, K: int, out=None, stream=None):
+    """Exact integer sums isums[n][g] of the Q6_K x Q8 path, one per
+    16-element group (test hook)."""
+    torch = _torch()
+    _weights(W, N, K, Q6K_BLOCK_BYTES)
+    _dev_tensor(xq, torch.int8, K, "xq")
+    out = _out(out, xq.device, torch.int32, N * (K // 16), "isums")
+    _check("gemvq_q6k_q8_isums", lib().gemvq_q6k_q8_isums(W.data_ptr(), xq.data_ptr(), out.data_ptr(), N, K,
+                                                          _stream(xq, stream)))
+    return out.view(N, K // 16)

@@ -89,9 +89,9 @@ size_t gemvq_lm_head_argmax_ws_bytes(int64_t N, int64_t K)
 int gemvq_tile_geometry(int kind, int64_t N, int64_t K, int64_t out[7])
 {
     if (!out) return GEMVQ_ERR_NULL;
-    if (kind < 0 || kind > 3) return GEMVQ_ERR_SHAPE;
+    if (kind < 0 || kind > 4) return GEMVQ_ERR_SHAPE;
     size_t wb = 0;
-    if (int st = check_shape(N, K, kind == 1 ? 210 : 144, &wb)) return st;
+    if (int st = check_shape(N, K, (kind == 1 || kind == 4) ? 210 : 144, &wb)) return st;
     const gemvq::Plan pl = gemvq::make_plan(N, K, kind);
     out[0] = pl.waves;
     out[1] = pl.rows_tile;
@@ -186,6 +186,20 @@ int q4k_q8_gemv(const void *W, const int8_t *xq, const uint16_t *xd, float *y, i
     return status_of(gemvq::launch_q4k_q8_gemv(W, xq, xd, y, N, K, cus, (hipStream_t)stream));
 }
 
+int q6k_q8_gemv(const void *W, const int8_t *xq, const uint16_t *xd, float *y, int64_t N, int64_t K, void *stream)
+{
+    if (!W || !xq || !xd || !y) return GEMVQ_ERR_NULL;
+    size_t wb = 0;
+    if (int st = check_shape(N, K, 210, &wb)) return st;
+    if (!aligned(W, 4) || !aligned(xq, 16) || !aligned(xd, 4) || !aligned(y, 4)) return GEMVQ_ERR_ALIGN;
+    const size_t ny = (size_t)N * 4;
+    if (overlap(y, ny, W, wb) || overlap(y, ny, xq, (size_t)K) || overlap(y, ny, xd, (size_t)(K / 32) * 2))
+        return GEMVQ_ERR_ALIAS;
+    int cus = 0;
+    if (int st = device_cus(&cus)) return st;
+    return status_of(gemvq::launch_q6k_q8_gemv(W, xq, xd, y, N, K, cus, (hipStream_t)stream));
+}
+
 int swiglu_gemv(const void *Wg, const void *Wu, const float *x, float *h, int64_t N, int64_t K, void *stream)
 {
     if (!Wg || !Wu || !x || !h) return GEMVQ_ERR_NULL;
@@ -260,6 +274,18 @@ int gemvq_q4k_q8_isums(const void *W, const int8_t *xq, int32_t *isums, int64_t 
     const size_t ni = (size_t)N * (size_t)(K / 32) * 4;
     if (overlap(isums, ni, W, wb) || overlap(isums, ni, xq, (size_t)K)) return GEMVQ_ERR_ALIAS;
     return status_of(gemvq::launch_q4k_q8_isums(W, xq, isums, N, K, (hipStream_t)stream));
+}
+
+int gemvq_q6k_q8_isums(const void *W, const int8_t *xq, int32_t *isums, int64_t N, int64_t K, void *stream)
+{
+    if (!W || !xq || !isums) return GEMVQ_ERR_NULL;
+    size_t wb = 0;
+    if (int st = check_shape(N, K, 210, &wb)) return st;
+    if (N * (K / 16) > (int64_t)1 << 40) return GEMVQ_ERR_SHAPE;
+    if (!aligned(W, 4) || !aligned(xq, 16) || !aligned(isums, 4)) return GEMVQ_ERR_ALIGN;
+    const size_t ni = (size_t)N * (size_t)(K / 16) * 4;
+    if (overlap(isums, ni, W, wb) || overlap(isums, ni, xq, (size_t)K)) return GEMVQ_ERR_ALIAS;
+    return status_of(gemvq::launch_q6k_q8_isums(W, xq, isums, N, K, (hipStream_t)stream));
 }
 
 }  // extern "C"

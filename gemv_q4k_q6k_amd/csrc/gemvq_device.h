@@ -309,25 +309,47 @@ struct Q6KX {
     float sx[4];     // sum over i of xs[s][i]
 };
 
+// Quants of dword k of a Q6_K part: byte j of q[s] is the 6-bit quant (0..63)
+// of weight 128n + 32s + l0 + 4k + j, assembled from its ql nibble and its qh
+// bit pair with one v_and_or_b32 each.
+__device__ __forceinline__ void q6k_quants(const Q6KRaw &r, int k, uint32_t (&q)[4])
+{
+    const uint32_t sh = r.shift;
+    const uint32_t a = __builtin_amdgcn_alignbyte(r.a[k + 1], r.a[k], sh);
+    const uint32_t b = __builtin_amdgcn_alignbyte(r.b[k + 1], r.b[k], sh);
+    const uint32_t h = __builtin_amdgcn_alignbyte(r.h[k + 1], r.h[k], sh);
+    q[0] = and_or(h << 4, 0x30303030u, a & 0x0F0F0F0Fu);
+    q[1] = and_or(h << 2, 0x30303030u, b & 0x0F0F0F0Fu);
+    q[2] = and_or(h, 0x30303030u, (a >> 4) & 0x0F0F0F0Fu);
+    q[3] = and_or(h >> 2, 0x30303030u, (b >> 4) & 0x0F0F0F0Fu);
+}
+
+// The four int8 scales of part u: sc[s] = sc[8n + (u&1) + 2s], bytes (u&1) + 2s
+// of the 8-byte scale window.
+__device__ __forceinline__ void q6k_scales(const Q6KRaw &r, int u, int (&sc)[4])
+{
+    const uint32_t sh = r.shift;
+    const uint32_t s0 = __builtin_amdgcn_alignbyte(r.s[1], r.s[0], sh);
+    const uint32_t s1 = __builtin_amdgcn_alignbyte(r.s[2], r.s[1], sh);
+    const uint32_t bo = (uint32_t)(u & 1) * 8u;
+    sc[0] = __builtin_amdgcn_sbfe((int)s0, bo, 8);
+    sc[1] = __builtin_amdgcn_sbfe((int)s0, bo + 16u, 8);
+    sc[2] = __builtin_amdgcn_sbfe((int)s1, bo, 8);
+    sc[3] = __builtin_amdgcn_sbfe((int)s1, bo + 16u, 8);
+}
+
 // Dot product of one Q6_K part: quant bytes are assembled per dword (4 quants
 // of one group s), spread into halves 1024+q with v_perm_b32 and multiplied in
 // f32.  sum (q-32) x = acc - 1056 * sum x.
 __device__ __forceinline__ float q6k_dot(const Q6KRaw &r, const Q6KX &x, int u)
 {
-    const uint32_t sh = r.shift;
     float acc[4][2];
 #pragma unroll
     for (int s = 0; s < 4; ++s) acc[s][0] = acc[s][1] = 0.f;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        const uint32_t a = __builtin_amdgcn_alignbyte(r.a[k + 1], r.a[k], sh);
-        const uint32_t b = __builtin_amdgcn_alignbyte(r.b[k + 1], r.b[k], sh);
-        const uint32_t h = __builtin_amdgcn_alignbyte(r.h[k + 1], r.h[k], sh);
         uint32_t q[4];
-        q[0] = and_or(h << 4, 0x30303030u, a & 0x0F0F0F0Fu);
-        q[1] = and_or(h << 2, 0x30303030u, b & 0x0F0F0F0Fu);
-        q[2] = and_or(h, 0x30303030u, (a >> 4) & 0x0F0F0F0Fu);
-        q[3] = and_or(h >> 2, 0x30303030u, (b >> 4) & 0x0F0F0F0Fu);
+        q6k_quants(r, k, q);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             // bytes 0,2 and 1,3 of q[s] under the 0x64 exponent byte -> halves 1024+q
@@ -339,19 +361,57 @@ __device__ __forceinline__ float q6k_dot(const Q6KRaw &r, const Q6KX &x, int u)
             acc[s][1] = __builtin_fmaf((float)o.y, x.xs[s][4 * k + 3], acc[s][1]);
         }
     }
-    // scales sc[8n + (u&1) + 2s]: bytes (u&1) + 2s of the 8-byte window
-    const uint32_t s0 = __builtin_amdgcn_alignbyte(r.s[1], r.s[0], sh);
-    const uint32_t s1 = __builtin_amdgcn_alignbyte(r.s[2], r.s[1], sh);
-    const uint32_t bo = (uint32_t)(u & 1) * 8u;
-    const int sc0 = __builtin_amdgcn_sbfe((int)s0, bo, 8);
-    const int sc1 = __builtin_amdgcn_sbfe((int)s0, bo + 16u, 8);
-    const int sc2 = __builtin_amdgcn_sbfe((int)s1, bo, 8);
-    const int sc3 = __builtin_amdgcn_sbfe((int)s1, bo + 16u, 8);
+    int sc[4];
+    q6k_scales(r, u, sc);
     const float d = half_lo(r.dbits);
-    const float t0 = (float)sc0 * ((acc[0][0] + acc[0][1]) - 1056.f * x.sx[0]);
-    const float t1 = (float)sc1 * ((acc[1][0] + acc[1][1]) - 1056.f * x.sx[1]);
-    const float t2 = (float)sc2 * ((acc[2][0] + acc[2][1]) - 1056.f * x.sx[2]);
-    const float t3 = (float)sc3 * ((acc[3][0] + acc[3][1]) - 1056.f * x.sx[3]);
+    const float t0 = (float)sc[0] * ((acc[0][0] + acc[0][1]) - 1056.f * x.sx[0]);
+    const float t1 = (float)sc[1] * ((acc[1][0] + acc[1][1]) - 1056.f * x.sx[1]);
+    const float t2 = (float)sc[2] * ((acc[2][0] + acc[2][1]) - 1056.f * x.sx[2]);
+    const float t3 = (float)sc[3] * ((acc[3][0] + acc[3][1]) - 1056.f * x.sx[3]);
+    return d * ((t0 + t1) + (t2 + t3));
+}
+
+// ------------------------------------------------------------ Q6_K x Q8
+
+// Q8 activation slice of a Q6_K part u: group s holds the 16 int8 values
+// x[128n + 32s + l0 + i] in four dwords, the scale of the 32-element Q8 block
+// they lie in (block 4n + s of the super-block) as f32, and their integer sum.
+struct Q6Q8X {
+    uint32_t q[4][4];
+    float d[4];
+    int32_t sx[4];
+};
+
+// Exact integer sums of one part: is[s] = sum_i (q6 - 32) * q8 over group s.
+// The 6-bit quants (0..63) are valid signed bytes, so v_dot4_i32_i8 takes
+// them as they are and the -32 offset is removed with the group's q8 sum.
+__device__ __forceinline__ void q6k_q8_isums(const Q6KRaw &r, const Q6Q8X &x, int32_t (&is)[4])
+{
+    int32_t acc[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        uint32_t q[4];
+        q6k_quants(r, k, q);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) acc[s] = __builtin_amdgcn_sdot4((int)q[s], (int)x.q[s][k], acc[s], false);
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) is[s] = acc[s] - 32 * x.sx[s];
+}
+
+// |sc * isum| <= 128 * 16 * 32 * 127 < 2^24, so each group term is exact in
+// f32 before its Q8 scale is applied.
+__device__ __forceinline__ float q6k_q8_dot(const Q6KRaw &r, const Q6Q8X &x, int u)
+{
+    int32_t is[4];
+    q6k_q8_isums(r, x, is);
+    int sc[4];
+    q6k_scales(r, u, sc);
+    const float d = half_lo(r.dbits);
+    const float t0 = (float)(sc[0] * is[0]) * x.d[0];
+    const float t1 = (float)(sc[1] * is[1]) * x.d[1];
+    const float t2 = (float)(sc[2] * is[2]) * x.d[2];
+    const float t3 = (float)(sc[3] * is[3]) * x.d[3];
     return d * ((t0 + t1) + (t2 + t3));
 }
 

@@ -21,7 +21,9 @@
 
 namespace gemvq {
 
-enum Kind : int { kQ4K = 0, kQ6K = 1, kQ4KQ8 = 2, kSwiglu = 3 };
+enum Kind : int { kQ4K = 0, kQ6K = 1, kQ4KQ8 = 2, kSwiglu = 3, kQ6KQ8 = 4 };
+constexpr bool is_q8(int kind) { return kind == kQ4KQ8 || kind == kQ6KQ8; }   // int8 activation
+constexpr bool is_q6(int kind) { return kind == kQ6K || kind == kQ6KQ8; }     // Q6_K weights
 enum Epi : int { kStore = 0, kArgmax = 1, kArgmaxMasked = 2 };
 constexpr bool is_argmax(int epi) { return epi != kStore; }
 
@@ -64,6 +66,7 @@ template <> struct XSlice<kQ4K> { Q4KX v; };
 template <> struct XSlice<kSwiglu> { Q4KX v; };
 template <> struct XSlice<kQ6K> { Q6KX v; };
 template <> struct XSlice<kQ4KQ8> { Q8X v; };
+template <> struct XSlice<kQ6KQ8> { Q6Q8X v; };
 
 // Layout of the activation staged in LDS: 16 bytes of padding after every
 // 256 bytes.  A lane's slice is 64 consecutive bytes (Q8) or 64 consecutive
@@ -197,6 +200,36 @@ __device__ __forceinline__ void finish_x(Q8X &xs)
     xs.sh = sh;
 }
 
+// Q8 part u of a Q6_K block b: group s = x[256b + 128n + 32s + l0 + i], i < 16,
+// and the scale of Q8 block 8b + 4n + s.
+template <bool PADDED = false>
+__device__ __forceinline__ void load_x(Q6Q8X &xs, const int8_t *qsrc, const uint16_t *dsrc, int b, int u)
+{
+    const int n = u >> 1, l0 = 16 * (u & 1);
+    const uint32_t o = (uint32_t)(kQK * b + 128 * n + l0);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const uint32_t os = o + 32u * (uint32_t)s;
+        const uint32_t *p = (const uint32_t *)(qsrc + (PADDED ? lds_pad(os) : os));
+#pragma unroll
+        for (int k = 0; k < 4; ++k) xs.q[s][k] = p[k];
+        xs.d[s] = dsrc ? (float)__builtin_bit_cast(_Float16, dsrc[8 * b + 4 * n + s]) : 0.f;
+    }
+}
+
+// Integer sums of the slice's four 16-element groups.
+__device__ __forceinline__ void finish_x(Q6Q8X &xs)
+{
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        int32_t t = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) t = __builtin_amdgcn_sdot4((int)xs.q[s][k], 0x01010101, t, false);
+        pin(t);
+        xs.sx[s] = t;
+    }
+}
+
 // ------------------------------------------------------- per-kind traits
 
 template <int KIND> struct Traits;
@@ -215,6 +248,11 @@ template <> struct Traits<kQ6K> {
     static constexpr int kBytes = kQ6KBytes;
     static constexpr int kOuts = 1;
 };
+template <> struct Traits<kQ6KQ8> {
+    typedef Q6KRaw Raw;
+    static constexpr int kBytes = kQ6KBytes;
+    static constexpr int kOuts = 1;
+};
 template <> struct Traits<kSwiglu> {
     typedef Q4KRaw Raw;
     static constexpr int kBytes = kQ4KBytes;
@@ -229,7 +267,7 @@ struct RawSet {
 template <int KIND>
 __device__ __forceinline__ void zero_raw(RawSet<KIND> &rs)
 {
-    if constexpr (KIND == kQ6K) {
+    if constexpr (is_q6(KIND)) {
         q6k_zero(rs.r[0]);
     } else {
         q4k_zero(rs.r[0]);
@@ -242,6 +280,8 @@ __device__ __forceinline__ void dot_raw(const RawSet<KIND> &rs, const XSlice<KIN
 {
     if constexpr (KIND == kQ6K) {
         out[0] = q6k_dot(rs.r[0], xs.v, part);
+    } else if constexpr (KIND == kQ6KQ8) {
+        out[0] = q6k_q8_dot(rs.r[0], xs.v, part);
     } else if constexpr (KIND == kQ4KQ8) {
         out[0] = q4k_q8_dot(rs.r[0], xs.v, part);
     } else {
@@ -389,7 +429,7 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_kernel(GemvArgs a)
         const int tt = t < t_end ? t : t_end - 1;
         const uint32_t off = valid_tile(t) ? lane_off : 0u;
         const int64_t tb = (int64_t)tt * tile_stride;
-        if constexpr (KIND == kQ6K) {
+        if constexpr (is_q6(KIND)) {
             q6k_load(rs.r[0], a.W + tb, off, part);
         } else {
             q4k_load(rs.r[0], a.W + tb, off, part);
@@ -403,9 +443,9 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_kernel(GemvArgs a)
     constexpr int kXRegs = 8;   // float4 (or 16 int8) staged per thread through registers
     u32x4 xr[kXRegs];
     if constexpr (XLDS) {
-        const int step = KIND == kQ4KQ8 ? 16 : 4;   // elements per 16-byte load
-        const uint8_t *src = KIND == kQ4KQ8 ? (const uint8_t *)a.xq : (const uint8_t *)a.x;
-        const int esz = KIND == kQ4KQ8 ? 1 : 4;
+        const int step = is_q8(KIND) ? 16 : 4;   // elements per 16-byte load
+        const uint8_t *src = is_q8(KIND) ? (const uint8_t *)a.xq : (const uint8_t *)a.x;
+        const int esz = is_q8(KIND) ? 1 : 4;
 #pragma unroll
         for (int r = 0; r < kXRegs; ++r) {
             const int i = (tid + r * (int)blockDim.x) * step;
@@ -416,7 +456,7 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_kernel(GemvArgs a)
     const int xb = lane_on ? b : 0;
     if constexpr (!XLDS) {
         // each lane reads its own slice (no other lane of the tile shares it)
-        if constexpr (KIND == kQ4KQ8)
+        if constexpr (is_q8(KIND))
             load_x(xs.v, a.xq, a.xd, xb, part);
         else
             load_x(xs.v, a.x, xb, part);
@@ -432,9 +472,9 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_kernel(GemvArgs a)
     // loads waiting on every outstanding memory operation.
     if constexpr (XLDS) {
         // registers staged above, then any remainder straight through
-        const int step = KIND == kQ4KQ8 ? 16 : 4;
-        const uint8_t *src = KIND == kQ4KQ8 ? (const uint8_t *)a.xq : (const uint8_t *)a.x;
-        const int esz = KIND == kQ4KQ8 ? 1 : 4;
+        const int step = is_q8(KIND) ? 16 : 4;
+        const uint8_t *src = is_q8(KIND) ? (const uint8_t *)a.xq : (const uint8_t *)a.x;
+        const int esz = is_q8(KIND) ? 1 : 4;
 #pragma unroll
         for (int r = 0; r < kXRegs; ++r) {
             const int i = (tid + r * (int)blockDim.x) * step;
@@ -444,7 +484,7 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_kernel(GemvArgs a)
             *(u32x4 *)(smem + lds_pad((uint32_t)(i * esz))) = *(const u32x4 *)(src + (size_t)i * esz);
         __syncthreads();
     }
-    if constexpr (KIND == kQ4KQ8) {
+    if constexpr (is_q8(KIND)) {
         if constexpr (XLDS) load_x<true>(xs.v, (const int8_t *)smem, a.xd, xb, part);
         finish_x(xs.v);
     } else {
@@ -541,7 +581,7 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_kernel(GemvArgs a)
 // wherever it sits (fixed lane layout, halves added in order), so equal rows
 // give equal bits.
 template <int KIND>
-constexpr int wave_max_threads() { return (KIND == kQ4KQ8 || KIND == kQ4K) ? 1024 : 768; }
+constexpr int wave_max_threads() { return (is_q8(KIND) || KIND == kQ4K) ? 1024 : 768; }
 constexpr int kWaveMaxThreads = 1024;   // the largest of wave_max_threads
 
 template <int KIND, int EPI, int STEPS>
@@ -592,7 +632,7 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_wave_kernel(Gem
 #pragma unroll
         for (int st = 0; st < STEPS; ++st) {
             const uint32_t off = v ? (uint32_t)((p * a.nb + b + 16 * st) * BYTES) : 0u;
-            if constexpr (KIND == kQ6K) {
+            if constexpr (is_q6(KIND)) {
                 q6k_load(rs[st].r[0], a.W + ub, off, part);
             } else {
                 q4k_load(rs[st].r[0], a.W + ub, off, part);
@@ -604,10 +644,10 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_wave_kernel(Gem
     // activation loads first, then the first two units of every wave (a
     // register or two per thread cover x for any workgroup of 4+ waves;
     // smaller workgroups load the rest below)
-    constexpr int kXRegs = KIND == kQ4KQ8 ? 1 : 2;
-    const int step = KIND == kQ4KQ8 ? 16 : 4;
-    const int esz = KIND == kQ4KQ8 ? 1 : 4;
-    const uint8_t *src = KIND == kQ4KQ8 ? (const uint8_t *)a.xq : (const uint8_t *)a.x;
+    constexpr int kXRegs = is_q8(KIND) ? 1 : 2;
+    const int step = is_q8(KIND) ? 16 : 4;
+    const int esz = is_q8(KIND) ? 1 : 4;
+    const uint8_t *src = is_q8(KIND) ? (const uint8_t *)a.xq : (const uint8_t *)a.x;
     u32x4 xr[kXRegs];
 #pragma unroll
     for (int r = 0; r < kXRegs; ++r) {
@@ -644,7 +684,7 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_wave_kernel(Gem
         *(u32x4 *)(smem + lds_pad((uint32_t)(i * esz))) = *(const u32x4 *)(src + (size_t)i * esz);
     __syncthreads();
     XSlice<KIND> xs[STEPS];
-    if constexpr (KIND == kQ4KQ8) {
+    if constexpr (is_q8(KIND)) {
 #pragma unroll
         for (int st = 0; st < STEPS; ++st) {
             load_x<true>(xs[st].v, (const int8_t *)smem, a.xd, b + 16 * st, part);
@@ -788,7 +828,7 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_rows_kernel(Gem
             Wb = a.Wm[m];
             ub = (int64_t)(uu - a.ustart[m]) * unit_stride;
         }
-        if constexpr (KIND == kQ6K) {
+        if constexpr (is_q6(KIND)) {
             q6k_load(rs.r[0], Wb + ub, off, part);
         } else {
             q4k_load(rs.r[0], Wb + ub, off, part);
@@ -811,10 +851,10 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_rows_kernel(Gem
     };
 
     // activation loads first
-    constexpr int kXRegs = KIND == kQ4KQ8 ? 1 : 2;
-    const int xstep = KIND == kQ4KQ8 ? 16 : 4;
-    const int esz = KIND == kQ4KQ8 ? 1 : 4;
-    const uint8_t *src = KIND == kQ4KQ8 ? (const uint8_t *)a.xq : (const uint8_t *)a.x;
+    constexpr int kXRegs = is_q8(KIND) ? 1 : 2;
+    const int xstep = is_q8(KIND) ? 16 : 4;
+    const int esz = is_q8(KIND) ? 1 : 4;
+    const uint8_t *src = is_q8(KIND) ? (const uint8_t *)a.xq : (const uint8_t *)a.x;
     u32x4 xr[kXRegs];
 #pragma unroll
     for (int r = 0; r < kXRegs; ++r) {
@@ -864,7 +904,7 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_rows_kernel(Gem
     __syncthreads();
     const float *sx = (const float *)smem;
     const float *ssum = (const float *)(smem + lds_pad(4u * (uint32_t)K));
-    if constexpr (KIND != kQ4KQ8) {
+    if constexpr (!is_q8(KIND)) {
         float *w = (float *)ssum;
         for (int g = tid; g < K / 16; g += blockDim.x) w[g] = sum16(x_at<true>(sx, 16 * g));
         __syncthreads();
@@ -873,7 +913,7 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_rows_kernel(Gem
     auto slice = [&](int st) {
         const int c = block_of(st);
         const int cb = c >= 0 ? c : 0;   // idle lanes read any valid slice
-        if constexpr (KIND == kQ4KQ8) {
+        if constexpr (is_q8(KIND)) {
             load_x<true>(xs.v, (const int8_t *)smem, a.xd, cb, part);
             finish_x(xs.v);
         } else {
@@ -994,6 +1034,31 @@ __global__ __launch_bounds__(256) void q4k_q8_isums_kernel(const uint8_t *__rest
     isums[blk * 8 + 2 * part + 1] = ish;
 }
 
+// Integer sums of every (row, 16-element group) of the Q6_K x Q8 GEMV with
+// its decode and dot code (q6k_load + q6k_q8_isums); one thread per (row,
+// block, part), each part covering 4 groups.
+__global__ __launch_bounds__(256) void q6k_q8_isums_kernel(const uint8_t *__restrict__ W, const int8_t *__restrict__ xq,
+                                                          int32_t *__restrict__ isums, int64_t N, int nb)
+{
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t total = N * nb * kParts;
+    if (gid >= total) return;
+    const int part = (int)(gid & 3);
+    const int64_t blk = gid >> 2;   // row * nb + b
+    const int b = (int)(blk % nb);
+    Q6Q8X xs;
+    load_x(xs, xq, nullptr, b, part);
+    finish_x(xs);
+    Q6KRaw r;
+    q6k_load(r, W + blk * kQ6KBytes, 0u, part);
+    int32_t is[4];
+    q6k_q8_isums(r, xs, is);
+    // group s of part u is 16-element group 8n + 2s + (u & 1) of the block
+    const int n = part >> 1;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) isums[blk * 16 + 8 * n + 2 * s + (part & 1)] = is[s];
+}
+
 // ------------------------------------------------------------ launch plan
 
 // Plan of a wave-unit or row-stream launch (every row reduced inside one
@@ -1002,17 +1067,17 @@ __global__ __launch_bounds__(256) void q4k_q8_isums_kernel(const uint8_t *__rest
 static bool finish_wave_plan(Plan &pl, int64_t N, int64_t K, int kind)
 {
     pl.wave_local = 1;
-    pl.waves = (kind == kQ4KQ8 || (kind == kQ4K && pl.steps == 2) ? 1024 : 768) / 64;   // the most; the launch decides
+    pl.waves = (is_q8(kind) || (kind == kQ4K && pl.steps == 2) ? 1024 : 768) / 64;   // the most; the launch decides
     pl.threads = pl.waves * 64;
     pl.rows_tile = 64 / pl.lanes_row;
     pl.tiles = (N + pl.rows_tile - 1) / pl.rows_tile;
     // chunk of units whose bytes are a whole number of 128-byte lines
-    const int64_t unit_bytes = (int64_t)pl.rows_tile * pl.nb * (kind == kQ6K ? 210 : 144);
+    const int64_t unit_bytes = (int64_t)pl.rows_tile * pl.nb * (is_q6(kind) ? 210 : 144);
     pl.chunk_shift = 0;
     while (((unit_bytes << pl.chunk_shift) & 127) != 0) ++pl.chunk_shift;
-    const size_t xb = (kind == kQ4KQ8) ? (size_t)K : (size_t)K * 4;
+    const size_t xb = is_q8(kind) ? (size_t)K : (size_t)K * 4;
     pl.x_in_lds = 1;
-    pl.lds_bytes = xb + xb / 16 + ((kind == kQ4KQ8) ? 0 : (size_t)(K / 16) * 4);
+    pl.lds_bytes = xb + xb / 16 + (is_q8(kind) ? 0 : (size_t)(K / 16) * 4);
     pl.grid = 0;
     return pl.lds_bytes <= 65536;   // larger x (f32, K > ~15000) goes to the tile kernel
 }
@@ -1087,10 +1152,10 @@ Plan make_plan(int64_t N, int64_t K, int kind)
     pl.rows_tile = pl.threads / pl.lanes_row;
     pl.tiles = (N + pl.rows_tile - 1) / pl.rows_tile;
     const int outs = (kind == kSwiglu) ? 2 : 1;
-    const size_t xbytes = (kind == kQ4KQ8) ? (size_t)K : (size_t)K * 4;
+    const size_t xbytes = is_q8(kind) ? (size_t)K : (size_t)K * 4;
     // Staging x through LDS pays when several rows of a tile read the same
     // slice; with one row per tile every element has a single reader.
-    const size_t sums = (kind == kQ4KQ8) ? 0 : (size_t)(K / 16) * 4;
+    const size_t sums = is_q8(kind) ? 0 : (size_t)(K / 16) * 4;
     const size_t xpadded = xbytes + xbytes / 16;   // 16 bytes of padding per 256 (lds_pad)
     pl.x_in_lds = (pl.rows_tile > 1 && xpadded + sums <= 65536) ? 1 : 0;
     const size_t red = (size_t)2 * outs * pl.rows_tile * pl.nb * 4;   // two buffers
@@ -1282,6 +1347,18 @@ hipError_t launch_q4k_q8_gemv(const void *W, const int8_t *xq, const uint16_t *x
     return launch<kQ4KQ8, kStore>(pl, a, cus, s);
 }
 
+hipError_t launch_q6k_q8_gemv(const void *W, const int8_t *xq, const uint16_t *xd, float *y, int64_t N, int64_t K,
+                              int cus, hipStream_t s)
+{
+    Plan pl = make_plan(N, K, kQ6KQ8);
+    GemvArgs a = base_args(pl, N);
+    a.W = (const uint8_t *)W;
+    a.xq = xq;
+    a.xd = xd;
+    a.y = y;
+    return launch<kQ6KQ8, kStore>(pl, a, cus, s);
+}
+
 hipError_t launch_lm_head_argmax(const void *W, const float *x, const uint32_t *mask, uint32_t *out_idx,
                                  float *out_max, void *ws, int64_t N, int64_t K, int cus, hipStream_t s,
                                  const Timing &tm)
@@ -1348,6 +1425,21 @@ hipError_t launch_q4k_q8_isums(const void *W, const int8_t *xq, int32_t *isums, 
     const int threads = 256;
     const int64_t blocks = (total + threads - 1) / threads;
     hipLaunchKernelGGL(q4k_q8_isums_kernel, dim3((unsigned)blocks), dim3(threads), 0, s, (const uint8_t *)W, xq, isums,
+                       N, nb);
+    return hipGetLastError();
+}
+
+}  // namespace gemvq
+
+namespace gemvq {
+
+hipError_t launch_q6k_q8_isums(const void *W, const int8_t *xq, int32_t *isums, int64_t N, int64_t K, hipStream_t s)
+{
+    const int nb = (int)(K / kQK);
+    const int64_t total = N * nb * kParts;
+    const int threads = 256;
+    const int64_t blocks = (total + threads - 1) / threads;
+    hipLaunchKernelGGL(q6k_q8_isums_kernel, dim3((unsigned)blocks), dim3(threads), 0, s, (const uint8_t *)W, xq, isums,
                        N, nb);
     return hipGetLastError();
 }

@@ -58,6 +58,8 @@ hipError_t launch_swiglu_gemv(const void *Wg, const void *Wu, const float *x, fl
                               hipStream_t s);
 hipError_t launch_q4k_q8_gemv(const void *W, const int8_t *xq, const uint16_t *xd, float *y, int64_t N, int64_t K,
                               int cus, hipStream_t s);
+hipError_t launch_q6k_q8_gemv(const void *W, const int8_t *xq, const uint16_t *xd, float *y, int64_t N, int64_t K,
+                              int cus, hipStream_t s);
 // mask: nullptr, or the banned-row bitmask of lm_head_argmax_masked
 hipError_t launch_lm_head_argmax(const void *W, const float *x, const uint32_t *mask, uint32_t *out_idx,
                                  float *out_max, void *ws, int64_t N, int64_t K, int cus, hipStream_t s,
@@ -65,6 +67,7 @@ hipError_t launch_lm_head_argmax(const void *W, const float *x, const uint32_t *
 hipError_t launch_q4k_gemv_multi(const void *const *W, const int64_t *N, float *const *y, const float *const *r,
                                  int count, const float *x, int64_t K, int cus, hipStream_t s);
 hipError_t launch_q8_quantize(const float *x, int8_t *xq, uint16_t *xd, int64_t K, hipStream_t s);
+hipError_t launch_q6k_q8_isums(const void *W, const int8_t *xq, int32_t *isums, int64_t N, int64_t K, hipStream_t s);
 hipError_t launch_q4k_q8_isums(const void *W, const int8_t *xq, int32_t *isums, int64_t N, int64_t K, hipStream_t s);
 
 }  // namespace gemvq

@@ -108,6 +108,20 @@ int q4k_q8_gemv(const void *W, const int8_t *xq, const uint16_t *xd, float *y,
                 int64_t N, int64_t K, void *stream);
 
 /*
+ * Q6_K x Q8 integer-dot GEMV, the int8 ffn_down: on the pages' q8 fast path
+ * the down projection consumes an already quantized activation (memra-engine
+ * decode.rs `ffn_swiglu_decode`: the SwiGLU epilogue emits the q8 form of its
+ * product and ffn_down reads it through `matmul_pre`).  Per 16-element group
+ * g of row n the integer sum isum_g = sum (q6 - 32) * q8 is exact;
+ * y[n] = d * sum_g sc_g * isum_g * d8_(g/2), with d8 the scale of the Q8 block
+ * the group lies in.
+ *   W: Q6_K N x K.  xq, xd: a Q8 activation of length K (q8_quantize,
+ *   rms_norm_q8 or swiglu_q8_gemv output).  y: float[N].
+ */
+int q6k_q8_gemv(const void *W, const int8_t *xq, const uint16_t *xd, float *y,
+                int64_t N, int64_t K, void *stream);
+
+/*
  * Fused gate/up SwiGLU GEMV: h[n] = silu(g[n]) * u[n], g = Wg x, u = Wu x,
  * silu(z) = z / (1 + e^-z), both matrices read in one pass that shares x
  * (memra-engine decode.rs `ffn_swiglu_decode`: down @ (silu(gate@z) * (up@z));
@@ -185,9 +199,19 @@ int gemvq_q4k_q8_isums(const void *W, const int8_t *xq, int32_t *isums,
                        int64_t N, int64_t K, void *stream);
 
 /*
+ * Test hook for the Q6_K x Q8 path: isums[n][g] = sum_{i<16}
+ * (q6[n][16g+i] - 32) * xq[16g+i] from the same device decode and dot code as
+ * q6k_q8_gemv.
+ *   isums: int32[N][K/16].
+ */
+int gemvq_q6k_q8_isums(const void *W, const int8_t *xq, int32_t *isums,
+                       int64_t N, int64_t K, void *stream);
+
+/*
  * Launch geometry of the GEMV kernels for an N x K matrix (host-only, no HIP
  * call; for tests and tuning).  kind: 0 = Q4_K (q4k_gemv), 1 = Q6_K (q6k_gemv,
- * lm_head_argmax), 2 = Q4_K x Q8 (q4k_q8_gemv), 3 = SwiGLU (swiglu_gemv).
+ * lm_head_argmax), 2 = Q4_K x Q8 (q4k_q8_gemv), 3 = SwiGLU (swiglu_gemv),
+ * 4 = Q6_K x Q8 (q6k_q8_gemv).
  * out[0] = waves per workgroup, out[1] = rows per tile, out[2] = tiles,
  * out[3] = 1 if a row's partial sums reduce inside one wave, out[4] = 1 if the
  * activation is staged through LDS, out[5] = dynamic LDS bytes, out[6] =

@@ -12,6 +12,8 @@ SMALL_Q6K = [(1, 256), (4, 256), (100, 768), (1000, 1024), (257, 9728), (33, 128
              (3, 32768), (65, 2048), (5, 16384)]
 SMALL_SWIGLU = [(1, 256), (100, 1024), (333, 2560), (50, 8192), (7, 16384)]
 SMALL_Q8 = [(1, 256), (1000, 1024), (333, 2560), (77, 8192), (50, 9728), (3, 32768)]
+SMALL_Q6K_Q8 = [(1, 256), (100, 768), (1000, 1024), (333, 2560), (257, 9728), (3, 32768), (5, 16384),
+                (65, 2048), (9, 4352)]
 
 
 def kernel_path(kind, N, K):
@@ -34,5 +36,7 @@ REQUIRED_PATHS = {
     gq.KIND_Q6K: {"wave1", "rows1", "tile-lds", "tile"},
     gq.KIND_SWIGLU: {"wave1", "tile-lds", "tile"},
     gq.KIND_Q4K_Q8: {"wave1", "wave2", "rows1", "tile-lds", "tile"},
+    gq.KIND_Q6K_Q8: {"wave1", "rows1", "tile-lds", "tile"},
 }
-CASES = {gq.KIND_Q4K: SMALL_Q4K, gq.KIND_Q6K: SMALL_Q6K, gq.KIND_SWIGLU: SMALL_SWIGLU, gq.KIND_Q4K_Q8: SMALL_Q8}
+CASES = {gq.KIND_Q4K: SMALL_Q4K, gq.KIND_Q6K: SMALL_Q6K, gq.KIND_SWIGLU: SMALL_SWIGLU, gq.KIND_Q4K_Q8: SMALL_Q8,
+         gq.KIND_Q6K_Q8: SMALL_Q6K_Q8}

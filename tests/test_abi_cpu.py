@@ -75,6 +75,9 @@ def test_null_pointers():
     _rejected(L.lm_head_argmax(A, B, C, None, None, 1 << 20, 4, 256, None), gq.ERR_NULL)
     _rejected(L.lm_head_argmax_timed(A, B, C, None, None, 1 << 20, 4, 256, None, None, None), gq.ERR_NULL)
     _rejected(L.gemvq_q4k_q8_isums(A, B, None, 4, 256, None), gq.ERR_NULL)
+    _rejected(L.q6k_q8_gemv(A, B, C, None, 4, 256, None), gq.ERR_NULL)
+    _rejected(L.q6k_q8_gemv(None, B, C, D, 4, 256, None), gq.ERR_NULL)
+    _rejected(L.gemvq_q6k_q8_isums(A, None, C, 4, 256, None), gq.ERR_NULL)
     _rejected(L.lm_head_argmax_masked(A, B, None, C, D, E, 1 << 20, 4, 256, None), gq.ERR_NULL)
 
 
@@ -89,6 +92,8 @@ def test_bad_shapes(N, K):
     _rejected(L.lm_head_argmax(A, B, C, D, E, 1 << 20, N, K, None), gq.ERR_SHAPE)
     _rejected(L.lm_head_argmax_timed(A, B, C, D, E, 1 << 20, N, K, None, A, B), gq.ERR_SHAPE)
     _rejected(L.gemvq_q4k_q8_isums(A, B, C, N, K, None), gq.ERR_SHAPE)
+    _rejected(L.q6k_q8_gemv(A, B, C, D, N, K, None), gq.ERR_SHAPE)
+    _rejected(L.gemvq_q6k_q8_isums(A, B, C, N, K, None), gq.ERR_SHAPE)
 
 
 def test_q8_bad_shapes():
@@ -111,6 +116,10 @@ def test_alignment():
     _rejected(L.lm_head_argmax(A, B, C + 1, D, E, 1 << 20, 4, 256, None), gq.ERR_ALIGN)
     _rejected(L.lm_head_argmax_timed(A, B, C + 1, D, E, 1 << 20, 4, 256, None, None, None), gq.ERR_ALIGN)
     _rejected(L.gemvq_q4k_q8_isums(A, B, C + 2, 4, 256, None), gq.ERR_ALIGN)
+    _rejected(L.q6k_q8_gemv(A + 2, B, C, D, 4, 256, None), gq.ERR_ALIGN)    # Q6_K weights need 4 B
+    _rejected(L.q6k_q8_gemv(A, B + 8, C, D, 4, 256, None), gq.ERR_ALIGN)    # xq needs 16 B
+    _rejected(L.q6k_q8_gemv(A, B, C + 2, D, 4, 256, None), gq.ERR_ALIGN)    # xd needs 4 B
+    _rejected(L.gemvq_q6k_q8_isums(A, B, C + 2, 4, 256, None), gq.ERR_ALIGN)
     _rejected(L.lm_head_argmax_masked(A, B, C + 2, D, None, E, 1 << 20, 4, 256, None), gq.ERR_ALIGN)
 
 
@@ -141,6 +150,9 @@ def test_aliasing():
     _rejected(L.lm_head_argmax_masked(A, B, C, C, None, E, ws, N, K, None), gq.ERR_ALIAS)   # idx over the mask
     _rejected(L.lm_head_argmax_masked(A, B, E + 64, C, None, E, ws, N, K, None), gq.ERR_ALIAS)  # mask inside ws
     _rejected(L.gemvq_q4k_q8_isums(A, B, B, N, K, None), gq.ERR_ALIAS)
+    _rejected(L.q6k_q8_gemv(A, B, C, B + 16, N, K, None), gq.ERR_ALIAS)         # y inside xq
+    _rejected(L.q6k_q8_gemv(A, B, C, A + 100, N, K, None), gq.ERR_ALIAS)        # y inside W
+    _rejected(L.gemvq_q6k_q8_isums(A, B, A, N, K, None), gq.ERR_ALIAS)
 
 
 def test_binding_rejects_host_tensors():

@@ -22,6 +22,7 @@ def test_parity_cases_cover_every_path(kind):
     (gq.KIND_Q6K, 2560, 9728, "tile-lds"),
     (gq.KIND_Q4K_Q8, 28_672, 8192, "wave2"),
     (gq.KIND_Q4K, 28_672, 8192, "rows2"),
+    (gq.KIND_Q6K_Q8, 2560, 9728, "tile-lds"),
 ])
 def test_workload_paths(kind, N, K, path):
     """The benchmarked workloads run the kernels their parity tests cover."""

@@ -54,10 +54,10 @@ def lane_offsets(geo, nb, B, N):
     return offsets, c, P * nb * B
 
 
-def q6k_windows(N, K, tiles_to_check=None):
+def q6k_windows(N, K, tiles_to_check=None, kind=gq.KIND_Q6K):
     """(lowest byte read, one past the highest, end of the matrix)."""
     nb = K // 256
-    geo = gq.tile_geometry(gq.KIND_Q6K, N, K)
+    geo = gq.tile_geometry(kind, N, K)
     offsets, u, stride = lane_offsets(geo, nb, 210, N)
     n, l0 = u >> 1, 16 * (u & 1)
     lo, hi = None, None
@@ -106,17 +106,19 @@ def ends_of(geo):
 SHAPES = [(N, K) for N in (1, 2, 3, 5, 7, 21, 100, 257) for K in range(256, 10241, 256)]
 
 
+@pytest.mark.parametrize("kind", [gq.KIND_Q6K, gq.KIND_Q6K_Q8])
 @pytest.mark.parametrize("N,K", SHAPES)
-def test_q6k_loads_in_bounds(N, K):
-    lo, hi, end = q6k_windows(N, K)
+def test_q6k_loads_in_bounds(N, K, kind):
+    lo, hi, end = q6k_windows(N, K, kind=kind)
     assert W_BASE <= lo and hi <= end, (N, K, lo - W_BASE, hi - end)
 
 
 @pytest.mark.parametrize("N,K", [(248_320, 1024), (2560, 9728), (100, 768), (99_999, 768), (12_345, 3328),
                                  (7, 16384), (3, 32768), (1001, 12288)])
-def test_q6k_loads_in_bounds_large(N, K):
-    geo = gq.tile_geometry(gq.KIND_Q6K, N, K)
-    lo, hi, end = q6k_windows(N, K, ends_of(geo))
+@pytest.mark.parametrize("kind", [gq.KIND_Q6K, gq.KIND_Q6K_Q8])
+def test_q6k_loads_in_bounds_large(N, K, kind):
+    geo = gq.tile_geometry(kind, N, K)
+    lo, hi, end = q6k_windows(N, K, ends_of(geo), kind)
     assert W_BASE <= lo and hi <= end
 
 
@@ -137,7 +139,7 @@ def test_q4k_loads_in_bounds_large(kind, N, K):
     assert W_BASE <= lo and hi <= end
 
 
-@pytest.mark.parametrize("kind", [gq.KIND_Q4K, gq.KIND_Q6K, gq.KIND_Q4K_Q8, gq.KIND_SWIGLU])
+@pytest.mark.parametrize("kind", [gq.KIND_Q4K, gq.KIND_Q6K, gq.KIND_Q4K_Q8, gq.KIND_SWIGLU, gq.KIND_Q6K_Q8])
 @pytest.mark.parametrize("K", [256, 768, 1024, 1280, 2560, 4096, 4352, 8192, 9728, 12288, 16384, 32768])
 def test_every_block_quarter_served_once(kind, K):
     """Each (row of a unit or tile, super-block, quarter) is taken by exactly

@@ -70,7 +70,7 @@ def q6k_abs_rows(W, x, N, K):
     return np.abs(Wf) @ np.abs(x.astype(np.float64))
 
 
-from parity_shapes import SMALL_Q4K, SMALL_Q6K, SMALL_SWIGLU, SMALL_Q8  # noqa: E402
+from parity_shapes import SMALL_Q4K, SMALL_Q6K, SMALL_SWIGLU, SMALL_Q8, SMALL_Q6K_Q8  # noqa: E402
 
 
 @pytest.mark.parametrize("N,K", SMALL_Q4K)
@@ -432,6 +432,44 @@ def test_q4k_f32_c5_shape_full(dev):
     N, K = synth.C5_Q8
     y = gq().q4k_gemv(up(W, dev), up(x, dev), N, K).cpu().numpy()
     check_f32("C5 f32 q4k", y, oracle.q4k_gemv(W, x, N, K))
+
+
+# ------------------------------------------------------------ Q6_K x Q8
+def test_q6k_q8_isums_exact(dev):
+    for N, K in [(1, 256), (37, 1024), (300, 2560), (64, 8192), (5, 9728), (3, 32768)]:
+        r = synth.rng_for(7000 + N)
+        W = synth.q6k_weights(r, N, K)
+        x = synth.activation_outliers(r, K)
+        q, d = oracle.q8_quantize(x)
+        got = gq().q6k_q8_isums(up(W, dev), up(q, dev), N, K).cpu().numpy()
+        assert np.array_equal(got, oracle.q6k_q8_isums(W, q, N, K)), (N, K)
+
+
+@pytest.mark.parametrize("N,K", SMALL_Q6K_Q8)
+def test_q6k_q8_gemv_small(dev, N, K):
+    r = synth.rng_for(7500 + N + K)
+    W = synth.q6k_weights(r, N, K)
+    x = synth.activation_outliers(r, K)
+    q, d = oracle.q8_quantize(x)
+    y = gq().q6k_q8_gemv(up(W, dev), up(q, dev), up(d.view(np.int16), dev), N, K).cpu().numpy()
+    check_f32(f"q6k_q8 {N}x{K}", y, oracle.q6k_q8_gemv(W, q, d, N, K))
+
+
+def test_q6k_q8_down_full(dev):
+    """The int8 ffn_down at its full shape (Q6_K 2560 x 9728) on a quantized
+    SwiGLU-like activation; the quantization is the device's own."""
+    N, K = 2560, 9728
+    r = synth.rng_for(7777)
+    W = synth.q6k_weights(r, N, K)
+    h = synth.activation_outliers(r, K)
+    dW = up(W, dev)
+    xq, xd = gq().q8_quantize(up(h, dev))
+    q, d = oracle.q8_quantize(h)
+    assert np.array_equal(xq.cpu().numpy(), q) and np.array_equal(xd.cpu().numpy().view(np.uint16), d)
+    y = gq().q6k_q8_gemv(dW, xq, xd, N, K).cpu().numpy()
+    check_f32("q6k_q8 2560x9728", y, oracle.q6k_q8_gemv(W, q, d, N, K))
+    isums = gq().q6k_q8_isums(dW[:64], xq, 64, K).cpu().numpy()      # first 64 rows, exact
+    assert np.array_equal(isums, oracle.q6k_q8_isums(W[:64], q, 64, K))
 
 
 # ------------------------------------------------------------ masked argmax
