@@ -21,7 +21,7 @@ __all__ = [
     "GemvqError", "lib", "exported_names", "header_names",
     "q4k_gemv", "q4k_gemv_multi", "q6k_gemv", "q8_quantize", "q4k_q8_gemv", "swiglu_gemv",
     "lm_head_argmax", "lm_head_argmax_timed", "lm_head_argmax_masked", "lm_head_argmax_ws_bytes", "q4k_q8_isums", "strerror", "tile_geometry",
-    "q6k_q8_gemv", "q6k_q8_isums",
+    "q6k_q8_gemv", "q6k_q8_isums", "swiglu_q8_gemv", "swiglu_q8_ws_bytes", "rms_norm_q8", "add_rms_norm_q8",
     "Q4K_BLOCK_BYTES", "Q6K_BLOCK_BYTES", "LIB_PATH", "HEADER_PATH",
 ]
 
@@ -32,7 +32,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "gemvq.h")
 Q4K_BLOCK_BYTES = 144
 Q6K_BLOCK_BYTES = 210
 
-OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_WORKSPACE, ERR_ALIAS, ERR_HIP = range(7)
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_WORKSPACE, ERR_ALIAS, ERR_HIP, ERR_VALUE = range(8)
 
 
 class GemvqError(RuntimeError):
@@ -55,6 +55,10 @@ _SIGS = {
     "swiglu_gemv": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _P]),
     "q6k_q8_gemv": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _P]),
     "gemvq_q6k_q8_isums": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P]),
+    "swiglu_q8_gemv": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _I64, _I64, _P]),
+    "gemvq_swiglu_q8_ws_bytes": (ctypes.c_size_t, [_I64]),
+    "rms_norm_q8": (ctypes.c_int, [_P, _P, ctypes.c_float, _P, _P, _P, _I64, _P]),
+    "add_rms_norm_q8": (ctypes.c_int, [_P, _P, _P, ctypes.c_float, _P, _P, _P, _P, _I64, _P]),
     "lm_head_argmax": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_size_t, _I64, _I64, _P]),
     "lm_head_argmax_timed": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_size_t, _I64, _I64, _P, _P, _P]),
     "lm_head_argmax_masked": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_size_t, _I64, _I64, _P]),
@@ -94,7 +98,7 @@ def exported_names() -> list[str]:
     return sorted(_SIGS)
 
 
-KIND_Q4K, KIND_Q6K, KIND_Q4K_Q8, KIND_SWIGLU, KIND_Q6K_Q8 = range(5)
+KIND_Q4K, KIND_Q6K, KIND_Q4K_Q8, KIND_SWIGLU, KIND_Q6K_Q8, KIND_SWIGLU_Q8 = range(6)
 
 
 def tile_geometry(kind: int, N: int, K: int) -> dict:
@@ -252,6 +256,70 @@ def swiglu_gemv(Wg, Wu, x, N: int, K: int, h=None, stream=None):
     _check("swiglu_gemv", lib().swiglu_gemv(Wg.data_ptr(), Wu.data_ptr(), x.data_ptr(), h.data_ptr(), N, K,
                                             _stream(x, stream)))
     return h
+
+
+def swiglu_q8_ws_bytes(N: int) -> int:
+    return int(lib().gemvq_swiglu_q8_ws_bytes(N))
+
+
+def swiglu_q8_gemv(Wg, Wu, x, N: int, K: int, workspace, hq=None, hd=None, h=None, stream=None):
+    """(hq int8[N], hd int16[N/32]): the Q8 encoding of silu(Wg x) * (Wu x),
+    written by the GEMV itself (N % 32 == 0).  `h` (float32[N]), if given,
+    also receives the f32 product.  `workspace` is a uint8 device tensor of
+    at least swiglu_q8_ws_bytes(N) bytes, zero-filled before its first use;
+    every call leaves it reusable."""
+    torch = _torch()
+    _weights(Wg, N, K, Q4K_BLOCK_BYTES, "Wg")
+    _weights(Wu, N, K, Q4K_BLOCK_BYTES, "Wu")
+    _dev_tensor(x, torch.float32, K, "x")
+    if not isinstance(workspace, torch.Tensor) or workspace.device.type != "cuda" or workspace.dtype != torch.uint8:
+        raise TypeError("workspace: expected a uint8 device tensor")
+    hq = _out(hq, x.device, torch.int8, N, "hq")
+    hd = _out(hd, x.device, torch.int16, N // 32, "hd")
+    if h is not None:
+        _dev_tensor(h, torch.float32, N, "h")
+    _check("swiglu_q8_gemv", lib().swiglu_q8_gemv(Wg.data_ptr(), Wu.data_ptr(), x.data_ptr(),
+                                                  h.data_ptr() if h is not None else None, hq.data_ptr(),
+                                                  hd.data_ptr(), workspace.data_ptr(), workspace.numel(), N, K,
+                                                  _stream(x, stream)))
+    return hq, hd
+
+
+def rms_norm_q8(x, w, eps: float, xq=None, xd=None, y=None, stream=None):
+    """(xq int8[K], xd int16[K/32]): Q8 encoding of w * x / sqrt(mean(x^2) +
+    eps).  `y` (float32[K]), if given, also receives the f32 norm."""
+    return _rms(x, None, w, eps, None, xq, xd, y, stream)
+
+
+def add_rms_norm_q8(x, r, w, eps: float, res=None, xq=None, xd=None, y=None, stream=None):
+    """(res, xq, xd): res = x + r (f32; may be x or r itself), then the Q8
+    encoding of the RMS norm of res."""
+    torch = _torch()
+    res = _out(res, x.device, torch.float32, x.numel(), "res")
+    xq, xd = _rms(x, r, w, eps, res, xq, xd, y, stream)
+    return res, xq, xd
+
+
+def _rms(x, r, w, eps, res, xq, xd, y, stream):
+    torch = _torch()
+    K = x.numel()
+    _dev_tensor(x, torch.float32, K, "x")
+    _dev_tensor(w, torch.float32, K, "w")
+    if r is not None:
+        _dev_tensor(r, torch.float32, K, "r")
+    xq = _out(xq, x.device, torch.int8, K, "xq")
+    xd = _out(xd, x.device, torch.int16, K // 32, "xd")
+    if y is not None:
+        _dev_tensor(y, torch.float32, K, "y")
+    yp = y.data_ptr() if y is not None else None
+    if r is None:
+        _check("rms_norm_q8", lib().rms_norm_q8(x.data_ptr(), w.data_ptr(), float(eps), yp, xq.data_ptr(),
+                                                xd.data_ptr(), K, _stream(x, stream)))
+    else:
+        _check("add_rms_norm_q8", lib().add_rms_norm_q8(x.data_ptr(), r.data_ptr(), w.data_ptr(), float(eps),
+                                                        res.data_ptr(), yp, xq.data_ptr(), xd.data_ptr(), K,
+                                                        _stream(x, stream)))
+    return xq, xd
 
 
 def lm_head_argmax_ws_bytes(N: int, K: int) -> int:

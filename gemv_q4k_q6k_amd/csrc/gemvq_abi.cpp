@@ -75,6 +75,7 @@ const char *gemvq_strerror(int status)
     case GEMVQ_ERR_WORKSPACE: return "workspace too small";
     case GEMVQ_ERR_ALIAS: return "an output overlaps an input";
     case GEMVQ_ERR_HIP: return "HIP runtime error at launch";
+    case GEMVQ_ERR_VALUE: return "an argument value is out of range";
     default: return "unknown status";
     }
 }
@@ -89,10 +90,11 @@ size_t gemvq_lm_head_argmax_ws_bytes(int64_t N, int64_t K)
 int gemvq_tile_geometry(int kind, int64_t N, int64_t K, int64_t out[7])
 {
     if (!out) return GEMVQ_ERR_NULL;
-    if (kind < 0 || kind > 4) return GEMVQ_ERR_SHAPE;
+    if (kind < 0 || kind > 5) return GEMVQ_ERR_SHAPE;
     size_t wb = 0;
     if (int st = check_shape(N, K, (kind == 1 || kind == 4) ? 210 : 144, &wb)) return st;
-    const gemvq::Plan pl = gemvq::make_plan(N, K, kind);
+    if (kind == 5 && N % 32 != 0) return GEMVQ_ERR_SHAPE;
+    const gemvq::Plan pl = kind == 5 ? gemvq::make_swiglu_q8_plan(N, K) : gemvq::make_plan(N, K, kind);
     out[0] = pl.waves;
     out[1] = pl.rows_tile;
     out[2] = pl.tiles;
@@ -211,6 +213,79 @@ int swiglu_gemv(const void *Wg, const void *Wu, const float *x, float *h, int64_
     int cus = 0;
     if (int st = device_cus(&cus)) return st;
     return status_of(gemvq::launch_swiglu_gemv(Wg, Wu, x, h, N, K, cus, (hipStream_t)stream));
+}
+
+size_t gemvq_swiglu_q8_ws_bytes(int64_t N)
+{
+    if (N < 32 || N > kMaxN || N % 32 != 0) return 0;
+    return gemvq::swiglu_q8_ws_bytes(N);
+}
+
+int swiglu_q8_gemv(const void *Wg, const void *Wu, const float *x, float *h, int8_t *hq, uint16_t *hd,
+                   void *workspace, size_t ws_bytes, int64_t N, int64_t K, void *stream)
+{
+    if (!Wg || !Wu || !x || !hq || !hd || !workspace) return GEMVQ_ERR_NULL;
+    size_t wb = 0;
+    if (int st = check_shape(N, K, 144, &wb)) return st;
+    if (N % 32 != 0) return GEMVQ_ERR_SHAPE;
+    if (!aligned(Wg, 16) || !aligned(Wu, 16) || !aligned(x, 16) || (h && !aligned(h, 4)) || !aligned(hq, 16) ||
+        !aligned(hd, 4) || !aligned(workspace, 256))
+        return GEMVQ_ERR_ALIGN;
+    if (ws_bytes < gemvq::swiglu_q8_ws_bytes(N)) return GEMVQ_ERR_WORKSPACE;
+    const size_t nx = (size_t)K * 4, nh = h ? (size_t)N * 4 : 0, nq = (size_t)N, nd = (size_t)(N / 32) * 2;
+    const void *ins[3] = {Wg, Wu, x};
+    const size_t nins[3] = {wb, wb, nx};
+    const void *outs[4] = {h, hq, hd, workspace};
+    const size_t nouts[4] = {nh, nq, nd, ws_bytes};
+    for (int o = 0; o < 4; ++o) {
+        for (int i = 0; i < 3; ++i)
+            if (overlap(outs[o], nouts[o], ins[i], nins[i])) return GEMVQ_ERR_ALIAS;
+        for (int p = o + 1; p < 4; ++p)
+            if (overlap(outs[o], nouts[o], outs[p], nouts[p])) return GEMVQ_ERR_ALIAS;
+    }
+    int cus = 0;
+    if (int st = device_cus(&cus)) return st;
+    return status_of(gemvq::launch_swiglu_q8_gemv(Wg, Wu, x, h, hq, hd, workspace, N, K, cus, (hipStream_t)stream));
+}
+
+// Shared checks of rms_norm_q8 and add_rms_norm_q8 (r and res both null for the former).
+static int rms_norm_q8_impl(const float *x, const float *r, const float *w, float eps, float *res, float *y,
+                            int8_t *xq, uint16_t *xd, int64_t K, void *stream)
+{
+    if (K < 32 || K > gemvq::kMaxNormK || K % 32 != 0) return GEMVQ_ERR_SHAPE;
+    if (!(eps >= 0.0f) || eps > 3.0e38f) return GEMVQ_ERR_VALUE;   // rejects NaN, negative and infinite eps
+    if (!aligned(x, 4) || (r && !aligned(r, 4)) || !aligned(w, 4) || (res && !aligned(res, 4)) ||
+        (y && !aligned(y, 4)) || !aligned(xq, 16) || !aligned(xd, 4))
+        return GEMVQ_ERR_ALIGN;
+    const size_t nv = (size_t)K * 4, nq = (size_t)K, nd = (size_t)(K / 32) * 2;
+    const void *ins[3] = {x, r, w};
+    const size_t nins[3] = {nv, r ? nv : 0, nv};
+    const void *outs[4] = {res, y, xq, xd};
+    const size_t nouts[4] = {res ? nv : 0, y ? nv : 0, nq, nd};
+    for (int o = 0; o < 4; ++o) {
+        for (int i = 0; i < 3; ++i) {
+            // the residual may be written over x or r exactly (in place), nothing else
+            if (o == 0 && i < 2 && outs[0] == ins[i]) continue;
+            if (overlap(outs[o], nouts[o], ins[i], nins[i])) return GEMVQ_ERR_ALIAS;
+        }
+        for (int p = o + 1; p < 4; ++p)
+            if (overlap(outs[o], nouts[o], outs[p], nouts[p])) return GEMVQ_ERR_ALIAS;
+    }
+    return status_of(gemvq::launch_rms_norm_q8(x, r, w, eps, res, y, xq, xd, K, (hipStream_t)stream));
+}
+
+int rms_norm_q8(const float *x, const float *w, float eps, float *y, int8_t *xq, uint16_t *xd, int64_t K,
+                void *stream)
+{
+    if (!x || !w || !xq || !xd) return GEMVQ_ERR_NULL;
+    return rms_norm_q8_impl(x, nullptr, w, eps, nullptr, y, xq, xd, K, stream);
+}
+
+int add_rms_norm_q8(const float *x, const float *r, const float *w, float eps, float *res, float *y, int8_t *xq,
+                    uint16_t *xd, int64_t K, void *stream)
+{
+    if (!x || !r || !w || !res || !xq || !xd) return GEMVQ_ERR_NULL;
+    return rms_norm_q8_impl(x, r, w, eps, res, y, xq, xd, K, stream);
 }
 
 static int lm_head_argmax_impl(const void *W, const float *x, const uint32_t *mask, uint32_t *out_idx, float *out_max,

@@ -24,8 +24,10 @@ namespace gemvq {
 enum Kind : int { kQ4K = 0, kQ6K = 1, kQ4KQ8 = 2, kSwiglu = 3, kQ6KQ8 = 4 };
 constexpr bool is_q8(int kind) { return kind == kQ4KQ8 || kind == kQ6KQ8; }   // int8 activation
 constexpr bool is_q6(int kind) { return kind == kQ6K || kind == kQ6KQ8; }     // Q6_K weights
-enum Epi : int { kStore = 0, kArgmax = 1, kArgmaxMasked = 2 };
-constexpr bool is_argmax(int epi) { return epi != kStore; }
+// kQ8Emit: the tile kernel's rows are also encoded as a Q8 activation (the
+// SwiGLU product feeding an int8 down projection)
+enum Epi : int { kStore = 0, kArgmax = 1, kArgmaxMasked = 2, kQ8Emit = 3 };
+constexpr bool is_argmax(int epi) { return epi == kArgmax || epi == kArgmaxMasked; }
 
 
 struct GemvArgs {
@@ -56,6 +58,13 @@ struct GemvArgs {
     const float *rm[kMaxMulti];   // residual added to y, or nullptr
     int64_t Nm[kMaxMulti];
     int ustart[kMaxMulti + 1];
+    // Q8 emission (EPI == kQ8Emit): codes and scales of the rows, the byte
+    // offset of the row values in the workspace (ws), and of the workgroup's
+    // row buffer in LDS
+    int8_t *hq;
+    uint16_t *hd;
+    uint32_t emit_vals_off;
+    uint32_t emit_lds_off;
 };
 
 // ------------------------------------------------------- activation setup
@@ -385,6 +394,78 @@ __device__ void argmax_finish(const GemvArgs &a, uint64_t best, int holder, int 
     }
 }
 
+// ------------------------------------------------------------ Q8 emission
+
+// Q8 encoding of one 32-element block held one value per lane of a 32-lane
+// half-wave (lane l holds element l): amax by a lane-max tree (exact,
+// order-free), d = amax/127 and q = round(v/d) in f32 with correctly rounded
+// division (the HIP default), q rounded half away from zero (roundf) and
+// clamped to [-127, 127]; the scale is stored as the fp16 of d (round to
+// nearest even).  Every producer of Q8 activations uses this one function,
+// so their codes agree bit for bit on equal inputs.
+__device__ __forceinline__ int8_t q8_encode(float v, uint16_t &dbits)
+{
+    float amax = fabsf(v);
+#pragma unroll
+    for (int m = 1; m < 32; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 32));
+    const float d = amax / 127.0f;
+    int q = 0;
+    if (d != 0.0f) {
+        float r = roundf(v / d);
+        r = fminf(fmaxf(r, -127.0f), 127.0f);
+        q = (int)r;
+    }
+    dbits = __builtin_bit_cast(uint16_t, (_Float16)d);
+    return (int8_t)q;
+}
+
+// Q8 encoding of the rows a workgroup of the tile kernel computed, [r0, r1)
+// (values in LDS).  A 32-row block that lies inside the range is encoded
+// right here.  A block shared with other workgroups goes through the
+// workspace: each sharer publishes its rows with returning atomic exchanges
+// (device scope, coherent across the XCDs, performed before the count),
+// then adds its row count to the block's counter; the sharer whose count
+// completes 32 reads the block back, encodes it and clears the counter, so
+// every counter is zero again between calls.  No workgroup waits for
+// another.  Workspace: counters (u32 per block) at ws[0], row values at
+// ws[emit_vals_off].
+__device__ void q8_emit_finish(const GemvArgs &a, const float *s_h, int64_t r0, int64_t r1)
+{
+    __syncthreads();   // every row of the range is in LDS
+    if (r1 <= r0) return;
+    const int l = threadIdx.x & 31;
+    const int hw = (int)(threadIdx.x >> 5), nhw = (int)(blockDim.x >> 5);
+    uint32_t *cnt = (uint32_t *)a.ws;
+    uint32_t *vals = (uint32_t *)(a.ws + a.emit_vals_off);
+    const int64_t jb = r0 >> 5, je = (r1 - 1) >> 5;
+    for (int64_t j = jb + hw; j <= je; j += nhw) {   // uniform over the half-wave
+        const int64_t b0 = j << 5;
+        const int64_t lo = b0 > r0 ? b0 : r0;
+        const int64_t hi = b0 + 32 < r1 ? b0 + 32 : r1;
+        const int64_t row = b0 + l;
+        const bool mine = row >= lo && row < hi;
+        float v = mine ? s_h[row - r0] : 0.f;
+        if (lo != b0 || hi != b0 + 32) {
+            if (mine) {
+                const uint32_t old = __hip_atomic_exchange(vals + row, __float_as_uint(v), __ATOMIC_RELAXED,
+                                                           __HIP_MEMORY_SCOPE_AGENT);
+                asm volatile("" ::"v"(old) : "memory");   // consumed: performed before the count below
+            }
+            uint32_t prev = 0;
+            if (l == 0)
+                prev = __hip_atomic_fetch_add(cnt + j, (uint32_t)(hi - lo), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            prev = (uint32_t)__shfl((int)prev, 0, 32);
+            if (prev + (uint32_t)(hi - lo) != 32u) continue;   // another sharer completes the block
+            v = __uint_as_float(__hip_atomic_load(vals + row, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+            if (l == 0) __hip_atomic_store(cnt + j, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        uint16_t dbits;
+        const int8_t q = q8_encode(v, dbits);
+        a.hq[row] = q;
+        if (l == 0) a.hd[j] = dbits;
+    }
+}
+
 // ------------------------------------------------------------------ kernel
 
 // Tile kernel, for rows that do not fit an aligned power-of-two lane group of
@@ -504,6 +585,10 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_kernel(GemvArgs a)
 
     float *red = (float *)smem;   // [2][OUTS][rows_tile][nb]
     const int red_stride = OUTS * a.rows_tile * a.nb;
+    // Q8 emission: the workgroup's rows [r_begin, r_end) are kept in LDS
+    float *s_h = (float *)(smem + a.emit_lds_off);
+    const int64_t r_begin = (int64_t)t_begin * a.rows_tile;
+    const int64_t r_end = (int64_t)t_end * a.rows_tile < a.N ? (int64_t)t_end * a.rows_tile : a.N;
     uint64_t best = 0;   // running argmax key (argmax kernels)
     int buf = 0;
     // dot, row reduction and epilogue of tile t (workgroup-uniform control flow)
@@ -538,9 +623,17 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_kernel(GemvArgs a)
                         for (; c < a.nb; ++c) acc += src[c];
                         r[o] = acc;
                     }
-                    uint32_t mw = 0;
-                    if constexpr (EPI == kArgmaxMasked) mw = a.mask[row >> 5];
-                    emit_row<KIND, EPI>(a, row, r, best, mw);
+                    if constexpr (EPI == kQ8Emit) {
+                        // the SwiGLU product exactly as the store epilogue writes it
+                        const float g = r[0], u = r[1];
+                        const float hv = g * u / (1.0f + expf(-g));
+                        s_h[row - r_begin] = hv;
+                        if (a.y) a.y[row] = hv;
+                    } else {
+                        uint32_t mw = 0;
+                        if constexpr (EPI == kArgmaxMasked) mw = a.mask[row >> 5];
+                        emit_row<KIND, EPI>(a, row, r, best, mw);
+                    }
                 }
             }
             buf ^= 1;   // the next tile writes the other half; one barrier per tile suffices
@@ -563,6 +656,7 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_kernel(GemvArgs a)
         // the row-sum threads hold the keys
         argmax_finish(a, best, tid < a.rows_tile ? tid : -1, a.rows_tile);
     }
+    if constexpr (EPI == kQ8Emit) q8_emit_finish(a, s_h, r_begin, r_end);
 }
 
 // ------------------------------------------------------ wave-unit kernel
@@ -985,28 +1079,81 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_rows_kernel(Gem
 
 // --------------------------------------------------------- Q8 quantize
 
-// One 32-lane half-wave per 32-element block: amax by a lane-max tree (exact,
-// order-free), d = amax/127 and q = round(x/d) in f32 with correctly rounded
-// division (the HIP default), q rounded half away from zero (roundf).
+// One 32-lane half-wave per 32-element block.
 __global__ __launch_bounds__(256) void q8_quantize_kernel(const float *__restrict__ x, int8_t *__restrict__ xq,
                                                          uint16_t *__restrict__ xd, int K)
 {
     const int gid = blockIdx.x * blockDim.x + threadIdx.x;
     const bool on = gid < K;
     const float v = on ? x[gid] : 0.f;
-    float amax = fabsf(v);
-#pragma unroll
-    for (int m = 1; m < 32; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 32));
-    const float d = amax / 127.0f;
-    int q = 0;
-    if (d != 0.0f) {
-        float r = roundf(v / d);
-        r = fminf(fmaxf(r, -127.0f), 127.0f);
-        q = (int)r;
-    }
+    uint16_t dbits;
+    const int8_t q = q8_encode(v, dbits);
     if (on) {
-        xq[gid] = (int8_t)q;
-        if ((gid & 31) == 0) xd[gid >> 5] = __builtin_bit_cast(uint16_t, (_Float16)d);
+        xq[gid] = q;
+        if ((gid & 31) == 0) xd[gid >> 5] = dbits;
+    }
+}
+
+// ------------------------------------------------------ RMS norm -> Q8
+
+// y = w * x / sqrt(mean(x^2) + eps), then the Q8 encoding of y (memra-engine
+// decode.rs `rms_norm_q8_1`, and `add_rms_norm_q8_1` with ADD: x is first
+// replaced by x + r, which is also written to res as the new residual).  One
+// workgroup of 1024 threads: half-wave h owns blocks h, h + 32, ..., lane l
+// element l of each, so every value stays in the register of the lane that
+// encodes it.  All loads are issued up front (clamped to the last block, so
+// no branch separates them); the sum of squares is added per lane in block
+// order, then by a fixed shuffle tree, then over the 16 waves in order.
+// res may be x or r itself (each element is read, then written, by one lane;
+// those pointers carry no __restrict__ for that reason).
+constexpr int kNormThreads = 1024;
+constexpr int kNormPer = 32;   // blocks per half-wave: K <= 32 * 32 * 32
+
+template <bool ADD>
+__global__ __launch_bounds__(kNormThreads) void rms_norm_q8_kernel(const float *x, const float *r,
+                                                                  const float *__restrict__ w, float eps,
+                                                                  float *res, float *__restrict__ y,
+                                                                  int8_t *__restrict__ xq, uint16_t *__restrict__ xd,
+                                                                  int K)
+{
+    __shared__ float s_part[kNormThreads / 64];
+    const int tid = threadIdx.x, hw = tid >> 5, l = tid & 31;
+    const int blocks = K >> 5;
+    float v[kNormPer], wv[kNormPer];
+#pragma unroll
+    for (int i = 0; i < kNormPer; ++i) {
+        const int j = hw + 32 * i;
+        const int e = 32 * (j < blocks ? j : blocks - 1) + l;
+        v[i] = x[e];
+        if constexpr (ADD) v[i] = v[i] + r[e];
+        wv[i] = w[e];
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < kNormPer; ++i) {
+        const bool on = hw + 32 * i < blocks;
+        ss += on ? v[i] * v[i] : 0.f;
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) ss += __shfl_xor(ss, off);
+    if ((tid & 63) == 0) s_part[tid >> 6] = ss;
+    __syncthreads();
+    float tot = 0.f;
+#pragma unroll
+    for (int i = 0; i < kNormThreads / 64; ++i) tot += s_part[i];
+    const float inv = 1.0f / sqrtf(tot / (float)K + eps);
+#pragma unroll
+    for (int i = 0; i < kNormPer; ++i) {
+        const int j = hw + 32 * i;
+        if (j < blocks) {   // half-wave-uniform
+            const int e = 32 * j + l;
+            if constexpr (ADD) res[e] = v[i];
+            const float yv = (v[i] * inv) * wv[i];
+            if (y) y[e] = yv;
+            uint16_t dbits;
+            xq[e] = q8_encode(yv, dbits);
+            if (l == 0) xd[j] = dbits;
+        }
     }
 }
 
@@ -1123,11 +1270,12 @@ static bool plan_in_wave(Plan &pl, int64_t N, int64_t K, int kind)
     return finish_wave_plan(pl, N, K, kind);
 }
 
-Plan make_plan(int64_t N, int64_t K, int kind)
+// Tile-kernel plan; `extra_lds` bytes of LDS are reserved past the kernel's
+// own (the Q8 emission's row buffer), and x is staged through LDS only if
+// everything fits in 64 KiB.
+static Plan make_tile_plan(int64_t N, int64_t K, int kind, size_t extra_lds)
 {
     Plan pl{};
-    if (plan_in_wave(pl, N, K, kind)) return pl;
-    pl = Plan{};
     pl.nb = (int)(K / kQK);
     pl.wave_local = 0;
     pl.rows_kernel = 0;
@@ -1157,13 +1305,22 @@ Plan make_plan(int64_t N, int64_t K, int kind)
     // slice; with one row per tile every element has a single reader.
     const size_t sums = is_q8(kind) ? 0 : (size_t)(K / 16) * 4;
     const size_t xpadded = xbytes + xbytes / 16;   // 16 bytes of padding per 256 (lds_pad)
-    pl.x_in_lds = (pl.rows_tile > 1 && xpadded + sums <= 65536) ? 1 : 0;
     const size_t red = (size_t)2 * outs * pl.rows_tile * pl.nb * 4;   // two buffers
+    pl.x_in_lds = (pl.rows_tile > 1 && xpadded + sums + extra_lds <= 65536) ? 1 : 0;
     pl.lds_bytes = (pl.x_in_lds ? xpadded + sums : 0);
     if (red > pl.lds_bytes) pl.lds_bytes = red;
     pl.grid = 0;   // set by the launcher from the occupancy
     return pl;
 }
+
+Plan make_plan(int64_t N, int64_t K, int kind)
+{
+    Plan pl{};
+    if (plan_in_wave(pl, N, K, kind)) return pl;
+    return make_tile_plan(N, K, kind, 0);
+}
+
+Plan make_swiglu_q8_plan(int64_t N, int64_t K) { return make_tile_plan(N, K, kSwiglu, (size_t)4 * kEmitRows + 16); }
 
 // Resident workgroups per CU of a kernel at a block size and LDS size,
 // cached (occupancy depends only on those and the compiled kernel).
@@ -1233,6 +1390,12 @@ static hipError_t launch_mode(Plan &pl, GemvArgs a, int cus, hipStream_t s, cons
     const void *fn2 = (const void *)gemv_kernel<KIND, EPI, 2, XLDS>;
     pl.grid = grid_for(pl, fn2, cus, KIND == kSwiglu ? 2 : 4);
     if (is_argmax(EPI) && pl.grid > kArgmaxMaxGrid) pl.grid = kArgmaxMaxGrid;   // one workspace slot each
+    if constexpr (EPI == kQ8Emit) {
+        // a workgroup's rows must fit its LDS row buffer
+        const int64_t per = kEmitRows / pl.rows_tile;
+        const int64_t need = (pl.tiles + per - 1) / per;
+        if (pl.grid < need) pl.grid = (int)need;
+    }
     a.tiles_q = (int)(pl.tiles / pl.grid);
     a.tiles_r = (int)(pl.tiles % pl.grid);
     if (a.tiles_q >= 2 || (a.tiles_q == 1 && a.tiles_r > 0))
@@ -1347,6 +1510,25 @@ hipError_t launch_q4k_q8_gemv(const void *W, const int8_t *xq, const uint16_t *x
     return launch<kQ4KQ8, kStore>(pl, a, cus, s);
 }
 
+hipError_t launch_swiglu_q8_gemv(const void *Wg, const void *Wu, const float *x, float *h, int8_t *hq, uint16_t *hd,
+                                 void *ws, int64_t N, int64_t K, int cus, hipStream_t s)
+{
+    Plan pl = make_swiglu_q8_plan(N, K);
+    GemvArgs a = base_args(pl, N);
+    a.W = (const uint8_t *)Wg;
+    a.W2 = (const uint8_t *)Wu;
+    a.x = x;
+    a.y = h;
+    a.hq = hq;
+    a.hd = hd;
+    a.ws = (uint8_t *)ws;
+    a.emit_vals_off = (uint32_t)swiglu_q8_vals_offset(N);
+    a.emit_lds_off = (uint32_t)((pl.lds_bytes + 15) & ~(size_t)15);
+    pl.lds_bytes = a.emit_lds_off + (size_t)4 * kEmitRows;
+    return pl.x_in_lds ? launch_mode<kSwiglu, kQ8Emit, true>(pl, a, cus, s, Timing{})
+                       : launch_mode<kSwiglu, kQ8Emit, false>(pl, a, cus, s, Timing{});
+}
+
 hipError_t launch_q6k_q8_gemv(const void *W, const int8_t *xq, const uint16_t *xd, float *y, int64_t N, int64_t K,
                               int cus, hipStream_t s)
 {
@@ -1441,6 +1623,22 @@ hipError_t launch_q6k_q8_isums(const void *W, const int8_t *xq, int32_t *isums, 
     const int64_t blocks = (total + threads - 1) / threads;
     hipLaunchKernelGGL(q6k_q8_isums_kernel, dim3((unsigned)blocks), dim3(threads), 0, s, (const uint8_t *)W, xq, isums,
                        N, nb);
+    return hipGetLastError();
+}
+
+}  // namespace gemvq
+
+namespace gemvq {
+
+hipError_t launch_rms_norm_q8(const float *x, const float *r, const float *w, float eps, float *res, float *y,
+                              int8_t *xq, uint16_t *xd, int64_t K, hipStream_t s)
+{
+    if (r)
+        hipLaunchKernelGGL(rms_norm_q8_kernel<true>, dim3(1), dim3(kNormThreads), 0, s, x, r, w, eps, res, y, xq, xd,
+                           (int)K);
+    else
+        hipLaunchKernelGGL(rms_norm_q8_kernel<false>, dim3(1), dim3(kNormThreads), 0, s, x, r, w, eps, res, y, xq, xd,
+                           (int)K);
     return hipGetLastError();
 }
 

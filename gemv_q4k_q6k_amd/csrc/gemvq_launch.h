@@ -44,6 +44,7 @@ struct Plan {
 };
 
 Plan make_plan(int64_t N, int64_t K, int kind);
+Plan make_swiglu_q8_plan(int64_t N, int64_t K);   // always the tile kernel
 
 // Optional device timestamps of one launch: the kernel's own start and end
 // are recorded into these caller-created events when they are not null.
@@ -68,6 +69,18 @@ hipError_t launch_q4k_gemv_multi(const void *const *W, const int64_t *N, float *
                                  int count, const float *x, int64_t K, int cus, hipStream_t s);
 hipError_t launch_q8_quantize(const float *x, int8_t *xq, uint16_t *xd, int64_t K, hipStream_t s);
 hipError_t launch_q6k_q8_isums(const void *W, const int8_t *xq, int32_t *isums, int64_t N, int64_t K, hipStream_t s);
+// swiglu_q8_gemv: rows a tile-kernel workgroup keeps in LDS for the Q8
+// emission; workspace = one u32 counter per 32-row block, then the N row
+// values from offset swiglu_q8_vals_offset(N).
+constexpr int kEmitRows = 2048;
+constexpr size_t swiglu_q8_vals_offset(int64_t N) { return (((size_t)(N / 32) * 4) + 255) & ~(size_t)255; }
+constexpr size_t swiglu_q8_ws_bytes(int64_t N) { return swiglu_q8_vals_offset(N) + (size_t)N * 4; }
+hipError_t launch_swiglu_q8_gemv(const void *Wg, const void *Wu, const float *x, float *h, int8_t *hq, uint16_t *hd,
+                                 void *ws, int64_t N, int64_t K, int cus, hipStream_t s);
+// r == nullptr: rms_norm_q8; otherwise add_rms_norm_q8 (res receives x + r).  K % 32 == 0, K <= kMaxNormK.
+constexpr int64_t kMaxNormK = 32768;
+hipError_t launch_rms_norm_q8(const float *x, const float *r, const float *w, float eps, float *res, float *y,
+                              int8_t *xq, uint16_t *xd, int64_t K, hipStream_t s);
 hipError_t launch_q4k_q8_isums(const void *W, const int8_t *xq, int32_t *isums, int64_t N, int64_t K, hipStream_t s);
 
 }  // namespace gemvq

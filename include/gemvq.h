@@ -49,6 +49,7 @@ extern "C" {
 #define GEMVQ_ERR_WORKSPACE 4  /* workspace too small */
 #define GEMVQ_ERR_ALIAS     5  /* an output overlaps an input */
 #define GEMVQ_ERR_HIP       6  /* the HIP runtime reported an error at launch */
+#define GEMVQ_ERR_VALUE     7  /* a scalar argument is out of range (eps) */
 
 /*
  * y[n] = sum_k W[n,k] * x[k] over a Q4_K matrix, f32 activation, f32 result.
@@ -133,6 +134,56 @@ int swiglu_gemv(const void *Wg, const void *Wu, const float *x, float *h,
                 int64_t N, int64_t K, void *stream);
 
 /*
+ * SwiGLU GEMV that emits its product as a Q8 activation: the producer-side
+ * quantization of memra-engine decode.rs `ffn_swiglu_decode` (the SwiGLU
+ * epilogue writes the q8 form of silu(gate)*up, `silu_mul_scaled_q8_1`, and
+ * the down projection reads it directly, with no separate quantize launch),
+ * stated there to be bit-identical to the unfused sequence.  Here hq/hd equal
+ * q8_quantize applied to the h that swiglu_gemv writes whenever swiglu_gemv
+ * runs its tile kernel for the same N x K (every K/256 that is not a power of
+ * two up to 16, e.g. K = 2560); for other K the rows are summed in another
+ * order and only the parity bound holds.  Pair with q6k_q8_gemv.
+ *   Wg, Wu: Q4_K N x K.  x: float[K].  N % 32 == 0.
+ *   h: float[N] or NULL (the f32 product is also written when given).
+ *   hq: int8[N], hd: uint16[N/32] (fp16 scale bits), as q8_quantize writes.
+ *   workspace: >= gemvq_swiglu_q8_ws_bytes(N) bytes, 256-byte aligned; its
+ *   first N/32 * 4 bytes (per-block counters) must be zero before the first
+ *   call, and every call leaves them zero; the rest needs no initial value.
+ *   Calls that share a workspace must not run concurrently.
+ */
+int swiglu_q8_gemv(const void *Wg, const void *Wu, const float *x, float *h, int8_t *hq, uint16_t *hd,
+                   void *workspace, size_t ws_bytes, int64_t N, int64_t K, void *stream);
+
+/* Workspace bytes swiglu_q8_gemv needs for N rows (0 if N is not a positive
+ * multiple of 32).  Host-only. */
+size_t gemvq_swiglu_q8_ws_bytes(int64_t N);
+
+/*
+ * RMS norm that emits a Q8 activation (memra-engine decode.rs
+ * `rms_norm_q8_1`: the attention-input norm writes the quantized activation
+ * of the following projections directly).  The pages name the norm and its
+ * eps without writing it out; this is the usual RMS norm,
+ *   y[i] = w[i] * x[i] / sqrt(sum_j x[j]^2 / K + eps),
+ * followed by the Q8 encoding of y exactly as q8_quantize does it.
+ *   x, w: float[K], K % 32 == 0, 32 <= K <= 32768.  eps >= 0 and finite.
+ *   y: float[K] or NULL (the f32 norm is also written when given).
+ *   xq: int8[K], xd: uint16[K/32].
+ * Runs as one workgroup (a latency-bound vector op).
+ */
+int rms_norm_q8(const float *x, const float *w, float eps, float *y, int8_t *xq, uint16_t *xd, int64_t K,
+                void *stream);
+
+/*
+ * Residual add, RMS norm and Q8 encoding in one launch (memra-engine
+ * decode.rs `add_rms_norm_q8_1`: the post-attention residual add, the FFN
+ * norm and its quantization; the sum is the new residual stream).
+ *   res[i] = x[i] + r[i] (f32, written); then rms_norm_q8 of res.
+ *   res may be x or r itself (in-place update); no other overlap.
+ */
+int add_rms_norm_q8(const float *x, const float *r, const float *w, float eps, float *res, float *y, int8_t *xq,
+                    uint16_t *xd, int64_t K, void *stream);
+
+/*
  * lm_head GEMV over Q6_K rows with an on-device argmax: writes the FIRST index
  * of the maximum row value (NaN rows never win; -0 == +0; all-NaN gives 0) to
  * out_idx[0] and, if out_max is not NULL, that value to out_max[0].  No logits
@@ -211,7 +262,8 @@ int gemvq_q6k_q8_isums(const void *W, const int8_t *xq, int32_t *isums,
  * Launch geometry of the GEMV kernels for an N x K matrix (host-only, no HIP
  * call; for tests and tuning).  kind: 0 = Q4_K (q4k_gemv), 1 = Q6_K (q6k_gemv,
  * lm_head_argmax), 2 = Q4_K x Q8 (q4k_q8_gemv), 3 = SwiGLU (swiglu_gemv),
- * 4 = Q6_K x Q8 (q6k_q8_gemv).
+ * 4 = Q6_K x Q8 (q6k_q8_gemv), 5 = SwiGLU with Q8 emission (swiglu_q8_gemv,
+ * N % 32 == 0).
  * out[0] = waves per workgroup, out[1] = rows per tile, out[2] = tiles,
  * out[3] = 1 if a row's partial sums reduce inside one wave, out[4] = 1 if the
  * activation is staged through LDS, out[5] = dynamic LDS bytes, out[6] =

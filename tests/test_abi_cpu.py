@@ -186,3 +186,55 @@ def test_multi_rejections():
     _rejected(L.q4k_gemv_multi(W3, N3, _arr(P, [A + 64, C + 4096, C + 8192]), None, 3, B, 2560, None), gq.ERR_ALIAS)
     R3 = _arr(P, [None, C, None])      # residual of matrix 1 overlaps y[0]
     _rejected(L.q4k_gemv_multi(W3, N3, Y3, R3, 3, B, 2560, None), gq.ERR_ALIAS)
+
+
+def test_swiglu_q8_rejections():
+    L = gq.lib()
+    N, K = 64, 512
+    ws = gq.swiglu_q8_ws_bytes(N)
+    assert ws >= N * 4 + (N // 32) * 4 and gq.swiglu_q8_ws_bytes(33) == 0 and gq.swiglu_q8_ws_bytes(0) == 0
+    ok = dict(Wg=A, Wu=B, x=C, h=None, hq=D, hd=D + 4096, ws=E, wsb=ws, N=N, K=K)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return L.swiglu_q8_gemv(a["Wg"], a["Wu"], a["x"], a["h"], a["hq"], a["hd"], a["ws"], a["wsb"],
+                                a["N"], a["K"], None)
+    _rejected(call(hq=None), gq.ERR_NULL)
+    _rejected(call(ws=None), gq.ERR_NULL)
+    _rejected(call(N=48), gq.ERR_SHAPE)                    # N % 32 != 0
+    _rejected(call(K=300), gq.ERR_SHAPE)
+    _rejected(call(wsb=ws - 1), gq.ERR_WORKSPACE)
+    _rejected(call(hq=D + 8), gq.ERR_ALIGN)                # hq needs 16 B
+    _rejected(call(hd=D + 4096 + 2), gq.ERR_ALIGN)
+    _rejected(call(ws=E + 128), gq.ERR_ALIGN)              # workspace 256 B
+    _rejected(call(h=C + (1 << 20) + 2), gq.ERR_ALIGN)
+    _rejected(call(hq=A + 64), gq.ERR_ALIAS)               # hq inside Wg
+    _rejected(call(hd=D + 16), gq.ERR_ALIAS)               # hd inside hq
+    _rejected(call(h=E + 256), gq.ERR_ALIAS)               # h inside the workspace
+    _rejected(call(ws=C), gq.ERR_ALIAS)                    # workspace over x
+
+
+def test_rms_norm_q8_rejections():
+    L = gq.lib()
+    K = 256
+    _rejected(L.rms_norm_q8(None, B, 1e-5, None, D, D + 4096, K, None), gq.ERR_NULL)
+    _rejected(L.rms_norm_q8(A, B, 1e-5, None, None, D + 4096, K, None), gq.ERR_NULL)
+    _rejected(L.add_rms_norm_q8(A, None, B, 1e-5, C, None, D, D + 4096, K, None), gq.ERR_NULL)
+    _rejected(L.add_rms_norm_q8(A, C, B, 1e-5, None, None, D, D + 4096, K, None), gq.ERR_NULL)
+    for bad_k in (0, 16, 33, 32768 + 32):
+        _rejected(L.rms_norm_q8(A, B, 1e-5, None, D, D + 4096, bad_k, None), gq.ERR_SHAPE)
+    for bad_eps in (-1e-6, float("nan"), float("inf")):
+        _rejected(L.rms_norm_q8(A, B, bad_eps, None, D, D + 4096, K, None), gq.ERR_VALUE)
+    _rejected(L.rms_norm_q8(A + 2, B, 1e-5, None, D, D + 4096, K, None), gq.ERR_ALIGN)
+    _rejected(L.rms_norm_q8(A, B, 1e-5, None, D + 4, D + 4096, K, None), gq.ERR_ALIGN)   # xq needs 16 B
+    _rejected(L.rms_norm_q8(A, B, 1e-5, None, D, D + 4098, K, None), gq.ERR_ALIGN)
+    _rejected(L.rms_norm_q8(A, B, 1e-5, A + 64, D, D + 4096, K, None), gq.ERR_ALIAS)     # y over x
+    _rejected(L.rms_norm_q8(A, B, 1e-5, None, B + 16, D + 4096, K, None), gq.ERR_ALIAS)  # xq over w
+    _rejected(L.rms_norm_q8(A, B, 1e-5, D + 64, D, D + 4096, K, None), gq.ERR_ALIAS)     # y over xq
+    # the residual output may be x or r itself, but not a shifted copy of either
+    _rejected(L.add_rms_norm_q8(A, C, B, 1e-5, A + 4, None, D, D + 4096, K, None), gq.ERR_ALIAS)
+    _rejected(L.add_rms_norm_q8(A, C, B, 1e-5, C - 4, None, D, D + 4096, K, None), gq.ERR_ALIAS)
+    _rejected(L.add_rms_norm_q8(A, C, B, 1e-5, B, None, D, D + 4096, K, None), gq.ERR_ALIAS)   # res over w
+    # in place is allowed past the alias checks: make the call fail on alignment instead
+    _rejected(L.add_rms_norm_q8(A, C, B, 1e-5, A, None, D + 4, D + 4096, K, None), gq.ERR_ALIGN)
+    _rejected(L.add_rms_norm_q8(A, C, B, 1e-5, C, None, D + 4, D + 4096, K, None), gq.ERR_ALIGN)

@@ -130,6 +130,17 @@ def test_q4k_loads_in_bounds(kind, N, K):
     assert W_BASE <= lo and hi <= end
 
 
+@pytest.mark.parametrize("N,K", [(32, 256), (96, 1024), (320, 2560), (64, 8192), (32, 32768), (2048, 4352),
+                                 (9728, 2560), (4096, 14336)])
+def test_swiglu_q8_loads_in_bounds(N, K):
+    """The SwiGLU Q8-emission launch (always the tile kernel) at shapes that
+    are multiples of 32 rows."""
+    geo = gq.tile_geometry(gq.KIND_SWIGLU_Q8, N, K)
+    assert geo["wave_local"] == 0
+    lo, hi, end = q4k_windows(gq.KIND_SWIGLU_Q8, N, K, ends_of(geo))
+    assert W_BASE <= lo and hi <= end
+
+
 @pytest.mark.parametrize("kind,N,K", [(gq.KIND_Q4K, 9728, 2560), (gq.KIND_SWIGLU, 9728, 2560),
                                       (gq.KIND_Q4K, 2560, 9728), (gq.KIND_Q4K_Q8, 28_672, 8192),
                                       (gq.KIND_Q4K, 28_672, 8192), (gq.KIND_Q4K, 4096, 2560)])

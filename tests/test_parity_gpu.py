@@ -599,3 +599,159 @@ def test_q4k_gemv_multi_matches_single_rows(dev):
     for W, N, y in zip(Ws, Ns, out):
         assert ps.kernel_path(gq().KIND_Q4K, N, K) == "rows1"
         assert torch.equal(y, gq().q4k_gemv(W, dx, N, K))
+
+
+# ------------------------------------------------ Q8 emission (norm, SwiGLU)
+def check_q8_codes(name, q_gpu, d_gpu, v_gpu, v_orc):
+    """Q8 codes the device decided on its own f32 values, against the oracle's
+    codes of its f64 values rounded to f32.  Both encoders take the same f32
+    decisions, so the codes agree except where the two inputs straddle a
+    rounding boundary: a block's fp16 scale may differ by one step only if the
+    oracle's f32 amax/127 lies within the block's measured input error of an
+    fp16 midpoint, and a code may differ by one only in such a block or where
+    the oracle's quotient lies that close to a half-integer."""
+    q_gpu = np.asarray(q_gpu).astype(np.int64)
+    dg = np.asarray(d_gpu).view(np.uint16).astype(np.int64)
+    v_gpu = np.asarray(v_gpu, np.float64)
+    v32 = np.asarray(v_orc, np.float64).astype(np.float32)
+    q_o, d_o = oracle.q8_quantize(v32)
+    nb = d_o.size
+    vo = v32.reshape(nb, 32).astype(np.float64)
+    amax = np.abs(vo).max(axis=1)
+    err = np.abs(v_gpu.reshape(nb, 32) - vo).max(axis=1) / np.where(amax > 0, amax, 1.0)
+    d32 = (amax.astype(np.float32) / np.float32(127)).astype(np.float64)
+    # distance of d32 to the nearest fp16 rounding midpoint, relative to d32
+    h = d32.astype(np.float16).astype(np.float64)
+    up_ = np.nextafter(d32.astype(np.float16), np.float16(np.inf)).astype(np.float64)
+    dn_ = np.nextafter(d32.astype(np.float16), np.float16(-np.inf)).astype(np.float64)
+    mid = np.minimum(np.abs(d32 - (h + up_) / 2), np.abs(d32 - (h + dn_) / 2)) / np.where(d32 > 0, d32, 1.0)
+    dd = np.abs(dg - d_o.astype(np.int64))
+    assert dd.max() <= 1, name
+    scale_ok = (dd == 0) | (mid <= 2 * err + 1e-7)
+    assert scale_ok.all(), (name, np.nonzero(~scale_ok)[0][:5])
+    dq = np.abs(q_gpu - q_o.astype(np.int64)).reshape(nb, 32)
+    assert dq.max() <= 1, name
+    t = np.abs(vo / np.where(d32 > 0, d32, 1.0)[:, None])
+    near_half = np.abs(t - np.floor(t) - 0.5) <= 254 * err[:, None] + 1e-5
+    code_ok = (dq == 0) | near_half | (dd != 0)[:, None]
+    assert code_ok.all(), (name, np.argwhere(~code_ok)[:5])
+    print(f"{name}: scales differing {int((dd != 0).sum())}/{nb}, codes differing {int((dq != 0).sum())}/{q_o.size}, "
+          f"max block input error {err.max():.2e}", flush=True)
+
+
+SWIGLU_Q8_SHAPES = [(32, 256), (96, 1024), (160, 768), (320, 2560), (64, 8192), (32, 16384), (2048, 4352),
+                    (9728, 2560)]
+
+
+@pytest.mark.parametrize("N,K", SWIGLU_Q8_SHAPES)
+def test_swiglu_q8_gemv(dev, N, K):
+    from parity_shapes import kernel_path
+    r = synth.rng_for(8100 + N + K)
+    Wg, Wu = synth.q4k_weights(r, N, K), synth.q4k_weights(r, N, K)
+    x = synth.activation(r, K)
+    dWg, dWu, dx = up(Wg, dev), up(Wu, dev), up(x, dev)
+    ws = torch.zeros(gq().swiglu_q8_ws_bytes(N), dtype=torch.uint8, device=dev)
+    h = torch.empty(N, device=dev)
+    hq, hd = gq().swiglu_q8_gemv(dWg, dWu, dx, N, K, ws, h=h)
+    h_orc = oracle.swiglu(Wg, Wu, x, N, K)[0]
+    hg = h.cpu().numpy()
+    check_f32(f"swiglu_q8 h {N}x{K}", hg, h_orc)
+    check_q8_codes(f"swiglu_q8 codes {N}x{K}", hq.cpu().numpy(), hd.cpu().numpy(), hg, h_orc)
+    assert int(torch.count_nonzero(ws[: (N // 32) * 4]).item()) == 0      # counters back at zero
+    # without the f32 output the codes are the same
+    hq2, hd2 = gq().swiglu_q8_gemv(dWg, dWu, dx, N, K, ws)
+    assert torch.equal(hq2, hq) and torch.equal(hd2, hd)
+    # bit-identical to the unfused device sequence when swiglu_gemv runs the same tile kernel
+    if kernel_path(gq().KIND_SWIGLU, N, K).startswith("tile"):
+        h3 = gq().swiglu_gemv(dWg, dWu, dx, N, K)
+        q3, d3 = gq().q8_quantize(h3)
+        assert torch.equal(h3, h) and torch.equal(q3, hq) and torch.equal(d3, hd)
+
+
+def test_swiglu_q8_reuse_and_graph(dev):
+    """Back-to-back calls on one workspace with changing inputs, then the
+    same call captured in a HIP graph and replayed: every result matches a
+    fresh eager call."""
+    N, K = 9728, 2560
+    r = synth.rng_for(8200)
+    Wg, Wu = up(synth.q4k_weights(r, N, K), dev), up(synth.q4k_weights(r, N, K), dev)
+    ws = torch.zeros(gq().swiglu_q8_ws_bytes(N), dtype=torch.uint8, device=dev)
+    x = torch.empty(K, device=dev)
+    hq, hd = torch.empty(N, dtype=torch.int8, device=dev), torch.empty(N // 32, dtype=torch.int16, device=dev)
+    ref_ws = torch.zeros_like(ws)
+    for i in range(3):
+        x.copy_(torch.from_numpy(synth.activation(synth.rng_for(8300 + i), K)))
+        gq().swiglu_q8_gemv(Wg, Wu, x, N, K, ws, hq=hq, hd=hd)
+        q_ref, d_ref = gq().swiglu_q8_gemv(Wg, Wu, x, N, K, ref_ws)
+        assert torch.equal(hq, q_ref) and torch.equal(hd, d_ref), i
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        gq().swiglu_q8_gemv(Wg, Wu, x, N, K, ws, hq=hq, hd=hd)
+    for i in range(3):
+        x.copy_(torch.from_numpy(synth.activation(synth.rng_for(8400 + i), K)))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        q_ref, d_ref = gq().swiglu_q8_gemv(Wg, Wu, x, N, K, ref_ws)
+        assert torch.equal(hq, q_ref) and torch.equal(hd, d_ref), i
+        assert int(torch.count_nonzero(ws[: (N // 32) * 4]).item()) == 0
+
+
+@pytest.mark.parametrize("K,eps", [(32, 1e-6), (256, 1e-5), (992, 0.0), (2560, 1e-6), (8192, 1e-5),
+                                   (32768, 1e-6)])
+def test_rms_norm_q8(dev, K, eps):
+    r = synth.rng_for(8500 + K)
+    x = synth.activation_outliers(r, K)
+    w = r.uniform(0.5, 1.5, K).astype(np.float32)
+    y = torch.empty(K, device=dev)
+    xq, xd = gq().rms_norm_q8(up(x, dev), up(w, dev), eps, y=y)
+    _, y_orc, _, _ = oracle.rms_norm_q8(x, w, eps)
+    yg = y.cpu().numpy()
+    check_f32(f"rms_norm {K}", yg, y_orc)
+    check_q8_codes(f"rms_norm_q8 {K}", xq.cpu().numpy(), xd.cpu().numpy(), yg, y_orc)
+    q2, d2 = gq().q8_quantize(y)                     # the unfused encoder on the same values
+    assert torch.equal(q2, xq) and torch.equal(d2, xd)
+
+
+def test_rms_norm_q8_special_inputs(dev):
+    K = 512
+    ones = up(np.ones(K, np.float32), dev)
+    # constant input, eps = 0: y = 1 everywhere, codes 127, scale fp16(1/127)
+    xq, xd = gq().rms_norm_q8(up(np.full(K, 0.75, np.float32), dev), ones, 0.0)
+    _, _, q_o, d_o = oracle.rms_norm_q8(np.full(K, 0.75, np.float32), np.ones(K, np.float32), 0.0)
+    assert np.array_equal(xq.cpu().numpy(), q_o) and np.array_equal(xd.cpu().numpy().view(np.uint16), d_o)
+    # zero input with eps > 0: all codes and scales zero
+    xq, xd = gq().rms_norm_q8(up(np.zeros(K, np.float32), dev), ones, 1e-6)
+    assert int(torch.count_nonzero(xq).item()) == 0 and int(torch.count_nonzero(xd).item()) == 0
+    # a single nonzero element (eps = 0) becomes sqrt(K) * w and code +-127
+    e = np.zeros(K, np.float32)
+    e[100] = -3.0
+    y = torch.empty(K, device=dev)
+    xq, xd = gq().rms_norm_q8(up(e, dev), ones, 0.0, y=y)
+    assert abs(float(y[100].item()) + np.sqrt(K)) <= 1e-5 * np.sqrt(K)
+    assert int(xq[100].item()) == -127 and int(torch.count_nonzero(xq).item()) == 1
+
+
+def test_add_rms_norm_q8(dev):
+    K, eps = 8192, 1e-5
+    r_ = synth.rng_for(8600)
+    x = synth.activation_outliers(r_, K)
+    res_in = synth.activation(r_, K)
+    w = r_.uniform(0.5, 1.5, K).astype(np.float32)
+    dx, dr, dw = up(x, dev), up(res_in, dev), up(w, dev)
+    y = torch.empty(K, device=dev)
+    res, xq, xd = gq().add_rms_norm_q8(dx, dr, dw, eps, y=y)
+    res_o, y_o, _, _ = oracle.rms_norm_q8(x, w, eps, res_in)
+    assert np.array_equal(res.cpu().numpy(), res_o)           # one f32 add per element, exact
+    yg = y.cpu().numpy()
+    check_f32("add_rms_norm y", yg, y_o)
+    check_q8_codes("add_rms_norm_q8", xq.cpu().numpy(), xd.cpu().numpy(), yg, y_o)
+    # in place over x, and over r: the same results
+    for which in ("x", "r"):
+        dx2, dr2 = up(x, dev), up(res_in, dev)
+        tgt = dx2 if which == "x" else dr2
+        res2, xq2, xd2 = gq().add_rms_norm_q8(dx2, dr2, dw, eps, res=tgt)
+        assert res2.data_ptr() == tgt.data_ptr()
+        assert np.array_equal(tgt.cpu().numpy(), res_o), which
+        assert torch.equal(xq2, xq) and torch.equal(xd2, xd), which
