@@ -254,8 +254,8 @@ static int rms_norm_q8_impl(const float *x, const float *r, const float *w, floa
 {
     if (K < 32 || K > gemvq::kMaxNormK || K % 32 != 0) return GEMVQ_ERR_SHAPE;
     if (!(eps >= 0.0f) || eps > 3.0e38f) return GEMVQ_ERR_VALUE;   // rejects NaN, negative and infinite eps
-    if (!aligned(x, 4) || (r && !aligned(r, 4)) || !aligned(w, 4) || (res && !aligned(res, 4)) ||
-        (y && !aligned(y, 4)) || !aligned(xq, 16) || !aligned(xd, 4))
+    if (!aligned(x, 16) || (r && !aligned(r, 16)) || !aligned(w, 16) || (res && !aligned(res, 16)) ||
+        (y && !aligned(y, 16)) || !aligned(xq, 16) || !aligned(xd, 4))
         return GEMVQ_ERR_ALIGN;
     const size_t nv = (size_t)K * 4, nq = (size_t)K, nd = (size_t)(K / 32) * 2;
     const void *ins[3] = {x, r, w};

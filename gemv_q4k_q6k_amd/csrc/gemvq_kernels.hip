@@ -403,20 +403,27 @@ __device__ void argmax_finish(const GemvArgs &a, uint64_t best, int holder, int 
 // clamped to [-127, 127]; the scale is stored as the fp16 of d (round to
 // nearest even).  Every producer of Q8 activations uses this one function,
 // so their codes agree bit for bit on equal inputs.
-__device__ __forceinline__ int8_t q8_encode(float v, uint16_t &dbits)
+__device__ __forceinline__ float q8_scale(float amax) { return amax / 127.0f; }
+__device__ __forceinline__ uint16_t q8_scale_bits(float d) { return __builtin_bit_cast(uint16_t, (_Float16)d); }
+__device__ __forceinline__ int q8_code(float v, float d)
 {
-    float amax = fabsf(v);
-#pragma unroll
-    for (int m = 1; m < 32; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 32));
-    const float d = amax / 127.0f;
     int q = 0;
     if (d != 0.0f) {
         float r = roundf(v / d);
         r = fminf(fmaxf(r, -127.0f), 127.0f);
         q = (int)r;
     }
-    dbits = __builtin_bit_cast(uint16_t, (_Float16)d);
-    return (int8_t)q;
+    return q;
+}
+
+__device__ __forceinline__ int8_t q8_encode(float v, uint16_t &dbits)
+{
+    float amax = fabsf(v);
+#pragma unroll
+    for (int m = 1; m < 32; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 32));
+    const float d = q8_scale(amax);
+    dbits = q8_scale_bits(d);
+    return (int8_t)q8_code(v, d);
 }
 
 // Q8 encoding of the rows a workgroup of the tile kernel computed, [r0, r1)
@@ -1099,17 +1106,19 @@ __global__ __launch_bounds__(256) void q8_quantize_kernel(const float *__restric
 // y = w * x / sqrt(mean(x^2) + eps), then the Q8 encoding of y (memra-engine
 // decode.rs `rms_norm_q8_1`, and `add_rms_norm_q8_1` with ADD: x is first
 // replaced by x + r, which is also written to res as the new residual).  One
-// workgroup of 1024 threads: half-wave h owns blocks h, h + 32, ..., lane l
-// element l of each, so every value stays in the register of the lane that
-// encodes it.  All loads are issued up front (clamped to the last block, so
-// no branch separates them); the sum of squares is added per lane in block
-// order, then by a fixed shuffle tree, then over the 16 waves in order.
-// res may be x or r itself (each element is read, then written, by one lane;
-// those pointers carry no __restrict__ for that reason).
+// workgroup of 1024 threads; in pass p thread t holds the four elements from
+// 4096p + 4t (16-byte loads), so a 32-element Q8 block sits in 8 consecutive
+// lanes and is encoded there (the block maximum by a 3-step xor tree, then
+// the same q8_scale / q8_code as every other producer).  All loads are issued
+// up front, clamped to the vector's last four elements (no branch separates
+// them); PASSES is the power of two >= K/4096.  The sum of squares is added
+// per lane in element order, then by a fixed shuffle tree, then over the 16
+// waves in order.  res may be x or r itself (each element is read, then
+// written, by one lane; those pointers carry no __restrict__ for that reason).
 constexpr int kNormThreads = 1024;
-constexpr int kNormPer = 32;   // blocks per half-wave: K <= 32 * 32 * 32
+constexpr int kNormSpan = 4 * kNormThreads;   // elements per pass
 
-template <bool ADD>
+template <bool ADD, int PASSES>
 __global__ __launch_bounds__(kNormThreads) void rms_norm_q8_kernel(const float *x, const float *r,
                                                                   const float *__restrict__ w, float eps,
                                                                   float *res, float *__restrict__ y,
@@ -1117,22 +1126,26 @@ __global__ __launch_bounds__(kNormThreads) void rms_norm_q8_kernel(const float *
                                                                   int K)
 {
     __shared__ float s_part[kNormThreads / 64];
-    const int tid = threadIdx.x, hw = tid >> 5, l = tid & 31;
-    const int blocks = K >> 5;
-    float v[kNormPer], wv[kNormPer];
+    const int tid = threadIdx.x;
+    float4 v[PASSES], wv[PASSES];
 #pragma unroll
-    for (int i = 0; i < kNormPer; ++i) {
-        const int j = hw + 32 * i;
-        const int e = 32 * (j < blocks ? j : blocks - 1) + l;
-        v[i] = x[e];
-        if constexpr (ADD) v[i] = v[i] + r[e];
-        wv[i] = w[e];
+    for (int p = 0; p < PASSES; ++p) {
+        const int e = kNormSpan * p + 4 * tid;
+        const int ec = e < K ? e : K - 4;
+        v[p] = *(const float4 *)(x + ec);
+        if constexpr (ADD) {
+            const float4 t = *(const float4 *)(r + ec);
+            v[p] = make_float4(v[p].x + t.x, v[p].y + t.y, v[p].z + t.z, v[p].w + t.w);
+        }
+        wv[p] = *(const float4 *)(w + ec);
     }
     float ss = 0.f;
 #pragma unroll
-    for (int i = 0; i < kNormPer; ++i) {
-        const bool on = hw + 32 * i < blocks;
-        ss += on ? v[i] * v[i] : 0.f;
+    for (int p = 0; p < PASSES; ++p) {
+        const bool on = kNormSpan * p + 4 * tid < K;
+        const float4 a = v[p];
+        const float q = (((a.x * a.x) + (a.y * a.y)) + (a.z * a.z)) + (a.w * a.w);
+        ss += on ? q : 0.f;
     }
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) ss += __shfl_xor(ss, off);
@@ -1143,16 +1156,22 @@ __global__ __launch_bounds__(kNormThreads) void rms_norm_q8_kernel(const float *
     for (int i = 0; i < kNormThreads / 64; ++i) tot += s_part[i];
     const float inv = 1.0f / sqrtf(tot / (float)K + eps);
 #pragma unroll
-    for (int i = 0; i < kNormPer; ++i) {
-        const int j = hw + 32 * i;
-        if (j < blocks) {   // half-wave-uniform
-            const int e = 32 * j + l;
-            if constexpr (ADD) res[e] = v[i];
-            const float yv = (v[i] * inv) * wv[i];
-            if (y) y[e] = yv;
-            uint16_t dbits;
-            xq[e] = q8_encode(yv, dbits);
-            if (l == 0) xd[j] = dbits;
+    for (int p = 0; p < PASSES; ++p) {
+        const int e = kNormSpan * p + 4 * tid;
+        if (e < K) {   // uniform over each 8-lane block group (K % 32 == 0)
+            if constexpr (ADD) *(float4 *)(res + e) = v[p];
+            const float4 a = v[p], b = wv[p];
+            const float4 yv = make_float4((a.x * inv) * b.x, (a.y * inv) * b.y, (a.z * inv) * b.z, (a.w * inv) * b.w);
+            if (y) *(float4 *)(y + e) = yv;
+            float amax = fmaxf(fmaxf(fabsf(yv.x), fabsf(yv.y)), fmaxf(fabsf(yv.z), fabsf(yv.w)));
+#pragma unroll
+            for (int m = 1; m < 8; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 8));
+            const float d = q8_scale(amax);
+            const uint32_t packed = (uint32_t)(uint8_t)q8_code(yv.x, d) | ((uint32_t)(uint8_t)q8_code(yv.y, d) << 8) |
+                                    ((uint32_t)(uint8_t)q8_code(yv.z, d) << 16) |
+                                    ((uint32_t)(uint8_t)q8_code(yv.w, d) << 24);
+            *(uint32_t *)(xq + e) = packed;
+            if ((tid & 7) == 0) xd[e >> 5] = q8_scale_bits(d);
         }
     }
 }
@@ -1630,15 +1649,29 @@ hipError_t launch_q6k_q8_isums(const void *W, const int8_t *xq, int32_t *isums, 
 
 namespace gemvq {
 
+template <bool ADD>
+static void launch_norm(const float *x, const float *r, const float *w, float eps, float *res, float *y, int8_t *xq,
+                        uint16_t *xd, int K, hipStream_t s)
+{
+    const int passes = (K + kNormSpan - 1) / kNormSpan;
+    const dim3 g(1), b(kNormThreads);
+    if (passes <= 1)
+        hipLaunchKernelGGL((rms_norm_q8_kernel<ADD, 1>), g, b, 0, s, x, r, w, eps, res, y, xq, xd, K);
+    else if (passes <= 2)
+        hipLaunchKernelGGL((rms_norm_q8_kernel<ADD, 2>), g, b, 0, s, x, r, w, eps, res, y, xq, xd, K);
+    else if (passes <= 4)
+        hipLaunchKernelGGL((rms_norm_q8_kernel<ADD, 4>), g, b, 0, s, x, r, w, eps, res, y, xq, xd, K);
+    else
+        hipLaunchKernelGGL((rms_norm_q8_kernel<ADD, 8>), g, b, 0, s, x, r, w, eps, res, y, xq, xd, K);
+}
+
 hipError_t launch_rms_norm_q8(const float *x, const float *r, const float *w, float eps, float *res, float *y,
                               int8_t *xq, uint16_t *xd, int64_t K, hipStream_t s)
 {
     if (r)
-        hipLaunchKernelGGL(rms_norm_q8_kernel<true>, dim3(1), dim3(kNormThreads), 0, s, x, r, w, eps, res, y, xq, xd,
-                           (int)K);
+        launch_norm<true>(x, r, w, eps, res, y, xq, xd, (int)K, s);
     else
-        hipLaunchKernelGGL(rms_norm_q8_kernel<false>, dim3(1), dim3(kNormThreads), 0, s, x, r, w, eps, res, y, xq, xd,
-                           (int)K);
+        launch_norm<false>(x, r, w, eps, res, y, xq, xd, (int)K, s);
     return hipGetLastError();
 }
 

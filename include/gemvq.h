@@ -168,6 +168,7 @@ size_t gemvq_swiglu_q8_ws_bytes(int64_t N);
  *   x, w: float[K], K % 32 == 0, 32 <= K <= 32768.  eps >= 0 and finite.
  *   y: float[K] or NULL (the f32 norm is also written when given).
  *   xq: int8[K], xd: uint16[K/32].
+ *   Alignment: every float vector (x, w, y, and r, res below) 16 bytes.
  * Runs as one workgroup (a latency-bound vector op).
  */
 int rms_norm_q8(const float *x, const float *w, float eps, float *y, int8_t *xq, uint16_t *xd, int64_t K,

@@ -208,6 +208,7 @@ def test_swiglu_q8_rejections():
     _rejected(call(hd=D + 4096 + 2), gq.ERR_ALIGN)
     _rejected(call(ws=E + 128), gq.ERR_ALIGN)              # workspace 256 B
     _rejected(call(h=C + (1 << 20) + 2), gq.ERR_ALIGN)
+    _rejected(call(x=C + 4), gq.ERR_ALIGN)
     _rejected(call(hq=A + 64), gq.ERR_ALIAS)               # hq inside Wg
     _rejected(call(hd=D + 16), gq.ERR_ALIAS)               # hd inside hq
     _rejected(call(h=E + 256), gq.ERR_ALIAS)               # h inside the workspace
@@ -226,14 +227,18 @@ def test_rms_norm_q8_rejections():
     for bad_eps in (-1e-6, float("nan"), float("inf")):
         _rejected(L.rms_norm_q8(A, B, bad_eps, None, D, D + 4096, K, None), gq.ERR_VALUE)
     _rejected(L.rms_norm_q8(A + 2, B, 1e-5, None, D, D + 4096, K, None), gq.ERR_ALIGN)
+    _rejected(L.rms_norm_q8(A, B + 4, 1e-5, None, D, D + 4096, K, None), gq.ERR_ALIGN)       # w needs 16 B
+    _rejected(L.rms_norm_q8(A, B, 1e-5, E + 8, D, D + 4096, K, None), gq.ERR_ALIGN)          # y needs 16 B
+    _rejected(L.add_rms_norm_q8(A, C + 4, B, 1e-5, E, None, D, D + 4096, K, None), gq.ERR_ALIGN)  # r
+    _rejected(L.add_rms_norm_q8(A, C, B, 1e-5, E + 4, None, D, D + 4096, K, None), gq.ERR_ALIGN)  # res
     _rejected(L.rms_norm_q8(A, B, 1e-5, None, D + 4, D + 4096, K, None), gq.ERR_ALIGN)   # xq needs 16 B
     _rejected(L.rms_norm_q8(A, B, 1e-5, None, D, D + 4098, K, None), gq.ERR_ALIGN)
     _rejected(L.rms_norm_q8(A, B, 1e-5, A + 64, D, D + 4096, K, None), gq.ERR_ALIAS)     # y over x
     _rejected(L.rms_norm_q8(A, B, 1e-5, None, B + 16, D + 4096, K, None), gq.ERR_ALIAS)  # xq over w
     _rejected(L.rms_norm_q8(A, B, 1e-5, D + 64, D, D + 4096, K, None), gq.ERR_ALIAS)     # y over xq
     # the residual output may be x or r itself, but not a shifted copy of either
-    _rejected(L.add_rms_norm_q8(A, C, B, 1e-5, A + 4, None, D, D + 4096, K, None), gq.ERR_ALIAS)
-    _rejected(L.add_rms_norm_q8(A, C, B, 1e-5, C - 4, None, D, D + 4096, K, None), gq.ERR_ALIAS)
+    _rejected(L.add_rms_norm_q8(A, C, B, 1e-5, A + 16, None, D, D + 4096, K, None), gq.ERR_ALIAS)
+    _rejected(L.add_rms_norm_q8(A, C, B, 1e-5, C - 16, None, D, D + 4096, K, None), gq.ERR_ALIAS)
     _rejected(L.add_rms_norm_q8(A, C, B, 1e-5, B, None, D, D + 4096, K, None), gq.ERR_ALIAS)   # res over w
     # in place is allowed past the alias checks: make the call fail on alignment instead
     _rejected(L.add_rms_norm_q8(A, C, B, 1e-5, A, None, D + 4, D + 4096, K, None), gq.ERR_ALIGN)
