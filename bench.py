@@ -327,6 +327,51 @@ def breakdown(gq, sets, v, reps=24):
             gq.q4k_gemv(m, xq, n, K, y=y)
     timeit("q4k_gemv_x3_separate_4096+1024+1024x2560", three, sets_, nbytes)
     del sets_, mats
+    # producer-side Q8 emission on the SwiGLU FFN of the 4B-class layer: the
+    # int8 down projection, the SwiGLU that emits Q8 itself, and the whole FFN
+    # (gate/up + down) on the f32 path, the unfused int8 path and the fused one
+    N, K = synth.C4_SWIGLU
+    hq = torch.empty(N, dtype=torch.int8, device=dev)
+    hd = torch.empty(N // 32, dtype=torch.int16, device=dev)
+    wsq = torch.zeros(gq.swiglu_q8_ws_bytes(N), dtype=torch.uint8, device=dev)
+    gq.swiglu_gemv(s0["c4Wg"], s0["c4Wu"], v["c4x"], N, K, h=v["h"])
+    gq.q8_quantize(v["h"], xq=hq, xd=hd)
+    ffn = list(zip(copies(s0["c4Wg"]), copies(s0["c4Wu"]), copies(s0["c4Wd"])))
+    gu_bytes = 2 * N * K // 256 * 144
+    d_bytes = K * N // 256 * 210
+    timeit("q6k_q8_gemv_2560x9728", lambda w: gq.q6k_q8_gemv(w[2], hq, hd, K, N, y=v["yd"]), ffn,
+           d_bytes + N + N // 16 + 4 * K)
+    timeit("swiglu_q8_gemv_9728x2560", lambda w: gq.swiglu_q8_gemv(w[0], w[1], v["c4x"], N, K, wsq, hq=hq, hd=hd),
+           ffn, gu_bytes + 4 * K + N + N // 16)
+
+    def ffn_f32(w):
+        gq.swiglu_gemv(w[0], w[1], v["c4x"], N, K, h=v["h"])
+        gq.q6k_gemv(w[2], v["h"], K, N, y=v["yd"])
+
+    def ffn_q8_unfused(w):
+        gq.swiglu_gemv(w[0], w[1], v["c4x"], N, K, h=v["h"])
+        gq.q8_quantize(v["h"], xq=hq, xd=hd)
+        gq.q6k_q8_gemv(w[2], hq, hd, K, N, y=v["yd"])
+
+    def ffn_q8_fused(w):
+        gq.swiglu_q8_gemv(w[0], w[1], v["c4x"], N, K, wsq, hq=hq, hd=hd)
+        gq.q6k_q8_gemv(w[2], hq, hd, K, N, y=v["yd"])
+    for name, fn in (("ffn_f32_swiglu+q6k", ffn_f32), ("ffn_q8_swiglu+quantize+q6k_q8", ffn_q8_unfused),
+                     ("ffn_q8_swiglu_q8+q6k_q8", ffn_q8_fused)):
+        timeit(name, fn, ffn, gu_bytes + d_bytes)
+    del ffn
+    # norm producers at the 70B-class hidden size (K = 8192)
+    K = synth.C5_Q8[1]
+    r = synth.rng_for(78)
+    z = torch.from_numpy(synth.activation(r, K)).to(dev)
+    z2 = torch.from_numpy(synth.activation(r, K)).to(dev)
+    wn = torch.from_numpy(r.uniform(0.5, 1.5, K).astype(np.float32)).to(dev)
+    res = torch.empty(K, dtype=torch.float32, device=dev)
+    timeit("rms_norm_q8_8192", lambda w: gq.rms_norm_q8(z, wn, 1e-5, xq=v["xq"], xd=v["xd"]), [()],
+           2 * 4 * K + K + K // 16)
+    timeit("add_rms_norm_q8_8192",
+           lambda w: gq.add_rms_norm_q8(z, z2, wn, 1e-5, res=res, xq=v["xq"], xd=v["xd"]), [()],
+           4 * 4 * K + K + K // 16)
     torch.cuda.empty_cache()
     return out
 
