@@ -220,6 +220,18 @@ def q6k_q8_gemv(W, xq, xd, N: int, K: int) -> np.ndarray:
     return y
 
 
+def q8_gemv_batch(fmt: str, W, xq, xd, N: int, K: int, m: int) -> np.ndarray:
+    """Batched int8-activation GEMV (memra-engine decode.rs, the lockstep
+    multi-stream decode and `full_attn_decode_batched`: one weight read
+    serves m activation vectors): Y[j] = W * xdq_j for j < m, each row of Y
+    the single-vector GEMV of that vector.  xq: int8[m, K], xd: fp16 bits
+    [m, K/32], fmt "q4k" or "q6k".  Returns f64 [m, N]."""
+    gemv = {"q4k": q4k_q8_gemv, "q6k": q6k_q8_gemv}[fmt]
+    xq = np.asarray(xq, np.int8).reshape(m, K)
+    xd = np.asarray(xd, np.uint16).reshape(m, K // 32)
+    return np.stack([gemv(W, xq[j], xd[j], N, K) for j in range(m)])
+
+
 # ------------------------------------------------ norms and Q8 emission
 # memra-engine decode.rs names the producers that emit a quantized activation
 # directly: `rms_norm_q8_1` (norm, then quantize), `add_rms_norm_q8_1`

@@ -536,3 +536,29 @@ def test_swiglu_q8_properties():
     assert np.all(np.abs(q.astype(np.int64)).reshape(-1, 32).max(axis=1) == 127)
     # rows 3 and 40 are equal by construction and sit in different blocks
     assert h[3] == h[40]
+
+
+# ------------------------------------------------------------------ batched Q8 GEMV
+@pytest.mark.parametrize("fmt", ["q4k", "q6k"])
+def test_q8_gemv_batch_vs_numpy(fmt):
+    """Y = W Xdq^T for m activation vectors at once, against numpy matmul
+    over the independently decoded matrix (catches a transposed operand or a
+    vector paired with the wrong scales)."""
+    rng = np.random.default_rng(31)
+    N, K, m = 6, 768, 5
+    if fmt == "q4k":
+        W, Wf = q4k_matrix_from_fields(random_q4k_fields(rng, N * K // 256), N, K)
+    else:
+        W, Wf = q6k_matrix_from_fields(random_q6k_fields(rng, N * K // 256), N, K)
+    X = (rng.standard_normal((m, K)) * rng.uniform(0.1, 10, (m, 1))).astype(np.float32)
+    qs, ds = zip(*[oracle.q8_quantize(X[j]) for j in range(m)])
+    xq, xd = np.stack(qs), np.stack(ds)
+    Y = oracle.q8_gemv_batch(fmt, W, xq, xd, N, K, m)
+    assert Y.shape == (m, N)
+    Xdq = np.repeat(xd.view(np.float16).astype(np.float64), 32, axis=1) * xq
+    assert np.allclose(Y, (Wf @ Xdq.T).T, rtol=1e-13, atol=1e-12)
+    # m = 1 is the single GEMV; reordering the vectors reorders the outputs
+    single = {"q4k": oracle.q4k_q8_gemv, "q6k": oracle.q6k_q8_gemv}[fmt]
+    assert np.array_equal(oracle.q8_gemv_batch(fmt, W, xq[:1], xd[:1], N, K, 1)[0], single(W, xq[0], xd[0], N, K))
+    perm = [3, 0, 4, 1, 2]
+    assert np.array_equal(oracle.q8_gemv_batch(fmt, W, xq[perm], xd[perm], N, K, m), Y[perm])
