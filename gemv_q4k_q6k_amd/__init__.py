@@ -21,7 +21,7 @@ __all__ = [
     "GemvqError", "lib", "exported_names", "header_names",
     "q4k_gemv", "q4k_gemv_multi", "q6k_gemv", "q8_quantize", "q4k_q8_gemv", "swiglu_gemv",
     "lm_head_argmax", "lm_head_argmax_timed", "lm_head_argmax_masked", "lm_head_argmax_ws_bytes", "q4k_q8_isums", "strerror", "tile_geometry",
-    "q6k_q8_gemv", "q6k_q8_isums", "swiglu_q8_gemv", "swiglu_q8_ws_bytes", "rms_norm_q8", "add_rms_norm_q8",
+    "q6k_q8_gemv", "q6k_q8_isums", "swiglu_q8_gemv", "swiglu_q8_ws_bytes", "rms_norm_q8", "q4k_q8_gemv_batch", "q6k_q8_gemv_batch", "add_rms_norm_q8",
     "Q4K_BLOCK_BYTES", "Q6K_BLOCK_BYTES", "LIB_PATH", "HEADER_PATH",
 ]
 
@@ -54,6 +54,8 @@ _SIGS = {
     "q4k_q8_gemv": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _P]),
     "swiglu_gemv": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _P]),
     "q6k_q8_gemv": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _P]),
+    "q4k_q8_gemv_batch": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, ctypes.c_int, _P]),
+    "q6k_q8_gemv_batch": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, ctypes.c_int, _P]),
     "gemvq_q6k_q8_isums": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P]),
     "swiglu_q8_gemv": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _I64, _I64, _P]),
     "gemvq_swiglu_q8_ws_bytes": (ctypes.c_size_t, [_I64]),
@@ -98,7 +100,8 @@ def exported_names() -> list[str]:
     return sorted(_SIGS)
 
 
-KIND_Q4K, KIND_Q6K, KIND_Q4K_Q8, KIND_SWIGLU, KIND_Q6K_Q8, KIND_SWIGLU_Q8 = range(6)
+(KIND_Q4K, KIND_Q6K, KIND_Q4K_Q8, KIND_SWIGLU, KIND_Q6K_Q8, KIND_SWIGLU_Q8, KIND_Q4K_Q8_BATCH,
+ KIND_Q6K_Q8_BATCH) = range(8)
 
 
 def tile_geometry(kind: int, N: int, K: int) -> dict:
@@ -244,6 +247,28 @@ def q6k_q8_gemv(W, xq, xd, N: int, K: int, y=None, stream=None):
     _check("q6k_q8_gemv", lib().q6k_q8_gemv(W.data_ptr(), xq.data_ptr(), xd.data_ptr(), y.data_ptr(), N, K,
                                             _stream(xq, stream)))
     return y
+
+
+def q4k_q8_gemv_batch(W, xq, xd, N: int, K: int, m: int, y=None, stream=None):
+    """Y[j] = W xdq_j for m Q8 vectors (xq int8[m*K], xd int16[m*K/32], back
+    to back) through one Q4_K matrix; returns float32 [m, N]."""
+    return _batch("q4k_q8_gemv_batch", Q4K_BLOCK_BYTES, W, xq, xd, N, K, m, y, stream)
+
+
+def q6k_q8_gemv_batch(W, xq, xd, N: int, K: int, m: int, y=None, stream=None):
+    """As q4k_q8_gemv_batch for a Q6_K matrix."""
+    return _batch("q6k_q8_gemv_batch", Q6K_BLOCK_BYTES, W, xq, xd, N, K, m, y, stream)
+
+
+def _batch(name, block, W, xq, xd, N, K, m, y, stream):
+    torch = _torch()
+    _weights(W, N, K, block)
+    _dev_tensor(xq, torch.int8, m * K, "xq")
+    _dev_tensor(xd, torch.int16, m * (K // 32), "xd")
+    y = _out(y, xq.device, torch.float32, m * N, "y")
+    _check(name, getattr(lib(), name)(W.data_ptr(), xq.data_ptr(), xd.data_ptr(), y.data_ptr(), N, K, m,
+                                      _stream(xq, stream)))
+    return y.view(m, N)
 
 
 def swiglu_gemv(Wg, Wu, x, N: int, K: int, h=None, stream=None):

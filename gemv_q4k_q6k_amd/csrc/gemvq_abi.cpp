@@ -90,11 +90,14 @@ size_t gemvq_lm_head_argmax_ws_bytes(int64_t N, int64_t K)
 int gemvq_tile_geometry(int kind, int64_t N, int64_t K, int64_t out[7])
 {
     if (!out) return GEMVQ_ERR_NULL;
-    if (kind < 0 || kind > 5) return GEMVQ_ERR_SHAPE;
+    if (kind < 0 || kind > 7) return GEMVQ_ERR_SHAPE;
     size_t wb = 0;
-    if (int st = check_shape(N, K, (kind == 1 || kind == 4) ? 210 : 144, &wb)) return st;
+    if (int st = check_shape(N, K, (kind == 1 || kind == 4 || kind == 7) ? 210 : 144, &wb)) return st;
     if (kind == 5 && N % 32 != 0) return GEMVQ_ERR_SHAPE;
-    const gemvq::Plan pl = kind == 5 ? gemvq::make_swiglu_q8_plan(N, K) : gemvq::make_plan(N, K, kind);
+    const gemvq::Plan pl = kind == 5   ? gemvq::make_swiglu_q8_plan(N, K)
+                           : kind >= 6 ? gemvq::make_batch_plan(N, K, kind == 6 ? 2 : 4,
+                                                                gemvq::batch_slots(gemvq::kMaxBatch, kind == 7), nullptr)
+                                       : gemvq::make_plan(N, K, kind);
     out[0] = pl.waves;
     out[1] = pl.rows_tile;
     out[2] = pl.tiles;
@@ -200,6 +203,33 @@ int q6k_q8_gemv(const void *W, const int8_t *xq, const uint16_t *xd, float *y, i
     int cus = 0;
     if (int st = device_cus(&cus)) return st;
     return status_of(gemvq::launch_q6k_q8_gemv(W, xq, xd, y, N, K, cus, (hipStream_t)stream));
+}
+
+static int q8_gemv_batch_impl(bool q6k, const void *W, const int8_t *xq, const uint16_t *xd, float *y, int64_t N,
+                              int64_t K, int m, void *stream)
+{
+    if (!W || !xq || !xd || !y) return GEMVQ_ERR_NULL;
+    size_t wb = 0;
+    if (int st = check_shape(N, K, q6k ? 210 : 144, &wb)) return st;
+    if (m < 1 || m > gemvq::kMaxBatch || N * m > kMaxN) return GEMVQ_ERR_SHAPE;
+    if (!aligned(W, q6k ? 4 : 16) || !aligned(xq, 16) || !aligned(xd, 4) || !aligned(y, 4)) return GEMVQ_ERR_ALIGN;
+    const size_t ny = (size_t)N * m * 4, nq = (size_t)K * m, nd = (size_t)(K / 32) * 2 * m;
+    if (overlap(y, ny, W, wb) || overlap(y, ny, xq, nq) || overlap(y, ny, xd, nd)) return GEMVQ_ERR_ALIAS;
+    int cus = 0;
+    if (int st = device_cus(&cus)) return st;
+    return status_of(gemvq::launch_q8_gemv_batch(q6k, W, xq, xd, y, N, K, m, cus, (hipStream_t)stream));
+}
+
+int q4k_q8_gemv_batch(const void *W, const int8_t *xq, const uint16_t *xd, float *y, int64_t N, int64_t K, int m,
+                      void *stream)
+{
+    return q8_gemv_batch_impl(false, W, xq, xd, y, N, K, m, stream);
+}
+
+int q6k_q8_gemv_batch(const void *W, const int8_t *xq, const uint16_t *xd, float *y, int64_t N, int64_t K, int m,
+                      void *stream)
+{
+    return q8_gemv_batch_impl(true, W, xq, xd, y, N, K, m, stream);
 }
 
 int swiglu_gemv(const void *Wg, const void *Wu, const float *x, float *h, int64_t N, int64_t K, void *stream)

@@ -374,13 +374,25 @@ __device__ __forceinline__ float q6k_dot(const Q6KRaw &r, const Q6KX &x, int u)
 // ------------------------------------------------------------ Q6_K x Q8
 
 // Q8 activation slice of a Q6_K part u: group s holds the 16 int8 values
-// x[128n + 32s + l0 + i] in four dwords, the scale of the 32-element Q8 block
-// they lie in (block 4n + s of the super-block) as f32, and their integer sum.
+// x[128n + 32s + l0 + i] in four dwords; the fp16 scales of the 32-element Q8
+// blocks the groups lie in (block 4n + s of the super-block) and the groups'
+// integer sums (|sum| <= 16 * 127) are kept two to a dword, so a slice takes
+// 20 registers (the batched kernel holds up to eight).
 struct Q6Q8X {
     uint32_t q[4][4];
-    float d[4];
-    int32_t sx[4];
+    uint32_t d2[2];    // fp16 scale of group s in half s & 1 of d2[s >> 1]
+    uint32_t sx2[2];   // int16 sum of group s in half s & 1 of sx2[s >> 1]
 };
+
+__device__ __forceinline__ float q6q8_scale(const Q6Q8X &x, int s)
+{
+    return (s & 1) ? half_hi(x.d2[s >> 1]) : half_lo(x.d2[s >> 1]);
+}
+
+__device__ __forceinline__ int32_t q6q8_sum(const Q6Q8X &x, int s)
+{
+    return __builtin_amdgcn_sbfe((int)x.sx2[s >> 1], (uint32_t)(16 * (s & 1)), 16);
+}
 
 // Exact integer sums of one part: is[s] = sum_i (q6 - 32) * q8 over group s.
 // The 6-bit quants (0..63) are valid signed bytes, so v_dot4_i32_i8 takes
@@ -396,7 +408,7 @@ __device__ __forceinline__ void q6k_q8_isums(const Q6KRaw &r, const Q6Q8X &x, in
         for (int s = 0; s < 4; ++s) acc[s] = __builtin_amdgcn_sdot4((int)q[s], (int)x.q[s][k], acc[s], false);
     }
 #pragma unroll
-    for (int s = 0; s < 4; ++s) is[s] = acc[s] - 32 * x.sx[s];
+    for (int s = 0; s < 4; ++s) is[s] = acc[s] - 32 * q6q8_sum(x, s);
 }
 
 // |sc * isum| <= 128 * 16 * 32 * 127 < 2^24, so each group term is exact in
@@ -408,10 +420,10 @@ __device__ __forceinline__ float q6k_q8_dot(const Q6KRaw &r, const Q6Q8X &x, int
     int sc[4];
     q6k_scales(r, u, sc);
     const float d = half_lo(r.dbits);
-    const float t0 = (float)(sc[0] * is[0]) * x.d[0];
-    const float t1 = (float)(sc[1] * is[1]) * x.d[1];
-    const float t2 = (float)(sc[2] * is[2]) * x.d[2];
-    const float t3 = (float)(sc[3] * is[3]) * x.d[3];
+    const float t0 = (float)(sc[0] * is[0]) * q6q8_scale(x, 0);
+    const float t1 = (float)(sc[1] * is[1]) * q6q8_scale(x, 1);
+    const float t2 = (float)(sc[2] * is[2]) * q6q8_scale(x, 2);
+    const float t3 = (float)(sc[3] * is[3]) * q6q8_scale(x, 3);
     return d * ((t0 + t1) + (t2 + t3));
 }
 

@@ -65,6 +65,10 @@ struct GemvArgs {
     uint16_t *hd;
     uint32_t emit_vals_off;
     uint32_t emit_lds_off;
+    // batched GEMV (gemv_batch_kernel): vectors, and how many are staged in
+    // LDS per round
+    int batch;
+    int batch_round;
 };
 
 // ------------------------------------------------------- activation setup
@@ -222,21 +226,32 @@ __device__ __forceinline__ void load_x(Q6Q8X &xs, const int8_t *qsrc, const uint
         const uint32_t *p = (const uint32_t *)(qsrc + (PADDED ? lds_pad(os) : os));
 #pragma unroll
         for (int k = 0; k < 4; ++k) xs.q[s][k] = p[k];
-        xs.d[s] = dsrc ? (float)__builtin_bit_cast(_Float16, dsrc[8 * b + 4 * n + s]) : 0.f;
+    }
+    // the group scales are those of Q8 blocks 8b + 4n .. 8b + 4n + 3
+    xs.d2[0] = xs.d2[1] = 0u;
+    if (dsrc) {
+        const uint16_t *dp = dsrc + 8 * b + 4 * n;
+        xs.d2[0] = (uint32_t)dp[0] | ((uint32_t)dp[1] << 16);
+        xs.d2[1] = (uint32_t)dp[2] | ((uint32_t)dp[3] << 16);
     }
 }
 
-// Integer sums of the slice's four 16-element groups.
+// Integer sums of the slice's four 16-element groups, two to a dword.
 __device__ __forceinline__ void finish_x(Q6Q8X &xs)
 {
+    int32_t t[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-        int32_t t = 0;
+        t[s] = 0;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) t = __builtin_amdgcn_sdot4((int)xs.q[s][k], 0x01010101, t, false);
-        pin(t);
-        xs.sx[s] = t;
+        for (int k = 0; k < 4; ++k) t[s] = __builtin_amdgcn_sdot4((int)xs.q[s][k], 0x01010101, t[s], false);
     }
+    int32_t a = (int32_t)(((uint32_t)t[0] & 0xFFFFu) | ((uint32_t)t[1] << 16));
+    int32_t c = (int32_t)(((uint32_t)t[2] & 0xFFFFu) | ((uint32_t)t[3] << 16));
+    pin(a);
+    pin(c);
+    xs.sx2[0] = (uint32_t)a;
+    xs.sx2[1] = (uint32_t)c;
 }
 
 // ------------------------------------------------------- per-kind traits
@@ -652,10 +667,11 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_kernel(GemvArgs a)
     for (int t = t_begin; t < t_end; t += kPhase) {
 #pragma unroll
         for (int d = 0; d < kPhase; ++d) {
-            if (t + d < t_end) {   // workgroup-uniform
-                process(ring[d], t + d);
-                fetch(ring[d], t + d + kPhase);
-            }
+            if (t + d < t_end) process(ring[d], t + d);   // workgroup-uniform
+            // unconditional, so every iteration issues the same loads and the
+            // compiler's wait for a slot counts only the loads issued after
+            // it (a guarded fetch makes it drain every load at the loop head)
+            fetch(ring[d], t + d + kPhase);
         }
     }
 
@@ -1084,6 +1100,134 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_rows_kernel(Gem
     }
 }
 
+// ------------------------------------------------------ batched kernel
+
+// Batched int8-activation GEMV: y[j][n] = sum_k W[n,k] * xdq_j[k] for the
+// a.batch <= M vectors j (memra-engine decode.rs, lockstep multi-stream
+// decode: one weight read serves m streams).  The tile kernel's geometry and
+// row reduction, with M outputs per row: each lane dequantizes its quarter
+// super-block once and dots it against the M activation slices it keeps in
+// registers, so the weight stream is read once for all vectors.  The
+// vectors are staged through LDS a.batch_round at a time (at most ~60 KiB
+// per round) and each lane copies its slices into registers; slots past
+// a.batch repeat the last vector and are never stored.  A row's value for
+// vector j is summed exactly as the tile kernel sums it (quad sums, then the
+// K/256 block sums in column order), whatever M, the batch or the row's
+// position: results do not depend on the other vectors.
+template <int KIND, int M, int PHASE>
+__global__ __launch_bounds__(kMaxThreads) void gemv_batch_kernel(GemvArgs a)
+{
+    static_assert(is_q8(KIND), "batched GEMV takes Q8 activations");
+    constexpr int kPhase = PHASE;
+    extern __shared__ __align__(16) unsigned char smem[];
+    constexpr int BYTES = Traits<KIND>::kBytes;
+    const int tid = threadIdx.x;
+    const int p = (int)__umulhi((uint32_t)tid, a.lanes_row_magic);   // row within the tile
+    const int rr = tid - p * a.lanes_row;
+    const int b = rr >> 2;
+    const int part = rr & 3;
+    const bool lane_on = p < a.rows_tile;
+    const int K = a.nb * kQK;
+    const int P = a.rows_tile;
+
+    const int bid = blockIdx.x;
+    const int t_begin = bid * a.tiles_q + (bid < a.tiles_r ? bid : a.tiles_r);
+    const int t_end = t_begin + a.tiles_q + (bid < a.tiles_r ? 1 : 0);
+    const int last_rows = (int)(a.N - (a.tiles - 1) * P);
+    const int64_t tile_stride = (int64_t)P * a.nb * BYTES;
+    const uint32_t lane_off = (uint32_t)((p * a.nb + b) * BYTES);
+    auto valid_tile = [&](int t) { return lane_on && t < t_end && (t < a.tiles - 1 || p < last_rows); };
+    // unconditional loads, as in gemv_kernel
+    auto fetch = [&](RawSet<KIND> &rs, int t) {
+        const int tt = t < t_end ? t : t_end - 1;
+        const uint32_t off = valid_tile(t) ? lane_off : 0u;
+        const int64_t tb = (int64_t)tt * tile_stride;
+        if constexpr (is_q6(KIND))
+            q6k_load(rs.r[0], a.W + tb, off, part);
+        else
+            q4k_load(rs.r[0], a.W + tb, off, part);
+    };
+
+    RawSet<KIND> ring[kPhase];
+#pragma unroll
+    for (int d = 0; d < kPhase; ++d) fetch(ring[d], t_begin + d);
+
+    // activation slices, staged a.batch_round vectors at a time; a vector
+    // occupies K + K/16 bytes of LDS (lds_pad layout)
+    XSlice<KIND> xs[M];
+    const int xb = lane_on ? b : 0;
+    const int vbytes = K + K / 16;
+    for (int j0 = 0; j0 < M; j0 += a.batch_round) {   // workgroup-uniform
+        const int nv = M - j0 < a.batch_round ? M - j0 : a.batch_round;
+        for (int i = tid * 16; i < nv * K; i += (int)blockDim.x * 16) {
+            const int jj = i / K, kk = i - jj * K;
+            const int jv = j0 + jj < a.batch ? j0 + jj : a.batch - 1;
+            *(u32x4 *)(smem + jj * vbytes + lds_pad((uint32_t)kk)) = *(const u32x4 *)(a.xq + (size_t)jv * K + kk);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < M; ++j) {
+            if (j >= j0 && j < j0 + nv) {
+                const int jv = j < a.batch ? j : a.batch - 1;
+                load_x<true>(xs[j].v, (const int8_t *)(smem + (j - j0) * vbytes), a.xd + (size_t)jv * (K / 32), xb,
+                             part);
+                finish_x(xs[j].v);
+            }
+        }
+        __syncthreads();   // LDS is rewritten by the next round (or reused below)
+    }
+
+    float *red = (float *)smem;   // [2][M][rows_tile][nb]
+    const int red_stride = M * P * a.nb;
+    int buf = 0;
+    auto process = [&](const RawSet<KIND> &rs, int t) {
+        float ps[M];
+        const bool v = valid_tile(t);
+#pragma unroll
+        for (int j = 0; j < M; ++j) {
+            float q[2];
+            dot_raw<KIND>(rs, xs[j], part, q);
+            ps[j] = v ? q[0] : 0.f;
+        }
+        float *rb = red + buf * red_stride;
+#pragma unroll
+        for (int j = 0; j < M; ++j) {
+            const float q = quad_sum(ps[j]);
+            if (part == 0 && lane_on) rb[(j * P + p) * a.nb + b] = q;
+        }
+        __syncthreads();
+        // P * M <= 2 * blockDim.x (a row has at least 4 lanes and M <= 8):
+        // two fixed passes, so the number of stores per tile is static and
+        // the ring loads keep their counted waits
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+            const int i = tid + it * (int)blockDim.x;
+            const int j = i / P, pr = i - j * P;
+            const int64_t row = (int64_t)t * P + pr;
+            if (t < t_end && j < a.batch && row < a.N) {
+                const float *src = rb + (j * P + pr) * a.nb;
+                float acc = 0.f;
+                int c = 0;
+                for (; c + 4 <= a.nb; c += 4) {
+                    const float v0 = src[c], v1 = src[c + 1], v2 = src[c + 2], v3 = src[c + 3];
+                    acc = (((acc + v0) + v1) + v2) + v3;
+                }
+                for (; c < a.nb; ++c) acc += src[c];
+                a.y[(size_t)j * a.N + row] = acc;
+            }
+        }
+        buf ^= 1;
+    };
+
+    for (int t = t_begin; t < t_end; t += kPhase) {
+#pragma unroll
+        for (int d = 0; d < kPhase; ++d) {
+            if (t + d < t_end) process(ring[d], t + d);
+            fetch(ring[d], t + d + kPhase);   // unconditional, as in gemv_kernel
+        }
+    }
+}
+
 // --------------------------------------------------------- Q8 quantize
 
 // One 32-lane half-wave per 32-element block.
@@ -1341,6 +1485,22 @@ Plan make_plan(int64_t N, int64_t K, int kind)
 
 Plan make_swiglu_q8_plan(int64_t N, int64_t K) { return make_tile_plan(N, K, kSwiglu, (size_t)4 * kEmitRows + 16); }
 
+// Batched GEMV plan: the tile kernel's geometry (4 lanes per super-block, a
+// row across the workgroup), LDS for a round of staged vectors or the M-way
+// row reduction, whichever is larger.
+Plan make_batch_plan(int64_t N, int64_t K, int kind, int M, int *round)
+{
+    Plan pl = make_tile_plan(N, K, kind, 0);
+    const size_t vbytes = (size_t)K + (size_t)K / 16;
+    int r = (int)(kBatchStageBytes / vbytes);
+    r = r < 1 ? 1 : (r > M ? M : r);
+    if (round) *round = r;
+    pl.x_in_lds = 1;
+    const size_t red = (size_t)2 * M * pl.rows_tile * pl.nb * 4;
+    pl.lds_bytes = (size_t)r * vbytes > red ? (size_t)r * vbytes : red;
+    return pl;
+}
+
 // Resident workgroups per CU of a kernel at a block size and LDS size,
 // cached (occupancy depends only on those and the compiled kernel).
 static int occupancy(const void *fn, int threads, size_t lds)
@@ -1546,6 +1706,66 @@ hipError_t launch_swiglu_q8_gemv(const void *Wg, const void *Wu, const float *x,
     pl.lds_bytes = a.emit_lds_off + (size_t)4 * kEmitRows;
     return pl.x_in_lds ? launch_mode<kSwiglu, kQ8Emit, true>(pl, a, cus, s, Timing{})
                        : launch_mode<kSwiglu, kQ8Emit, false>(pl, a, cus, s, Timing{});
+}
+
+template <int KIND, int M>
+static hipError_t launch_batch_m(Plan &pl, GemvArgs a, int cus, hipStream_t s)
+{
+    const void *fn2 = (const void *)gemv_batch_kernel<KIND, M, 2>;
+    pl.grid = grid_for(pl, fn2, cus, 4);
+    a.tiles_q = (int)(pl.tiles / pl.grid);
+    a.tiles_r = (int)(pl.tiles % pl.grid);
+    if (a.tiles_q >= 2 || (a.tiles_q == 1 && a.tiles_r > 0))
+        launch_on(gemv_batch_kernel<KIND, M, 2>, pl, a, s, Timing{});
+    else
+        launch_on(gemv_batch_kernel<KIND, M, 1>, pl, a, s, Timing{});
+    return hipGetLastError();
+}
+
+template <int KIND>
+static hipError_t launch_batch_kind(Plan &pl, const GemvArgs &a, int M, int cus, hipStream_t s)
+{
+    switch (M) {
+    case 1: return launch_batch_m<KIND, 1>(pl, a, cus, s);
+    case 2: return launch_batch_m<KIND, 2>(pl, a, cus, s);
+    case 4: return launch_batch_m<KIND, 4>(pl, a, cus, s);
+    default:
+        if constexpr (KIND == kQ4KQ8) return launch_batch_m<KIND, 8>(pl, a, cus, s);
+        return hipErrorInvalidValue;   // not reached: batch_slots caps Q6_K at 4
+    }
+}
+
+// Vector slots of one launch for m vectors: 1, 2, 4 or 8.  Eight Q6_K x Q8
+// slices (20 registers each) next to the Q6_K blocks in flight exceed the
+// register file, so Q6_K launches take at most 4 and larger batches run in
+// launches of 4.
+int batch_slots(int m, bool q6k)
+{
+    const int cap = q6k ? 4 : kMaxBatch;
+    const int M = m <= 1 ? 1 : m <= 2 ? 2 : m <= 4 ? 4 : 8;
+    return M < cap ? M : cap;
+}
+
+hipError_t launch_q8_gemv_batch(bool q6k, const void *W, const int8_t *xq, const uint16_t *xd, float *y, int64_t N,
+                                int64_t K, int m, int cus, hipStream_t s)
+{
+    const int M = batch_slots(m, q6k);
+    int round = 1;
+    Plan pl = make_batch_plan(N, K, q6k ? kQ6KQ8 : kQ4KQ8, M, &round);
+    for (int j0 = 0; j0 < m; j0 += M) {
+        Plan p = pl;
+        GemvArgs a = base_args(p, N);
+        a.W = (const uint8_t *)W;
+        a.xq = xq + (size_t)j0 * K;
+        a.xd = xd + (size_t)j0 * (K / 32);
+        a.y = y + (size_t)j0 * N;
+        a.batch = m - j0 < M ? m - j0 : M;
+        a.batch_round = round;
+        const hipError_t e =
+            q6k ? launch_batch_kind<kQ6KQ8>(p, a, M, cus, s) : launch_batch_kind<kQ4KQ8>(p, a, M, cus, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_q6k_q8_gemv(const void *W, const int8_t *xq, const uint16_t *xd, float *y, int64_t N, int64_t K,

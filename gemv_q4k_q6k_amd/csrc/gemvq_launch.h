@@ -45,6 +45,14 @@ struct Plan {
 
 Plan make_plan(int64_t N, int64_t K, int kind);
 Plan make_swiglu_q8_plan(int64_t N, int64_t K);   // always the tile kernel
+// batched int8 GEMV: vectors per call, LDS bytes a round of staged vectors
+// may take, the kernel's vector slots for m vectors (1, 2, 4 or 8; Q6_K at
+// most 4, larger batches in launches of 4), and its plan (round = vectors
+// staged per round)
+constexpr int kMaxBatch = 8;
+constexpr size_t kBatchStageBytes = 61440;
+int batch_slots(int m, bool q6k);
+Plan make_batch_plan(int64_t N, int64_t K, int kind, int M, int *round);
 
 // Optional device timestamps of one launch: the kernel's own start and end
 // are recorded into these caller-created events when they are not null.
@@ -81,6 +89,8 @@ hipError_t launch_swiglu_q8_gemv(const void *Wg, const void *Wu, const float *x,
 constexpr int64_t kMaxNormK = 32768;
 hipError_t launch_rms_norm_q8(const float *x, const float *r, const float *w, float eps, float *res, float *y,
                               int8_t *xq, uint16_t *xd, int64_t K, hipStream_t s);
+hipError_t launch_q8_gemv_batch(bool q6k, const void *W, const int8_t *xq, const uint16_t *xd, float *y, int64_t N,
+                                int64_t K, int m, int cus, hipStream_t s);
 hipError_t launch_q4k_q8_isums(const void *W, const int8_t *xq, int32_t *isums, int64_t N, int64_t K, hipStream_t s);
 
 }  // namespace gemvq

@@ -134,6 +134,26 @@ int swiglu_gemv(const void *Wg, const void *Wu, const float *x, float *h,
                 int64_t N, int64_t K, void *stream);
 
 /*
+ * Batched int8-activation GEMV: Y[j] = W * xdq_j for m activation vectors,
+ * one pass over the weights (memra-engine decode.rs: the lockstep
+ * multi-stream decode advances m streams through one walk of the layers,
+ * and `full_attn_decode_batched` runs the weight-bound projections once for
+ * all m streams, one weight read serving m tokens).  Each output row is the
+ * single-vector Q8 GEMV of its vector, computed the same way whatever m and
+ * whatever the other vectors hold.
+ *   W: Q4_K (q4k_q8_gemv_batch) or Q6_K (q6k_q8_gemv_batch) N x K.
+ *   xq: int8[m][K], xd: uint16[m][K/32] (m Q8 activations back to back, e.g.
+ *   q8_quantize of the m vectors stored back to back as one vector of m*K).
+ *   y: float[m][N].  1 <= m <= 8.  A Q6_K launch takes at most 4 vectors
+ *   (their int8 slices next to the Q6_K blocks fill the register file), so
+ *   q6k_q8_gemv_batch with m > 4 reads the weights twice.
+ */
+int q4k_q8_gemv_batch(const void *W, const int8_t *xq, const uint16_t *xd, float *y,
+                      int64_t N, int64_t K, int m, void *stream);
+int q6k_q8_gemv_batch(const void *W, const int8_t *xq, const uint16_t *xd, float *y,
+                      int64_t N, int64_t K, int m, void *stream);
+
+/*
  * SwiGLU GEMV that emits its product as a Q8 activation: the producer-side
  * quantization of memra-engine decode.rs `ffn_swiglu_decode` (the SwiGLU
  * epilogue writes the q8 form of silu(gate)*up, `silu_mul_scaled_q8_1`, and
@@ -264,7 +284,8 @@ int gemvq_q6k_q8_isums(const void *W, const int8_t *xq, int32_t *isums,
  * call; for tests and tuning).  kind: 0 = Q4_K (q4k_gemv), 1 = Q6_K (q6k_gemv,
  * lm_head_argmax), 2 = Q4_K x Q8 (q4k_q8_gemv), 3 = SwiGLU (swiglu_gemv),
  * 4 = Q6_K x Q8 (q6k_q8_gemv), 5 = SwiGLU with Q8 emission (swiglu_q8_gemv,
- * N % 32 == 0).
+ * N % 32 == 0), 6 / 7 = batched Q4_K / Q6_K x Q8 (the geometry and the LDS of
+ * 8 vector slots).
  * out[0] = waves per workgroup, out[1] = rows per tile, out[2] = tiles,
  * out[3] = 1 if a row's partial sums reduce inside one wave, out[4] = 1 if the
  * activation is staged through LDS, out[5] = dynamic LDS bytes, out[6] =

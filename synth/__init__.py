@@ -89,6 +89,24 @@ def activation_outliers(rng: np.random.Generator, K: int, var: float = 2.0,
     return x.astype(np.float32)
 
 
+def q8_activations(rng: np.random.Generator, m: int, K: int):
+    """m Q8 activation vectors drawn directly in their stored form, for the
+    int8 GEMVs: (xq int8 [m, K], xd fp16 bits uint16 [m, K/32]).  Values
+    ~ U{-127..127}; one position of each 32-element block, drawn uniformly,
+    holds +-127 (a block's largest code is +-127 after quantization); scales
+    ~ fp16(U(1e-3, 1e-1)).  Draw order: values, the +-127 positions, their
+    signs, the scales."""
+    assert K % 32 == 0
+    q = rng.integers(-127, 128, (m, K)).astype(np.int8)
+    nb = K // 32
+    pos = rng.integers(0, 32, (m, nb))
+    sign = rng.integers(0, 2, (m, nb)) * 2 - 1
+    qb = q.reshape(m, nb, 32)
+    qb[np.arange(m)[:, None], np.arange(nb)[None, :], pos] = (127 * sign).astype(np.int8)
+    d = rng.uniform(1e-3, 1e-1, (m, nb)).astype(np.float16).view(np.uint16)
+    return qb.reshape(m, K), d
+
+
 # ----------------------------------------------------------- workloads
 # The five workloads (shapes and distributions) the path is specified on.
 C1_Q4K = (1024, 1024)

@@ -243,3 +243,21 @@ def test_rms_norm_q8_rejections():
     # in place is allowed past the alias checks: make the call fail on alignment instead
     _rejected(L.add_rms_norm_q8(A, C, B, 1e-5, A, None, D + 4, D + 4096, K, None), gq.ERR_ALIGN)
     _rejected(L.add_rms_norm_q8(A, C, B, 1e-5, C, None, D + 4, D + 4096, K, None), gq.ERR_ALIGN)
+
+
+def test_batch_rejections():
+    L = gq.lib()
+    for fn in (L.q4k_q8_gemv_batch, L.q6k_q8_gemv_batch):
+        _rejected(fn(None, B, C, D, 4, 256, 2, None), gq.ERR_NULL)
+        _rejected(fn(A, B, C, None, 4, 256, 2, None), gq.ERR_NULL)
+        for m in (0, -1, 9):
+            _rejected(fn(A, B, C, D, 4, 256, m, None), gq.ERR_SHAPE)
+        _rejected(fn(A, B, C, D, 4, 300, 2, None), gq.ERR_SHAPE)
+        _rejected(fn(A, B, C, D, (1 << 31) - 1, 256, 2, None), gq.ERR_SHAPE)   # N * m overflows
+        _rejected(fn(A, B + 4, C, D, 4, 256, 2, None), gq.ERR_ALIGN)            # xq needs 16 B
+        _rejected(fn(A, B, C + 2, D, 4, 256, 2, None), gq.ERR_ALIGN)
+        _rejected(fn(A, B, C, D + 2, 4, 256, 2, None), gq.ERR_ALIGN)
+        _rejected(fn(A, B, C, B + 256, 4, 256, 2, None), gq.ERR_ALIAS)         # y inside the second vector
+        _rejected(fn(A, B, C, C + 16, 4, 256, 2, None), gq.ERR_ALIAS)          # y over the second scales
+    _rejected(L.q4k_q8_gemv_batch(A + 4, B, C, D, 4, 256, 2, None), gq.ERR_ALIGN)   # Q4_K weights need 16 B
+    _rejected(L.q6k_q8_gemv_batch(A + 2, B, C, D, 4, 256, 2, None), gq.ERR_ALIGN)   # Q6_K weights need 4 B

@@ -106,7 +106,7 @@ def ends_of(geo):
 SHAPES = [(N, K) for N in (1, 2, 3, 5, 7, 21, 100, 257) for K in range(256, 10241, 256)]
 
 
-@pytest.mark.parametrize("kind", [gq.KIND_Q6K, gq.KIND_Q6K_Q8])
+@pytest.mark.parametrize("kind", [gq.KIND_Q6K, gq.KIND_Q6K_Q8, gq.KIND_Q6K_Q8_BATCH])
 @pytest.mark.parametrize("N,K", SHAPES)
 def test_q6k_loads_in_bounds(N, K, kind):
     lo, hi, end = q6k_windows(N, K, kind=kind)
@@ -115,14 +115,14 @@ def test_q6k_loads_in_bounds(N, K, kind):
 
 @pytest.mark.parametrize("N,K", [(248_320, 1024), (2560, 9728), (100, 768), (99_999, 768), (12_345, 3328),
                                  (7, 16384), (3, 32768), (1001, 12288)])
-@pytest.mark.parametrize("kind", [gq.KIND_Q6K, gq.KIND_Q6K_Q8])
+@pytest.mark.parametrize("kind", [gq.KIND_Q6K, gq.KIND_Q6K_Q8, gq.KIND_Q6K_Q8_BATCH])
 def test_q6k_loads_in_bounds_large(N, K, kind):
     geo = gq.tile_geometry(kind, N, K)
     lo, hi, end = q6k_windows(N, K, ends_of(geo), kind)
     assert W_BASE <= lo and hi <= end
 
 
-@pytest.mark.parametrize("kind", [gq.KIND_Q4K, gq.KIND_Q4K_Q8, gq.KIND_SWIGLU])
+@pytest.mark.parametrize("kind", [gq.KIND_Q4K, gq.KIND_Q4K_Q8, gq.KIND_SWIGLU, gq.KIND_Q4K_Q8_BATCH])
 @pytest.mark.parametrize("N,K", [(1, 256), (5, 768), (100, 2560), (257, 9728), (77, 8192), (1, 8192), (3, 32768),
                                  (9, 1280), (33, 4352), (5, 12288), (2, 16384)])
 def test_q4k_loads_in_bounds(kind, N, K):
@@ -150,7 +150,8 @@ def test_q4k_loads_in_bounds_large(kind, N, K):
     assert W_BASE <= lo and hi <= end
 
 
-@pytest.mark.parametrize("kind", [gq.KIND_Q4K, gq.KIND_Q6K, gq.KIND_Q4K_Q8, gq.KIND_SWIGLU, gq.KIND_Q6K_Q8])
+@pytest.mark.parametrize("kind", [gq.KIND_Q4K, gq.KIND_Q6K, gq.KIND_Q4K_Q8, gq.KIND_SWIGLU, gq.KIND_Q6K_Q8,
+                                  gq.KIND_Q4K_Q8_BATCH, gq.KIND_Q6K_Q8_BATCH])
 @pytest.mark.parametrize("K", [256, 768, 1024, 1280, 2560, 4096, 4352, 8192, 9728, 12288, 16384, 32768])
 def test_every_block_quarter_served_once(kind, K):
     """Each (row of a unit or tile, super-block, quarter) is taken by exactly
