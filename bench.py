@@ -360,6 +360,21 @@ def breakdown(gq, sets, v, reps=24):
                      ("ffn_q8_swiglu_q8+q6k_q8", ffn_q8_fused)):
         timeit(name, fn, ffn, gu_bytes + d_bytes)
     del ffn
+    # batched int8 GEMV: m Q8 activation vectors through one weight read, on
+    # the 70B-class FFN matrix and on the Q6_K lm_head
+    for name, fn, W_, (N, K), bpr in (
+            ("q4k_q8_gemv_batch_28672x8192", gq.q4k_q8_gemv_batch, s0["c5W"], synth.C5_Q8, 144),
+            ("q6k_q8_gemv_batch_248320x1024", gq.q6k_q8_gemv_batch, s0["c3W"], synth.C3_LM_HEAD, 210)):
+        xqb, xdb = synth.q8_activations(synth.rng_for(79), 8, K)
+        dq = torch.from_numpy(xqb.reshape(-1)).to(dev)
+        dd = torch.from_numpy(xdb.reshape(-1).view(np.int16)).to(dev)
+        yb = torch.empty(8 * N, dtype=torch.float32, device=dev)
+        wsb = [(w,) for w in copies(W_)]
+        for m in (1, 2, 4, 8):
+            timeit(f"{name}_m{m}",
+                   lambda w, m=m: fn(w[0], dq[:m * K], dd[:m * K // 32], N, K, m, y=yb[:m * N]), wsb,
+                   N * K // 256 * bpr + m * (K + K // 16 + 4 * N))
+        del wsb
     # norm producers at the 70B-class hidden size (K = 8192)
     K = synth.C5_Q8[1]
     r = synth.rng_for(78)
