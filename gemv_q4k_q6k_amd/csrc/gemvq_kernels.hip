@@ -1749,9 +1749,19 @@ int batch_slots(int m, bool q6k)
 hipError_t launch_q8_gemv_batch(bool q6k, const void *W, const int8_t *xq, const uint16_t *xd, float *y, int64_t N,
                                 int64_t K, int m, int cus, hipStream_t s)
 {
-    const int M = batch_slots(m, q6k);
+    int M = batch_slots(m, q6k);
     int round = 1;
     Plan pl = make_batch_plan(N, K, q6k ? kQ6KQ8 : kQ4KQ8, M, &round);
+    // Eight slots make a long-running launch VALU- and register-bound: with
+    // a lot of weight per compute unit two launches of four are faster
+    // (28,672 x 8192, 460 KB per CU: 88 us against 107 us); short launches,
+    // bound by start-up, keep the single pass over the weights (9728 x 2560,
+    // 55 KB per CU: 13.9 us against 19.0 us).
+    const int64_t wbytes = N * (K / kQK) * (q6k ? kQ6KBytes : kQ4KBytes);
+    if (M == 8 && wbytes >= (int64_t)kBatchSplitBytesPerCu * cus) {
+        M = 4;
+        pl = make_batch_plan(N, K, q6k ? kQ6KQ8 : kQ4KQ8, M, &round);
+    }
     for (int j0 = 0; j0 < m; j0 += M) {
         Plan p = pl;
         GemvArgs a = base_args(p, N);

@@ -51,6 +51,7 @@ Plan make_swiglu_q8_plan(int64_t N, int64_t K);   // always the tile kernel
 // staged per round)
 constexpr int kMaxBatch = 8;
 constexpr size_t kBatchStageBytes = 61440;
+constexpr int64_t kBatchSplitBytesPerCu = 200 * 1024;   // weight bytes per CU above which 8 slots run as 2 x 4
 int batch_slots(int m, bool q6k);
 Plan make_batch_plan(int64_t N, int64_t K, int kind, int M, int *round);
 

@@ -146,7 +146,9 @@ int swiglu_gemv(const void *Wg, const void *Wu, const float *x, float *h,
  *   q8_quantize of the m vectors stored back to back as one vector of m*K).
  *   y: float[m][N].  1 <= m <= 8.  A Q6_K launch takes at most 4 vectors
  *   (their int8 slices next to the Q6_K blocks fill the register file), so
- *   q6k_q8_gemv_batch with m > 4 reads the weights twice.
+ *   q6k_q8_gemv_batch with m > 4 reads the weights twice; so does
+ *   q4k_q8_gemv_batch for large matrices (more than 200 KB of weights per
+ *   compute unit), where two passes of 4 vectors beat one of 8.
  */
 int q4k_q8_gemv_batch(const void *W, const int8_t *xq, const uint16_t *xd, float *y,
                       int64_t N, int64_t K, int m, void *stream);
