@@ -61,3 +61,16 @@ def test_shapes_of_workloads():
     assert synth.C3_LM_HEAD == (248_320, 1024)
     assert synth.C3_LM_HEAD[0] * 4 == 993_280   # f32 logits bytes of the unfused path
     assert synth.C5_Q8 == (28_672, 8192)
+
+
+def test_q8_activations():
+    m, K = 5, 1024
+    xq, xd = synth.q8_activations(synth.rng_for(3), m, K)
+    assert xq.shape == (m, K) and xq.dtype == np.int8 and xd.shape == (m, K // 32) and xd.dtype == np.uint16
+    assert xq.min() >= -127                                   # -128 never appears
+    # every 32-element block holds a +-127, as a quantized block does
+    assert np.all(np.abs(xq.astype(np.int64)).reshape(m, -1, 32).max(axis=2) == 127)
+    d = xd.view(np.float16).astype(np.float64)
+    assert d.min() >= 0.00099 and d.max() <= 0.1001
+    r = synth.rng_for(0)
+    assert _h(*synth.q8_activations(r, 3, 512)) == "dc3893e619f8532f"
