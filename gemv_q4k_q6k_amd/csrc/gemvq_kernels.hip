@@ -1567,7 +1567,13 @@ static hipError_t launch_mode(Plan &pl, GemvArgs a, int cus, hipStream_t s, cons
     // the occupancy of the deeper-pipelined kernel sizes the grid; if that
     // leaves at most one tile per workgroup the single-tile kernel runs
     const void *fn2 = (const void *)gemv_kernel<KIND, EPI, 2, XLDS>;
-    pl.grid = grid_for(pl, fn2, cus, KIND == kSwiglu ? 2 : 4);
+    // Fewest tiles per workgroup: a workgroup's start-up is mostly its copy
+    // of x, so a short x (<= 16 KiB: K <= 4096 in f32) is worth spreading
+    // over more workgroups of 3 tiles, a long one over fewer of 4 (measured:
+    // 9728 x 2560 6.85 us with 3 against 7.15 us with 4; 2560 x 9728 8.9 us
+    // with 3 against 7.2 us with 4).  The SwiGLU pair doubles a tile's work.
+    const int64_t x_bytes = (int64_t)pl.nb * kQK * (is_q8(KIND) ? 1 : 4);
+    pl.grid = grid_for(pl, fn2, cus, KIND == kSwiglu ? 2 : (x_bytes <= 16384 ? 3 : 4));
     if (is_argmax(EPI) && pl.grid > kArgmaxMaxGrid) pl.grid = kArgmaxMaxGrid;   // one workspace slot each
     if constexpr (EPI == kQ8Emit) {
         // a workgroup's rows must fit its LDS row buffer
