@@ -798,3 +798,32 @@ def test_q4k_q8_gemv_batch_full(dev):
         check_f32(f"C5 batch j={j}", Y[j], Yhat[j])
         y1 = gq().q4k_q8_gemv(dW, dq[j * K:(j + 1) * K], dd[j * (K // 32):(j + 1) * (K // 32)], N, K).cpu().numpy()
         check_f32(f"C5 single j={j}", y1, Yhat[j])
+
+
+def test_q6k_q8_gemv_batch_lm_head_full(dev, c3_full):
+    """The Q6_K lm_head matrix (248,320 x 1024) with 4 and with 6 Q8 vectors
+    (6 runs as launches of 4 and 2), against the oracle row by row."""
+    W, _, dW, _ = c3_full
+    N, K = synth.C3_LM_HEAD
+    for m in (4, 6):
+        xq, xd = synth.q8_activations(synth.rng_for(9200 + m), m, K)
+        Y = gq().q6k_q8_gemv_batch(dW, up(xq.reshape(-1), dev), up(xd.reshape(-1).view(np.int16), dev),
+                                   N, K, m).cpu().numpy()
+        Yhat = oracle.q8_gemv_batch("q6k", W, xq, xd, N, K, m)
+        for j in range(m):
+            check_f32(f"lm_head batch m={m} j={j}", Y[j], Yhat[j])
+
+
+def test_int8_ffn_pipeline_full(dev):
+    """The whole int8 FFN of the 4B-class layer at full size: SwiGLU that
+    emits Q8 (9728 x 2560), then the Q6_K x Q8 down projection (2560 x 9728),
+    against the oracle's composition (f64 SwiGLU, its Q8 encoding, the f64
+    Q6_K x Q8 GEMV).  Codes that straddle a rounding boundary between the two
+    sides move the output by far less than the tolerance."""
+    Wg, Wu, Wd, x = synth.c4_inputs(0)
+    N, K = synth.C4_SWIGLU
+    hq, hd = gq().swiglu_q8_gemv(up(Wg, dev), up(Wu, dev), up(x, dev), N, K,
+                                 torch.zeros(gq().swiglu_q8_ws_bytes(N), dtype=torch.uint8, device=dev))
+    y = gq().q6k_q8_gemv(up(Wd, dev), hq, hd, K, N).cpu().numpy()
+    _, q, d = oracle.swiglu_q8(Wg, Wu, x, N, K)
+    check_f32("int8 FFN 9728x2560 -> 2560x9728", y, oracle.q6k_q8_gemv(Wd, q, d, K, N))
