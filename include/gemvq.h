@@ -28,8 +28,10 @@
  *
  * Limits.  1 <= N <= 2^31 - 1; 256 <= K <= 32768; N * (K/256) * block_bytes
  * must fit in 63 bits.  Alignment: weights 16 B (Q4_K) or 4 B (Q6_K), float
- * vectors 16 B (inputs) / 4 B (outputs), int8 Q8 vector 16 B, Q8 scales 4 B.
- * Outputs may not overlap any input.
+ * vectors 16 B (inputs) / 4 B (outputs; the norms' outputs 16 B), int8 Q8
+ * vector 16 B, Q8 scales 4 B.  Outputs may not overlap any input, except
+ * where an entry point below allows an exact in-place update (a residual
+ * output over its residual input).
  */
 #ifndef GEMVQ_H
 #define GEMVQ_H
