@@ -22,6 +22,7 @@ on the host on a bounded sample.
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -559,6 +560,7 @@ def main():
     handles = [(a.cuda_event, b.cuda_event) for a, b in ev]
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    gc.disable()   # no collector pause between launches inside the timed region
     wall0 = time.perf_counter()
     t_start.record()
     for k in range(args.steps):
@@ -567,6 +569,7 @@ def main():
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    gc.enable()
     ms_total = t_start.elapsed_time(t_end)
     ms_step = ms_total / args.steps
     lm_us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1000.0
