@@ -339,11 +339,15 @@ __device__ __forceinline__ void emit_row(const GemvArgs &a, int64_t row, const f
 // 128-byte line of its own, so the atomics of different groups never meet):
 //   [0, 4)                     top counter: groups that have finished
 //   [128*(1+r), +4), r < 16    group counter r: finished workgroups g with g % 16 == r
-//   [kArgmaxSlot0 + 128*g, +8) workgroup g's best key (written every call)
-// The counters are zero between calls; the keys need no initial value.
+//   [kArgmaxSlot0 + 8*g, +8)   workgroup g's best key (written every call)
+// The counters are zero between calls; the keys need no initial value.  The
+// keys lie side by side, so the final reduction reads the grid's keys in
+// whole cache lines (one 512-byte load per 64 workgroups); each is written
+// once per call, at a different time, so sharing lines costs the exchanges
+// nothing measurable.
 __device__ __forceinline__ uint32_t *ws_top(uint8_t *ws) { return (uint32_t *)ws; }
 __device__ __forceinline__ uint32_t *ws_group(uint8_t *ws, int r) { return (uint32_t *)(ws + 128 * (1 + r)); }
-__device__ __forceinline__ uint64_t *ws_slot(uint8_t *ws, int g) { return (uint64_t *)(ws + kArgmaxSlot0 + 128 * (size_t)g); }
+__device__ __forceinline__ uint64_t *ws_slot(uint8_t *ws, int g) { return (uint64_t *)(ws + kArgmaxSlot0 + 8 * (size_t)g); }
 
 // Grid-level argmax without fences and without a hot spot: the threads'
 // running keys meet in LDS (one barrier); thread 0 publishes the workgroup's
@@ -381,14 +385,16 @@ __device__ void argmax_finish(const GemvArgs &a, uint64_t best, int holder, int 
     }
     last = (uint32_t)__shfl((int)last, 0);
     if (!last) return;
-    // every slot of the workspace is read unconditionally (no branch, so all
-    // loads are in flight together); slots of workgroups past the grid hold
-    // stale keys and are masked out
+    // the grid's slots in 64-key loads, all issued before the first is used
+    // (the guard is uniform); lanes past the grid read stale keys of the
+    // last load and are masked out
     constexpr int kPerLane = kArgmaxMaxGrid / 64;
+    const int loads = (G + 63) >> 6;
     uint64_t v[kPerLane];
 #pragma unroll
     for (int j = 0; j < kPerLane; ++j)
-        v[j] = __hip_atomic_load(ws_slot(a.ws, (int)threadIdx.x + 64 * j), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        v[j] = j < loads ? __hip_atomic_load(ws_slot(a.ws, (int)threadIdx.x + 64 * j), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                         : 0ull;
     uint64_t k = 0;
 #pragma unroll
     for (int j = 0; j < kPerLane; ++j) {

@@ -14,12 +14,12 @@ constexpr int kMaxThreads = 512;
 constexpr int64_t kMaxK = 32768;
 
 // lm_head_argmax workspace: counters in the first kArgmaxSlot0 bytes (zero
-// between calls), then one 128-byte slot per workgroup for its best key; the
+// between calls), then one 8-byte slot per workgroup for its best key; the
 // argmax launches use at most kArgmaxMaxGrid workgroups.
 constexpr int kArgmaxGroups = 16;
 constexpr size_t kArgmaxSlot0 = 4096;
 constexpr int kArgmaxMaxGrid = 1024;
-constexpr size_t kArgmaxWsBytes = kArgmaxSlot0 + 128 * (size_t)kArgmaxMaxGrid;
+constexpr size_t kArgmaxWsBytes = kArgmaxSlot0 + 8 * (size_t)kArgmaxMaxGrid;
 
 // Matrices one multi-output GEMV launch can take; x (f32) must fit in LDS.
 constexpr int kMaxMulti = 4;

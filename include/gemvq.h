@@ -224,7 +224,7 @@ int add_rms_norm_q8(const float *x, const float *r, const float *w, float eps, f
  * qualiaDB's top-1 per block and candidate merge).
  *   W: Q6_K N x K.  x: float[K].  out_idx: uint32[1].  out_max: float[1] or NULL.
  *   workspace: device memory of at least gemvq_lm_head_argmax_ws_bytes(N, K)
- *   (135,168) bytes, 256-B aligned.  Its first 4096 bytes (the counters)
+ *   (12,288) bytes, 256-B aligned.  Its first 4096 bytes (the counters)
  *   must be zero before the first call; every call leaves them zero again, so
  *   one workspace serves any number of calls in stream order (also inside a
  *   captured graph).  The rest holds per-workgroup keys and needs no initial

@@ -60,7 +60,7 @@ def test_strerror_and_ws_bytes():
         assert isinstance(gq.strerror(s), str) and gq.strerror(s)
     assert gq.strerror(99) == "unknown status"
     ws = gq.lm_head_argmax_ws_bytes(248_320, 1024)
-    assert ws >= 4096 + 128 * 1024 and ws % 256 == 0
+    assert ws >= 4096 + 8 * 1024 and ws % 256 == 0   # counters, then one 8-byte key per workgroup (up to 1024)
 
 
 def test_null_pointers():
