@@ -29,7 +29,6 @@ constexpr uint32_t kNoIndex = 0xFFFFFFFFu;
 
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-struct __attribute__((aligned(4))) U32x4A4 { uint32_t v[4]; };
 
 // f16 "magic" conversion: OR-ing a 10-bit integer m into the mantissa of
 // 1024.0h (0x6400) gives the exact half value 1024 + m.  Two such halves per
@@ -245,62 +244,52 @@ __device__ __forceinline__ float q4k_q8_dot(const Q4KRaw &r, const Q8X &x, int c
 // ---------------------------------------------------------------- Q6_K
 
 // A Q6_K block starts 2 bytes off a dword boundary when its flat index is odd.
-// Loads use dword-aligned addresses only and v_alignbyte_b32 re-aligns; every
-// dword read lies inside the block (or, for a misaligned block, in the 2 bytes
-// before it, which belong to the previous block of the same buffer).
+// Its fields are loaded with dword loads at their true (2-byte aligned)
+// addresses: the HSA code-object ABI for gfx9 runs the shader memory path in
+// unaligned mode, so a global dword load needs only byte alignment (the
+// compiler itself emits such loads for 2-byte aligned packed data on this
+// target).  Every byte read lies inside the block.
 struct Q6KRaw {
-    uint32_t a[5];   // ql[64n+l0 .. +16) plus one dword
-    uint32_t b[5];   // ql[64n+32+l0 .. +16) plus one dword
-    uint32_t h[5];   // qh[32n+l0 .. +16) plus one dword
-    uint32_t s[3];   // scale window sc[8n .. 8n+8) plus one dword
+    uint32_t a[4];   // ql[64n+l0 .. +16)
+    uint32_t b[4];   // ql[64n+32+l0 .. +16)
+    uint32_t h[4];   // qh[32n+l0 .. +16)
+    uint32_t s[2];   // scale window sc[8n .. 8n+8)
     uint32_t dbits;  // fp16 d in the low 16 bits
-    uint32_t shift;  // byte misalignment of the block (0 or 2)
 };
 
-__device__ __forceinline__ void load5(uint32_t (&o)[5], const uint32_t *p)
+struct __attribute__((packed, aligned(2))) U32x4A2 { uint32_t v[4]; };
+struct __attribute__((packed, aligned(2))) U32x2A2 { uint32_t v[2]; };
+
+__device__ __forceinline__ void load4(uint32_t (&o)[4], const uint8_t *p)
 {
-    const U32x4A4 v = *(const U32x4A4 *)p;
+    const U32x4A2 v = *(const U32x4A2 *)p;
     o[0] = v.v[0];
     o[1] = v.v[1];
     o[2] = v.v[2];
     o[3] = v.v[3];
-    o[4] = p[4];
 }
 
-// `tile` is workgroup-uniform, `off` the lane's byte offset of its block in
-// the tile.  Offsets are taken from the tile start rounded down to a dword
-// (`base`, still uniform), so the dword-aligned block start `al` is never
-// negative: a block that begins 2 bytes past a dword boundary at the very
-// start of a tile reads from the 2 bytes before it (the previous block of the
-// same matrix; the first block of the matrix is dword-aligned).  Pointer
-// arithmetic only: an integer round trip would lose the global address space
-// and turn every load into a flat load.
+// `tile` is the workgroup-uniform start of the unit or tile, `off` the lane's
+// byte offset of its block in it; part u = 2n + (l0 / 16) of the block.
 __device__ __forceinline__ void q6k_load(Q6KRaw &r, const uint8_t *__restrict__ tile, uint32_t off, int u)
 {
-    const uint32_t lead = (uint32_t)(uintptr_t)tile & 3u;      // uniform
-    const uint8_t *base = tile - lead;                          // dword-aligned, uniform
-    const uint32_t o = off + lead;                              // block start relative to base
-    const uint32_t sh = o & 3u;                                 // block misalignment (0 or 2)
-    const uint32_t al = o - sh;                                 // o rounded down to a dword: never below base
+    const uint8_t *blk = tile + off;
     const uint32_t n = (uint32_t)(u >> 1), l0 = 16u * (uint32_t)(u & 1);
-    load5(r.a, (const uint32_t *)(base + (al + 64u * n + l0)));
-    load5(r.b, (const uint32_t *)(base + (al + 64u * n + 32u + l0)));
-    load5(r.h, (const uint32_t *)(base + (al + 128u + 32u * n + l0)));
-    const uint32_t *sp = (const uint32_t *)(base + (al + 192u + 8u * n));
-    r.s[0] = sp[0];
-    r.s[1] = sp[1];
-    r.s[2] = sp[sh ? 2 : 1];   // the third dword is needed (and in bounds) only when misaligned
-    r.dbits = *(const uint16_t *)(base + (o + 208u));
-    r.shift = sh;
+    load4(r.a, blk + (64u * n + l0));
+    load4(r.b, blk + (64u * n + 32u + l0));
+    load4(r.h, blk + (128u + 32u * n + l0));
+    const U32x2A2 sc = *(const U32x2A2 *)(blk + (192u + 8u * n));
+    r.s[0] = sc.v[0];
+    r.s[1] = sc.v[1];
+    r.dbits = *(const uint16_t *)(blk + 208u);
 }
 
 __device__ __forceinline__ void q6k_zero(Q6KRaw &r)
 {
 #pragma unroll
-    for (int i = 0; i < 5; ++i) r.a[i] = r.b[i] = r.h[i] = 0u;
-    r.s[0] = r.s[1] = r.s[2] = 0u;
+    for (int i = 0; i < 4; ++i) r.a[i] = r.b[i] = r.h[i] = 0u;
+    r.s[0] = r.s[1] = 0u;
     r.dbits = 0u;
-    r.shift = 0u;
 }
 
 // Activation slice of a Q6_K part: xs[s][i] = x[128n + 32s + l0 + i].
@@ -314,10 +303,7 @@ struct Q6KX {
 // bit pair with one v_and_or_b32 each.
 __device__ __forceinline__ void q6k_quants(const Q6KRaw &r, int k, uint32_t (&q)[4])
 {
-    const uint32_t sh = r.shift;
-    const uint32_t a = __builtin_amdgcn_alignbyte(r.a[k + 1], r.a[k], sh);
-    const uint32_t b = __builtin_amdgcn_alignbyte(r.b[k + 1], r.b[k], sh);
-    const uint32_t h = __builtin_amdgcn_alignbyte(r.h[k + 1], r.h[k], sh);
+    const uint32_t a = r.a[k], b = r.b[k], h = r.h[k];
     q[0] = and_or(h << 4, 0x30303030u, a & 0x0F0F0F0Fu);
     q[1] = and_or(h << 2, 0x30303030u, b & 0x0F0F0F0Fu);
     q[2] = and_or(h, 0x30303030u, (a >> 4) & 0x0F0F0F0Fu);
@@ -328,9 +314,7 @@ __device__ __forceinline__ void q6k_quants(const Q6KRaw &r, int k, uint32_t (&q)
 // of the 8-byte scale window.
 __device__ __forceinline__ void q6k_scales(const Q6KRaw &r, int u, int (&sc)[4])
 {
-    const uint32_t sh = r.shift;
-    const uint32_t s0 = __builtin_amdgcn_alignbyte(r.s[1], r.s[0], sh);
-    const uint32_t s1 = __builtin_amdgcn_alignbyte(r.s[2], r.s[1], sh);
+    const uint32_t s0 = r.s[0], s1 = r.s[1];
     const uint32_t bo = (uint32_t)(u & 1) * 8u;
     sc[0] = __builtin_amdgcn_sbfe((int)s0, bo, 8);
     sc[1] = __builtin_amdgcn_sbfe((int)s0, bo + 16u, 8);

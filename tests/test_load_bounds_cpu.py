@@ -14,10 +14,9 @@ of each kernel) on the launch geometry the library itself reports
   row t // (4*nb), quarter t % 4 of super-block (t % (4*nb)) // 4.
 
 A lane of a unit or tile past the last row also loads the first super-block
-of that unit or tile.  Q6_K blocks are 210 bytes, so a unit can start 2
-bytes past a dword boundary; the loads then begin 2 bytes before the block,
-which must never fall before the matrix or wrap around (regression test for
-an unsigned underflow of that offset).
+of that unit or tile.  Q6_K blocks are 210 bytes, so a block can start 2
+bytes past a dword boundary; its fields are then read at their true
+(2-byte aligned) addresses, and every byte read must lie inside the block.
 """
 import numpy as np
 import pytest
@@ -65,18 +64,15 @@ def q6k_windows(N, K, tiles_to_check=None, kind=gq.KIND_Q6K):
     for t in ts:
         tile = W_BASE + t * stride
         for off in offsets(t):
-            lead = tile & 3
-            base = tile - lead
-            o = off + lead
-            sh = o & 3
-            al = o - sh
-            assert (al >= 0).all()
-            starts = [al + 64 * n + l0, al + 64 * n + 32 + l0, al + 128 + 32 * n + l0]
-            ends = [s_ + 20 for s_ in starts]                       # dwordx4 + one dword
-            ends.append(al + 192 + 8 * n + np.where(sh != 0, 12, 8))  # scale window
-            ends.append(o + 210)                                    # d at o + 208, 2 bytes
-            l_ = base + min(s_.min() for s_ in starts)
-            h_ = base + max(e.max() for e in ends)
+            blk = tile + off
+            assert (blk % 2 == 0).all()
+            starts = [blk + 64 * n + l0, blk + 64 * n + 32 + l0, blk + 128 + 32 * n + l0]
+            ends = [s_ + 16 for s_ in starts]          # 16-byte loads
+            ends.append(blk + 192 + 8 * n + 8)         # scale window
+            ends.append(blk + 210)                     # d at 208, 2 bytes
+            l_ = min(s_.min() for s_ in starts)
+            h_ = max(e.max() for e in ends)
+            assert (np.maximum.reduce(ends) <= blk + 210).all()   # inside the lane's own block
             lo = l_ if lo is None else min(lo, l_)
             hi = h_ if hi is None else max(hi, h_)
     return lo, hi, W_BASE + N * nb * 210
