@@ -80,6 +80,11 @@ template <> struct XSlice<kSwiglu> { Q4KX v; };
 template <> struct XSlice<kQ6K> { Q6KX v; };
 template <> struct XSlice<kQ4KQ8> { Q8X v; };
 template <> struct XSlice<kQ6KQ8> { Q6Q8X v; };
+// The wave-unit kernel holds Q6_K activations in fixed point (Q6KFX); every
+// other kernel and kind uses XSlice.
+struct FXSlice { Q6KFX v; };
+template <int KIND> struct WaveSlice { using T = XSlice<KIND>; };
+template <> struct WaveSlice<kQ6K> { using T = FXSlice; };
 
 // Layout of the activation staged in LDS: 16 bytes of padding after every
 // 256 bytes.  A lane's slice is 64 consecutive bytes (Q8) or 64 consecutive
@@ -299,8 +304,8 @@ __device__ __forceinline__ void zero_raw(RawSet<KIND> &rs)
     }
 }
 
-template <int KIND>
-__device__ __forceinline__ void dot_raw(const RawSet<KIND> &rs, const XSlice<KIND> &xs, int part, float (&out)[2])
+template <int KIND, class XS>
+__device__ __forceinline__ void dot_raw(const RawSet<KIND> &rs, const XS &xs, int part, float (&out)[2])
 {
     if constexpr (KIND == kQ6K) {
         out[0] = q6k_dot(rs.r[0], xs.v, part);
@@ -335,30 +340,25 @@ __device__ __forceinline__ void emit_row(const GemvArgs &a, int64_t row, const f
     }
 }
 
-// Workspace of lm_head_argmax (all offsets in bytes; every counter sits on a
-// 128-byte line of its own, so the atomics of different groups never meet):
-//   [0, 4)                     top counter: groups that have finished
-//   [128*(1+r), +4), r < 16    group counter r: finished workgroups g with g % 16 == r
-//   [kArgmaxSlot0 + 8*g, +8)   workgroup g's best key (written every call)
-// The counters are zero between calls; the keys need no initial value.  The
-// keys lie side by side, so the final reduction reads the grid's keys in
-// whole cache lines (one 512-byte load per 64 workgroups); each is written
-// once per call, at a different time, so sharing lines costs the exchanges
-// nothing measurable.
-__device__ __forceinline__ uint32_t *ws_top(uint8_t *ws) { return (uint32_t *)ws; }
-__device__ __forceinline__ uint32_t *ws_group(uint8_t *ws, int r) { return (uint32_t *)(ws + 128 * (1 + r)); }
-__device__ __forceinline__ uint64_t *ws_slot(uint8_t *ws, int g) { return (uint64_t *)(ws + kArgmaxSlot0 + 8 * (size_t)g); }
+// Workspace of lm_head_argmax (offsets in bytes; each word on a 128-byte line
+// of its own):
+//   [0, 4)      done counter: workgroups that have published their key
+//   [128, 136)  running key: the largest key published so far
+// Both are zero between calls.
+__device__ __forceinline__ uint32_t *ws_count(uint8_t *ws) { return (uint32_t *)ws; }
+__device__ __forceinline__ uint64_t *ws_key(uint8_t *ws) { return (uint64_t *)(ws + kArgmaxKeyOff); }
 
-// Grid-level argmax without fences and without a hot spot: the threads'
-// running keys meet in LDS (one barrier); thread 0 publishes the workgroup's
-// best key in its own slot with a returning atomic exchange (so it has been
-// performed at device scope before the count below), then counts the
-// workgroup done in its group's counter.  The last workgroup of a group clears
-// that counter and counts the group done in the top counter; the last group's
-// last workgroup reads every slot (device-scope atomic loads), writes the
-// 4-byte result and clears the top counter.  Device-scope atomics are coherent
-// across all XCDs, so no cache writeback or invalidation is needed, and with
-// at most 16 workgroups per counter the atomics barely queue.
+// Grid-level argmax without fences: the threads' running keys meet in LDS
+// (one barrier) and wave 0 folds them by shuffle.  Thread 0 then merges the
+// workgroup's key into the running key with a returning atomic max (device
+// scope, so it has been performed before the count below) and counts the
+// workgroup done.  The workgroup whose count completes the grid reads the
+// running key, writes the 4-byte result and sets both words back to zero.
+// Keys are order-keeping (argmax_key), so the largest key is the largest
+// value with the smallest index, whatever order the workgroups finish in.
+// Device-scope atomics are coherent across all XCDs, so no cache writeback
+// or invalidation is needed; the last workgroup waits for three dependent
+// round trips (max, count, read).
 // `holders` threads (0..holders-1) carry running keys.
 __device__ void argmax_finish(const GemvArgs &a, uint64_t best, int holder, int holders)
 {
@@ -366,41 +366,8 @@ __device__ void argmax_finish(const GemvArgs &a, uint64_t best, int holder, int 
     if (holder >= 0) s_key[holder] = best;
     __syncthreads();
     if (threadIdx.x >= 64) return;   // wave 0 finishes
-    const int G = (int)gridDim.x, g = (int)blockIdx.x;
-    const int groups = G < kArgmaxGroups ? G : kArgmaxGroups;
-    uint32_t last = 0;
-    if (threadIdx.x == 0) {
-        uint64_t k = 0;
-        for (int h = 0; h < holders; ++h) k = s_key[h] > k ? s_key[h] : k;
-        const uint64_t old = __hip_atomic_exchange(ws_slot(a.ws, g), k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        asm volatile("" ::"v"(old));   // consumed: the exchange is performed before the count
-        const int r = g % groups;
-        const int members = (G - r + groups - 1) / groups;   // workgroups g' < G with g' % groups == r
-        const uint32_t prev = __hip_atomic_fetch_add(ws_group(a.ws, r), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (prev == (uint32_t)members - 1) {
-            __hip_atomic_store(ws_group(a.ws, r), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const uint32_t t = __hip_atomic_fetch_add(ws_top(a.ws), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            last = (t == (uint32_t)groups - 1) ? 1u : 0u;
-        }
-    }
-    last = (uint32_t)__shfl((int)last, 0);
-    if (!last) return;
-    // the grid's slots in 64-key loads, all issued before the first is used
-    // (the guard is uniform); lanes past the grid read stale keys of the
-    // last load and are masked out
-    constexpr int kPerLane = kArgmaxMaxGrid / 64;
-    const int loads = (G + 63) >> 6;
-    uint64_t v[kPerLane];
-#pragma unroll
-    for (int j = 0; j < kPerLane; ++j)
-        v[j] = j < loads ? __hip_atomic_load(ws_slot(a.ws, (int)threadIdx.x + 64 * j), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                         : 0ull;
     uint64_t k = 0;
-#pragma unroll
-    for (int j = 0; j < kPerLane; ++j) {
-        const uint64_t w = ((int)threadIdx.x + 64 * j < G) ? v[j] : 0ull;
-        k = w > k ? w : k;
-    }
+    for (int h = (int)threadIdx.x; h < holders; h += 64) k = s_key[h] > k ? s_key[h] : k;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
         const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)k, off);
@@ -408,11 +375,18 @@ __device__ void argmax_finish(const GemvArgs &a, uint64_t best, int holder, int 
         const uint64_t o = ((uint64_t)hi << 32) | lo;
         k = o > k ? o : k;
     }
-    if (threadIdx.x == 0) {
-        a.out_idx[0] = k ? argmax_key_index(k) : 0u;
-        if (a.out_max) a.out_max[0] = k ? argmax_key_value(k) : __builtin_nanf("");
-        __hip_atomic_store(ws_top(a.ws), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x != 0) return;
+    if (k) {
+        const uint64_t old = __hip_atomic_fetch_max(ws_key(a.ws), k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        asm volatile("" ::"v"(old));   // consumed: the max is performed before the count
     }
+    const uint32_t prev = __hip_atomic_fetch_add(ws_count(a.ws), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (prev != gridDim.x - 1) return;
+    const uint64_t top = __hip_atomic_load(ws_key(a.ws), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    a.out_idx[0] = top ? argmax_key_index(top) : 0u;
+    if (a.out_max) a.out_max[0] = top ? argmax_key_value(top) : __builtin_nanf("");
+    __hip_atomic_store(ws_key(a.ws), 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(ws_count(a.ws), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ------------------------------------------------------------ Q8 emission
@@ -703,6 +677,69 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_kernel(GemvArgs a)
 // is staged in LDS once per CU.  A row's value is reduced the same way
 // wherever it sits (fixed lane layout, halves added in order), so equal rows
 // give equal bits.
+// Fixed-point activation of the wave-unit Q6_K kernel, in LDS after the
+// 16-element sums (`base`, 16-byte aligned): the high, middle and low byte
+// arrays of X (K bytes each, in the padded layout), then the per-group
+// exponents (K/16 ints).
+__device__ __forceinline__ uint32_t fx_bytes_stride(int K) { return lds_pad((uint32_t)K); }
+
+// Group g of the staged f32 activation (16 values in LDS) converted as Q6KFX
+// describes; one thread per group.
+__device__ void fx_stage_group(unsigned char *smem, uint32_t base, const float *sx, int K, int g)
+{
+    const float *v = x_at<true>(sx, 16 * g);
+    float m = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+    // scale so that the largest |X| is below 2^22 (m < 2^E); zero and
+    // non-finite groups keep e = 0 (their sum carries a non-finite value)
+    const int e = (m > 0.f && m <= 3.402823466e38f) ? 22 - __builtin_amdgcn_frexp_expf(m) : 0;
+    uint32_t hi[4], mid[4], lo[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        int X[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) X[j] = (int)rintf(__builtin_amdgcn_ldexpf(v[4 * k + j], e));
+        // bytes 0..2 of X[0..3], one byte of each element per dword
+        const uint32_t p01 = __builtin_amdgcn_perm((uint32_t)X[1], (uint32_t)X[0], 0x05010400u);   // X0.b0 X1.b0 X0.b1 X1.b1
+        const uint32_t p23 = __builtin_amdgcn_perm((uint32_t)X[3], (uint32_t)X[2], 0x05010400u);
+        const uint32_t r01 = __builtin_amdgcn_perm((uint32_t)X[1], (uint32_t)X[0], 0x07030602u);   // X0.b2 X1.b2 X0.b3 X1.b3
+        const uint32_t r23 = __builtin_amdgcn_perm((uint32_t)X[3], (uint32_t)X[2], 0x07030602u);
+        lo[k] = __builtin_amdgcn_perm(p23, p01, 0x05040100u);
+        mid[k] = __builtin_amdgcn_perm(p23, p01, 0x07060302u);
+        hi[k] = __builtin_amdgcn_perm(r23, r01, 0x05040100u);
+    }
+    const uint32_t stride = fx_bytes_stride(K);
+    const uint32_t o = lds_pad(16u * (uint32_t)g);
+    *(u32x4 *)(smem + base + o) = u32x4{hi[0], hi[1], hi[2], hi[3]};
+    *(u32x4 *)(smem + base + stride + o) = u32x4{mid[0], mid[1], mid[2], mid[3]};
+    *(u32x4 *)(smem + base + 2 * stride + o) = u32x4{lo[0], lo[1], lo[2], lo[3]};
+    ((int *)(smem + base + 3 * stride))[g] = -e;
+}
+
+// Lane slice of part u of block b from the staged fixed-point activation.
+__device__ __forceinline__ void fx_load(Q6KFX &xs, const unsigned char *smem, uint32_t base, const float *sums, int K,
+                                        int b, int u)
+{
+    const int n = u >> 1;
+    const uint32_t stride = fx_bytes_stride(K);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const int g = 16 * b + 8 * n + 2 * s + (u & 1);   // 16-element group of the slice's group s
+        const uint32_t o = lds_pad(16u * (uint32_t)g);
+        const u32x4 h = *(const u32x4 *)(smem + base + o);
+        const u32x4 m = *(const u32x4 *)(smem + base + stride + o);
+        const u32x4 l = *(const u32x4 *)(smem + base + 2 * stride + o);
+        xs.hi[s][0] = h.x; xs.hi[s][1] = h.y; xs.hi[s][2] = h.z; xs.hi[s][3] = h.w;
+        xs.mid[s][0] = m.x; xs.mid[s][1] = m.y; xs.mid[s][2] = m.z; xs.mid[s][3] = m.w;
+        xs.lo[s][0] = l.x; xs.lo[s][1] = l.y; xs.lo[s][2] = l.z; xs.lo[s][3] = l.w;
+        xs.e[s] = ((const int *)(smem + base + 3 * stride))[g];
+        float t = sums[g];
+        pin(t);
+        xs.sx[s] = t;
+    }
+}
+
 template <int KIND>
 constexpr int wave_max_threads() { return (is_q8(KIND) || KIND == kQ4K) ? 1024 : 768; }
 constexpr int kWaveMaxThreads = 1024;   // the largest of wave_max_threads
@@ -806,7 +843,7 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_wave_kernel(Gem
     for (int i = (tid + kXRegs * (int)blockDim.x) * step; i < K; i += (int)blockDim.x * step)
         *(u32x4 *)(smem + lds_pad((uint32_t)(i * esz))) = *(const u32x4 *)(src + (size_t)i * esz);
     __syncthreads();
-    XSlice<KIND> xs[STEPS];
+    typename WaveSlice<KIND>::T xs[STEPS];
     if constexpr (is_q8(KIND)) {
 #pragma unroll
         for (int st = 0; st < STEPS; ++st) {
@@ -816,12 +853,20 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_wave_kernel(Gem
     } else {
         const float *sx = (const float *)smem;
         float *ssum = (float *)(smem + lds_pad(4u * (uint32_t)K));
-        for (int g = tid; g < K / 16; g += blockDim.x) ssum[g] = sum16(x_at<true>(sx, 16 * g));
+        const uint32_t fx_base = lds_pad(4u * (uint32_t)K) + 4u * (uint32_t)(K / 16);
+        for (int g = tid; g < K / 16; g += blockDim.x) {
+            ssum[g] = sum16(x_at<true>(sx, 16 * g));
+            if constexpr (KIND == kQ6K) fx_stage_group(smem, fx_base, sx, K, g);
+        }
         __syncthreads();
 #pragma unroll
         for (int st = 0; st < STEPS; ++st) {
-            load_x<true>(xs[st].v, sx, b + 16 * st, part);
-            finish_x(xs[st].v, (const float *)ssum, b + 16 * st, part);
+            if constexpr (KIND == kQ6K) {
+                fx_load(xs[st].v, smem, fx_base, ssum, K, b + 16 * st, part);
+            } else {
+                load_x<true>(xs[st].v, sx, b + 16 * st, part);
+                finish_x(xs[st].v, (const float *)ssum, b + 16 * st, part);
+            }
         }
     }
 
@@ -1436,7 +1481,11 @@ static bool plan_in_wave(Plan &pl, int64_t N, int64_t K, int kind)
         pl.steps = 2;
         pl.lanes_row = 64;
     }
-    return finish_wave_plan(pl, N, K, kind);
+    const bool ok = finish_wave_plan(pl, N, K, kind);
+    // Q6_K: fixed-point activation (three padded byte arrays and the group
+    // exponents) after the f32 copy and its sums
+    if (kind == kQ6K) pl.lds_bytes += 3 * ((size_t)K + (size_t)K / 16) + (size_t)(K / 16) * 4;
+    return ok && pl.lds_bytes <= 65536;
 }
 
 // Tile-kernel plan; `extra_lds` bytes of LDS are reserved past the kernel's
@@ -1580,7 +1629,7 @@ static hipError_t launch_mode(Plan &pl, GemvArgs a, int cus, hipStream_t s, cons
     // with 3 against 7.2 us with 4).  The SwiGLU pair doubles a tile's work.
     const int64_t x_bytes = (int64_t)pl.nb * kQK * (is_q8(KIND) ? 1 : 4);
     pl.grid = grid_for(pl, fn2, cus, KIND == kSwiglu ? 2 : (x_bytes <= 16384 ? 3 : 4));
-    if (is_argmax(EPI) && pl.grid > kArgmaxMaxGrid) pl.grid = kArgmaxMaxGrid;   // one workspace slot each
+    if (is_argmax(EPI) && pl.grid > kArgmaxMaxGrid) pl.grid = kArgmaxMaxGrid;
     if constexpr (EPI == kQ8Emit) {
         // a workgroup's rows must fit its LDS row buffer
         const int64_t per = kEmitRows / pl.rows_tile;
@@ -1630,7 +1679,7 @@ static hipError_t launch_per_cu(Kern k, int max_waves, Plan &pl, const GemvArgs 
 {
     const int wmax = wave_kernel_waves((const void *)k, pl.lds_bytes, max_waves);
     int64_t grid = pl.tiles < cus ? pl.tiles : cus;
-    if (grid > kArgmaxMaxGrid) grid = kArgmaxMaxGrid;   // argmax: one workspace slot per workgroup
+    if (grid > kArgmaxMaxGrid) grid = kArgmaxMaxGrid;
     const int64_t per = (pl.tiles + grid - 1) / grid;   // units per workgroup
     pl.grid = (int)grid;
     pl.waves = (int)(per < wmax ? per : wmax);

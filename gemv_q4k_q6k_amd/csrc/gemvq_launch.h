@@ -13,13 +13,13 @@ namespace gemvq {
 constexpr int kMaxThreads = 512;
 constexpr int64_t kMaxK = 32768;
 
-// lm_head_argmax workspace: counters in the first kArgmaxSlot0 bytes (zero
-// between calls), then one 8-byte slot per workgroup for its best key; the
-// argmax launches use at most kArgmaxMaxGrid workgroups.
-constexpr int kArgmaxGroups = 16;
-constexpr size_t kArgmaxSlot0 = 4096;
+// lm_head_argmax workspace: a done counter and the running key, each on a
+// 128-byte line of its own inside the first kArgmaxZeroBytes (zero between
+// calls).  The argmax launches use at most kArgmaxMaxGrid workgroups.
+constexpr size_t kArgmaxKeyOff = 128;
+constexpr size_t kArgmaxZeroBytes = 4096;
 constexpr int kArgmaxMaxGrid = 1024;
-constexpr size_t kArgmaxWsBytes = kArgmaxSlot0 + 8 * (size_t)kArgmaxMaxGrid;
+constexpr size_t kArgmaxWsBytes = kArgmaxZeroBytes + 8 * (size_t)kArgmaxMaxGrid;
 
 // Matrices one multi-output GEMV launch can take; x (f32) must fit in LDS.
 constexpr int kMaxMulti = 4;

@@ -217,18 +217,19 @@ int add_rms_norm_q8(const float *x, const float *r, const float *w, float eps, f
  * from 248,320 f32 logits to a 4-byte token id; memra-engine decode.rs
  * `argmax_token_device_into`: the id stays in a persistent device word).
  * Two stages in one kernel: every workgroup reduces its rows to one (value,
- * index) candidate kept as an order-keeping 64-bit key in its own workspace
- * slot, and the last workgroup to finish (counted through per-group
- * counters) reduces the slots and writes the result (memra-engine decode.rs
- * names the same split, `argmax_partial_f32` + `argmax_final_f32`;
- * qualiaDB's top-1 per block and candidate merge).
+ * index) candidate kept as an order-keeping 64-bit key and merges it into a
+ * running key in the workspace with an atomic max; the last workgroup to
+ * finish (a done counter) reads the running key, writes the result and sets
+ * both words back to zero (memra-engine decode.rs names the same split,
+ * `argmax_partial_f32` + `argmax_final_f32`; qualiaDB's top-1 per block and
+ * candidate merge).
  *   W: Q6_K N x K.  x: float[K].  out_idx: uint32[1].  out_max: float[1] or NULL.
  *   workspace: device memory of at least gemvq_lm_head_argmax_ws_bytes(N, K)
  *   (12,288) bytes, 256-B aligned.  Its first 4096 bytes (the counters)
  *   must be zero before the first call; every call leaves them zero again, so
  *   one workspace serves any number of calls in stream order (also inside a
- *   captured graph).  The rest holds per-workgroup keys and needs no initial
- *   value.  Calls that share a workspace must not run concurrently.
+ *   captured graph).  The rest is reserved and needs no initial value.  Calls
+ *   that share a workspace must not run concurrently.
  */
 int lm_head_argmax(const void *W, const float *x, uint32_t *out_idx, float *out_max,
                    void *workspace, size_t ws_bytes, int64_t N, int64_t K, void *stream);
