@@ -273,15 +273,16 @@ __device__ __forceinline__ void load4(uint32_t (&o)[4], const uint8_t *p)
 // byte offset of its block in it; part u = 2n + (l0 / 16) of the block.
 __device__ __forceinline__ void q6k_load(Q6KRaw &r, const uint8_t *__restrict__ tile, uint32_t off, int u)
 {
-    const uint8_t *blk = tile + off;
+    // one 32-bit lane offset per field from the uniform base, so each load
+    // takes the scalar-base form (no 64-bit address arithmetic per lane)
     const uint32_t n = (uint32_t)(u >> 1), l0 = 16u * (uint32_t)(u & 1);
-    load4(r.a, blk + (64u * n + l0));
-    load4(r.b, blk + (64u * n + 32u + l0));
-    load4(r.h, blk + (128u + 32u * n + l0));
-    const U32x2A2 sc = *(const U32x2A2 *)(blk + (192u + 8u * n));
+    load4(r.a, tile + (off + 64u * n + l0));
+    load4(r.b, tile + (off + 64u * n + 32u + l0));
+    load4(r.h, tile + (off + 128u + 32u * n + l0));
+    const U32x2A2 sc = *(const U32x2A2 *)(tile + (off + 192u + 8u * n));
     r.s[0] = sc.v[0];
     r.s[1] = sc.v[1];
-    r.dbits = *(const uint16_t *)(blk + 208u);
+    r.dbits = *(const uint16_t *)(tile + (off + 208u));
 }
 
 __device__ __forceinline__ void q6k_zero(Q6KRaw &r)

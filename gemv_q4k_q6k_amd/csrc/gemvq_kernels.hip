@@ -781,7 +781,7 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_wave_kernel(Gem
         return (int)(u < units ? u : units);
     };
 
-    auto valid_unit = [&](int u) { return u < u_end && (u < units - 1 || p < last_rows); };
+    auto valid_unit = [&](int u) { return u < u_end - 1 || (u == u_end - 1 && p < last_rows); };
     // unconditional loads, as in gemv_kernel: a unit past the end re-reads
     // the unit `prev` this wave has just processed (still in its CU's cache),
     // an idle lane the unit's first super-block
@@ -870,7 +870,14 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_wave_kernel(Gem
         }
     }
 
-    uint64_t best = 0;
+    // argmax: the running best row of the lane.  Every lane of a row's group
+    // holds the row's value (the reductions end with the same bits in each),
+    // and a lane meets its rows in increasing index order (claims only grow),
+    // so a strictly larger value replaces the best and the first index of a
+    // maximum is kept.  bv starts as NaN (no row yet): the first non-NaN row
+    // is taken; NaN rows and banned rows never are.
+    float bv = __builtin_nanf("");
+    uint32_t bi = 0;
     // keep taking units until every ring slot comes back past the range (the
     // counter only grows, so once one claim is past it every later one is)
     auto active = [&]() {
@@ -895,7 +902,16 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_wave_kernel(Gem
                 float r[2];
 #pragma unroll
                 for (int o = 0; o < OUTS; ++o) r[o] = group_sum(v ? ps[o] : 0.f, a.lanes_row);
-                if (rr == 0 && v) emit_row<KIND, EPI>(a, (int64_t)unit[d] * a.rows_tile + p, r, best, mword[d]);
+                if constexpr (is_argmax(EPI)) {
+                    const uint32_t row = (uint32_t)unit[d] * (uint32_t)a.rows_tile + (uint32_t)p;
+                    bool take = v && !(r[0] <= bv) && r[0] == r[0];
+                    if constexpr (EPI == kArgmaxMasked) take = take && !((mword[d] >> (row & 31)) & 1u);
+                    bv = take ? r[0] : bv;
+                    bi = take ? row : bi;
+                } else {
+                    uint64_t unused = 0;
+                    if (rr == 0 && v) emit_row<KIND, EPI>(a, (int64_t)unit[d] * a.rows_tile + p, r, unused, mword[d]);
+                }
                 uint32_t c = 0;
                 if (lane == 0) c = __hip_atomic_fetch_add(&s_next, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
                 const int done = unit[d];
@@ -908,6 +924,7 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_wave_kernel(Gem
 
     if constexpr (is_argmax(EPI)) {
         // each wave's largest key reaches lane 0, then the workgroup's
+        uint64_t best = bv == bv ? argmax_key(bv, bi) : 0ull;
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) {
             const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)best, off);
