@@ -104,6 +104,39 @@ __device__ __forceinline__ float argmax_key_value(uint64_t k)
 
 __device__ __forceinline__ uint32_t argmax_key_index(uint64_t k) { return ~(uint32_t)k; }
 
+// Largest unsigned value over a fully active wave, returned uniformly: the
+// maximum within each row of 16 lanes by DPP (quad swaps, half-row and row
+// mirrors), then across the four rows by lane reads.  No LDS round trip, so
+// the chain is a few dozen cycles instead of the ~100-cycle latency of each
+// ds_bpermute step of a shuffle tree.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+    v = max(v, dpp_u<0xB1>(v));    // quad_perm [1,0,3,2]
+    v = max(v, dpp_u<0x4E>(v));    // quad_perm [2,3,0,1]
+    v = max(v, dpp_u<0x141>(v));   // row_half_mirror
+    v = max(v, dpp_u<0x140>(v));   // row_mirror
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+    const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+    const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+    return max(max(r0, r1), max(r2, r3));
+}
+
+// Largest argmax key over a fully active wave: the largest high word, then
+// the largest low word among the lanes that hold it.
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t k)
+{
+    const uint32_t hi = wave_max_u32((uint32_t)(k >> 32));
+    const uint32_t lo = wave_max_u32((uint32_t)(k >> 32) == hi ? (uint32_t)k : 0u);
+    return ((uint64_t)hi << 32) | lo;
+}
+
 // Keeps a computed value in a register (stops the compiler from recomputing
 // it inside a loop to save registers).
 __device__ __forceinline__ void pin(float &v) { asm volatile("" : "+v"(v)); }

@@ -349,7 +349,7 @@ __device__ __forceinline__ uint32_t *ws_count(uint8_t *ws) { return (uint32_t *)
 __device__ __forceinline__ uint64_t *ws_key(uint8_t *ws) { return (uint64_t *)(ws + kArgmaxKeyOff); }
 
 // Grid-level argmax without fences: the threads' running keys meet in LDS
-// (one barrier) and wave 0 folds them by shuffle.  Thread 0 then merges the
+// (one barrier) and wave 0 folds them with DPP and lane reads.  Thread 0 then merges the
 // workgroup's key into the running key with a returning atomic max (device
 // scope, so it has been performed before the count below) and counts the
 // workgroup done.  The workgroup whose count completes the grid reads the
@@ -368,13 +368,7 @@ __device__ void argmax_finish(const GemvArgs &a, uint64_t best, int holder, int 
     if (threadIdx.x >= 64) return;   // wave 0 finishes
     uint64_t k = 0;
     for (int h = (int)threadIdx.x; h < holders; h += 64) k = s_key[h] > k ? s_key[h] : k;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)k, off);
-        const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(k >> 32), off);
-        const uint64_t o = ((uint64_t)hi << 32) | lo;
-        k = o > k ? o : k;
-    }
+    k = wave_max_key(k);
     if (threadIdx.x != 0) return;
     if (k) {
         const uint64_t old = __hip_atomic_fetch_max(ws_key(a.ws), k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -925,13 +919,7 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_wave_kernel(Gem
     if constexpr (is_argmax(EPI)) {
         // each wave's largest key reaches lane 0, then the workgroup's
         uint64_t best = bv == bv ? argmax_key(bv, bi) : 0ull;
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)best, off);
-            const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(best >> 32), off);
-            const uint64_t o = ((uint64_t)hi << 32) | lo;
-            best = o > best ? o : best;
-        }
+        best = wave_max_key(best);
         argmax_finish(a, best, lane == 0 ? wave : -1, waves);
     }
 }
@@ -1157,13 +1145,7 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_rows_kernel(Gem
     }
 
     if constexpr (is_argmax(EPI)) {
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)best, off);
-            const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(best >> 32), off);
-            const uint64_t o = ((uint64_t)hi << 32) | lo;
-            best = o > best ? o : best;
-        }
+        best = wave_max_key(best);
         argmax_finish(a, best, lane == 0 ? wave : -1, waves);
     }
 }
