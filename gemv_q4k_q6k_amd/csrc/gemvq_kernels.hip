@@ -941,13 +941,13 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_wave_kernel(Gem
 // As in the wave-unit kernel there is one workgroup per CU, its waves take
 // units from an LDS counter, and the activation is staged in LDS once; the
 // slice of a step is re-read from LDS when a row has several steps.  Each wave
-// runs a pipeline of (unit, step) pairs, two in flight; a row's step sums are
+// runs a pipeline of (unit, step) pairs, one in flight; a row's step sums are
 // added in step order and reduced over its lane group, the same way for every
 // row.
 template <int KIND, int EPI, int MULTI>
 __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_rows_kernel(GemvArgs a)
 {
-    constexpr int kPhase = 2;
+    constexpr int kPhase = 1;   // one (unit, step) in flight per wave, as in the wave-unit kernel (measured faster)
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ uint32_t s_next;   // next unit to hand out, relative to the range
     constexpr int BYTES = Traits<KIND>::kBytes;
