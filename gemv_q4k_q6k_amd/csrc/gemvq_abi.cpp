@@ -87,7 +87,7 @@ size_t gemvq_lm_head_argmax_ws_bytes(int64_t N, int64_t K)
     return gemvq::kArgmaxWsBytes;
 }
 
-int gemvq_tile_geometry(int kind, int64_t N, int64_t K, int64_t out[7])
+int gemvq_tile_geometry(int kind, int64_t N, int64_t K, int64_t out[8])
 {
     if (!out) return GEMVQ_ERR_NULL;
     if (kind < 0 || kind > 7) return GEMVQ_ERR_SHAPE;
@@ -105,6 +105,7 @@ int gemvq_tile_geometry(int kind, int64_t N, int64_t K, int64_t out[7])
     out[4] = pl.x_in_lds;
     out[5] = (int64_t)pl.lds_bytes;
     out[6] = pl.wave_local ? pl.steps : 1;
+    out[7] = (pl.wave_local && !pl.rows_kernel) ? 1 : 0;
     return GEMVQ_OK;
 }
 

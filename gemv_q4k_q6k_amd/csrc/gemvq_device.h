@@ -389,26 +389,28 @@ __device__ __forceinline__ float q6k_dot(const Q6KRaw &r, const Q6KX &x, int u)
     return d * ((t0 + t1) + (t2 + t3));
 }
 
-// Activation slice of a Q6_K part in fixed point (wave-unit kernel).  Group s
-// (x[128n + 32s + l0 + i], i < 16) is held as X_i = rint(x_i * 2^e_s) with e_s
-// = 22 - E, E the binary exponent of the group's largest |x| (so |X_i| <=
-// 2^22 and the rounding error is at most 2^-23 of that largest value).  Each
-// X_i is split into three bytes, X_i = 65536*hi + 256*mid + lo (hi signed,
-// mid and lo unsigned), four elements to a dword, so a group's dot product
-// with the 6-bit quants is three exact integer dot products.  sx[s] is the
-// f32 sum of the group as in Q6KX (a non-finite activation makes it
-// non-finite, and with it every row value).
+// Activation slice of a Q6_K part in fixed point (wave-unit kernel).  The
+// part's 64 values (groups s = 0..3, x[128n + 32s + l0 + i], i < 16) share
+// one scale: X_i = rint(x_i * 2^(22-E)) with E the binary exponent of the
+// part's largest |x|, so |X_i| <= 2^22 and the rounding error is at most
+// 2^-23 of that largest value.  Each X_i is split into three bytes,
+// X_i = 65536*hi + 256*mid + lo (hi signed, mid and lo unsigned), four
+// elements to a dword, so a group's dot product with the 6-bit quants is
+// three exact integer dot products.  m[s] = -32 * sum_s * 2^(22-E) takes the
+// quants' offset off in the scaled domain, and e = E - 22 undoes the scale
+// once per part (a non-finite activation makes m non-finite, and with it
+// every row value).
 struct Q6KFX {
     uint32_t hi[4][4], mid[4][4], lo[4][4];
-    int e[4];        // -e_s: ldexp of an integer dot by e[s] undoes the scaling
-    float sx[4];
+    float m[4];
+    int e;
 };
 
 // Dot product of one Q6_K part against a fixed-point slice: per group, the
 // quant bytes (assembled as in q6k_dot) go through one sdot4 with the signed
 // high bytes and two udot4 with the unsigned middle and low bytes (all sums
-// exact), the three sums are joined in f32 and scaled back by 2^-e_s; the -32
-// offset comes off with the group's f32 sum.
+// exact); the three sums are joined in f32, the offset added, the group
+// scaled by its int8 scale, and the part's sum scaled back by 2^e and d.
 __device__ __forceinline__ float q6k_dot(const Q6KRaw &r, const Q6KFX &x, int u)
 {
     int32_t sh[4];
@@ -438,9 +440,9 @@ __device__ __forceinline__ float q6k_dot(const Q6KRaw &r, const Q6KFX &x, int u)
         // |sh| <= 16*63*64 and sm*256 + sl < 2^27: both convert exactly or
         // within one f32 rounding
         const float v = __builtin_fmaf((float)sh[s], 65536.f, (float)((sm[s] << 8) + sl[s]));
-        t[s] = (float)sc[s] * __builtin_fmaf(-32.f, x.sx[s], __builtin_amdgcn_ldexpf(v, x.e[s]));
+        t[s] = (float)sc[s] * (v + x.m[s]);
     }
-    return d * ((t[0] + t[1]) + (t[2] + t[3]));
+    return d * __builtin_amdgcn_ldexpf((t[0] + t[1]) + (t[2] + t[3]), x.e);
 }
 
 // ------------------------------------------------------------ Q6_K x Q8

@@ -673,20 +673,26 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_kernel(GemvArgs a)
 // give equal bits.
 // Fixed-point activation of the wave-unit Q6_K kernel, in LDS after the
 // 16-element sums (`base`, 16-byte aligned): the high, middle and low byte
-// arrays of X (K bytes each, in the padded layout), then the per-group
-// exponents (K/16 ints).
+// arrays of X (K bytes each, in the padded layout), then the per-part
+// exponents (K/64 ints).
 __device__ __forceinline__ uint32_t fx_bytes_stride(int K) { return lds_pad((uint32_t)K); }
 
-// Group g of the staged f32 activation (16 values in LDS) converted as Q6KFX
-// describes; one thread per group.
-__device__ void fx_stage_group(unsigned char *smem, uint32_t base, const float *sx, int K, int g)
+// Part slot t (K/16 of them; block t >> 4, part (t >> 2) & 3, group t & 3) of
+// the staged f32 activation converted as Q6KFX describes, one thread per
+// group: the four groups of a part sit in one quad of lanes, which share
+// their largest |x| by DPP.  Call with whole quads active.
+__device__ void fx_stage_group(unsigned char *smem, uint32_t base, const float *sx, int K, int t)
 {
+    const int blk = t >> 4, u = (t >> 2) & 3, s = t & 3;
+    const int g = 16 * blk + 8 * (u >> 1) + 2 * s + (u & 1);   // the group's 16-element index
     const float *v = x_at<true>(sx, 16 * g);
     float m = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
-    // scale so that the largest |X| is below 2^22 (m < 2^E); zero and
-    // non-finite groups keep e = 0 (their sum carries a non-finite value)
+    m = fmaxf(m, dpp_f<kDppQuadXor1>(m));
+    m = fmaxf(m, dpp_f<kDppQuadXor2>(m));
+    // scale so that the part's largest |X| is below 2^22 (m < 2^E); zero and
+    // non-finite parts keep scale 1 (their sums carry a non-finite value)
     const int e = (m > 0.f && m <= 3.402823466e38f) ? 22 - __builtin_amdgcn_frexp_expf(m) : 0;
     uint32_t hi[4], mid[4], lo[4];
 #pragma unroll
@@ -708,7 +714,7 @@ __device__ void fx_stage_group(unsigned char *smem, uint32_t base, const float *
     *(u32x4 *)(smem + base + o) = u32x4{hi[0], hi[1], hi[2], hi[3]};
     *(u32x4 *)(smem + base + stride + o) = u32x4{mid[0], mid[1], mid[2], mid[3]};
     *(u32x4 *)(smem + base + 2 * stride + o) = u32x4{lo[0], lo[1], lo[2], lo[3]};
-    ((int *)(smem + base + 3 * stride))[g] = -e;
+    if (s == 0) ((int *)(smem + base + 3 * stride))[t >> 2] = e;
 }
 
 // Lane slice of part u of block b from the staged fixed-point activation.
@@ -717,6 +723,7 @@ __device__ __forceinline__ void fx_load(Q6KFX &xs, const unsigned char *smem, ui
 {
     const int n = u >> 1;
     const uint32_t stride = fx_bytes_stride(K);
+    const int e = ((const int *)(smem + base + 3 * stride))[4 * b + u];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
         const int g = 16 * b + 8 * n + 2 * s + (u & 1);   // 16-element group of the slice's group s
@@ -727,11 +734,11 @@ __device__ __forceinline__ void fx_load(Q6KFX &xs, const unsigned char *smem, ui
         xs.hi[s][0] = h.x; xs.hi[s][1] = h.y; xs.hi[s][2] = h.z; xs.hi[s][3] = h.w;
         xs.mid[s][0] = m.x; xs.mid[s][1] = m.y; xs.mid[s][2] = m.z; xs.mid[s][3] = m.w;
         xs.lo[s][0] = l.x; xs.lo[s][1] = l.y; xs.lo[s][2] = l.z; xs.lo[s][3] = l.w;
-        xs.e[s] = ((const int *)(smem + base + 3 * stride))[g];
-        float t = sums[g];
+        float t = -32.f * __builtin_amdgcn_ldexpf(sums[g], e);
         pin(t);
-        xs.sx[s] = t;
+        xs.m[s] = t;
     }
+    xs.e = -e;
 }
 
 template <int KIND>
@@ -774,24 +781,36 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_wave_kernel(Gem
     const int64_t units = a.tiles;
     const int u_end = (int)units;
     const int last_rows = (int)(a.N - (units - 1) * a.rows_tile);
-    const int64_t unit_stride = (int64_t)a.rows_tile * a.nb * BYTES;
     auto umap = [&](int v) {
         const int sh = a.chunk_shift;
         const int64_t u = ((((int64_t)(v >> sh)) * gridDim.x + blockIdx.x) << sh) | (v & ((1 << sh) - 1));
         return (int)(u < units ? u : units);
     };
 
-    auto valid_unit = [&](int u) { return u < u_end - 1 || (u == u_end - 1 && p < last_rows); };
+    // Rows of unit u start at rbase(u).  On a ragged matrix the last unit is
+    // moved back to end at row N, and its lanes whose row the unit before
+    // already covered are not valid: every lane of every unit then reads
+    // inside the matrix at a lane offset that never changes (only with
+    // N < rows_tile do lanes past N read the unit's first super-block).
+    const bool shift_last = last_rows < a.rows_tile && a.N >= a.rows_tile;
+    const int64_t row_bytes = (int64_t)a.nb * BYTES;
+    auto rbase = [&](int u) -> int64_t {
+        return (shift_last && u == u_end - 1) ? a.N - a.rows_tile : (int64_t)u * a.rows_tile;
+    };
+    auto valid_unit = [&](int u) {
+        return u < u_end - 1 || (u == u_end - 1 && (shift_last ? p >= a.rows_tile - last_rows : p < last_rows));
+    };
+    uint32_t lane_off[STEPS];
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st) lane_off[st] = p < a.N ? (uint32_t)((p * a.nb + b + 16 * st) * BYTES) : 0u;
     // unconditional loads, as in gemv_kernel: a unit past the end re-reads
-    // the unit `prev` this wave has just processed (still in its CU's cache),
-    // an idle lane the unit's first super-block
+    // the unit `prev` this wave has just processed (still in its CU's cache)
     auto fetch = [&](RawSet<KIND> (&rs)[STEPS], int u, int prev) {
         const int uu = u < u_end ? u : prev;
-        const bool v = valid_unit(u);
-        const int64_t ub = (int64_t)uu * unit_stride;
+        const int64_t ub = rbase(uu) * row_bytes;
 #pragma unroll
         for (int st = 0; st < STEPS; ++st) {
-            const uint32_t off = v ? (uint32_t)((p * a.nb + b + 16 * st) * BYTES) : 0u;
+            const uint32_t off = lane_off[st];
             if constexpr (is_q6(KIND)) {
                 q6k_load(rs[st].r[0], a.W + ub, off, part);
             } else {
@@ -821,7 +840,7 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_wave_kernel(Gem
     uint32_t mword[kPhase];
     auto fetch_mask = [&](int d, int u, int prev) {
         if constexpr (EPI == kArgmaxMasked) {
-            int64_t row = (int64_t)(u < u_end ? u : prev) * a.rows_tile + p;
+            int64_t row = rbase(u < u_end ? u : prev) + p;
             row = row < a.N ? row : a.N - 1;
             mword[d] = a.mask[row >> 5];
         } else {
@@ -854,10 +873,10 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_wave_kernel(Gem
         const float *sx = (const float *)smem;
         float *ssum = (float *)(smem + lds_pad(4u * (uint32_t)K));
         const uint32_t fx_base = lds_pad(4u * (uint32_t)K) + 4u * (uint32_t)(K / 16);
-        for (int g = tid; g < K / 16; g += blockDim.x) {
-            ssum[g] = sum16(x_at<true>(sx, 16 * g));
-            if constexpr (KIND == kQ6K) fx_stage_group(smem, fx_base, sx, K, g);
-        }
+        for (int g = tid; g < K / 16; g += blockDim.x) ssum[g] = sum16(x_at<true>(sx, 16 * g));
+        // K/16 is a multiple of 16, so whole quads take part slots together
+        if constexpr (KIND == kQ6K)
+            for (int t = tid; t < K / 16; t += blockDim.x) fx_stage_group(smem, fx_base, sx, K, t);
         __syncthreads();
 #pragma unroll
         for (int st = 0; st < STEPS; ++st) {
@@ -903,14 +922,14 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_wave_kernel(Gem
 #pragma unroll
                 for (int o = 0; o < OUTS; ++o) r[o] = group_sum(v ? ps[o] : 0.f, a.lanes_row);
                 if constexpr (is_argmax(EPI)) {
-                    const uint32_t row = (uint32_t)unit[d] * (uint32_t)a.rows_tile + (uint32_t)p;
+                    const uint32_t row = (uint32_t)(rbase(unit[d]) + p);
                     bool take = v && !(r[0] <= bv) && r[0] == r[0];
                     if constexpr (EPI == kArgmaxMasked) take = take && !((mword[d] >> (row & 31)) & 1u);
                     bv = take ? r[0] : bv;
                     bi = take ? row : bi;
                 } else {
                     uint64_t unused = 0;
-                    if (rr == 0 && v) emit_row<KIND, EPI>(a, (int64_t)unit[d] * a.rows_tile + p, r, unused, mword[d]);
+                    if (rr == 0 && v) emit_row<KIND, EPI>(a, rbase(unit[d]) + p, r, unused, mword[d]);
                 }
                 uint32_t c = 0;
                 if (lane == 0) c = __hip_atomic_fetch_add(&s_next, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);

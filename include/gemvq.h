@@ -299,10 +299,13 @@ int gemvq_q6k_q8_isums(const void *W, const int8_t *xq, int32_t *isums,
  * launch uses as many as fit on a CU): with out[6] = 1 a tile is
  * 64 / (4*K/256) rows side by side; with out[6] = 2 (Q4_K x Q8 at
  * K = 8192) it is one row whose lane l takes quarter l%4 of super-blocks
- * l/4 and 16 + l/4.
+ * l/4 and 16 + l/4.  out[7] = 1 for the wave-unit kernel: there a lane's
+ * byte offset within a unit never changes, and on a ragged matrix the last
+ * unit starts at row N - rows (its lanes whose rows the unit before covered
+ * are idle); with N < rows, lanes past N read the unit's first super-block.
  * Returns GEMVQ_ERR_SHAPE for shapes the GEMV entry points reject.
  */
-int gemvq_tile_geometry(int kind, int64_t N, int64_t K, int64_t out[7]);
+int gemvq_tile_geometry(int kind, int64_t N, int64_t K, int64_t out[8]);
 
 /* Static description of a status code (never NULL). */
 const char *gemvq_strerror(int status);

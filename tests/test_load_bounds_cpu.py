@@ -28,9 +28,26 @@ W_BASE = 1 << 20          # any dword-aligned matrix address
 
 def lane_offsets(geo, nb, B, N):
     """(offsets(t) -> list over steps of per-lane byte offsets within unit or
-    tile t, quarter index per lane, bytes per unit or tile)."""
+    tile t, quarter index per lane, base(t) -> byte offset of unit or tile t
+    in the matrix)."""
     P, tiles = geo["rows_tile"], geo["tiles"]
     last_rows = N - (tiles - 1) * P
+    if geo.get("wave_unit"):
+        # wave-unit kernel: fixed lane offsets (lanes past N, only when
+        # N < P, read the first super-block); a ragged last unit starts at
+        # row N - P
+        group = 64 // P
+        lane = np.arange(64)
+        p, rr = lane // group, lane % group
+        b, c = rr >> 2, rr & 3
+        shift = last_rows < P and N >= P
+
+        def offsets_w(t):
+            return [np.where(p < N, (p * nb + b + 16 * st) * B, 0) for st in range(geo["steps"])]
+
+        def base_w(t):
+            return ((N - P) if (shift and t == tiles - 1) else t * P) * nb * B
+        return offsets_w, c, base_w
     if geo["wave_local"]:
         group = 64 // P
         lane = np.arange(64)
@@ -50,19 +67,19 @@ def lane_offsets(geo, nb, B, N):
             valid = (p < P) & ((t < tiles - 1) | (p < last_rows)) & (blk < nb)
             out.append(np.where(valid, (p * nb + blk) * B, 0))
         return out
-    return offsets, c, P * nb * B
+    return offsets, c, lambda t: t * P * nb * B
 
 
 def q6k_windows(N, K, tiles_to_check=None, kind=gq.KIND_Q6K):
     """(lowest byte read, one past the highest, end of the matrix)."""
     nb = K // 256
     geo = gq.tile_geometry(kind, N, K)
-    offsets, u, stride = lane_offsets(geo, nb, 210, N)
+    offsets, u, base = lane_offsets(geo, nb, 210, N)
     n, l0 = u >> 1, 16 * (u & 1)
     lo, hi = None, None
     ts = range(geo["tiles"]) if tiles_to_check is None else tiles_to_check
     for t in ts:
-        tile = W_BASE + t * stride
+        tile = W_BASE + base(t)
         for off in offsets(t):
             blk = tile + off
             assert (blk % 2 == 0).all()
@@ -81,11 +98,11 @@ def q6k_windows(N, K, tiles_to_check=None, kind=gq.KIND_Q6K):
 def q4k_windows(kind, N, K, tiles_to_check=None):
     nb = K // 256
     geo = gq.tile_geometry(kind, N, K)
-    offsets, c, stride = lane_offsets(geo, nb, 144, N)
+    offsets, c, base = lane_offsets(geo, nb, 144, N)
     lo, hi = None, None
     ts = range(geo["tiles"]) if tiles_to_check is None else tiles_to_check
     for t in ts:
-        tile = W_BASE + t * stride
+        tile = W_BASE + base(t)
         for off in offsets(t):
             l_ = tile + off.min()
             h_ = tile + max((off + 16).max(), (off + 32 * c + 48).max())
