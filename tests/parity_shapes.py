@@ -6,13 +6,13 @@ one parity case of every kind that can take it.
 """
 import gemv_q4k_q6k_amd as gq
 
-SMALL_Q4K = [(1, 256), (5, 256), (1000, 1024), (333, 2560), (77, 8192), (129, 9728), (17, 4352),
+SMALL_Q4K = [(1, 256), (5, 256), (1000, 1024), (1001, 1024), (3, 1024), (333, 2560), (77, 8192), (129, 9728), (17, 4352),
              (3, 32768), (70, 512), (130, 2048), (31, 4096), (9, 768), (6000, 2560), (5, 12288)]
-SMALL_Q6K = [(1, 256), (4, 256), (100, 768), (1000, 1024), (257, 9728), (33, 1280), (21, 2560),
+SMALL_Q6K = [(1, 256), (4, 256), (100, 768), (1000, 1024), (1001, 1024), (1003, 1024), (3, 1024), (250, 512), (257, 9728), (33, 1280), (21, 2560),
              (3, 32768), (65, 2048), (5, 16384)]
-SMALL_SWIGLU = [(1, 256), (100, 1024), (333, 2560), (50, 8192), (7, 16384)]
-SMALL_Q8 = [(1, 256), (1000, 1024), (333, 2560), (77, 8192), (50, 9728), (3, 32768)]
-SMALL_Q6K_Q8 = [(1, 256), (100, 768), (1000, 1024), (333, 2560), (257, 9728), (3, 32768), (5, 16384),
+SMALL_SWIGLU = [(1, 256), (100, 1024), (102, 1024), (333, 2560), (50, 8192), (7, 16384)]
+SMALL_Q8 = [(1, 256), (1000, 1024), (1003, 1024), (333, 2560), (77, 8192), (50, 9728), (3, 32768)]
+SMALL_Q6K_Q8 = [(1, 256), (100, 768), (1000, 1024), (1001, 1024), (333, 2560), (257, 9728), (3, 32768), (5, 16384),
                 (65, 2048), (9, 4352)]
 
 

@@ -301,6 +301,33 @@ def test_lm_head_constructed_ties(dev):
     assert int(gq().lm_head_argmax(up(Wsame, dev), dx, N, K, ws).item()) == 0
 
 
+def test_lm_head_ragged_last_unit(dev):
+    """Wave-unit lm_head on N = 4k + 1 rows (K = 1024, 4 rows per unit): the
+    last unit is moved back to rows N-4 .. N-1, and of those only row N-1 is
+    new.  A maximum (or a tie) among the re-read rows N-4 .. N-2 must be
+    found once, at its first index, and the new last row must still count."""
+    N, K = 20001, 1024
+    assert gq().tile_geometry(gq().KIND_Q6K, N, K)["wave_unit"] == 1
+    W, x = synth.c3_inputs(5, N=N)
+    ws = _ws(dev, N, K)
+    dx = up(x, dev)
+    top = oracle.argmax_first(oracle.q6k_gemv(W, x, N, K))
+    for pos in ([N - 2], [N - 1], [N - 3, N - 1], [N - 4, N - 2], [N - 5, N - 1]):
+        Wt = W.copy()
+        for q in pos:
+            Wt[q] = W[top]
+        expect = min(pos + [top])
+        idx = int(gq().lm_head_argmax(up(Wt, dev), dx, N, K, ws).item())
+        assert idx == expect, (pos, idx, expect)
+        # and without the original: the planted rows alone
+        Wt[top] = W[0] if top != 0 else W[1]
+        if top not in pos:
+            yt = oracle.q6k_gemv(Wt, x, N, K)
+            if oracle.argmax_first(yt) in pos:
+                idx = int(gq().lm_head_argmax(up(Wt, dev), dx, N, K, ws).item())
+                assert idx == min(pos), (pos, idx)
+
+
 def _q6k_row_with_d(row, nb, dbits):
     row = row.copy().reshape(nb, 210)
     row[:, 208] = dbits & 0xFF
