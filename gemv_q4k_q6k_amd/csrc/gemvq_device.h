@@ -236,6 +236,54 @@ __device__ __forceinline__ float q4k_dot(const Q4KRaw &r, const Q4KX &x, int c)
     return (dl * qxl - ml * x.sxl) + (dh * qxh - mh * x.sxh);
 }
 
+// Activation slice of a Q4_K part in fixed point (row-stream kernel): the
+// part's 64 values (x[256b + 64c + i], i < 64: the low sub-block's 32, then
+// the high one's) share one scale, X_i = rint(x_i * 2^(22-E)) with E the
+// binary exponent of the part's largest |x| (|X_i| <= 2^22, rounding error
+// at most 2^-23 of that value), split into a signed high byte and unsigned
+// middle and low bytes, four elements to a dword (dwords 0..7 low sub-block,
+// 8..15 high).  e = E - 22 undoes the scale; sxl and sxh are the f32 sums
+// of the two sub-blocks for the min term.
+struct Q4KFX {
+    uint32_t hi[16], mid[16], lo[16];
+    float sxl, sxh;
+    int e;
+};
+
+// Dot product of one Q4_K part against a fixed-point slice: the nibbles of
+// each quant dword (low nibbles: the low sub-block, high nibbles: the high
+// one) go through one sdot4 with the signed high bytes and two udot4 with the
+// unsigned middle and low bytes, exact in integers; each sub-block's three
+// sums are joined in f32, scaled by d*sc and back by 2^e, and the min term is
+// taken with the f32 sums.
+__device__ __forceinline__ float q4k_dot(const Q4KRaw &r, const Q4KFX &x, int c)
+{
+    uint32_t sc0, sc1, m0, m1;
+    q4k_scales(r.hdr, c, sc0, sc1, m0, m1);
+    const float d = half_lo(r.hdr.x);
+    const float dmin = half_hi(r.hdr.x);
+    const uint32_t w[8] = {r.q0.x, r.q0.y, r.q0.z, r.q0.w, r.q1.x, r.q1.y, r.q1.z, r.q1.w};
+    int32_t lh = 0, hh = 0;
+    uint32_t lm = 0u, ll = 0u, hm = 0u, hl = 0u;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const uint32_t qn = w[k] & 0x0F0F0F0Fu;           // low nibbles: weights 4k..4k+3 of the low sub-block
+        const uint32_t qm = (w[k] >> 4) & 0x0F0F0F0Fu;    // high nibbles: the same of the high sub-block
+        lh = __builtin_amdgcn_sdot4((int)qn, (int)x.hi[k], lh, false);
+        lm = __builtin_amdgcn_udot4(qn, x.mid[k], lm, false);
+        ll = __builtin_amdgcn_udot4(qn, x.lo[k], ll, false);
+        hh = __builtin_amdgcn_sdot4((int)qm, (int)x.hi[8 + k], hh, false);
+        hm = __builtin_amdgcn_udot4(qm, x.mid[8 + k], hm, false);
+        hl = __builtin_amdgcn_udot4(qm, x.lo[8 + k], hl, false);
+    }
+    // |lh| <= 32*15*64 and lm*256 + ll < 2^25: exact or one f32 rounding
+    const float ql = __builtin_fmaf((float)lh, 65536.f, (float)((lm << 8) + ll));
+    const float qh = __builtin_fmaf((float)hh, 65536.f, (float)((hm << 8) + hl));
+    const float dl = d * (float)sc0, dh = d * (float)sc1;
+    const float ml = dmin * (float)m0, mh = dmin * (float)m1;
+    return __builtin_amdgcn_ldexpf(dl * ql + dh * qh, x.e) - (ml * x.sxl + mh * x.sxh);
+}
+
 // ------------------------------------------------------------ Q4_K x Q8
 
 // Q8 activation slice of a Q4_K part: 32 int8 for each of sub-blocks 2c and

@@ -85,6 +85,10 @@ template <> struct XSlice<kQ6KQ8> { Q6Q8X v; };
 struct FXSlice { Q6KFX v; };
 template <int KIND> struct WaveSlice { using T = XSlice<KIND>; };
 template <> struct WaveSlice<kQ6K> { using T = FXSlice; };
+// The row-stream kernel holds f32 Q4_K activations in fixed point (Q4KFX).
+struct FX4Slice { Q4KFX v; };
+template <int KIND> struct RowsSlice { using T = XSlice<KIND>; };
+template <> struct RowsSlice<kQ4K> { using T = FX4Slice; };
 
 // Layout of the activation staged in LDS: 16 bytes of padding after every
 // 256 bytes.  A lane's slice is 64 consecutive bytes (Q8) or 64 consecutive
@@ -949,6 +953,74 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_wave_kernel(Gem
     }
 }
 
+// Fixed-point activation of the row-stream Q4_K kernel, in LDS: the high,
+// middle and low byte arrays of X (K bytes each, padded layout), then the
+// 16-element f32 sums (K/16), then the per-part exponents (K/64 ints).
+__device__ __forceinline__ uint32_t fx4_sums_off(int K) { return 3u * lds_pad((uint32_t)K); }
+__device__ __forceinline__ uint32_t fx4_exps_off(int K) { return fx4_sums_off(K) + 4u * (uint32_t)(K / 16); }
+
+// Group g (16 values v, in registers) of the activation: its f32 sum (added
+// in index order, as sum16 does) and its fixed-point bytes; the four groups
+// of a part sit in one quad of lanes and share their largest |x| by DPP.
+// Call with whole quads active.
+__device__ void fx4_stage_group(unsigned char *smem, int K, int g, const float (&v)[16])
+{
+    float t = 0.f, m = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        t += v[i];
+        m = fmaxf(m, fabsf(v[i]));
+    }
+    ((float *)(smem + fx4_sums_off(K)))[g] = t;
+    m = fmaxf(m, dpp_f<kDppQuadXor1>(m));
+    m = fmaxf(m, dpp_f<kDppQuadXor2>(m));
+    const int e = (m > 0.f && m <= 3.402823466e38f) ? 22 - __builtin_amdgcn_frexp_expf(m) : 0;
+    uint32_t hi[4], mid[4], lo[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        int X[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) X[j] = (int)rintf(__builtin_amdgcn_ldexpf(v[4 * k + j], e));
+        const uint32_t p01 = __builtin_amdgcn_perm((uint32_t)X[1], (uint32_t)X[0], 0x05010400u);
+        const uint32_t p23 = __builtin_amdgcn_perm((uint32_t)X[3], (uint32_t)X[2], 0x05010400u);
+        const uint32_t r01 = __builtin_amdgcn_perm((uint32_t)X[1], (uint32_t)X[0], 0x07030602u);
+        const uint32_t r23 = __builtin_amdgcn_perm((uint32_t)X[3], (uint32_t)X[2], 0x07030602u);
+        lo[k] = __builtin_amdgcn_perm(p23, p01, 0x05040100u);
+        mid[k] = __builtin_amdgcn_perm(p23, p01, 0x07060302u);
+        hi[k] = __builtin_amdgcn_perm(r23, r01, 0x05040100u);
+    }
+    const uint32_t stride = lds_pad((uint32_t)K);
+    const uint32_t o = lds_pad(16u * (uint32_t)g);
+    *(u32x4 *)(smem + o) = u32x4{hi[0], hi[1], hi[2], hi[3]};
+    *(u32x4 *)(smem + stride + o) = u32x4{mid[0], mid[1], mid[2], mid[3]};
+    *(u32x4 *)(smem + 2 * stride + o) = u32x4{lo[0], lo[1], lo[2], lo[3]};
+    if ((g & 3) == 0) ((int *)(smem + fx4_exps_off(K)))[g >> 2] = e;
+}
+
+// Lane slice of part c of block b from the staged fixed-point activation.
+__device__ __forceinline__ void fx4_load(Q4KFX &xs, const unsigned char *smem, int K, int b, int c)
+{
+    const uint32_t stride = lds_pad((uint32_t)K);
+    const int P = 4 * b + c;   // the part's 64 values start at element 64P
+    const uint32_t o = lds_pad(64u * (uint32_t)P);   // 64 bytes inside one padded 256-byte span
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const u32x4 h = *(const u32x4 *)(smem + o + 16 * q);
+        const u32x4 m = *(const u32x4 *)(smem + stride + o + 16 * q);
+        const u32x4 l = *(const u32x4 *)(smem + 2 * stride + o + 16 * q);
+        xs.hi[4 * q] = h.x; xs.hi[4 * q + 1] = h.y; xs.hi[4 * q + 2] = h.z; xs.hi[4 * q + 3] = h.w;
+        xs.mid[4 * q] = m.x; xs.mid[4 * q + 1] = m.y; xs.mid[4 * q + 2] = m.z; xs.mid[4 * q + 3] = m.w;
+        xs.lo[4 * q] = l.x; xs.lo[4 * q + 1] = l.y; xs.lo[4 * q + 2] = l.z; xs.lo[4 * q + 3] = l.w;
+    }
+    const float *sums = (const float *)(smem + fx4_sums_off(K));
+    float sl = sums[4 * P] + sums[4 * P + 1], sh = sums[4 * P + 2] + sums[4 * P + 3];
+    pin(sl);
+    pin(sh);
+    xs.sxl = sl;
+    xs.sxh = sh;
+    xs.e = -((const int *)(smem + fx4_exps_off(K)))[P];
+}
+
 // ---------------------------------------------------- row-stream kernel
 
 // Every other shape (K/256 not a power of two up to 16, or more than 16
@@ -1048,12 +1120,29 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_rows_kernel(Gem
         return r;
     };
 
+    // f32 Q4_K takes the activation in fixed point (Q4KFX): each thread
+    // loads the 16 values of group tid first, and converts them after the
+    // first weight loads are out
+    constexpr bool kFx = KIND == kQ4K;
+    float xg[16];
+    if constexpr (kFx) {
+        if (tid < K / 16) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 f = *(const float4 *)(a.x + 16 * tid + 4 * q);
+                xg[4 * q] = f.x;
+                xg[4 * q + 1] = f.y;
+                xg[4 * q + 2] = f.z;
+                xg[4 * q + 3] = f.w;
+            }
+        }
+    }
     // activation loads first
-    constexpr int kXRegs = is_q8(KIND) ? 1 : 2;
+    constexpr int kXRegs = kFx ? 0 : (is_q8(KIND) ? 1 : 2);
     const int xstep = is_q8(KIND) ? 16 : 4;
     const int esz = is_q8(KIND) ? 1 : 4;
     const uint8_t *src = is_q8(KIND) ? (const uint8_t *)a.xq : (const uint8_t *)a.x;
-    u32x4 xr[kXRegs];
+    u32x4 xr[kXRegs > 0 ? kXRegs : 1];
 #pragma unroll
     for (int r = 0; r < kXRegs; ++r) {
         const int i = (tid + r * (int)blockDim.x) * xstep;
@@ -1092,26 +1181,47 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_rows_kernel(Gem
         advance();
     }
 
+    if constexpr (kFx) {
+        // K/16 is a multiple of 16 and blockDim of 64, so whole quads convert
+        // together
+        if (tid < K / 16) fx4_stage_group(smem, K, tid, xg);
+        for (int g = tid + (int)blockDim.x; g < K / 16; g += blockDim.x) {
+            float v[16];
 #pragma unroll
-    for (int r = 0; r < kXRegs; ++r) {
-        const int i = (tid + r * (int)blockDim.x) * xstep;
-        if (i < K) *(u32x4 *)(smem + lds_pad((uint32_t)(i * esz))) = xr[r];
+            for (int q = 0; q < 4; ++q) {
+                const float4 f = *(const float4 *)(a.x + 16 * g + 4 * q);
+                v[4 * q] = f.x;
+                v[4 * q + 1] = f.y;
+                v[4 * q + 2] = f.z;
+                v[4 * q + 3] = f.w;
+            }
+            fx4_stage_group(smem, K, g, v);
+        }
+        __syncthreads();
+    } else {
+#pragma unroll
+        for (int r = 0; r < kXRegs; ++r) {
+            const int i = (tid + r * (int)blockDim.x) * xstep;
+            if (i < K) *(u32x4 *)(smem + lds_pad((uint32_t)(i * esz))) = xr[r];
+        }
+        for (int i = (tid + kXRegs * (int)blockDim.x) * xstep; i < K; i += (int)blockDim.x * xstep)
+            *(u32x4 *)(smem + lds_pad((uint32_t)(i * esz))) = *(const u32x4 *)(src + (size_t)i * esz);
+        __syncthreads();
     }
-    for (int i = (tid + kXRegs * (int)blockDim.x) * xstep; i < K; i += (int)blockDim.x * xstep)
-        *(u32x4 *)(smem + lds_pad((uint32_t)(i * esz))) = *(const u32x4 *)(src + (size_t)i * esz);
-    __syncthreads();
     const float *sx = (const float *)smem;
     const float *ssum = (const float *)(smem + lds_pad(4u * (uint32_t)K));
-    if constexpr (!is_q8(KIND)) {
+    if constexpr (!is_q8(KIND) && !kFx) {
         float *w = (float *)ssum;
         for (int g = tid; g < K / 16; g += blockDim.x) w[g] = sum16(x_at<true>(sx, 16 * g));
         __syncthreads();
     }
-    XSlice<KIND> xs;
+    typename RowsSlice<KIND>::T xs;
     auto slice = [&](int st) {
         const int c = block_of(st);
         const int cb = c >= 0 ? c : 0;   // idle lanes read any valid slice
-        if constexpr (is_q8(KIND)) {
+        if constexpr (kFx) {
+            fx4_load(xs.v, smem, K, cb, part);
+        } else if constexpr (is_q8(KIND)) {
             load_x<true>(xs.v, (const int8_t *)smem, a.xd, cb, part);
             finish_x(xs.v);
         } else {
@@ -1477,7 +1587,12 @@ static bool plan_rows(Plan &pl, int64_t N, int64_t K, int kind)
     int g = 4;
     while (g < 4 * pl.nb && g < 64) g *= 2;
     pl.lanes_row = g;   // lanes per row: a power of two holding min(nb, 16) super-blocks
-    return finish_wave_plan(pl, N, K, kind);
+    if (kind != kQ4K) return finish_wave_plan(pl, N, K, kind);
+    finish_wave_plan(pl, N, K, kind);
+    // f32 Q4_K: fixed-point activation (three padded byte arrays, the
+    // 16-element sums and the part exponents) instead of the f32 copy
+    pl.lds_bytes = 3 * ((size_t)K + (size_t)K / 16) + (size_t)(K / 16) * 4 + (size_t)(K / 64) * 4;
+    return pl.lds_bytes <= 65536;
 }
 
 // Plan of a wave-unit or row-stream launch (every row reduced inside one

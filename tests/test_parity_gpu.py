@@ -383,7 +383,12 @@ def test_swiglu_c4_layer(dev):
 
 
 def test_swiglu_gate_equals_up(dev):
-    N, K = 512, 2560
+    # a shape on which q4k_gemv runs the tile kernel, as swiglu_gemv does, so
+    # g is summed with the same arithmetic (the row-stream kernel takes the
+    # activation in fixed point)
+    N, K = 6400, 2560
+    assert gq().tile_geometry(gq().KIND_Q4K, N, K)["wave_local"] == 0
+    assert gq().tile_geometry(gq().KIND_SWIGLU, N, K)["wave_local"] == 0
     r = synth.rng_for(11)
     Wg = synth.q4k_weights(r, N, K)
     x = synth.activation(r, K)
