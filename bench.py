@@ -255,8 +255,9 @@ def breakdown(gq, sets, v, reps=24):
         return [t] + [t.clone() for _ in range(n - 1)]
 
     def timeit(name, fn, ws, nbytes):
-        # ws: list of per-copy weight tuples
-        for r in range(2):
+        # ws: list of per-copy weight tuples; every copy is touched twice
+        # before the capture (first touches of fresh copies are slower)
+        for r in range(2 * len(ws)):
             fn(ws[r % len(ws)])
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
