@@ -89,6 +89,10 @@ template <> struct WaveSlice<kQ6K> { using T = FXSlice; };
 struct FX4Slice { Q4KFX v; };
 template <int KIND> struct RowsSlice { using T = XSlice<KIND>; };
 template <> struct RowsSlice<kQ4K> { using T = FX4Slice; };
+// The tile kernel holds Q6_K activations in fixed point (Q6KFX) when it
+// stages them in LDS.
+template <int KIND, bool FX> struct TileSlice { using T = XSlice<KIND>; };
+template <> struct TileSlice<kQ6K, true> { using T = FXSlice; };
 
 // Layout of the activation staged in LDS: 16 bytes of padding after every
 // 256 bytes.  A lane's slice is 64 consecutive bytes (Q8) or 64 consecutive
@@ -468,6 +472,182 @@ __device__ void q8_emit_finish(const GemvArgs &a, const float *s_h, int64_t r0, 
 
 // ------------------------------------------------------------------ kernel
 
+// Fixed-point activation of the row-stream and tile kernels, in LDS: the high,
+// middle and low byte arrays of X (K bytes each, padded layout), then the
+// 16-element f32 sums (K/16), then the per-part exponents (K/64 ints).
+__device__ __forceinline__ uint32_t fx4_sums_off(int K) { return 3u * lds_pad((uint32_t)K); }
+__device__ __forceinline__ uint32_t fx4_exps_off(int K) { return fx4_sums_off(K) + 4u * (uint32_t)(K / 16); }
+
+// Group g (16 values v, in registers) of the activation: its f32 sum (added
+// in index order, as sum16 does) and its fixed-point bytes; the four groups
+// of a part sit in one quad of lanes and share their largest |x| by DPP.
+// Call with whole quads active.
+__device__ void fx4_stage_group(unsigned char *smem, int K, int g, const float (&v)[16])
+{
+    float t = 0.f, m = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        t += v[i];
+        m = fmaxf(m, fabsf(v[i]));
+    }
+    ((float *)(smem + fx4_sums_off(K)))[g] = t;
+    m = fmaxf(m, dpp_f<kDppQuadXor1>(m));
+    m = fmaxf(m, dpp_f<kDppQuadXor2>(m));
+    const int e = (m > 0.f && m <= 3.402823466e38f) ? 22 - __builtin_amdgcn_frexp_expf(m) : 0;
+    uint32_t hi[4], mid[4], lo[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        int X[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) X[j] = (int)rintf(__builtin_amdgcn_ldexpf(v[4 * k + j], e));
+        const uint32_t p01 = __builtin_amdgcn_perm((uint32_t)X[1], (uint32_t)X[0], 0x05010400u);
+        const uint32_t p23 = __builtin_amdgcn_perm((uint32_t)X[3], (uint32_t)X[2], 0x05010400u);
+        const uint32_t r01 = __builtin_amdgcn_perm((uint32_t)X[1], (uint32_t)X[0], 0x07030602u);
+        const uint32_t r23 = __builtin_amdgcn_perm((uint32_t)X[3], (uint32_t)X[2], 0x07030602u);
+        lo[k] = __builtin_amdgcn_perm(p23, p01, 0x05040100u);
+        mid[k] = __builtin_amdgcn_perm(p23, p01, 0x07060302u);
+        hi[k] = __builtin_amdgcn_perm(r23, r01, 0x05040100u);
+    }
+    const uint32_t stride = lds_pad((uint32_t)K);
+    const uint32_t o = lds_pad(16u * (uint32_t)g);
+    *(u32x4 *)(smem + o) = u32x4{hi[0], hi[1], hi[2], hi[3]};
+    *(u32x4 *)(smem + stride + o) = u32x4{mid[0], mid[1], mid[2], mid[3]};
+    *(u32x4 *)(smem + 2 * stride + o) = u32x4{lo[0], lo[1], lo[2], lo[3]};
+    if ((g & 3) == 0) ((int *)(smem + fx4_exps_off(K)))[g >> 2] = e;
+}
+
+// Lane slice of part c of block b from the staged fixed-point activation.
+__device__ __forceinline__ void fx4_load(Q4KFX &xs, const unsigned char *smem, int K, int b, int c)
+{
+    const uint32_t stride = lds_pad((uint32_t)K);
+    const int P = 4 * b + c;   // the part's 64 values start at element 64P
+    const uint32_t o = lds_pad(64u * (uint32_t)P);   // 64 bytes inside one padded 256-byte span
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const u32x4 h = *(const u32x4 *)(smem + o + 16 * q);
+        const u32x4 m = *(const u32x4 *)(smem + stride + o + 16 * q);
+        const u32x4 l = *(const u32x4 *)(smem + 2 * stride + o + 16 * q);
+        xs.hi[4 * q] = h.x; xs.hi[4 * q + 1] = h.y; xs.hi[4 * q + 2] = h.z; xs.hi[4 * q + 3] = h.w;
+        xs.mid[4 * q] = m.x; xs.mid[4 * q + 1] = m.y; xs.mid[4 * q + 2] = m.z; xs.mid[4 * q + 3] = m.w;
+        xs.lo[4 * q] = l.x; xs.lo[4 * q + 1] = l.y; xs.lo[4 * q + 2] = l.z; xs.lo[4 * q + 3] = l.w;
+    }
+    const float *sums = (const float *)(smem + fx4_sums_off(K));
+    float sl = sums[4 * P] + sums[4 * P + 1], sh = sums[4 * P + 2] + sums[4 * P + 3];
+    pin(sl);
+    pin(sh);
+    xs.sxl = sl;
+    xs.sxh = sh;
+    xs.e = -((const int *)(smem + fx4_exps_off(K)))[P];
+}
+
+// The same layout for Q6_K parts (tile kernel): part slot t (block t >> 4,
+// part (t >> 2) & 3, group t & 3 of the part) is 16-element group g of the
+// activation; the exponent sits at the part's index 4*block + part.  One
+// thread per slot, values in registers, whole quads active.
+__device__ __forceinline__ int fx6_group_of_slot(int t)
+{
+    const int blk = t >> 4, u = (t >> 2) & 3, sg = t & 3;
+    return 16 * blk + 8 * (u >> 1) + 2 * sg + (u & 1);
+}
+
+__device__ void fx6_stage_slot(unsigned char *smem, int K, int t, const float (&v)[16])
+{
+    const int g = fx6_group_of_slot(t);
+    float sum = 0.f, m = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        sum += v[i];
+        m = fmaxf(m, fabsf(v[i]));
+    }
+    ((float *)(smem + fx4_sums_off(K)))[g] = sum;
+    m = fmaxf(m, dpp_f<kDppQuadXor1>(m));
+    m = fmaxf(m, dpp_f<kDppQuadXor2>(m));
+    const int e = (m > 0.f && m <= 3.402823466e38f) ? 22 - __builtin_amdgcn_frexp_expf(m) : 0;
+    uint32_t hi[4], mid[4], lo[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        int X[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) X[j] = (int)rintf(__builtin_amdgcn_ldexpf(v[4 * k + j], e));
+        const uint32_t p01 = __builtin_amdgcn_perm((uint32_t)X[1], (uint32_t)X[0], 0x05010400u);
+        const uint32_t p23 = __builtin_amdgcn_perm((uint32_t)X[3], (uint32_t)X[2], 0x05010400u);
+        const uint32_t r01 = __builtin_amdgcn_perm((uint32_t)X[1], (uint32_t)X[0], 0x07030602u);
+        const uint32_t r23 = __builtin_amdgcn_perm((uint32_t)X[3], (uint32_t)X[2], 0x07030602u);
+        lo[k] = __builtin_amdgcn_perm(p23, p01, 0x05040100u);
+        mid[k] = __builtin_amdgcn_perm(p23, p01, 0x07060302u);
+        hi[k] = __builtin_amdgcn_perm(r23, r01, 0x05040100u);
+    }
+    const uint32_t stride = lds_pad((uint32_t)K);
+    const uint32_t o = lds_pad(16u * (uint32_t)g);
+    *(u32x4 *)(smem + o) = u32x4{hi[0], hi[1], hi[2], hi[3]};
+    *(u32x4 *)(smem + stride + o) = u32x4{mid[0], mid[1], mid[2], mid[3]};
+    *(u32x4 *)(smem + 2 * stride + o) = u32x4{lo[0], lo[1], lo[2], lo[3]};
+    if ((t & 3) == 0) ((int *)(smem + fx4_exps_off(K)))[t >> 2] = e;
+}
+
+__device__ __forceinline__ void fx6_load(Q6KFX &xs, const unsigned char *smem, int K, int b, int u)
+{
+    const int n = u >> 1;
+    const uint32_t stride = lds_pad((uint32_t)K);
+    const int e = ((const int *)(smem + fx4_exps_off(K)))[4 * b + u];
+    const float *sums = (const float *)(smem + fx4_sums_off(K));
+#pragma unroll
+    for (int sg = 0; sg < 4; ++sg) {
+        const int g = 16 * b + 8 * n + 2 * sg + (u & 1);
+        const uint32_t o = lds_pad(16u * (uint32_t)g);
+        const u32x4 h = *(const u32x4 *)(smem + o);
+        const u32x4 m = *(const u32x4 *)(smem + stride + o);
+        const u32x4 l = *(const u32x4 *)(smem + 2 * stride + o);
+        xs.hi[sg][0] = h.x; xs.hi[sg][1] = h.y; xs.hi[sg][2] = h.z; xs.hi[sg][3] = h.w;
+        xs.mid[sg][0] = m.x; xs.mid[sg][1] = m.y; xs.mid[sg][2] = m.z; xs.mid[sg][3] = m.w;
+        xs.lo[sg][0] = l.x; xs.lo[sg][1] = l.y; xs.lo[sg][2] = l.z; xs.lo[sg][3] = l.w;
+        float t = -32.f * __builtin_amdgcn_ldexpf(sums[g], e);
+        pin(t);
+        xs.m[sg] = t;
+    }
+    xs.e = -e;
+}
+
+// Stages the f32 activation of a tile or row-stream launch in fixed point:
+// thread tid converts slot tid and slot tid + blockDim from the values it
+// loaded first (xg0, xg1), then any further slots straight from x.
+template <int KIND>
+__device__ __forceinline__ void fx_stage_all(unsigned char *smem, const float *x, int K, const float (&xg0)[16],
+                                             const float (&xg1)[16])
+{
+    const int slots = K / 16, tid = (int)threadIdx.x, bd = (int)blockDim.x;
+    auto stage = [&](int t, const float (&v)[16]) {
+        if constexpr (KIND == kQ6K) fx6_stage_slot(smem, K, t, v);
+        else fx4_stage_group(smem, K, t, v);
+    };
+    if (tid < slots) stage(tid, xg0);
+    if (tid + bd < slots) stage(tid + bd, xg1);
+    for (int t = tid + 2 * bd; t < slots; t += bd) {
+        const int g = KIND == kQ6K ? fx6_group_of_slot(t) : t;
+        float v[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float4 f = *(const float4 *)(x + 16 * g + 4 * q);
+            v[4 * q] = f.x; v[4 * q + 1] = f.y; v[4 * q + 2] = f.z; v[4 * q + 3] = f.w;
+        }
+        stage(t, v);
+    }
+}
+
+// The 16 values of slot t of the activation (t < K/16), for the preload.
+template <int KIND>
+__device__ __forceinline__ void fx_preload(float (&v)[16], const float *x, int K, int t)
+{
+    if (t < K / 16) {
+        const int g = KIND == kQ6K ? fx6_group_of_slot(t) : t;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float4 f = *(const float4 *)(x + 16 * g + 4 * q);
+            v[4 * q] = f.x; v[4 * q + 1] = f.y; v[4 * q + 2] = f.z; v[4 * q + 3] = f.w;
+        }
+    }
+}
+
 // Tile kernel, for rows that do not fit an aligned power-of-two lane group of
 // one wave: a tile of rows spans the workgroup, each super-block's quad sum
 // goes through LDS and one thread per row adds the K/256 block sums in order.
@@ -521,9 +701,20 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_kernel(GemvArgs a)
     // The activation's global loads go first, then the first weight tiles:
     // vector-memory counters retire in issue order, so staging x waits only
     // for x while the weight tiles stay in flight behind it.
-    constexpr int kXRegs = 8;   // float4 (or 16 int8) staged per thread through registers
+    // Q6_K activations staged in LDS are held in fixed point (two slots of 16
+    // values per thread loaded first, converted after the weight loads go
+    // out).  Q4_K and the SwiGLU pair keep f32 here: their mid-size launches
+    // are bound by start-up, which the conversion lengthens (measured slower
+    // at 2560 x 9728 and 9728 x 2560; Q6_K 2560 x 9728 is faster).
+    constexpr bool kFx = XLDS && KIND == kQ6K;
+    float xg0[16], xg1[16];
+    if constexpr (kFx) {
+        fx_preload<KIND>(xg0, a.x, K, tid);
+        fx_preload<KIND>(xg1, a.x, K, tid + (int)blockDim.x);
+    }
+    constexpr int kXRegs = kFx ? 1 : 8;   // float4 (or 16 int8) staged per thread through registers
     u32x4 xr[kXRegs];
-    if constexpr (XLDS) {
+    if constexpr (XLDS && !kFx) {
         const int step = is_q8(KIND) ? 16 : 4;   // elements per 16-byte load
         const uint8_t *src = is_q8(KIND) ? (const uint8_t *)a.xq : (const uint8_t *)a.x;
         const int esz = is_q8(KIND) ? 1 : 4;
@@ -533,7 +724,7 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_kernel(GemvArgs a)
             if (i < K) xr[r] = *(const u32x4 *)(src + (size_t)i * esz);
         }
     }
-    XSlice<KIND> xs;
+    typename TileSlice<KIND, kFx>::T xs;
     const int xb = lane_on ? b : 0;
     if constexpr (!XLDS) {
         // each lane reads its own slice (no other lane of the tile shares it)
@@ -551,7 +742,12 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_kernel(GemvArgs a)
     // space visible to the compiler (LDS reads stay ds_read, global reads stay
     // global_load) instead of a generic pointer that would turn both into flat
     // loads waiting on every outstanding memory operation.
-    if constexpr (XLDS) {
+    if constexpr (kFx) {
+        fx_stage_all<KIND>(smem, a.x, K, xg0, xg1);
+        __syncthreads();
+        if constexpr (KIND == kQ6K) fx6_load(xs.v, smem, K, xb, part);
+        else fx4_load(xs.v, smem, K, xb, part);
+    } else if constexpr (XLDS) {
         // registers staged above, then any remainder straight through
         const int step = is_q8(KIND) ? 16 : 4;
         const uint8_t *src = is_q8(KIND) ? (const uint8_t *)a.xq : (const uint8_t *)a.x;
@@ -565,7 +761,9 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_kernel(GemvArgs a)
             *(u32x4 *)(smem + lds_pad((uint32_t)(i * esz))) = *(const u32x4 *)(src + (size_t)i * esz);
         __syncthreads();
     }
-    if constexpr (is_q8(KIND)) {
+    if constexpr (kFx) {
+        // slice loaded above
+    } else if constexpr (is_q8(KIND)) {
         if constexpr (XLDS) load_x<true>(xs.v, (const int8_t *)smem, a.xd, xb, part);
         finish_x(xs.v);
     } else {
@@ -951,74 +1149,6 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_wave_kernel(Gem
         best = wave_max_key(best);
         argmax_finish(a, best, lane == 0 ? wave : -1, waves);
     }
-}
-
-// Fixed-point activation of the row-stream Q4_K kernel, in LDS: the high,
-// middle and low byte arrays of X (K bytes each, padded layout), then the
-// 16-element f32 sums (K/16), then the per-part exponents (K/64 ints).
-__device__ __forceinline__ uint32_t fx4_sums_off(int K) { return 3u * lds_pad((uint32_t)K); }
-__device__ __forceinline__ uint32_t fx4_exps_off(int K) { return fx4_sums_off(K) + 4u * (uint32_t)(K / 16); }
-
-// Group g (16 values v, in registers) of the activation: its f32 sum (added
-// in index order, as sum16 does) and its fixed-point bytes; the four groups
-// of a part sit in one quad of lanes and share their largest |x| by DPP.
-// Call with whole quads active.
-__device__ void fx4_stage_group(unsigned char *smem, int K, int g, const float (&v)[16])
-{
-    float t = 0.f, m = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        t += v[i];
-        m = fmaxf(m, fabsf(v[i]));
-    }
-    ((float *)(smem + fx4_sums_off(K)))[g] = t;
-    m = fmaxf(m, dpp_f<kDppQuadXor1>(m));
-    m = fmaxf(m, dpp_f<kDppQuadXor2>(m));
-    const int e = (m > 0.f && m <= 3.402823466e38f) ? 22 - __builtin_amdgcn_frexp_expf(m) : 0;
-    uint32_t hi[4], mid[4], lo[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        int X[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) X[j] = (int)rintf(__builtin_amdgcn_ldexpf(v[4 * k + j], e));
-        const uint32_t p01 = __builtin_amdgcn_perm((uint32_t)X[1], (uint32_t)X[0], 0x05010400u);
-        const uint32_t p23 = __builtin_amdgcn_perm((uint32_t)X[3], (uint32_t)X[2], 0x05010400u);
-        const uint32_t r01 = __builtin_amdgcn_perm((uint32_t)X[1], (uint32_t)X[0], 0x07030602u);
-        const uint32_t r23 = __builtin_amdgcn_perm((uint32_t)X[3], (uint32_t)X[2], 0x07030602u);
-        lo[k] = __builtin_amdgcn_perm(p23, p01, 0x05040100u);
-        mid[k] = __builtin_amdgcn_perm(p23, p01, 0x07060302u);
-        hi[k] = __builtin_amdgcn_perm(r23, r01, 0x05040100u);
-    }
-    const uint32_t stride = lds_pad((uint32_t)K);
-    const uint32_t o = lds_pad(16u * (uint32_t)g);
-    *(u32x4 *)(smem + o) = u32x4{hi[0], hi[1], hi[2], hi[3]};
-    *(u32x4 *)(smem + stride + o) = u32x4{mid[0], mid[1], mid[2], mid[3]};
-    *(u32x4 *)(smem + 2 * stride + o) = u32x4{lo[0], lo[1], lo[2], lo[3]};
-    if ((g & 3) == 0) ((int *)(smem + fx4_exps_off(K)))[g >> 2] = e;
-}
-
-// Lane slice of part c of block b from the staged fixed-point activation.
-__device__ __forceinline__ void fx4_load(Q4KFX &xs, const unsigned char *smem, int K, int b, int c)
-{
-    const uint32_t stride = lds_pad((uint32_t)K);
-    const int P = 4 * b + c;   // the part's 64 values start at element 64P
-    const uint32_t o = lds_pad(64u * (uint32_t)P);   // 64 bytes inside one padded 256-byte span
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const u32x4 h = *(const u32x4 *)(smem + o + 16 * q);
-        const u32x4 m = *(const u32x4 *)(smem + stride + o + 16 * q);
-        const u32x4 l = *(const u32x4 *)(smem + 2 * stride + o + 16 * q);
-        xs.hi[4 * q] = h.x; xs.hi[4 * q + 1] = h.y; xs.hi[4 * q + 2] = h.z; xs.hi[4 * q + 3] = h.w;
-        xs.mid[4 * q] = m.x; xs.mid[4 * q + 1] = m.y; xs.mid[4 * q + 2] = m.z; xs.mid[4 * q + 3] = m.w;
-        xs.lo[4 * q] = l.x; xs.lo[4 * q + 1] = l.y; xs.lo[4 * q + 2] = l.z; xs.lo[4 * q + 3] = l.w;
-    }
-    const float *sums = (const float *)(smem + fx4_sums_off(K));
-    float sl = sums[4 * P] + sums[4 * P + 1], sh = sums[4 * P + 2] + sums[4 * P + 3];
-    pin(sl);
-    pin(sh);
-    xs.sxl = sl;
-    xs.sxh = sh;
-    xs.e = -((const int *)(smem + fx4_exps_off(K)))[P];
 }
 
 // ---------------------------------------------------- row-stream kernel
@@ -1663,8 +1793,11 @@ static Plan make_tile_plan(int64_t N, int64_t K, int kind, size_t extra_lds)
     const size_t sums = is_q8(kind) ? 0 : (size_t)(K / 16) * 4;
     const size_t xpadded = xbytes + xbytes / 16;   // 16 bytes of padding per 256 (lds_pad)
     const size_t red = (size_t)2 * outs * pl.rows_tile * pl.nb * 4;   // two buffers
-    pl.x_in_lds = (pl.rows_tile > 1 && xpadded + sums + extra_lds <= 65536) ? 1 : 0;
-    pl.lds_bytes = (pl.x_in_lds ? xpadded + sums : 0);
+    // Q6_K activations go to LDS in fixed point: three padded byte arrays,
+    // the 16-element sums and the part exponents
+    const size_t staged = kind == kQ6K ? 3 * ((size_t)K + (size_t)K / 16) + sums + (size_t)(K / 64) * 4 : xpadded + sums;
+    pl.x_in_lds = (pl.rows_tile > 1 && staged + extra_lds <= 65536) ? 1 : 0;
+    pl.lds_bytes = (pl.x_in_lds ? staged : 0);
     if (red > pl.lds_bytes) pl.lds_bytes = red;
     pl.grid = 0;   // set by the launcher from the occupancy
     return pl;
