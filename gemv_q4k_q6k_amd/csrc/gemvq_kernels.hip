@@ -873,76 +873,6 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_kernel(GemvArgs a)
 // is staged in LDS once per CU.  A row's value is reduced the same way
 // wherever it sits (fixed lane layout, halves added in order), so equal rows
 // give equal bits.
-// Fixed-point activation of the wave-unit Q6_K kernel, in LDS after the
-// 16-element sums (`base`, 16-byte aligned): the high, middle and low byte
-// arrays of X (K bytes each, in the padded layout), then the per-part
-// exponents (K/64 ints).
-__device__ __forceinline__ uint32_t fx_bytes_stride(int K) { return lds_pad((uint32_t)K); }
-
-// Part slot t (K/16 of them; block t >> 4, part (t >> 2) & 3, group t & 3) of
-// the staged f32 activation converted as Q6KFX describes, one thread per
-// group: the four groups of a part sit in one quad of lanes, which share
-// their largest |x| by DPP.  Call with whole quads active.
-__device__ void fx_stage_group(unsigned char *smem, uint32_t base, const float *sx, int K, int t)
-{
-    const int blk = t >> 4, u = (t >> 2) & 3, s = t & 3;
-    const int g = 16 * blk + 8 * (u >> 1) + 2 * s + (u & 1);   // the group's 16-element index
-    const float *v = x_at<true>(sx, 16 * g);
-    float m = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
-    m = fmaxf(m, dpp_f<kDppQuadXor1>(m));
-    m = fmaxf(m, dpp_f<kDppQuadXor2>(m));
-    // scale so that the part's largest |X| is below 2^22 (m < 2^E); zero and
-    // non-finite parts keep scale 1 (their sums carry a non-finite value)
-    const int e = (m > 0.f && m <= 3.402823466e38f) ? 22 - __builtin_amdgcn_frexp_expf(m) : 0;
-    uint32_t hi[4], mid[4], lo[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        int X[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) X[j] = (int)rintf(__builtin_amdgcn_ldexpf(v[4 * k + j], e));
-        // bytes 0..2 of X[0..3], one byte of each element per dword
-        const uint32_t p01 = __builtin_amdgcn_perm((uint32_t)X[1], (uint32_t)X[0], 0x05010400u);   // X0.b0 X1.b0 X0.b1 X1.b1
-        const uint32_t p23 = __builtin_amdgcn_perm((uint32_t)X[3], (uint32_t)X[2], 0x05010400u);
-        const uint32_t r01 = __builtin_amdgcn_perm((uint32_t)X[1], (uint32_t)X[0], 0x07030602u);   // X0.b2 X1.b2 X0.b3 X1.b3
-        const uint32_t r23 = __builtin_amdgcn_perm((uint32_t)X[3], (uint32_t)X[2], 0x07030602u);
-        lo[k] = __builtin_amdgcn_perm(p23, p01, 0x05040100u);
-        mid[k] = __builtin_amdgcn_perm(p23, p01, 0x07060302u);
-        hi[k] = __builtin_amdgcn_perm(r23, r01, 0x05040100u);
-    }
-    const uint32_t stride = fx_bytes_stride(K);
-    const uint32_t o = lds_pad(16u * (uint32_t)g);
-    *(u32x4 *)(smem + base + o) = u32x4{hi[0], hi[1], hi[2], hi[3]};
-    *(u32x4 *)(smem + base + stride + o) = u32x4{mid[0], mid[1], mid[2], mid[3]};
-    *(u32x4 *)(smem + base + 2 * stride + o) = u32x4{lo[0], lo[1], lo[2], lo[3]};
-    if (s == 0) ((int *)(smem + base + 3 * stride))[t >> 2] = e;
-}
-
-// Lane slice of part u of block b from the staged fixed-point activation.
-__device__ __forceinline__ void fx_load(Q6KFX &xs, const unsigned char *smem, uint32_t base, const float *sums, int K,
-                                        int b, int u)
-{
-    const int n = u >> 1;
-    const uint32_t stride = fx_bytes_stride(K);
-    const int e = ((const int *)(smem + base + 3 * stride))[4 * b + u];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        const int g = 16 * b + 8 * n + 2 * s + (u & 1);   // 16-element group of the slice's group s
-        const uint32_t o = lds_pad(16u * (uint32_t)g);
-        const u32x4 h = *(const u32x4 *)(smem + base + o);
-        const u32x4 m = *(const u32x4 *)(smem + base + stride + o);
-        const u32x4 l = *(const u32x4 *)(smem + base + 2 * stride + o);
-        xs.hi[s][0] = h.x; xs.hi[s][1] = h.y; xs.hi[s][2] = h.z; xs.hi[s][3] = h.w;
-        xs.mid[s][0] = m.x; xs.mid[s][1] = m.y; xs.mid[s][2] = m.z; xs.mid[s][3] = m.w;
-        xs.lo[s][0] = l.x; xs.lo[s][1] = l.y; xs.lo[s][2] = l.z; xs.lo[s][3] = l.w;
-        float t = -32.f * __builtin_amdgcn_ldexpf(sums[g], e);
-        pin(t);
-        xs.m[s] = t;
-    }
-    xs.e = -e;
-}
-
 template <int KIND>
 constexpr int wave_max_threads() { return (is_q8(KIND) || KIND == kQ4K) ? 1024 : 768; }
 constexpr int kWaveMaxThreads = 1024;   // the largest of wave_max_threads
@@ -1022,14 +952,22 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_wave_kernel(Gem
         }
     };
 
-    // activation loads first, then the first two units of every wave (a
-    // register or two per thread cover x for any workgroup of 4+ waves;
-    // smaller workgroups load the rest below)
-    constexpr int kXRegs = is_q8(KIND) ? 1 : 2;
+    // activation loads first, then the first unit of every wave (a register
+    // or two per thread cover x for any workgroup of 4+ waves; smaller
+    // workgroups load the rest below).  Q6_K takes the activation in fixed
+    // point: each thread loads two 16-value slots and converts them once the
+    // weight loads are out.
+    constexpr bool kFx = KIND == kQ6K;
+    float xg0[16], xg1[16];
+    if constexpr (kFx) {
+        fx_preload<KIND>(xg0, a.x, K, tid);
+        fx_preload<KIND>(xg1, a.x, K, tid + (int)blockDim.x);
+    }
+    constexpr int kXRegs = kFx ? 0 : (is_q8(KIND) ? 1 : 2);
     const int step = is_q8(KIND) ? 16 : 4;
     const int esz = is_q8(KIND) ? 1 : 4;
     const uint8_t *src = is_q8(KIND) ? (const uint8_t *)a.xq : (const uint8_t *)a.x;
-    u32x4 xr[kXRegs];
+    u32x4 xr[kXRegs > 0 ? kXRegs : 1];
 #pragma unroll
     for (int r = 0; r < kXRegs; ++r) {
         const int i = (tid + r * (int)blockDim.x) * step;
@@ -1056,16 +994,23 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_wave_kernel(Gem
         fetch_mask(d, unit[d], u_end - 1);
     }
     if (tid == 0) s_next = (uint32_t)(kPhase * waves);
+    if constexpr (kFx) {
+        fx_stage_all<KIND>(smem, a.x, K, xg0, xg1);
+    } else {
 #pragma unroll
-    for (int r = 0; r < kXRegs; ++r) {
-        const int i = (tid + r * (int)blockDim.x) * step;
-        if (i < K) *(u32x4 *)(smem + lds_pad((uint32_t)(i * esz))) = xr[r];
+        for (int r = 0; r < kXRegs; ++r) {
+            const int i = (tid + r * (int)blockDim.x) * step;
+            if (i < K) *(u32x4 *)(smem + lds_pad((uint32_t)(i * esz))) = xr[r];
+        }
+        for (int i = (tid + kXRegs * (int)blockDim.x) * step; i < K; i += (int)blockDim.x * step)
+            *(u32x4 *)(smem + lds_pad((uint32_t)(i * esz))) = *(const u32x4 *)(src + (size_t)i * esz);
     }
-    for (int i = (tid + kXRegs * (int)blockDim.x) * step; i < K; i += (int)blockDim.x * step)
-        *(u32x4 *)(smem + lds_pad((uint32_t)(i * esz))) = *(const u32x4 *)(src + (size_t)i * esz);
     __syncthreads();
     typename WaveSlice<KIND>::T xs[STEPS];
-    if constexpr (is_q8(KIND)) {
+    if constexpr (kFx) {
+#pragma unroll
+        for (int st = 0; st < STEPS; ++st) fx6_load(xs[st].v, smem, K, b + 16 * st, part);
+    } else if constexpr (is_q8(KIND)) {
 #pragma unroll
         for (int st = 0; st < STEPS; ++st) {
             load_x<true>(xs[st].v, (const int8_t *)smem, a.xd, b + 16 * st, part);
@@ -1074,20 +1019,12 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_wave_kernel(Gem
     } else {
         const float *sx = (const float *)smem;
         float *ssum = (float *)(smem + lds_pad(4u * (uint32_t)K));
-        const uint32_t fx_base = lds_pad(4u * (uint32_t)K) + 4u * (uint32_t)(K / 16);
         for (int g = tid; g < K / 16; g += blockDim.x) ssum[g] = sum16(x_at<true>(sx, 16 * g));
-        // K/16 is a multiple of 16, so whole quads take part slots together
-        if constexpr (KIND == kQ6K)
-            for (int t = tid; t < K / 16; t += blockDim.x) fx_stage_group(smem, fx_base, sx, K, t);
         __syncthreads();
 #pragma unroll
         for (int st = 0; st < STEPS; ++st) {
-            if constexpr (KIND == kQ6K) {
-                fx_load(xs[st].v, smem, fx_base, ssum, K, b + 16 * st, part);
-            } else {
-                load_x<true>(xs[st].v, sx, b + 16 * st, part);
-                finish_x(xs[st].v, (const float *)ssum, b + 16 * st, part);
-            }
+            load_x<true>(xs[st].v, sx, b + 16 * st, part);
+            finish_x(xs[st].v, (const float *)ssum, b + 16 * st, part);
         }
     }
 
@@ -1751,9 +1688,9 @@ static bool plan_in_wave(Plan &pl, int64_t N, int64_t K, int kind)
         pl.lanes_row = 64;
     }
     const bool ok = finish_wave_plan(pl, N, K, kind);
-    // Q6_K: fixed-point activation (three padded byte arrays and the group
-    // exponents) after the f32 copy and its sums
-    if (kind == kQ6K) pl.lds_bytes += 3 * ((size_t)K + (size_t)K / 16) + (size_t)(K / 16) * 4;
+    // Q6_K: fixed-point activation (three padded byte arrays, the 16-element
+    // sums and the part exponents) instead of the f32 copy
+    if (kind == kQ6K) pl.lds_bytes = 3 * ((size_t)K + (size_t)K / 16) + (size_t)(K / 16) * 4 + (size_t)(K / 64) * 4;
     return ok && pl.lds_bytes <= 65536;
 }
 
