@@ -80,17 +80,15 @@ template <> struct XSlice<kSwiglu> { Q4KX v; };
 template <> struct XSlice<kQ6K> { Q6KX v; };
 template <> struct XSlice<kQ4KQ8> { Q8X v; };
 template <> struct XSlice<kQ6KQ8> { Q6Q8X v; };
-// The wave-unit kernel holds Q6_K activations in fixed point (Q6KFX); every
-// other kernel and kind uses XSlice.
+// Slices in fixed point: the wave-unit kernel holds Q6_K activations as
+// Q6KFX, the row-stream kernel f32 Q4_K ones as Q4KFX, and the tile kernel
+// Q6_K ones as Q6KFX when it stages x in LDS; everything else uses XSlice.
 struct FXSlice { Q6KFX v; };
 template <int KIND> struct WaveSlice { using T = XSlice<KIND>; };
 template <> struct WaveSlice<kQ6K> { using T = FXSlice; };
-// The row-stream kernel holds f32 Q4_K activations in fixed point (Q4KFX).
 struct FX4Slice { Q4KFX v; };
 template <int KIND> struct RowsSlice { using T = XSlice<KIND>; };
 template <> struct RowsSlice<kQ4K> { using T = FX4Slice; };
-// The tile kernel holds Q6_K activations in fixed point (Q6KFX) when it
-// stages them in LDS.
 template <int KIND, bool FX> struct TileSlice { using T = XSlice<KIND>; };
 template <> struct TileSlice<kQ6K, true> { using T = FXSlice; };
 
