@@ -1186,21 +1186,13 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_rows_kernel(Gem
     };
 
     // f32 Q4_K takes the activation in fixed point (Q4KFX): each thread
-    // loads the 16 values of group tid first, and converts them after the
-    // first weight loads are out
+    // loads two 16-value groups first, and converts them after the first
+    // weight loads are out
     constexpr bool kFx = KIND == kQ4K;
-    float xg[16];
+    float xg0[16], xg1[16];
     if constexpr (kFx) {
-        if (tid < K / 16) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float4 f = *(const float4 *)(a.x + 16 * tid + 4 * q);
-                xg[4 * q] = f.x;
-                xg[4 * q + 1] = f.y;
-                xg[4 * q + 2] = f.z;
-                xg[4 * q + 3] = f.w;
-            }
-        }
+        fx_preload<KIND>(xg0, a.x, K, tid);
+        fx_preload<KIND>(xg1, a.x, K, tid + (int)blockDim.x);
     }
     // activation loads first
     constexpr int kXRegs = kFx ? 0 : (is_q8(KIND) ? 1 : 2);
@@ -1247,21 +1239,7 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_rows_kernel(Gem
     }
 
     if constexpr (kFx) {
-        // K/16 is a multiple of 16 and blockDim of 64, so whole quads convert
-        // together
-        if (tid < K / 16) fx4_stage_group(smem, K, tid, xg);
-        for (int g = tid + (int)blockDim.x; g < K / 16; g += blockDim.x) {
-            float v[16];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float4 f = *(const float4 *)(a.x + 16 * g + 4 * q);
-                v[4 * q] = f.x;
-                v[4 * q + 1] = f.y;
-                v[4 * q + 2] = f.z;
-                v[4 * q + 3] = f.w;
-            }
-            fx4_stage_group(smem, K, g, v);
-        }
+        fx_stage_all<KIND>(smem, a.x, K, xg0, xg1);
         __syncthreads();
     } else {
 #pragma unroll
