@@ -355,15 +355,22 @@ __device__ __forceinline__ void load4(uint32_t (&o)[4], const uint8_t *p)
 __device__ __forceinline__ void q6k_load(Q6KRaw &r, const uint8_t *__restrict__ tile, uint32_t off, int u)
 {
     // one 32-bit lane offset per field from the uniform base, so each load
-    // takes the scalar-base form (no 64-bit address arithmetic per lane)
+    // takes the scalar-base form (no 64-bit address arithmetic per lane).  The
+    // empty asm marks each offset as (re)defined where it is used: when the
+    // offsets do not change across a loop, the compiler would otherwise
+    // widen them to 64 bits outside it and add them to the base with a
+    // 64-bit VALU add per load.
     const uint32_t n = (uint32_t)(u >> 1), l0 = 16u * (uint32_t)(u & 1);
-    load4(r.a, tile + (off + 64u * n + l0));
-    load4(r.b, tile + (off + 64u * n + 32u + l0));
-    load4(r.h, tile + (off + 128u + 32u * n + l0));
-    const U32x2A2 sc = *(const U32x2A2 *)(tile + (off + 192u + 8u * n));
+    uint32_t oa = off + 64u * n + l0, ob = off + 64u * n + 32u + l0, oh = off + 128u + 32u * n + l0;
+    uint32_t os = off + 192u + 8u * n, od = off + 208u;
+    asm volatile("" : "+v"(oa), "+v"(ob), "+v"(oh), "+v"(os), "+v"(od));
+    load4(r.a, tile + oa);
+    load4(r.b, tile + ob);
+    load4(r.h, tile + oh);
+    const U32x2A2 sc = *(const U32x2A2 *)(tile + os);
     r.s[0] = sc.v[0];
     r.s[1] = sc.v[1];
-    r.dbits = *(const uint16_t *)(tile + (off + 208u));
+    r.dbits = *(const uint16_t *)(tile + od);
 }
 
 __device__ __forceinline__ void q6k_zero(Q6KRaw &r)
