@@ -155,11 +155,13 @@ struct Q4KRaw {
 // global_load with an SGPR base, a VGPR offset and an immediate.
 __device__ __forceinline__ void q4k_load(Q4KRaw &r, const uint8_t *__restrict__ tile, uint32_t off, int c)
 {
-    const uint8_t *blk = tile + off;
-    r.hdr = *(const u32x4 *)(blk);
-    const uint8_t *qs = tile + (off + 32u * (uint32_t)c);
-    r.q0 = *(const u32x4 *)(qs + 16);
-    r.q1 = *(const u32x4 *)(qs + 32);
+    // 32-bit offsets from the uniform base, pinned where they are used (see
+    // q6k_load)
+    uint32_t oh = off, oq = off + 32u * (uint32_t)c + 16u;
+    asm volatile("" : "+v"(oh), "+v"(oq));
+    r.hdr = *(const u32x4 *)(tile + oh);
+    r.q0 = *(const u32x4 *)(tile + oq);
+    r.q1 = *(const u32x4 *)(tile + oq + 16u);
 }
 
 __device__ __forceinline__ void q4k_zero(Q4KRaw &r)
