@@ -880,11 +880,11 @@ template <int KIND, int EPI, int STEPS>
 __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_wave_kernel(GemvArgs a)
 {
     // one unit in flight per wave (the next unit's loads are issued as soon
-    // as the current one is consumed): with 12-16 waves per CU that keeps
-    // ~40-70 KB per CU in flight, and measured faster than two units per
+    // as the current one is consumed): with 8-16 waves per CU that keeps
+    // ~37-70 KB per CU in flight, and measured faster than two units per
     // wave (lm_head 36.4 against 37.6 us, Q4_K x Q8 28,672 x 8192 24.8
-    // against 26.3 us): more outstanding requests only queue at the memory
-    // side.
+    // against 26.3 us, both with 12-16 waves): more outstanding requests
+    // only queue at the memory side.
     constexpr int kPhase = 1;
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ uint32_t s_next;   // next unit to hand out, relative to the range
