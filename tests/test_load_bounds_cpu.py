@@ -195,6 +195,8 @@ def test_every_block_quarter_served_once(kind, K):
 def test_two_step_rows():
     geo = gq.tile_geometry(gq.KIND_Q4K_Q8, 28_672, 8192)
     assert geo["wave_local"] == 1 and geo["steps"] == 2 and geo["rows_tile"] == 1 and geo["tiles"] == 28_672
+    # rows of two halves launch 8 waves per CU (each wave walks 14 of the 112 rows a CU gets)
+    assert geo["waves"] == 8 and geo["wave_unit"] == 1
 
 
 def test_geometry_rejects_bad_shapes():
