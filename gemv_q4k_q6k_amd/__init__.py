@@ -106,10 +106,11 @@ def exported_names() -> list[str]:
 
 def tile_geometry(kind: int, N: int, K: int) -> dict:
     """Launch geometry the library uses for an N x K matrix (host-only)."""
-    out = (ctypes.c_int64 * 8)()
+    out = (ctypes.c_int64 * 11)()
     _check("gemvq_tile_geometry", lib().gemvq_tile_geometry(kind, N, K, ctypes.cast(out, ctypes.c_void_p)))
     return {"waves": out[0], "rows_tile": out[1], "tiles": out[2], "wave_local": out[3],
-            "x_in_lds": out[4], "lds_bytes": out[5], "steps": out[6], "wave_unit": out[7]}
+            "x_in_lds": out[4], "lds_bytes": out[5], "steps": out[6], "wave_unit": out[7],
+            "resident": out[8], "phase": out[9], "grid": out[10]}
 
 
 def strerror(status: int) -> str:

@@ -87,17 +87,18 @@ size_t gemvq_lm_head_argmax_ws_bytes(int64_t N, int64_t K)
     return gemvq::kArgmaxWsBytes;
 }
 
-int gemvq_tile_geometry(int kind, int64_t N, int64_t K, int64_t out[8])
+int gemvq_tile_geometry(int kind, int64_t N, int64_t K, int64_t out[11])
 {
+    constexpr int kHookCus = 256;   // MI355X
     if (!out) return GEMVQ_ERR_NULL;
     if (kind < 0 || kind > 7) return GEMVQ_ERR_SHAPE;
     size_t wb = 0;
     if (int st = check_shape(N, K, (kind == 1 || kind == 4 || kind == 7) ? 210 : 144, &wb)) return st;
     if (kind == 5 && N % 32 != 0) return GEMVQ_ERR_SHAPE;
-    const gemvq::Plan pl = kind == 5   ? gemvq::make_swiglu_q8_plan(N, K)
+    const gemvq::Plan pl = kind == 5   ? gemvq::make_swiglu_q8_plan(N, K, kHookCus)
                            : kind >= 6 ? gemvq::make_batch_plan(N, K, kind == 6 ? 2 : 4,
                                                                 gemvq::batch_slots(gemvq::kMaxBatch, kind == 7), nullptr)
-                                       : gemvq::make_plan(N, K, kind);
+                                       : gemvq::make_plan(N, K, kind, kHookCus);
     out[0] = pl.waves;
     out[1] = pl.rows_tile;
     out[2] = pl.tiles;
@@ -106,6 +107,9 @@ int gemvq_tile_geometry(int kind, int64_t N, int64_t K, int64_t out[8])
     out[5] = (int64_t)pl.lds_bytes;
     out[6] = pl.wave_local ? pl.steps : 1;
     out[7] = (pl.wave_local && !pl.rows_kernel) ? 1 : 0;
+    out[8] = pl.resident;
+    out[9] = pl.resident ? pl.phase : 0;
+    out[10] = pl.resident ? pl.grid : 0;
     return GEMVQ_OK;
 }
 

@@ -69,6 +69,8 @@ struct GemvArgs {
     // LDS per round
     int batch;
     int batch_round;
+    // tile kernel: byte offset of the row-reduction buffer in LDS
+    uint32_t red_off;
 };
 
 // ------------------------------------------------------- activation setup
@@ -653,8 +655,14 @@ __device__ __forceinline__ void fx_preload(float (&v)[16], const float *x, int K
 // which workgroups own a single tile.  XLDS: the activation (and its
 // 16-element sums) is staged through LDS because several rows of a tile
 // share it; otherwise each lane reads its own slice.
-template <int KIND, int EPI, int PHASE, bool XLDS>
-__global__ __launch_bounds__(kMaxThreads) void gemv_kernel(GemvArgs a)
+// RES: the CU-resident form, for mid-size matrices (a few tiles per CU).
+// At most one workgroup per CU; it owns PHASE tiles or fewer and issues the
+// loads of all of them before anything else waits, so the CU's whole share
+// of the matrix is in flight at once.  Every tile's block sums then go to a
+// buffer of their own and one barrier precedes the row sums, which are
+// added in the same order as in the ring form (same bits).
+template <int KIND, int EPI, int PHASE, bool XLDS, bool RES = false>
+__global__ __launch_bounds__(RES ? kResThreads : kMaxThreads) void gemv_kernel(GemvArgs a)
 {
     constexpr int kPhase = PHASE;
     extern __shared__ __align__(16) unsigned char smem[];
@@ -710,7 +718,9 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_kernel(GemvArgs a)
         fx_preload<KIND>(xg0, a.x, K, tid);
         fx_preload<KIND>(xg1, a.x, K, tid + (int)blockDim.x);
     }
-    constexpr int kXRegs = kFx ? 1 : 8;   // float4 (or 16 int8) staged per thread through registers
+    // float4 (or 16 int8) staged per thread through registers; a resident
+    // workgroup has 768 threads, so 4 cover K <= 12288 in f32
+    constexpr int kXRegs = kFx ? 1 : (RES ? 4 : 8);
     u32x4 xr[kXRegs];
     if constexpr (XLDS && !kFx) {
         const int step = is_q8(KIND) ? 16 : 4;   // elements per 16-byte load
@@ -777,9 +787,11 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_kernel(GemvArgs a)
             finish_x(xs.v, (const float *)nullptr, xb, part);
         }
     }
-    __syncthreads();   // LDS is reused for row reductions below
+    // LDS is reused for row reductions below (the resident form keeps them
+    // in a region of their own, past the staged activation)
+    if constexpr (!RES) __syncthreads();
 
-    float *red = (float *)smem;   // [2][OUTS][rows_tile][nb]
+    float *red = (float *)(smem + a.red_off);   // ring: [2][OUTS][rows_tile][nb]; resident: [PHASE][...]
     const int red_stride = OUTS * a.rows_tile * a.nb;
     // Q8 emission: the workgroup's rows [r_begin, r_end) are kept in LDS
     float *s_h = (float *)(smem + a.emit_lds_off);
@@ -787,54 +799,77 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_kernel(GemvArgs a)
     const int64_t r_end = (int64_t)t_end * a.rows_tile < a.N ? (int64_t)t_end * a.rows_tile : a.N;
     uint64_t best = 0;   // running argmax key (argmax kernels)
     int buf = 0;
-    // dot, row reduction and epilogue of tile t (workgroup-uniform control flow)
-    auto process = [&](const RawSet<KIND> &rs, int t) {
+    // this lane's quarter-block sums of tile t into the reduction buffer rb
+    auto block_sums = [&](const RawSet<KIND> &rs, int t, float *rb) {
         float ps[2];
         dot_raw<KIND>(rs, xs, part, ps);
         const bool v = valid_tile(t);
 #pragma unroll
-        for (int o = 0; o < OUTS; ++o) ps[o] = v ? ps[o] : 0.f;
-        {
-            float *rb = red + buf * red_stride;
-#pragma unroll
-            for (int o = 0; o < OUTS; ++o) {
-                const float q = quad_sum(ps[o]);
-                if (part == 0 && lane_on) rb[(o * a.rows_tile + p) * a.nb + b] = q;
-            }
-            __syncthreads();
-            if (tid < a.rows_tile && t < t_end) {
-                const int64_t row = (int64_t)t * a.rows_tile + tid;
-                if (row < a.N) {
-                    float r[2];
-#pragma unroll
-                    for (int o = 0; o < OUTS; ++o) {
-                        // block sums added in column order; loads issued four at a time
-                        const float *src = rb + (o * a.rows_tile + tid) * a.nb;
-                        float acc = 0.f;
-                        int c = 0;
-                        for (; c + 4 <= a.nb; c += 4) {
-                            const float v0 = src[c], v1 = src[c + 1], v2 = src[c + 2], v3 = src[c + 3];
-                            acc = (((acc + v0) + v1) + v2) + v3;
-                        }
-                        for (; c < a.nb; ++c) acc += src[c];
-                        r[o] = acc;
-                    }
-                    if constexpr (EPI == kQ8Emit) {
-                        // the SwiGLU product exactly as the store epilogue writes it
-                        const float g = r[0], u = r[1];
-                        const float hv = g * u / (1.0f + expf(-g));
-                        s_h[row - r_begin] = hv;
-                        if (a.y) a.y[row] = hv;
-                    } else {
-                        uint32_t mw = 0;
-                        if constexpr (EPI == kArgmaxMasked) mw = a.mask[row >> 5];
-                        emit_row<KIND, EPI>(a, row, r, best, mw);
-                    }
-                }
-            }
-            buf ^= 1;   // the next tile writes the other half; one barrier per tile suffices
+        for (int o = 0; o < OUTS; ++o) {
+            const float q = quad_sum(v ? ps[o] : 0.f);
+            if (part == 0 && lane_on) rb[(o * a.rows_tile + p) * a.nb + b] = q;
         }
     };
+    // row pr of tile t from its block sums in rb: added in column order
+    // (loads issued four at a time), then the epilogue
+    auto row_out = [&](const float *rb, int t, int pr) {
+        const int64_t row = (int64_t)t * a.rows_tile + pr;
+        if (row >= a.N) return;
+        float r[2];
+#pragma unroll
+        for (int o = 0; o < OUTS; ++o) {
+            const float *src = rb + (o * a.rows_tile + pr) * a.nb;
+            float acc = 0.f;
+            int c = 0;
+            for (; c + 4 <= a.nb; c += 4) {
+                const float v0 = src[c], v1 = src[c + 1], v2 = src[c + 2], v3 = src[c + 3];
+                acc = (((acc + v0) + v1) + v2) + v3;
+            }
+            for (; c < a.nb; ++c) acc += src[c];
+            r[o] = acc;
+        }
+        if constexpr (EPI == kQ8Emit) {
+            // the SwiGLU product exactly as the store epilogue writes it
+            const float g = r[0], u = r[1];
+            const float hv = g * u / (1.0f + expf(-g));
+            s_h[row - r_begin] = hv;
+            if (a.y) a.y[row] = hv;
+        } else {
+            uint32_t mw = 0;
+            if constexpr (EPI == kArgmaxMasked) mw = a.mask[row >> 5];
+            emit_row<KIND, EPI>(a, row, r, best, mw);
+        }
+    };
+    // dot, row reduction and epilogue of tile t (workgroup-uniform control flow)
+    auto process = [&](const RawSet<KIND> &rs, int t) {
+        float *rb = red + buf * red_stride;
+        block_sums(rs, t, rb);
+        __syncthreads();
+        if (tid < a.rows_tile && t < t_end) row_out(rb, t, tid);
+        buf ^= 1;   // the next tile writes the other half; one barrier per tile suffices
+    };
+
+    if constexpr (RES) {
+        // every tile of the range is already in flight: block sums of each
+        // into a buffer of its own, one barrier, then one thread per row
+#pragma unroll
+        for (int d = 0; d < kPhase; ++d)
+            if (t_begin + d < t_end) block_sums(ring[d], t_begin + d, red + d * red_stride);   // uniform
+        __syncthreads();
+        const int nrows = kPhase * a.rows_tile;
+        for (int j = tid; j < nrows; j += (int)blockDim.x) {
+            const int d = j / a.rows_tile;
+            if (t_begin + d < t_end) row_out(red + d * red_stride, t_begin + d, j - d * a.rows_tile);
+        }
+        if constexpr (is_argmax(EPI)) {
+            // every wave folds its threads' keys first (all lanes active here)
+            const int lane = tid & 63;
+            best = wave_max_key(best);
+            argmax_finish(a, best, lane == 0 ? (tid >> 6) : -1, (int)(blockDim.x >> 6));
+        }
+        if constexpr (EPI == kQ8Emit) q8_emit_finish(a, s_h, r_begin, r_end);
+        return;
+    }
 
     // ring of kPhase tiles in flight per lane: tile t+kPhase is fetched right
     // after tile t is consumed
@@ -1673,10 +1708,72 @@ static bool plan_in_wave(Plan &pl, int64_t N, int64_t K, int kind)
     return ok && pl.lds_bytes <= 65536;
 }
 
+// Most tiles a CU-resident workgroup holds in flight, by kind: the raw
+// blocks of every tile and the activation slice stay in registers (at most
+// 168 VGPRs with three waves per SIMD), so the SwiGLU pair (two matrices per
+// tile) takes two.
+static int res_max_phase(int kind) { return kind == kSwiglu ? 2 : kResMaxPhase; }
+
+// Bytes of LDS the tile kernel stages the activation in (f32 padded copy and
+// its 16-element sums; int8 padded copy; or the fixed-point Q6_K form).
+static size_t tile_staged_bytes(int64_t K, int kind)
+{
+    const size_t xbytes = is_q8(kind) ? (size_t)K : (size_t)K * 4;
+    const size_t sums = is_q8(kind) ? 0 : (size_t)(K / 16) * 4;
+    if (kind == kQ6K) return 3 * ((size_t)K + (size_t)K / 16) + sums + (size_t)(K / 64) * 4;
+    return xbytes + xbytes / 16 + sums;   // 16 bytes of padding per 256 (lds_pad)
+}
+
+// CU-resident tile plan (gemv_kernel<..., RES = true>), or false.  Waves per
+// workgroup w in {4, 8, 12} (one workgroup per CU, whole SIMDs); each w gives
+// rows per tile R = 64w / (4 nb) and a busiest CU of ceil(tiles / cus) tiles.
+// The plan takes the w whose busiest CU has the fewest rows (then the fewest
+// idle lanes, then fewer waves), if that CU's tiles fit in flight at once.
+// The grid is the fewest workgroups that keep to that many tiles each.
+static bool plan_resident(Plan &pl, int64_t N, int64_t K, int kind, size_t extra_lds, int cus)
+{
+    int best_w = 0, best_per = 0;
+    int64_t best_rows = INT64_MAX;
+    double best_u = -1.0;
+    for (int w = 4; w <= kResThreads / 64; w += 4) {
+        const int rows = 64 * w / pl.lanes_row;
+        if (rows < 1) continue;
+        const int64_t tiles = (N + rows - 1) / rows;
+        const int64_t per = (tiles + cus - 1) / cus;
+        if (per > res_max_phase(kind)) continue;
+        const int64_t busiest = per * rows;
+        const double util = (double)(rows * pl.lanes_row) / (64.0 * w);
+        if (busiest < best_rows || (busiest == best_rows && util > best_u + 1e-9)) {
+            best_rows = busiest;
+            best_u = util;
+            best_w = w;
+            best_per = (int)per;
+        }
+    }
+    if (!best_w) return false;
+    pl.waves = best_w;
+    pl.threads = 64 * best_w;
+    pl.rows_tile = pl.threads / pl.lanes_row;
+    pl.tiles = (N + pl.rows_tile - 1) / pl.rows_tile;
+    pl.phase = best_per;
+    pl.grid = (int)((pl.tiles + best_per - 1) / best_per);
+    const int outs = (kind == kSwiglu) ? 2 : 1;
+    const size_t red = (size_t)pl.phase * outs * pl.rows_tile * pl.nb * 4;
+    const size_t staged = (tile_staged_bytes(K, kind) + 15) & ~(size_t)15;
+    if (red + extra_lds > 65536) return false;
+    pl.x_in_lds = (pl.rows_tile > 1 && staged + red + extra_lds <= 65536) ? 1 : 0;
+    pl.red_off = pl.x_in_lds ? staged : 0;
+    pl.lds_bytes = pl.red_off + red;
+    pl.resident = 1;
+    return true;
+}
+
 // Tile-kernel plan; `extra_lds` bytes of LDS are reserved past the kernel's
 // own (the Q8 emission's row buffer), and x is staged through LDS only if
-// everything fits in 64 KiB.
-static Plan make_tile_plan(int64_t N, int64_t K, int kind, size_t extra_lds)
+// everything fits in 64 KiB.  With `resident` the CU-resident form is taken
+// when a CU's share of the tiles fits in flight at once; otherwise the ring
+// form walks contiguous tile ranges.
+static Plan make_tile_plan(int64_t N, int64_t K, int kind, size_t extra_lds, int cus, bool resident)
 {
     Plan pl{};
     pl.nb = (int)(K / kQK);
@@ -1684,6 +1781,10 @@ static Plan make_tile_plan(int64_t N, int64_t K, int kind, size_t extra_lds)
     pl.rows_kernel = 0;
     pl.steps = 1;
     pl.lanes_row = kParts * pl.nb;
+    if (resident && plan_resident(pl, N, K, kind, extra_lds, cus)) return pl;
+    pl.resident = 0;
+    pl.phase = 0;
+    pl.red_off = 0;
     // tile kernel: 1, 2, 4 or 8 waves (a workgroup of another size leaves SIMDs
     // unevenly loaded and fewer workgroups fit on a CU); fewest idle lanes,
     // ties to fewer waves; at least one row per tile
@@ -1703,15 +1804,12 @@ static Plan make_tile_plan(int64_t N, int64_t K, int kind, size_t extra_lds)
     pl.rows_tile = pl.threads / pl.lanes_row;
     pl.tiles = (N + pl.rows_tile - 1) / pl.rows_tile;
     const int outs = (kind == kSwiglu) ? 2 : 1;
-    const size_t xbytes = is_q8(kind) ? (size_t)K : (size_t)K * 4;
-    // Staging x through LDS pays when several rows of a tile read the same
-    // slice; with one row per tile every element has a single reader.
-    const size_t sums = is_q8(kind) ? 0 : (size_t)(K / 16) * 4;
-    const size_t xpadded = xbytes + xbytes / 16;   // 16 bytes of padding per 256 (lds_pad)
     const size_t red = (size_t)2 * outs * pl.rows_tile * pl.nb * 4;   // two buffers
-    // Q6_K activations go to LDS in fixed point: three padded byte arrays,
-    // the 16-element sums and the part exponents
-    const size_t staged = kind == kQ6K ? 3 * ((size_t)K + (size_t)K / 16) + sums + (size_t)(K / 64) * 4 : xpadded + sums;
+    // Staging x through LDS pays when several rows of a tile read the same
+    // slice; with one row per tile every element has a single reader.  Q6_K
+    // activations go to LDS in fixed point (three padded byte arrays, the
+    // 16-element sums and the part exponents).
+    const size_t staged = tile_staged_bytes(K, kind);
     pl.x_in_lds = (pl.rows_tile > 1 && staged + extra_lds <= 65536) ? 1 : 0;
     pl.lds_bytes = (pl.x_in_lds ? staged : 0);
     if (red > pl.lds_bytes) pl.lds_bytes = red;
@@ -1719,21 +1817,24 @@ static Plan make_tile_plan(int64_t N, int64_t K, int kind, size_t extra_lds)
     return pl;
 }
 
-Plan make_plan(int64_t N, int64_t K, int kind)
+Plan make_plan(int64_t N, int64_t K, int kind, int cus)
 {
     Plan pl{};
     if (plan_in_wave(pl, N, K, kind)) return pl;
-    return make_tile_plan(N, K, kind, 0);
+    return make_tile_plan(N, K, kind, 0, cus, true);
 }
 
-Plan make_swiglu_q8_plan(int64_t N, int64_t K) { return make_tile_plan(N, K, kSwiglu, (size_t)4 * kEmitRows + 16); }
+Plan make_swiglu_q8_plan(int64_t N, int64_t K, int cus)
+{
+    return make_tile_plan(N, K, kSwiglu, (size_t)4 * kEmitRows + 16, cus, true);
+}
 
 // Batched GEMV plan: the tile kernel's geometry (4 lanes per super-block, a
 // row across the workgroup), LDS for a round of staged vectors or the M-way
 // row reduction, whichever is larger.
 Plan make_batch_plan(int64_t N, int64_t K, int kind, int M, int *round)
 {
-    Plan pl = make_tile_plan(N, K, kind, 0);
+    Plan pl = make_tile_plan(N, K, kind, 0, 0, false);
     const size_t vbytes = (size_t)K + (size_t)K / 16;
     int r = (int)(kBatchStageBytes / vbytes);
     r = r < 1 ? 1 : (r > M ? M : r);
@@ -1789,6 +1890,7 @@ static GemvArgs base_args(const Plan &pl, int64_t N)
     a.x_in_lds = pl.x_in_lds;
     a.steps = pl.steps;
     a.chunk_shift = pl.chunk_shift;
+    a.red_off = (uint32_t)pl.red_off;
     return a;
 }
 
@@ -1804,9 +1906,30 @@ static void launch_on(Kern k, const Plan &pl, const GemvArgs &a, hipStream_t s, 
         hipLaunchKernelGGL(k, dim3(pl.grid), dim3(pl.threads), pl.lds_bytes, s, a);
 }
 
+// CU-resident tile launch: pl.grid workgroups of pl.threads, each owning at
+// most pl.phase contiguous tiles (all in flight at once).
+template <int KIND, int EPI, bool XLDS>
+static hipError_t launch_resident(Plan &pl, GemvArgs a, hipStream_t s, const Timing &tm)
+{
+    a.tiles_q = (int)(pl.tiles / pl.grid);
+    a.tiles_r = (int)(pl.tiles % pl.grid);
+    switch (pl.phase) {
+    case 1: launch_on(gemv_kernel<KIND, EPI, 1, XLDS, true>, pl, a, s, tm); break;
+    case 2: launch_on(gemv_kernel<KIND, EPI, 2, XLDS, true>, pl, a, s, tm); break;
+    default:
+        if constexpr (KIND != kSwiglu) {
+            if (pl.phase == 3) launch_on(gemv_kernel<KIND, EPI, 3, XLDS, true>, pl, a, s, tm);
+            else launch_on(gemv_kernel<KIND, EPI, kResMaxPhase, XLDS, true>, pl, a, s, tm);
+        }
+        break;
+    }
+    return hipGetLastError();
+}
+
 template <int KIND, int EPI, bool XLDS>
 static hipError_t launch_mode(Plan &pl, GemvArgs a, int cus, hipStream_t s, const Timing &tm)
 {
+    if (pl.resident) return launch_resident<KIND, EPI, XLDS>(pl, a, s, tm);
     // the occupancy of the deeper-pipelined kernel sizes the grid; if that
     // leaves at most one tile per workgroup the single-tile kernel runs
     const void *fn2 = (const void *)gemv_kernel<KIND, EPI, 2, XLDS>;
@@ -1902,7 +2025,7 @@ static hipError_t launch(Plan &pl, const GemvArgs &a, int cus, hipStream_t s, co
 
 hipError_t launch_q4k_gemv(const void *W, const float *x, float *y, int64_t N, int64_t K, int cus, hipStream_t s)
 {
-    Plan pl = make_plan(N, K, kQ4K);
+    Plan pl = make_plan(N, K, kQ4K, cus);
     GemvArgs a = base_args(pl, N);
     a.W = (const uint8_t *)W;
     a.x = x;
@@ -1912,7 +2035,7 @@ hipError_t launch_q4k_gemv(const void *W, const float *x, float *y, int64_t N, i
 
 hipError_t launch_q6k_gemv(const void *W, const float *x, float *y, int64_t N, int64_t K, int cus, hipStream_t s)
 {
-    Plan pl = make_plan(N, K, kQ6K);
+    Plan pl = make_plan(N, K, kQ6K, cus);
     GemvArgs a = base_args(pl, N);
     a.W = (const uint8_t *)W;
     a.x = x;
@@ -1923,7 +2046,7 @@ hipError_t launch_q6k_gemv(const void *W, const float *x, float *y, int64_t N, i
 hipError_t launch_swiglu_gemv(const void *Wg, const void *Wu, const float *x, float *h, int64_t N, int64_t K, int cus,
                               hipStream_t s)
 {
-    Plan pl = make_plan(N, K, kSwiglu);
+    Plan pl = make_plan(N, K, kSwiglu, cus);
     GemvArgs a = base_args(pl, N);
     a.W = (const uint8_t *)Wg;
     a.W2 = (const uint8_t *)Wu;
@@ -1935,7 +2058,7 @@ hipError_t launch_swiglu_gemv(const void *Wg, const void *Wu, const float *x, fl
 hipError_t launch_q4k_q8_gemv(const void *W, const int8_t *xq, const uint16_t *xd, float *y, int64_t N, int64_t K,
                               int cus, hipStream_t s)
 {
-    Plan pl = make_plan(N, K, kQ4KQ8);
+    Plan pl = make_plan(N, K, kQ4KQ8, cus);
     GemvArgs a = base_args(pl, N);
     a.W = (const uint8_t *)W;
     a.xq = xq;
@@ -1947,7 +2070,7 @@ hipError_t launch_q4k_q8_gemv(const void *W, const int8_t *xq, const uint16_t *x
 hipError_t launch_swiglu_q8_gemv(const void *Wg, const void *Wu, const float *x, float *h, int8_t *hq, uint16_t *hd,
                                  void *ws, int64_t N, int64_t K, int cus, hipStream_t s)
 {
-    Plan pl = make_swiglu_q8_plan(N, K);
+    Plan pl = make_swiglu_q8_plan(N, K, cus);
     GemvArgs a = base_args(pl, N);
     a.W = (const uint8_t *)Wg;
     a.W2 = (const uint8_t *)Wu;
@@ -2036,7 +2159,7 @@ hipError_t launch_q8_gemv_batch(bool q6k, const void *W, const int8_t *xq, const
 hipError_t launch_q6k_q8_gemv(const void *W, const int8_t *xq, const uint16_t *xd, float *y, int64_t N, int64_t K,
                               int cus, hipStream_t s)
 {
-    Plan pl = make_plan(N, K, kQ6KQ8);
+    Plan pl = make_plan(N, K, kQ6KQ8, cus);
     GemvArgs a = base_args(pl, N);
     a.W = (const uint8_t *)W;
     a.xq = xq;
@@ -2049,7 +2172,7 @@ hipError_t launch_lm_head_argmax(const void *W, const float *x, const uint32_t *
                                  float *out_max, void *ws, int64_t N, int64_t K, int cus, hipStream_t s,
                                  const Timing &tm)
 {
-    Plan pl = make_plan(N, K, kQ6K);
+    Plan pl = make_plan(N, K, kQ6K, cus);
     GemvArgs a = base_args(pl, N);
     a.W = (const uint8_t *)W;
     a.x = x;

@@ -41,10 +41,23 @@ struct Plan {
     int x_in_lds;    // activation staged through LDS
     size_t lds_bytes;
     int grid;        // workgroups (one resident wave; set at launch)
+    // tile kernel, CU-resident form: one workgroup per CU (at most), each
+    // with all `phase` tiles of its row range in flight from the start; the
+    // row-reduction buffer then sits at red_off, past the staged activation
+    int resident;
+    int phase;
+    size_t red_off;
 };
 
-Plan make_plan(int64_t N, int64_t K, int kind);
-Plan make_swiglu_q8_plan(int64_t N, int64_t K);   // always the tile kernel
+// Threads of a CU-resident tile workgroup (12 waves, three per SIMD) and the
+// most tiles one holds in flight.
+constexpr int kResThreads = 768;
+constexpr int kResMaxPhase = 4;
+
+// `cus`: compute units of the device the launch runs on (the tile kernel's
+// CU-resident form splits the rows over them)
+Plan make_plan(int64_t N, int64_t K, int kind, int cus);
+Plan make_swiglu_q8_plan(int64_t N, int64_t K, int cus);   // always the tile kernel
 // batched int8 GEMV: vectors per call, LDS bytes a round of staged vectors
 // may take, the kernel's vector slots for m vectors (1, 2, 4 or 8; Q6_K at
 // most 4, larger batches in launches of 4), and its plan (round = vectors

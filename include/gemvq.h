@@ -303,9 +303,15 @@ int gemvq_q6k_q8_isums(const void *W, const int8_t *xq, int32_t *isums,
  * byte offset within a unit never changes, and on a ragged matrix the last
  * unit starts at row N - rows (its lanes whose rows the unit before covered
  * are idle); with N < rows, lanes past N read the unit's first super-block.
+ * out[8] = 1 for the tile kernel's CU-resident form (one workgroup per CU at
+ * most, each owning contiguous tiles, out[9] of them or fewer, all in flight
+ * at once; workgroup w owns tiles [w*q + min(w, r), ...) with q, r the
+ * quotient and remainder of the tiles over the out[10] workgroups), 0 for
+ * the ring form (out[9] = out[10] = 0).  The resident choice depends on the
+ * device's CU count; this hook assumes 256 (MI355X).
  * Returns GEMVQ_ERR_SHAPE for shapes the GEMV entry points reject.
  */
-int gemvq_tile_geometry(int kind, int64_t N, int64_t K, int64_t out[8]);
+int gemvq_tile_geometry(int kind, int64_t N, int64_t K, int64_t out[11]);
 
 /* Static description of a status code (never NULL). */
 const char *gemvq_strerror(int status);

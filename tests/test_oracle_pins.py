@@ -562,3 +562,99 @@ def test_q8_gemv_batch_vs_numpy(fmt):
     assert np.array_equal(oracle.q8_gemv_batch(fmt, W, xq[:1], xd[:1], N, K, 1)[0], single(W, xq[0], xd[0], N, K))
     perm = [3, 0, 4, 1, 2]
     assert np.array_equal(oracle.q8_gemv_batch(fmt, W, xq[perm], xd[perm], N, K, m), Y[perm])
+
+
+# ---------------------------------------------------------------------------
+# Whole-matrix dequantizers and the multi-output GEMV.  They compose pinned
+# block decoders and the pinned GEMV; these pins catch a slip in the
+# composition itself: blocks placed in the wrong row or column, a reshape
+# that transposes, a residual added to the wrong output or twice.
+
+
+@pytest.mark.parametrize("N,nb", [(1, 1), (3, 2), (5, 7), (2, 38)])
+def test_q4k_dequantize_vs_independent_encoder(N, nb):
+    """The matrix the independent encoder builds from random fields (weights
+    computed directly from the fields) equals the oracle's dequantization of
+    the packed bytes, element for element and in the same N x K layout."""
+    rng = np.random.default_rng(900 + 10 * N + nb)
+    K = 256 * nb
+    raw, w = q4k_matrix_from_fields(random_q4k_fields(rng, N * nb), N, K)
+    got = oracle.q4k_dequantize(raw.reshape(-1), N, K)
+    assert got.shape == (N, K)
+    assert np.array_equal(got, w)
+
+
+@pytest.mark.parametrize("N,nb", [(1, 1), (3, 2), (5, 7), (2, 38)])
+def test_q6k_dequantize_vs_independent_encoder(N, nb):
+    rng = np.random.default_rng(950 + 10 * N + nb)
+    K = 256 * nb
+    raw, w = q6k_matrix_from_fields(random_q6k_fields(rng, N * nb), N, K)
+    got = oracle.q6k_dequantize(raw.reshape(-1), N, K)
+    assert got.shape == (N, K)
+    assert np.array_equal(got, w)
+
+
+def test_dequantize_block_placement():
+    """A block whose weights are all one known value, planted at (row r,
+    column block c) of an otherwise all-zero matrix, shows up exactly at
+    rows r, columns 256c .. 256c+255 (and nowhere else) -- in both formats,
+    on a non-square block grid so a transposed reshape cannot pass."""
+    N, nb = 3, 5
+    K = 256 * nb
+    for r, c in [(0, 0), (1, 3), (2, 4)]:
+        # Q4_K: d = 1, every scale 1 and quant 7, min 0 -> every weight 7
+        blk = pack_q4k(f16_bits(1.0), f16_bits(0.0), [1] * 8, [0] * 8, [7] * 256)
+        W = np.zeros((N, nb, 144), np.uint8)
+        W[r, c] = blk
+        got = oracle.q4k_dequantize(W.reshape(-1), N, K)
+        want = np.zeros((N, K))
+        want[r, 256 * c:256 * (c + 1)] = 7.0
+        assert np.array_equal(got, want), (r, c)
+        # Q6_K: an all-zero block decodes to -32*d*sc = +-0 only with sc = 0;
+        # plant d = 0.5, sc = 2, q = 40 -> every weight 0.5*2*8 = 8, and make
+        # every other block all zero (quants 0 give -32*d*sc = -0.0 with d = 0)
+        blk6 = pack_q6k(f16_bits(0.5), [2] * 16, [40] * 256)
+        W6 = np.zeros((N, nb, 210), np.uint8)
+        W6[r, c] = blk6
+        got6 = oracle.q6k_dequantize(W6.reshape(-1), N, K)
+        want6 = np.zeros((N, K))
+        want6[r, 256 * c:256 * (c + 1)] = 8.0
+        assert np.array_equal(got6, want6), (r, c)
+
+
+def test_q4k_gemv_multi_composition():
+    """y_i = W_i x + r_i: each output is the single-matrix GEMV of its own
+    matrix plus its own residual (f32 widened to f64), matrices of different
+    row counts, one without a residual."""
+    rng = np.random.default_rng(971)
+    K = 512
+    Ns = [7, 3, 11]
+    mats = [q4k_matrix_from_fields(random_q4k_fields(rng, n * K // 256), n, K) for n in Ns]
+    x = rng.standard_normal(K).astype(np.float32)
+    res = [rng.standard_normal(Ns[0]).astype(np.float32) * 100, None, rng.standard_normal(Ns[2]).astype(np.float32)]
+    ys = oracle.q4k_gemv_multi([m[0].reshape(-1) for m in mats], Ns, x, K, res)
+    assert [y.shape for y in ys] == [(n,) for n in Ns]
+    for (raw, w), n, r, y in zip(mats, Ns, res, ys):
+        want = w @ x.astype(np.float64) + (0.0 if r is None else r.astype(np.float64))
+        assert np.allclose(y, want, rtol=1e-12, atol=1e-12)
+        single = oracle.q4k_gemv(raw.reshape(-1), x, n, K)
+        assert np.array_equal(y, single + (0.0 if r is None else r.astype(np.float64)))
+
+
+def test_q4k_gemv_multi_residual_only_and_one_hot():
+    """All-zero matrices give exactly the residual on its own output (and 0
+    where none is given); a one-hot x extracts column k of each matrix."""
+    rng = np.random.default_rng(972)
+    K, Ns = 768, [4, 9]
+    zero = [np.zeros(n * K // 256 * 144, np.uint8) for n in Ns]
+    r0 = rng.standard_normal(Ns[0]).astype(np.float32)
+    ys = oracle.q4k_gemv_multi(zero, Ns, rng.standard_normal(K).astype(np.float32), K, [r0, None])
+    assert np.array_equal(ys[0], r0.astype(np.float64))
+    assert np.array_equal(ys[1], np.zeros(Ns[1]))
+    mats = [q4k_matrix_from_fields(random_q4k_fields(rng, n * K // 256), n, K) for n in Ns]
+    for k in (0, 300, K - 1):
+        e = np.zeros(K, np.float32)
+        e[k] = 1.0
+        ys = oracle.q4k_gemv_multi([m[0].reshape(-1) for m in mats], Ns, e, K)
+        for (raw, w), y in zip(mats, ys):
+            assert np.array_equal(y, w[:, k])
