@@ -93,6 +93,20 @@ template <int KIND> struct RowsSlice { using T = XSlice<KIND>; };
 template <> struct RowsSlice<kQ4K> { using T = FX4Slice; };
 template <int KIND, bool FX> struct TileSlice { using T = XSlice<KIND>; };
 template <> struct TileSlice<kQ6K, true> { using T = FXSlice; };
+template <> struct TileSlice<kQ4K, true> { using T = FX4Slice; };
+template <> struct TileSlice<kSwiglu, true> { using T = FX4Slice; };
+
+// Activation form of the tile kernel when it stages x in LDS: fixed point
+// (true) or f32.  Q6_K always takes fixed point (its f32 dot needs two more
+// byte permutes per four weights).  The resident SwiGLU pair takes it too:
+// its two dot products per quarter block make it VALU-bound once the weight
+// stream has arrived (f32: ~1.75 VALU operations per weight, fixed point
+// ~1.1), while a single resident Q4_K matrix keeps f32, which measured
+// faster there (the conversion sits on its start-up path).
+constexpr bool tile_fx(int kind, bool xlds, bool res)
+{
+    return xlds && (kind == kQ6K || (res && kind == kSwiglu));
+}
 
 // Layout of the activation staged in LDS: 16 bytes of padding after every
 // 256 bytes.  A lane's slice is 64 consecutive bytes (Q8) or 64 consecutive
@@ -707,12 +721,21 @@ __global__ __launch_bounds__(RES ? kResThreads : kMaxThreads) void gemv_kernel(G
     // The activation's global loads go first, then the first weight tiles:
     // vector-memory counters retire in issue order, so staging x waits only
     // for x while the weight tiles stay in flight behind it.
-    // Q6_K activations staged in LDS are held in fixed point (two slots of 16
-    // values per thread loaded first, converted after the weight loads go
-    // out).  Q4_K and the SwiGLU pair keep f32 here: their mid-size launches
-    // are bound by start-up, which the conversion lengthens (measured slower
-    // at 2560 x 9728 and 9728 x 2560; Q6_K 2560 x 9728 is faster).
-    constexpr bool kFx = XLDS && KIND == kQ6K;
+    // A fixed-point activation (tile_fx) is staged from two slots of 16
+    // values per thread, loaded first and converted once the x loads are in.
+    // In the ring form Q4_K and the SwiGLU pair keep f32: their launches of
+    // many short-lived workgroups are bound by start-up, which the
+    // conversion lengthens (measured slower at 2560 x 9728 and 9728 x 2560).
+    constexpr bool kFx = tile_fx(KIND, XLDS, RES);
+    // The resident SwiGLU pair runs its whole activation path (loads, fixed-
+    // point staging, barrier, slice) before it issues the weight loads.  A
+    // barrier after the weight loads completes only once every wave has
+    // issued all of them, and issue is throttled by the memory pipeline, so
+    // the dot products could start only when most of the stream had arrived
+    // (measured with device timestamps: x ready ~4 us into a ~8 us launch).
+    // The other kinds measured as fast or faster with their weight loads
+    // first.
+    constexpr bool kXFirst = RES && XLDS && KIND == kSwiglu;
     float xg0[16], xg1[16];
     if constexpr (kFx) {
         fx_preload<KIND>(xg0, a.x, K, tid);
@@ -742,8 +765,10 @@ __global__ __launch_bounds__(RES ? kResThreads : kMaxThreads) void gemv_kernel(G
             load_x(xs.v, a.x, xb, part);
     }
     RawSet<KIND> ring[kPhase];
+    if constexpr (!kXFirst) {
 #pragma unroll
-    for (int d = 0; d < kPhase; ++d) fetch(ring[d], t_begin + d);
+        for (int d = 0; d < kPhase; ++d) fetch(ring[d], t_begin + d);
+    }
 
     // ---- activation slice into registers (through LDS when several rows of
     // a tile share it).  The two branches keep the source pointer's address
@@ -786,6 +811,10 @@ __global__ __launch_bounds__(RES ? kResThreads : kMaxThreads) void gemv_kernel(G
         } else {
             finish_x(xs.v, (const float *)nullptr, xb, part);
         }
+    }
+    if constexpr (kXFirst) {
+#pragma unroll
+        for (int d = 0; d < kPhase; ++d) fetch(ring[d], t_begin + d);
     }
     // LDS is reused for row reductions below (the resident form keeps them
     // in a region of their own, past the staged activation)
@@ -1716,11 +1745,11 @@ static int res_max_phase(int kind) { return kind == kSwiglu ? 2 : kResMaxPhase; 
 
 // Bytes of LDS the tile kernel stages the activation in (f32 padded copy and
 // its 16-element sums; int8 padded copy; or the fixed-point Q6_K form).
-static size_t tile_staged_bytes(int64_t K, int kind)
+static size_t tile_staged_bytes(int64_t K, int kind, bool res)
 {
     const size_t xbytes = is_q8(kind) ? (size_t)K : (size_t)K * 4;
     const size_t sums = is_q8(kind) ? 0 : (size_t)(K / 16) * 4;
-    if (kind == kQ6K) return 3 * ((size_t)K + (size_t)K / 16) + sums + (size_t)(K / 64) * 4;
+    if (tile_fx(kind, true, res)) return 3 * ((size_t)K + (size_t)K / 16) + sums + (size_t)(K / 64) * 4;
     return xbytes + xbytes / 16 + sums;   // 16 bytes of padding per 256 (lds_pad)
 }
 
@@ -1759,7 +1788,7 @@ static bool plan_resident(Plan &pl, int64_t N, int64_t K, int kind, size_t extra
     pl.grid = (int)((pl.tiles + best_per - 1) / best_per);
     const int outs = (kind == kSwiglu) ? 2 : 1;
     const size_t red = (size_t)pl.phase * outs * pl.rows_tile * pl.nb * 4;
-    const size_t staged = (tile_staged_bytes(K, kind) + 15) & ~(size_t)15;
+    const size_t staged = (tile_staged_bytes(K, kind, true) + 15) & ~(size_t)15;
     if (red + extra_lds > 65536) return false;
     pl.x_in_lds = (pl.rows_tile > 1 && staged + red + extra_lds <= 65536) ? 1 : 0;
     pl.red_off = pl.x_in_lds ? staged : 0;
@@ -1809,7 +1838,7 @@ static Plan make_tile_plan(int64_t N, int64_t K, int kind, size_t extra_lds, int
     // slice; with one row per tile every element has a single reader.  Q6_K
     // activations go to LDS in fixed point (three padded byte arrays, the
     // 16-element sums and the part exponents).
-    const size_t staged = tile_staged_bytes(K, kind);
+    const size_t staged = tile_staged_bytes(K, kind, false);
     pl.x_in_lds = (pl.rows_tile > 1 && staged + extra_lds <= 65536) ? 1 : 0;
     pl.lds_bytes = (pl.x_in_lds ? staged : 0);
     if (red > pl.lds_bytes) pl.lds_bytes = red;

@@ -382,22 +382,31 @@ def test_swiglu_c4_layer(dev):
     check_f32("C4 layer", y_np, oracle.q6k_gemv_f64x(Wd, hhat, K, N))
 
 
-def test_swiglu_gate_equals_up(dev):
-    # a shape on which q4k_gemv runs the tile kernel, as swiglu_gemv does, so
-    # g is summed with the same arithmetic (the row-stream kernel takes the
-    # activation in fixed point)
-    N, K = 6400, 2560
-    assert gq().tile_geometry(gq().KIND_Q4K, N, K)["wave_local"] == 0
-    assert gq().tile_geometry(gq().KIND_SWIGLU, N, K)["wave_local"] == 0
+@pytest.mark.parametrize("N,K,tol", [
+    # ring form of the tile kernel for the pair, resident f32 form for the
+    # single matrix: the same f32 row arithmetic, so h = g^2 sigmoid(g) from
+    # q4k_gemv's own g up to the rounding of the epilogue
+    (12000, 2560, 1e-5),
+    # resident forms: the pair stages x in 23-bit fixed point, the single
+    # matrix keeps f32; each g is within ~1e-5 of the largest |g| of the
+    # exact one, so h and g^2 sigmoid(g) agree to a few 1e-5 of the largest h
+    (6400, 2560, 1e-4),
+])
+def test_swiglu_gate_equals_up(dev, N, K, tol):
+    sw = gq().tile_geometry(gq().KIND_SWIGLU, N, K)
+    q4 = gq().tile_geometry(gq().KIND_Q4K, N, K)
+    assert sw["wave_local"] == 0 and q4["wave_local"] == 0
+    assert (sw["resident"], q4["resident"]) == ((0, 1) if tol == 1e-5 else (1, 1))
     r = synth.rng_for(11)
     Wg = synth.q4k_weights(r, N, K)
     x = synth.activation(r, K)
     dWg = up(Wg, dev)
     h = gq().swiglu_gemv(dWg, dWg, up(x, dev), N, K).cpu().numpy()
     g = gq().q4k_gemv(dWg, up(x, dev), N, K).cpu().numpy().astype(np.float64)
-    # same row arithmetic for gate and up: h = g^2 sigmoid(g) from the GPU's own g
     ref = g * g / (1.0 + np.exp(-g))
-    assert np.max(np.abs(h - ref)) <= 1e-5 * np.max(np.abs(ref))
+    e = float(np.max(np.abs(h - ref)) / np.max(np.abs(ref)))
+    print(f"swiglu gate=up {N}x{K}: {e:.3e}", flush=True)
+    assert e <= tol
 
 
 # -------------------------------------------------------------------- Q8
@@ -693,8 +702,10 @@ def test_swiglu_q8_gemv(dev, N, K):
     # without the f32 output the codes are the same
     hq2, hd2 = gq().swiglu_q8_gemv(dWg, dWu, dx, N, K, ws)
     assert torch.equal(hq2, hq) and torch.equal(hd2, hd)
-    # bit-identical to the unfused device sequence when swiglu_gemv runs the same tile kernel
-    if kernel_path(gq().KIND_SWIGLU, N, K).startswith("tile"):
+    # bit-identical to the unfused device sequence when swiglu_gemv runs the
+    # same tile kernel form (same activation form, same row sums)
+    path = kernel_path(gq().KIND_SWIGLU, N, K)
+    if path.startswith("tile") and path == kernel_path(gq().KIND_SWIGLU_Q8, N, K):
         h3 = gq().swiglu_gemv(dWg, dWu, dx, N, K)
         q3, d3 = gq().q8_quantize(h3)
         assert torch.equal(h3, h) and torch.equal(q3, hq) and torch.equal(d3, hd)
