@@ -20,7 +20,7 @@ import threading
 __all__ = [
     "GemvqError", "lib", "exported_names", "header_names",
     "q4k_gemv", "q4k_gemv_multi", "q6k_gemv", "q8_quantize", "q4k_q8_gemv", "swiglu_gemv",
-    "lm_head_argmax", "lm_head_argmax_timed", "lm_head_argmax_masked", "lm_head_argmax_ws_bytes", "q4k_q8_isums", "strerror", "tile_geometry",
+    "lm_head_argmax", "lm_head_argmax_timed", "lm_head_argmax_masked", "lm_head_argmax_noalloc", "lm_head_argmax_ws_bytes", "q4k_q8_isums", "strerror", "tile_geometry",
     "q6k_q8_gemv", "q6k_q8_isums", "swiglu_q8_gemv", "swiglu_q8_ws_bytes", "rms_norm_q8", "q4k_q8_gemv_batch", "q6k_q8_gemv_batch", "add_rms_norm_q8",
     "Q4K_BLOCK_BYTES", "Q6K_BLOCK_BYTES", "LIB_PATH", "HEADER_PATH",
 ]
@@ -64,6 +64,7 @@ _SIGS = {
     "lm_head_argmax": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_size_t, _I64, _I64, _P]),
     "lm_head_argmax_timed": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_size_t, _I64, _I64, _P, _P, _P]),
     "lm_head_argmax_masked": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_size_t, _I64, _I64, _P]),
+    "lm_head_argmax_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _P]),
     "gemvq_lm_head_argmax_ws_bytes": (ctypes.c_size_t, [_I64, _I64]),
     "gemvq_q4k_q8_isums": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P]),
     "gemvq_strerror": (ctypes.c_char_p, [ctypes.c_int]),
@@ -392,6 +393,25 @@ def lm_head_argmax_masked(W, x, mask, N: int, K: int, workspace, out_idx=None, o
             or mask.numel() < words or not mask.is_contiguous()):
         raise TypeError(f"mask: expected a contiguous int32/uint32 device tensor of at least {words} words")
     return _lm_head(W, x, N, K, workspace, out_idx, out_max, want_max, stream, None, mask)
+
+
+def lm_head_argmax_noalloc(W, x, N: int, K: int, out_idx=None, out_max=None, want_max: bool = False, stream=None):
+    """lm_head_argmax with the library's own per-GPU workspace (no workspace
+    argument; the C entry point allocates nothing).  Calls that overlap on one
+    GPU race; calls in stream order are safe.  Pass out_idx (and out_max) to
+    keep the call free of torch allocations as well."""
+    torch = _torch()
+    _weights(W, N, K, Q6K_BLOCK_BYTES)
+    _dev_tensor(x, torch.float32, K, "x")
+    out_idx = _out(out_idx, x.device, torch.int32, 1, "out_idx")
+    if want_max and out_max is None:
+        out_max = torch.empty(1, dtype=torch.float32, device=x.device)
+    if out_max is not None:
+        _dev_tensor(out_max, torch.float32, 1, "out_max")
+    _check("lm_head_argmax_noalloc", lib().lm_head_argmax_noalloc(
+        W.data_ptr(), x.data_ptr(), out_idx.data_ptr(), out_max.data_ptr() if out_max is not None else None,
+        N, K, _stream(x, stream)))
+    return (out_idx, out_max) if out_max is not None else out_idx
 
 
 def _lm_head(W, x, N, K, workspace, out_idx, out_max, want_max, stream, events, mask=None):

@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <mutex>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -60,6 +61,38 @@ int device_cus(int *cus)
 }
 
 int status_of(hipError_t e) { return e == hipSuccess ? GEMVQ_OK : GEMVQ_ERR_HIP; }
+
+// Workspace of lm_head_argmax_noalloc: the 12,288 bytes lm_head_argmax takes
+// from its caller (a done counter and the running key, then a reserved
+// area), here a file-scope device array.  Every GPU the library runs on holds
+// its own copy, at its own address, until the process ends.  In host code the
+// name `scratch` is only a stand-in for the symbol: its device address comes
+// from hipGetSymbolAddress, once per device, and only that address is ever
+// passed to a kernel.
+static __device__ __align__(256) uint8_t scratch[gemvq::kArgmaxWsBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices];   // device address of `scratch` per device ordinal
+
+// `scratch`'s address on the current device.  The first call for a device
+// looks it up and clears the counters (first kArgmaxZeroBytes) with a fill
+// kernel on `s`, which orders the clear before the argmax launch that
+// follows on the same stream; every argmax launch leaves them zero again.
+int scratch_on_current_device(hipStream_t s, void **out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GEMVQ_ERR_HIP;
+    std::lock_guard<std::mutex> g(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return GEMVQ_ERR_HIP;
+        if (gemvq::launch_fill_zero(p, gemvq::kArgmaxZeroBytes, s) != hipSuccess) return GEMVQ_ERR_HIP;
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return GEMVQ_OK;
+}
 
 }  // namespace
 
@@ -365,6 +398,26 @@ int lm_head_argmax_timed(const void *W, const float *x, uint32_t *out_idx, float
     tm.start = (hipEvent_t)start_event;
     tm.stop = (hipEvent_t)stop_event;
     return lm_head_argmax_impl(W, x, nullptr, out_idx, out_max, workspace, ws_bytes, N, K, stream, tm);
+}
+
+int lm_head_argmax_noalloc(const void *W, const float *x, uint32_t *out_idx, float *out_max, int64_t N, int64_t K,
+                           void *stream)
+{
+    if (!W || !x || !out_idx) return GEMVQ_ERR_NULL;
+    size_t wb = 0;
+    if (int st = check_shape(N, K, 210, &wb)) return st;
+    if (!aligned(W, 4) || !aligned(x, 16) || !aligned(out_idx, 4) || (out_max && !aligned(out_max, 4)))
+        return GEMVQ_ERR_ALIGN;
+    const size_t nx = (size_t)K * 4;
+    if (overlap(out_idx, 4, W, wb) || overlap(out_idx, 4, x, nx)) return GEMVQ_ERR_ALIAS;
+    if (out_max && (overlap(out_max, 4, W, wb) || overlap(out_max, 4, x, nx) || overlap(out_max, 4, out_idx, 4)))
+        return GEMVQ_ERR_ALIAS;
+    int cus = 0;
+    if (int st = device_cus(&cus)) return st;
+    void *ws = nullptr;
+    if (int st = scratch_on_current_device((hipStream_t)stream, &ws)) return st;
+    return status_of(gemvq::launch_lm_head_argmax(W, x, nullptr, out_idx, out_max, ws, N, K, cus,
+                                                  (hipStream_t)stream, gemvq::Timing{}));
 }
 
 int lm_head_argmax_masked(const void *W, const float *x, const uint32_t *mask, uint32_t *out_idx, float *out_max,

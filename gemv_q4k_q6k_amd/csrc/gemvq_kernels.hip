@@ -2248,6 +2248,18 @@ hipError_t launch_q4k_gemv_multi(const void *const *W, const int64_t *N, float *
     return launch_per_cu(gemv_rows_kernel<kQ4K, kStore, 1>, pl.waves, pl, a, cus, s, Timing{});
 }
 
+__global__ __launch_bounds__(256) void fill_zero_kernel(u32x4 *p, int n16)
+{
+    for (int i = (int)threadIdx.x; i < n16; i += (int)blockDim.x) p[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
+hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s)
+{
+    if (bytes % 16 != 0 || bytes > 65536 || ((uintptr_t)p & 15) != 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(1), dim3(256), 0, s, (u32x4 *)p, (int)(bytes / 16));
+    return hipGetLastError();
+}
+
 hipError_t launch_q8_quantize(const float *x, int8_t *xq, uint16_t *xd, int64_t K, hipStream_t s)
 {
     const int threads = 256;

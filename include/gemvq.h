@@ -263,6 +263,24 @@ int lm_head_argmax_masked(const void *W, const float *x, const uint32_t *mask, u
                           float *out_max, void *workspace, size_t ws_bytes, int64_t N, int64_t K,
                           void *stream);
 
+/*
+ * lm_head_argmax for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same kernel, result, checks and errors, but the workspace is the
+ * library's own file-scope device array of gemvq_lm_head_argmax_ws_bytes()
+ * (12,288) bytes, one per GPU, held until the process ends; no call
+ * allocates.  The first call on a GPU looks up the array's address and clears
+ * its counters with a small kernel on `stream`, ordered before the argmax
+ * launch; every call leaves them zero.  Any shape lm_head_argmax accepts fits
+ * the array (the argmax grid, and so the workspace, has a fixed maximum).
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (concurrent streams, or threads without ordering) race and give wrong
+ * results; calls ordered on one stream, or in one captured graph, are safe.
+ *   W, x, out_idx, out_max, N, K, stream: as lm_head_argmax.
+ */
+int lm_head_argmax_noalloc(const void *W, const float *x, uint32_t *out_idx, float *out_max,
+                           int64_t N, int64_t K, void *stream);
+
 /* Workspace bytes lm_head_argmax needs for an N x K call (host-only, no HIP call). */
 size_t gemvq_lm_head_argmax_ws_bytes(int64_t N, int64_t K);
 

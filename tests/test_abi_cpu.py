@@ -261,3 +261,22 @@ def test_batch_rejections():
         _rejected(fn(A, B, C, C + 16, 4, 256, 2, None), gq.ERR_ALIAS)          # y over the second scales
     _rejected(L.q4k_q8_gemv_batch(A + 4, B, C, D, 4, 256, 2, None), gq.ERR_ALIGN)   # Q4_K weights need 16 B
     _rejected(L.q6k_q8_gemv_batch(A + 2, B, C, D, 4, 256, 2, None), gq.ERR_ALIGN)   # Q6_K weights need 4 B
+
+
+def test_lm_head_argmax_noalloc_rejections():
+    """The no-allocation lm_head entry point checks its arguments like
+    lm_head_argmax (no workspace argument), before any HIP call."""
+    L = gq.lib()
+    _rejected(L.lm_head_argmax_noalloc(None, B, C, None, 4, 256, None), gq.ERR_NULL)
+    _rejected(L.lm_head_argmax_noalloc(A, None, C, None, 4, 256, None), gq.ERR_NULL)
+    _rejected(L.lm_head_argmax_noalloc(A, B, None, D, 4, 256, None), gq.ERR_NULL)
+    _rejected(L.lm_head_argmax_noalloc(A, B, C, None, 0, 256, None), gq.ERR_SHAPE)
+    _rejected(L.lm_head_argmax_noalloc(A, B, C, None, 4, 300, None), gq.ERR_SHAPE)
+    _rejected(L.lm_head_argmax_noalloc(A, B, C, None, 4, 65536, None), gq.ERR_SHAPE)
+    _rejected(L.lm_head_argmax_noalloc(A + 2, B, C, None, 4, 256, None), gq.ERR_ALIGN)
+    _rejected(L.lm_head_argmax_noalloc(A, B + 4, C, None, 4, 256, None), gq.ERR_ALIGN)
+    _rejected(L.lm_head_argmax_noalloc(A, B, C + 1, None, 4, 256, None), gq.ERR_ALIGN)
+    _rejected(L.lm_head_argmax_noalloc(A, B, C, D + 2, 4, 256, None), gq.ERR_ALIGN)
+    _rejected(L.lm_head_argmax_noalloc(A, B, A + 64, None, 4, 256, None), gq.ERR_ALIAS)   # idx inside W
+    _rejected(L.lm_head_argmax_noalloc(A, B, B + 16, None, 4, 256, None), gq.ERR_ALIAS)   # idx inside x
+    _rejected(L.lm_head_argmax_noalloc(A, B, C, C, 4, 256, None), gq.ERR_ALIAS)           # max == idx
