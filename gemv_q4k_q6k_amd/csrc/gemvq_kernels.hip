@@ -370,16 +370,21 @@ __device__ __forceinline__ void emit_row(const GemvArgs &a, int64_t row, const f
 __device__ __forceinline__ uint32_t *ws_count(uint8_t *ws) { return (uint32_t *)ws; }
 __device__ __forceinline__ uint64_t *ws_key(uint8_t *ws) { return (uint64_t *)(ws + kArgmaxKeyOff); }
 
-// Grid-level argmax without fences: the threads' running keys meet in LDS
-// (one barrier) and wave 0 folds them with DPP and lane reads.  Thread 0 then merges the
+// Grid-level argmax: the threads' running keys meet in LDS (one barrier) and
+// wave 0 folds them with DPP and lane reads.  Thread 0 then merges the
 // workgroup's key into the running key with a returning atomic max (device
-// scope, so it has been performed before the count below) and counts the
-// workgroup done.  The workgroup whose count completes the grid reads the
-// running key, writes the 4-byte result and sets both words back to zero.
-// Keys are order-keeping (argmax_key), so the largest key is the largest
-// value with the smallest index, whatever order the workgroups finish in.
-// Device-scope atomics are coherent across all XCDs, so no cache writeback
-// or invalidation is needed; the last workgroup waits for three dependent
+// scope) and counts the workgroup done.  The max's returned value is consumed
+// behind a compiler memory barrier before the count is issued, so the count
+// leaves the CU only after the max has been performed at the device's
+// coherence point; the workgroup whose count completes the grid then reads
+// the running key there with a device-scope load and sees every merged key.
+// It writes the 4-byte result and sets both words back to zero.  Keys are
+// order-keeping (argmax_key), so the largest key is the largest value with
+// the smallest index, whatever order the workgroups finish in.  A release
+// add and an acquire load would state the same order in the memory model,
+// but on this target they write back and invalidate the XCD's L2 (measured:
+// the timed lm_head 37.12 -> 37.80 us); device-scope atomics need neither to
+// be coherent across the XCDs.  The last workgroup waits for three dependent
 // round trips (max, count, read).
 // `holders` threads (0..holders-1) carry running keys.
 __device__ void argmax_finish(const GemvArgs &a, uint64_t best, int holder, int holders)
@@ -394,7 +399,7 @@ __device__ void argmax_finish(const GemvArgs &a, uint64_t best, int holder, int 
     if (threadIdx.x != 0) return;
     if (k) {
         const uint64_t old = __hip_atomic_fetch_max(ws_key(a.ws), k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        asm volatile("" ::"v"(old));   // consumed: the max is performed before the count
+        asm volatile("" ::"v"(old) : "memory");   // consumed: the max is performed before the count
     }
     const uint32_t prev = __hip_atomic_fetch_add(ws_count(a.ws), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (prev != gridDim.x - 1) return;
@@ -446,7 +451,10 @@ __device__ __forceinline__ int8_t q8_encode(float v, uint16_t &dbits)
 // completes 32 reads the block back, encodes it and clears the counter, so
 // every counter is zero again between calls.  No workgroup waits for
 // another.  Workspace: counters (u32 per block) at ws[0], row values at
-// ws[emit_vals_off].
+// ws[emit_vals_off].  As in argmax_finish, the order of the exchanges before
+// the count comes from consuming their returned values behind a compiler
+// memory barrier; a release add and acquire loads measured 10.5 -> 13.8 us
+// at 9728 x 2560 (L2 writeback and invalidation).
 __device__ void q8_emit_finish(const GemvArgs &a, const float *s_h, int64_t r0, int64_t r1)
 {
     __syncthreads();   // every row of the range is in LDS

@@ -89,6 +89,30 @@ def activation_outliers(rng: np.random.Generator, K: int, var: float = 2.0,
     return x.astype(np.float32)
 
 
+def activation_wide_range(rng: np.random.Generator, K: int) -> np.ndarray:
+    """f32[K] with a wide dynamic range inside every aligned 64-value part
+    (stress input for kernels that scale each part to a common exponent).
+
+    Draw order: N(0, 1) values (K); per part, one index U{0..63} (K/64) and
+    one sign (K/64).  The drawn entry of every part becomes
+    sign * 1e4 * (1 + |value|); then every 7th part (part p with p % 7 == 3) is scaled by 1e-6,
+    every 13th (p % 13 == 5) by 1e-30 and every 11th (p % 11 == 9) set to zero,
+    in that order."""
+    assert K % 64 == 0
+    x = rng.standard_normal(K)
+    parts = K // 64
+    idx = rng.integers(0, 64, parts)
+    sign = np.where(rng.integers(0, 2, parts) == 0, -1.0, 1.0)
+    x = x.reshape(parts, 64)
+    rows = np.arange(parts)
+    x[rows, idx] = sign * 1e4 * (1.0 + np.abs(x[rows, idx]))
+    p = np.arange(parts)
+    x[p % 7 == 3] *= 1e-6
+    x[p % 13 == 5] *= 1e-30
+    x[p % 11 == 9] = 0.0
+    return x.reshape(K).astype(np.float32)
+
+
 def q8_activations(rng: np.random.Generator, m: int, K: int):
     """m Q8 activation vectors drawn directly in their stored form, for the
     int8 GEMVs: (xq int8 [m, K], xd fp16 bits uint16 [m, K/32]).  Values

@@ -6,11 +6,16 @@ replayed any number of times (the graph-replay decode loop of memra-engine
 decode.rs, `decode_step_dc_cap`).  Each replay is checked bit for bit against
 the same calls made eagerly on the same inputs, with the inputs changed and
 other GPU work done between replays, so the graph is known to read its inputs
-live and to reset its own state.
+live and to reset its own state.  Every replay's outputs are also checked
+against the CPU oracle on the same inputs (as the pages' graph-decode gate
+compares the captured step with the uncaptured reference): f32 outputs
+within E-inf <= 2e-3, the Q8 activation exact, both argmaxes equal to the
+oracle's whenever its top-2 gap exceeds 1e-3.
 """
 import numpy as np
 import pytest
 
+import oracle
 import synth
 
 torch = pytest.importorskip("torch")
@@ -30,16 +35,31 @@ def up(a, dev):
     return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
 
+def rel_err(y, yhat):
+    return float(np.max(np.abs(np.asarray(y, np.float64) - yhat)) / np.max(np.abs(yhat)))
+
+
+def masked_gap(yhat, mask_bits):
+    """Top-2 gap over the allowed rows (f64)."""
+    v = np.where(mask_bits, -np.inf, yhat)
+    i = int(np.argmax(v))
+    rest = np.delete(v, i)
+    return float(v[i] - np.max(rest))
+
+
 def test_decode_step_graph_replays(dev):
     import gemv_q4k_q6k_amd as gq
     r = synth.rng_for(2024)
     shapes = {"attn": (4096, 2560), "lm": (20_000, 1024), "ffn": (2048, 2560), "q8": (3000, 8192)}
-    Wa = up(synth.q4k_weights(r, *shapes["attn"]), dev)
-    Wl = up(synth.q6k_weights(r, *shapes["lm"]), dev)
-    Wg = up(synth.q4k_weights(r, *shapes["ffn"]), dev)
-    Wu = up(synth.q4k_weights(r, *shapes["ffn"]), dev)
-    Wd = up(synth.q6k_weights(r, shapes["ffn"][1], shapes["ffn"][0]), dev)
-    W8 = up(synth.q4k_weights(r, *shapes["q8"]), dev)
+    host = {
+        "Wa": synth.q4k_weights(r, *shapes["attn"]),
+        "Wl": synth.q6k_weights(r, *shapes["lm"]),
+        "Wg": synth.q4k_weights(r, *shapes["ffn"]),
+        "Wu": synth.q4k_weights(r, *shapes["ffn"]),
+        "Wd": synth.q6k_weights(r, shapes["ffn"][1], shapes["ffn"][0]),
+        "W8": synth.q4k_weights(r, *shapes["q8"]),
+    }
+    Wa, Wl, Wg, Wu, Wd, W8 = (up(host[k], dev) for k in ("Wa", "Wl", "Wg", "Wu", "Wd", "W8"))
     N_lm, K_lm = shapes["lm"]
     mask_bits = np.random.default_rng(3).random(N_lm) < 0.5
     mask = up(np.packbits(np.concatenate([mask_bits, np.zeros((-N_lm) % 32, bool)]),
@@ -90,6 +110,32 @@ def test_decode_step_graph_replays(dev):
     with torch.cuda.graph(graph):
         step(og, ws, ws2)
 
+    def check_against_oracle(rep, o):
+        """The replayed step's outputs against the CPU oracle on the replay's inputs."""
+        g = {k: v.cpu().numpy() for k, v in o.items()}
+        xa_, xl_, xf_, x8_ = (t.cpu().numpy() for t in (xa, xl, xf, x8))
+        e = rel_err(g["ya"], oracle.q4k_gemv(host["Wa"], xa_, *shapes["attn"]))
+        assert e <= 2e-3, (rep, "ya", e)
+        yl = oracle.q6k_gemv(host["Wl"], xl_, N_lm, K_lm)
+        if oracle.top2_gap(yl) > 1e-3:
+            assert int(g["idx"][0]) == oracle.argmax_first(yl), (rep, "idx")
+        assert abs(float(g["vmax"][0]) - yl.max()) <= 2e-3 * np.max(np.abs(yl)), (rep, "vmax")
+        words = np.packbits(np.concatenate([mask_bits, np.zeros((-N_lm) % 32, bool)]), bitorder="little").view(np.uint32)
+        if masked_gap(yl, mask_bits) > 1e-3:
+            assert int(g["midx"][0]) == oracle.argmax_first_masked(yl, words), (rep, "midx")
+        assert not mask_bits[int(g["midx"][0])], (rep, "midx banned")
+        N_f, K_f = shapes["ffn"]
+        hhat = oracle.swiglu(host["Wg"], host["Wu"], xf_, N_f, K_f)[0]
+        e = rel_err(g["h"], hhat)
+        assert e <= 2e-3, (rep, "h", e)
+        e = rel_err(g["yd"], oracle.q6k_gemv_f64x(host["Wd"], hhat, K_f, N_f))
+        assert e <= 2e-3, (rep, "yd", e)
+        q, d = oracle.q8_quantize(x8_)
+        assert np.array_equal(g["xq"], q) and np.array_equal(g["xd"].view(np.uint16), d), (rep, "xq/xd")
+        e = rel_err(g["y8"], oracle.q4k_q8_gemv(host["W8"], q, d, *shapes["q8"]))
+        assert e <= 2e-3, (rep, "y8", e)
+        print(f"replay {rep}: outputs match the oracle", flush=True)
+
     ref_ws = torch.zeros_like(ws)
     ref_ws2 = torch.zeros_like(ws)
     for rep in range(4):
@@ -106,3 +152,4 @@ def test_decode_step_graph_replays(dev):
             assert torch.equal(og[k], oe[k]), (rep, k)
         for w in (ws, ws2):
             assert int(torch.count_nonzero(w[:4096]).item()) == 0, rep
+        check_against_oracle(rep, og)

@@ -870,3 +870,64 @@ def test_int8_ffn_pipeline_full(dev):
     y = gq().q6k_q8_gemv(up(Wd, dev), hq, hd, K, N).cpu().numpy()
     _, q, d = oracle.swiglu_q8(Wg, Wu, x, N, K)
     check_f32("int8 FFN 9728x2560 -> 2560x9728", y, oracle.q6k_q8_gemv(Wd, q, d, K, N))
+
+
+# ------------------------------------------------- fixed-point activations
+# Kernels that hold the f32 activation in 23-bit fixed point scale each
+# 64-value part to its largest |x|: an element's rounding error is at most
+# 2^-23 of that value.  These cases put a +-1e4 outlier in every part next to
+# ordinary, tiny (1e-6, 1e-30) and zero parts; the parity bounds stay those of
+# every f32 case (E-inf <= 2e-3, conditioned error <= 1e-4 where computed).
+WIDE_CASES = [
+    ("q6k", 3000, 1024, "wave1"),
+    ("q6k", 700, 9728, "tile-res-lds"),
+    ("q6k", 20000, 2560, "tile-ring-lds"),
+    ("q4k", 2000, 8192, "rows2"),
+    ("q4k", 333, 2560, "rows1"),
+    ("swiglu", 2000, 2560, "tile-res-lds"),
+]
+
+
+@pytest.mark.parametrize("fmt,N,K,path", WIDE_CASES)
+def test_fixed_point_wide_range(dev, fmt, N, K, path):
+    from parity_shapes import kernel_path
+    kind = {"q6k": gq().KIND_Q6K, "q4k": gq().KIND_Q4K, "swiglu": gq().KIND_SWIGLU}[fmt]
+    assert kernel_path(kind, N, K) == path
+    r = synth.rng_for(4400 + N + K)
+    x = synth.activation_wide_range(r, K)
+    print(f"wide-range {fmt} N={N} K={K} ({path})", flush=True)
+    if fmt == "swiglu":
+        Wg, Wu = synth.q4k_weights(r, N, K), synth.q4k_weights(r, N, K)
+        h = gq().swiglu_gemv(up(Wg, dev), up(Wu, dev), up(x, dev), N, K).cpu().numpy()
+        check_f32(f"wide swiglu {N}x{K}", h, oracle.swiglu(Wg, Wu, x, N, K)[0])
+        return
+    W = (synth.q6k_weights if fmt == "q6k" else synth.q4k_weights)(r, N, K)
+    run = gq().q6k_gemv if fmt == "q6k" else gq().q4k_gemv
+    y = run(up(W, dev), up(x, dev), N, K).cpu().numpy()
+    yhat = (oracle.q6k_gemv if fmt == "q6k" else oracle.q4k_gemv)(W, x, N, K)
+    cond = None
+    if N * K <= 20_000_000:
+        cond = (q6k_abs_rows if fmt == "q6k" else q4k_abs_rows)(W, x, N, K)
+    check_f32(f"wide {fmt} {N}x{K}", y, yhat, cond)
+
+
+@pytest.mark.parametrize("N", [20_000, 248_320])
+def test_lm_head_argmax_wide_range(dev, N):
+    """The lm_head argmax on a wide-range activation: the oracle's index when
+    its top-2 gap exceeds 1e-3, and always the first-index argmax of the
+    device's own Q6_K GEMV (same row values)."""
+    K = 1024
+    r = synth.rng_for(4500 + N)
+    W = synth.q6k_weights(r, N, K)
+    x = synth.activation_wide_range(r, K)
+    dW, dx = up(W, dev), up(x, dev)
+    ws = torch.zeros(gq().lm_head_argmax_ws_bytes(N, K), dtype=torch.uint8, device=dev)
+    idx = int(gq().lm_head_argmax(dW, dx, N, K, ws).item())
+    own = gq().q6k_gemv(dW, dx, N, K).cpu().numpy()
+    assert idx == oracle.argmax_first(own), idx
+    yhat = oracle.q6k_gemv(W, x, N, K)
+    check_f32(f"wide lm_head logits {N}", own, yhat)
+    gap = oracle.top2_gap(yhat)
+    print(f"wide lm_head N={N}: idx {idx}, oracle {oracle.argmax_first(yhat)}, gap {gap:.3e}", flush=True)
+    if gap > 1e-3:
+        assert idx == oracle.argmax_first(yhat)

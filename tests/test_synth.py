@@ -74,3 +74,20 @@ def test_q8_activations():
     assert d.min() >= 0.00099 and d.max() <= 0.1001
     r = synth.rng_for(0)
     assert _h(*synth.q8_activations(r, 3, 512)) == "dc3893e619f8532f"
+
+
+def test_activation_wide_range():
+    """One +-1e4 outlier in each 64-value part, some parts tiny or zero; f32."""
+    K = 64 * 100
+    a = synth.activation_wide_range(synth.rng_for(5), K)
+    b = synth.activation_wide_range(synth.rng_for(5), K)
+    assert a.dtype == np.float32 and np.array_equal(a, b)
+    parts = a.reshape(-1, 64).astype(np.float64)
+    for p, v in enumerate(parts):
+        m = np.max(np.abs(v))
+        if p % 11 == 9:
+            assert m == 0.0
+            continue
+        scale = (1e-6 if p % 7 == 3 else 1.0) * (1e-30 if p % 13 == 5 else 1.0)
+        assert 1e4 * scale <= m * (1 + 1e-6) and m < 1e5 * scale
+        assert np.sum(np.abs(v) > 100 * scale) == 1     # exactly one outlier
