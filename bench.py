@@ -3,10 +3,11 @@
 
 One step = one pass of the whole hot path over the five workloads' shapes, all
 enqueued on one stream:
-  1. Q4_K GEMV  4096x2560, 2560x9728, 9728x2560 (4B-class decode shapes)
-  2. lm_head Q6_K 248,320 x 1024 GEMV + fused first-index argmax (4-byte result)
-  3. fused gate/up SwiGLU GEMV (2 x Q4_K 9728x2560) + ffn_down Q6_K 2560x9728
-  4. Q8 quantize of an f32[8192] activation + Q4_K x Q8 GEMV 28672x8192
+  1. Q4_K GEMV 1024x1024 (config 1)
+  2. Q4_K GEMV  4096x2560, 2560x9728, 9728x2560 (4B-class decode shapes)
+  3. lm_head Q6_K 248,320 x 1024 GEMV + fused first-index argmax (4-byte result)
+  4. fused gate/up SwiGLU GEMV (2 x Q4_K 9728x2560) + ffn_down Q6_K 2560x9728
+  5. Q8 quantize of an f32[8192] activation + Q4_K x Q8 GEMV 28672x8192
 Weights are seeded synthetic data with the workloads' distributions.  Two
 copies of every weight buffer alternate between steps, so each buffer is
 re-read only after ~0.85 GB of other traffic and the 256 MB Infinity Cache
@@ -17,7 +18,10 @@ bytes streamed per step / time per step), plus the lm_head-argmax calls/s,
 a roofline entry for the dominant kernel (its algorithmic bytes / its average
 kernel duration: the lm_head launch itself records its start and end into HIP
 events on the launch stream, inside the timed region) and the CPU oracle timed
-on the host on a bounded sample.
+on the host on a bounded sample.  `configs` reports each workload on its own
+(us per call, GEMV/s, weight GB/s, fraction of 8 TB/s and of a plain
+streaming read of the same byte count, the oracle's time on one host thread
+and on all of them); `kernels` is the per-kernel breakdown.
 """
 from __future__ import annotations
 
@@ -63,14 +67,16 @@ def build_workload(dev):
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
     t0 = time.time()
+    c1 = synth.c1_inputs(0)
     c2 = [synth.c2_inputs(i) for i in range(3)]
     c3 = synth.c3_inputs(0)
     c4 = synth.c4_inputs(0)
     c5 = synth.c5_inputs(0)
-    host = {"c2": c2, "c3": c3, "c4": c4, "c5": c5}
+    host = {"c1": c1, "c2": c2, "c3": c3, "c4": c4, "c5": c5}
     sets = []
     for copy in range(2):
         s = {
+            "c1W": up(c1[0]),
             "c2W": [up(W) for W, _ in c2],
             "c3W": up(c3[0]),
             "c4Wg": up(c4[0]), "c4Wu": up(c4[1]), "c4Wd": up(c4[2]),
@@ -78,6 +84,8 @@ def build_workload(dev):
         }
         sets.append(s)
     vec = {
+        "c1x": up(c1[1]),
+        "c1y": torch.empty(synth.C1_Q4K[0], dtype=torch.float32, device=dev),
         "c2x": [up(x) for _, x in c2],
         "c3x": up(c3[1]),
         "c4x": up(c4[3]),
@@ -99,6 +107,8 @@ def build_workload(dev):
 def weight_bytes():
     import synth
     b = {}
+    N, K = synth.C1_Q4K
+    b["c1"] = N * K // 256 * 144
     b["c2"] = sum(N * K // 256 * 144 for N, K in synth.C2_Q4K)
     N, K = synth.C3_LM_HEAD
     b["c3"] = N * K // 256 * 210
@@ -126,6 +136,8 @@ def step_calls(gq, s, v):
     L = gq.lib()
     st = torch.cuda.current_stream().cuda_stream
     calls = []
+    N, K = synth.C1_Q4K
+    calls.append((L.q4k_gemv, (s["c1W"].data_ptr(), v["c1x"].data_ptr(), v["c1y"].data_ptr(), N, K, st)))
     for i, (N, K) in enumerate(synth.C2_Q4K):
         calls.append((L.q4k_gemv, (s["c2W"][i].data_ptr(), v["c2x"][i].data_ptr(), v["c2y"][i].data_ptr(), N, K, st)))
     N, K = synth.C3_LM_HEAD
@@ -157,6 +169,8 @@ def run_calls(calls, lm, events=None):
 def run_step(gq, s, v):
     """One pass of the hot path through the checked binding."""
     import synth
+    N, K = synth.C1_Q4K
+    gq.q4k_gemv(s["c1W"], v["c1x"], N, K, y=v["c1y"])
     for i, (N, K) in enumerate(synth.C2_Q4K):
         gq.q4k_gemv(s["c2W"][i], v["c2x"][i], N, K, y=v["c2y"][i])
     N, K = synth.C3_LM_HEAD
@@ -236,6 +250,69 @@ def self_check(gq, sets, v):
     return bool(ok)
 
 
+MIN_ROTATE_BYTES = 640 << 20     # weight copies per timed kernel: beyond the 256 MB Infinity Cache
+
+
+def graph_us(fn, ws, reps=24):
+    """Per-call device time of fn: `reps` calls (rotating through the
+    per-copy argument tuples ws) captured in one HIP graph, four warm
+    replays, then the median of 7 trials of 3 replays between two HIP events
+    (no host launch overhead).  Every copy is touched twice before the
+    capture (first touches of fresh copies run slower)."""
+    import torch
+    for r in range(2 * len(ws)):
+        fn(ws[r % len(ws)])
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for r in range(reps):
+            fn(ws[r % len(ws)])
+    for _ in range(4):
+        g.replay()
+    torch.cuda.synchronize()
+    trials = []
+    for _ in range(7):
+        st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        st.record()
+        for _ in range(3):
+            g.replay()
+        en.record()
+        torch.cuda.synchronize()
+        trials.append(st.elapsed_time(en) * 1000.0 / (reps * 3))
+    del g
+    return float(np.median(trials))
+
+
+READ_GRIDS = (256, 512, 1024, 2048, 4096, 8192)
+
+
+def read_ceiling(gq, dev, sizes, in_cache=()):
+    """Streaming-read time of each byte count: the library's plain read
+    kernel (16-byte loads, grid-stride) over slices of one pool, rotating
+    through >= 640 MB of slices (sizes listed in in_cache: one slice, read
+    again and again, as the in-cache config it matches), best of a few
+    grids.  {bytes: {"us", "GBps", "grid", "in_cache"}}."""
+    import torch
+    pool = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(256, dtype=torch.int32, device=dev)
+    out = {}
+    for S in sizes:
+        S16 = S - S % 16
+        stride = -(-S16 // 256) * 256
+        n = 1 if S in in_cache else max(2, min(pool.numel() // stride, -(-MIN_ROTATE_BYTES // S16)))
+        bufs = [(pool[i * stride:i * stride + S16],) for i in range(n)]
+        best = None
+        for grid in READ_GRIDS:
+            us = graph_us(lambda w, grid=grid: gq.stream_read(w[0], grid, sink), bufs)
+            if best is None or us < best[0]:
+                best = (us, grid)
+        out[S] = {"us": round(best[0], 2), "GBps": round(S16 / best[0] / 1e3, 1), "grid": best[1],
+                  "in_cache": S in in_cache}
+    del pool
+    torch.cuda.empty_cache()
+    return out
+
+
 def breakdown(gq, sets, v, reps=24):
     """Per-call device time of each kernel, not part of `value`: `reps`
     launches are captured in a HIP graph and replayed between two HIP events
@@ -254,63 +331,67 @@ def breakdown(gq, sets, v, reps=24):
         n = max(2, -(-min_bytes // t.numel()))
         return [t] + [t.clone() for _ in range(n - 1)]
 
-    def timeit(name, fn, ws, nbytes):
-        # ws: list of per-copy weight tuples; every copy is touched twice
-        # before the capture (first touches of fresh copies are slower)
-        for r in range(2 * len(ws)):
-            fn(ws[r % len(ws)])
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for r in range(reps):
-                fn(ws[r % len(ws)])
-        for _ in range(4):   # warm replays: the first after new weight copies run slower
-            g.replay()
-        torch.cuda.synchronize()
-        trials = []
-        for _ in range(7):   # the median of 7 trials of 3 replays each
-            st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            st.record()
-            for _ in range(3):
-                g.replay()
-            en.record()
-            torch.cuda.synchronize()
-            trials.append(st.elapsed_time(en) * 1000.0 / (reps * 3))
-        us = float(np.median(trials))
+    def timeit(name, fn, ws, nbytes, weight_bytes=None, in_cache=False):
+        """ws: list of per-copy weight tuples; nbytes: algorithmic bytes per
+        call; weight_bytes: the matrix bytes it streams (the read ceiling is
+        matched to them)."""
+        us = graph_us(fn, ws, reps)
         out[name] = {"us": round(us, 2), "GBps": round(nbytes / us / 1e3, 1),
-                     "frac_hbm_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4), "weight_copies": len(ws)}
-        del g
+                     "frac_hbm_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4), "weight_copies": len(ws),
+                     "weight_bytes": weight_bytes}
+        if in_cache:
+            out[name]["in_cache"] = True
 
     s0 = sets[0]
+    # config 1: 1024 x 1024 (590 KB) is read from the Infinity Cache after the
+    # first call; reported as such, not against the HBM roofline
+    N, K = synth.C1_Q4K
+    timeit("c1_q4k_gemv_1024x1024_in_cache", lambda w: gq.q4k_gemv(w[0], v["c1x"], N, K, y=v["c1y"]),
+           [(s0["c1W"],)], N * K // 256 * 144 + 4 * (N + K), N * K // 256 * 144, in_cache=True)
+    # config 2: the three decode shapes back to back, each rotating its copies
+    trip = list(zip(*[copies(s0["c2W"][i]) for i in range(3)]))
+
+    def c2_triple(w):
+        for i, (N, K) in enumerate(synth.C2_Q4K):
+            gq.q4k_gemv(w[i], v["c2x"][i], N, K, y=v["c2y"][i])
+    c2_bytes = sum(N * K // 256 * 144 for N, K in synth.C2_Q4K)
+    timeit("c2_q4k_gemv_triple", c2_triple, trip, c2_bytes + sum(4 * (N + K) for N, K in synth.C2_Q4K), c2_bytes)
+    del trip
     for i, (N, K) in enumerate(synth.C2_Q4K):
         ws = [(w,) for w in copies(s0["c2W"][i])]
         timeit(f"q4k_gemv_{N}x{K}", lambda w, i=i, N=N, K=K: gq.q4k_gemv(w[0], v["c2x"][i], N, K, y=v["c2y"][i]),
-               ws, N * K // 256 * 144 + 4 * (N + K))
+               ws, N * K // 256 * 144 + 4 * (N + K), N * K // 256 * 144)
         del ws
     N, K = synth.C3_LM_HEAD
     ws = [(w,) for w in copies(s0["c3W"])]
     timeit("q6k_gemv_248320x1024", lambda w: gq.q6k_gemv(w[0], v["c3x"], N, K, y=yl), ws,
-           N * K // 256 * 210 + 4 * (N + K))
+           N * K // 256 * 210 + 4 * (N + K), N * K // 256 * 210)
     timeit("lm_head_argmax_248320x1024", lambda w: gq.lm_head_argmax(w[0], v["c3x"], N, K, v["ws"], out_idx=v["idx"]),
-           ws, lm_head_algorithmic_bytes())
+           ws, lm_head_algorithmic_bytes(), N * K // 256 * 210)
     del ws
     N, K = synth.C4_SWIGLU
     ws = list(zip(copies(s0["c4Wg"]), copies(s0["c4Wu"])))
     timeit("swiglu_gemv_9728x2560", lambda w: gq.swiglu_gemv(w[0], w[1], v["c4x"], N, K, h=v["h"]), ws,
-           2 * N * K // 256 * 144 + 4 * (N + K))
+           2 * N * K // 256 * 144 + 4 * (N + K), 2 * N * K // 256 * 144)
     del ws
     ws = [(w,) for w in copies(s0["c4Wd"])]
     timeit("q6k_gemv_2560x9728", lambda w: gq.q6k_gemv(w[0], v["h"], K, N, y=v["yd"]), ws,
-           K * N // 256 * 210 + 4 * (N + K))
+           K * N // 256 * 210 + 4 * (N + K), K * N // 256 * 210)
     del ws
     N, K = synth.C5_Q8
     timeit("q8_quantize_8192", lambda w: gq.q8_quantize(v["c5x"], xq=v["xq"], xd=v["xd"]), [()],
            K * 4 + K + K // 16)
     ws = [(w,) for w in copies(s0["c5W"])]
     timeit("q4k_q8_gemv_28672x8192", lambda w: gq.q4k_q8_gemv(w[0], v["xq"], v["xd"], N, K, y=v["c5y"]), ws,
-           N * K // 256 * 144 + K + K // 16 + 4 * N)
+           N * K // 256 * 144 + K + K // 16 + 4 * N, N * K // 256 * 144)
+
+    def c5(w):
+        gq.q8_quantize(v["c5x"], xq=v["xq"], xd=v["xd"])
+        gq.q4k_q8_gemv(w[0], v["xq"], v["xd"], N, K, y=v["c5y"])
+    timeit("c5_q8_quantize+q4k_q8_gemv_28672x8192", c5, ws,
+           N * K // 256 * 144 + 4 * K + 2 * (K + K // 16) + 4 * N, N * K // 256 * 144)
     timeit("q4k_gemv_28672x8192", lambda w: gq.q4k_gemv(w[0], v["c5x"], N, K, y=v["c5y"]), ws,
-           N * K // 256 * 144 + 4 * (N + K))
+           N * K // 256 * 144 + 4 * (N + K), N * K // 256 * 144)
     del ws
     # the fused q/k/v projection of a 4B-class attention block (one launch for
     # three Q4_K matrices sharing x) against three separate launches
@@ -361,7 +442,7 @@ def breakdown(gq, sets, v, reps=24):
         gq.q6k_q8_gemv(w[2], hq, hd, K, N, y=v["yd"])
     for name, fn in (("ffn_f32_swiglu+q6k", ffn_f32), ("ffn_q8_swiglu+quantize+q6k_q8", ffn_q8_unfused),
                      ("ffn_q8_swiglu_q8+q6k_q8", ffn_q8_fused)):
-        timeit(name, fn, ffn, gu_bytes + d_bytes)
+        timeit(name, fn, ffn, gu_bytes + d_bytes, gu_bytes + d_bytes)
     del ffn
     # batched int8 GEMV: m Q8 activation vectors through one weight read, on
     # the 70B-class FFN matrix and on the Q6_K lm_head
@@ -433,77 +514,228 @@ def _pick(means, pred, what):
     return hits[0]
 
 
+def traffic_kernels():
+    """(tag, demangled-name pattern of the kernel's one instantiation in the
+    step, algorithmic bytes per launch, record path) of the kernels whose
+    HBM traffic is recorded."""
+    import synth
+    out = [("lm_head_argmax", r"gemv_(wave_)?kernel<1, 1,", lm_head_algorithmic_bytes(), PROFILE_TRAFFIC)]
+    N, K = synth.C4_SWIGLU
+    out.append(("swiglu_gemv_9728x2560", r"gemv_kernel<3, 0, \d, true, true>", 2 * N * K // 256 * 144 + 4 * (N + K),
+                os.path.join(ROOT, "profiles", "traffic_swiglu_gemv_9728x2560.json")))
+    out.append(("q6k_gemv_2560x9728", r"gemv_kernel<1, 0, \d, true, true>", K * N // 256 * 210 + 4 * (N + K),
+                os.path.join(ROOT, "profiles", "traffic_q6k_gemv_2560x9728.json")))
+    N, K = synth.C5_Q8
+    out.append(("q4k_q8_gemv_28672x8192", r"gemv_wave_kernel<2, 0, 2>", N * K // 256 * 144 + K + K // 16 + 4 * N,
+                os.path.join(ROOT, "profiles", "traffic_q4k_q8_gemv_28672x8192.json")))
+    return out
+
+
 def write_traffic(fetch_db, write_db, command):
     """Turn two rocprofv3 --pmc runs of `bench.py --calibration-copy` (one
-    with FETCH_SIZE, one with WRITE_SIZE) into HBM bytes per lm_head launch,
-    scaled by what the same counters read for the calibration copy, and store
-    them next to the kernel-source hash they were taken on."""
+    with FETCH_SIZE, one with WRITE_SIZE) into HBM bytes per launch of each
+    recorded kernel, scaled by what the same counters read for the
+    calibration copy, and store each next to the kernel-source hash it was
+    taken on."""
     known = CALIB_MIB << 20
-    is_lm = lambda k: re.search(r"gemv_(wave_)?kernel<1, 1,", k) is not None   # Q6_K rows, argmax epilogue
     is_cal = lambda k: CALIB_TAG in k
     fm, wm = _counter_means(fetch_db, "FETCH_SIZE"), _counter_means(write_db, "WRITE_SIZE")
-    lm_name, (lm_f, n_f) = _pick(fm, is_lm, "lm_head")
-    _, (lm_w, n_w) = _pick(wm, is_lm, "lm_head")
     cal_name, (cal_f, _) = _pick(fm, is_cal, "calibration")
     _, (cal_w, _) = _pick(wm, is_cal, "calibration")
     f_fac = known / (cal_f * 1024.0)
     w_fac = known / (cal_w * 1024.0)
-    fetch_b = lm_f * 1024.0 * f_fac
-    write_b = lm_w * 1024.0 * w_fac
-    out = {
-        "kernel": lm_name, "dispatches": {"fetch": n_f, "write": n_w},
-        "fetch_size_kib_per_dispatch": round(lm_f, 1), "write_size_kib_per_dispatch": round(lm_w, 1),
-        "calibration": {"kernel": cal_name, "bytes_read": known, "bytes_written": known,
-                        "fetch_size_kib": round(cal_f, 1), "write_size_kib": round(cal_w, 1),
-                        "fetch_factor": round(f_fac, 4), "write_factor": round(w_fac, 4)},
-        "hbm_fetch_bytes_per_launch": int(round(fetch_b)), "hbm_write_bytes_per_launch": int(round(write_b)),
-        "bytes_per_launch": int(round(fetch_b + write_b)),
-        "algorithmic_bytes_per_launch": lm_head_algorithmic_bytes(),
-        "kernel_source_hash": kernel_source_hash(),
-        "command": command,
-    }
-    os.makedirs(os.path.dirname(PROFILE_TRAFFIC), exist_ok=True)
-    with open(PROFILE_TRAFFIC, "w") as f:
-        json.dump(out, f, indent=1)
-        f.write("\n")
-    print(json.dumps(out))
+    for tag, pat, alg, path in traffic_kernels():
+        is_k = lambda k, pat=pat: re.search(pat, k) is not None
+        if tag != "lm_head_argmax" and not any(is_k(k) for k in fm):
+            continue     # counters taken on a step without this kernel
+        k_name, (k_f, n_f) = _pick(fm, is_k, tag)
+        _, (k_w, n_w) = _pick(wm, is_k, tag)
+        fetch_b = k_f * 1024.0 * f_fac
+        write_b = k_w * 1024.0 * w_fac
+        out = {
+            "kernel": k_name, "workload": tag, "dispatches": {"fetch": n_f, "write": n_w},
+            "fetch_size_kib_per_dispatch": round(k_f, 1), "write_size_kib_per_dispatch": round(k_w, 1),
+            "calibration": {"kernel": cal_name, "bytes_read": known, "bytes_written": known,
+                            "fetch_size_kib": round(cal_f, 1), "write_size_kib": round(cal_w, 1),
+                            "fetch_factor": round(f_fac, 4), "write_factor": round(w_fac, 4)},
+            "hbm_fetch_bytes_per_launch": int(round(fetch_b)), "hbm_write_bytes_per_launch": int(round(write_b)),
+            "bytes_per_launch": int(round(fetch_b + write_b)),
+            "algorithmic_bytes_per_launch": alg,
+            "traffic_over_algorithmic": round((fetch_b + write_b) / alg, 4),
+            "kernel_source_hash": kernel_source_hash(),
+            "command": command,
+        }
+        os.makedirs(os.path.dirname(path), exist_ok=True)
+        with open(path, "w") as f:
+            json.dump(out, f, indent=1)
+            f.write("\n")
+        print(json.dumps(out))
 
 
-def cpu_baseline(host, budget_s=12.0):
-    """The oracle as it stands, on the host cores, on whole steps of the same
-    workload until about budget_s seconds have passed."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_config_calls(host):
+    """{config: (one call of the oracle on that workload, weight bytes)}: the
+    f64 oracle's own functions on the seeded inputs the GPU runs."""
     import oracle
     import synth
-    wb = sum(weight_bytes().values())
-    steps = 0
-    t0 = time.time()
-    while True:
+    wb = weight_bytes()
+
+    def c1():
+        N, K = synth.C1_Q4K
+        oracle.q4k_gemv(host["c1"][0], host["c1"][1], N, K)
+
+    def c2():
         for i, (N, K) in enumerate(synth.C2_Q4K):
             oracle.q4k_gemv(host["c2"][i][0], host["c2"][i][1], N, K)
+
+    def c3():
         N, K = synth.C3_LM_HEAD
         oracle.argmax_first(oracle.q6k_gemv(host["c3"][0], host["c3"][1], N, K))
+
+    def c4():
         Wg, Wu, Wd, x = host["c4"]
         N, K = synth.C4_SWIGLU
         h, _, _ = oracle.swiglu(Wg, Wu, x, N, K)
         oracle.q6k_gemv_f64x(Wd, h, K, N)
+
+    def c5():
         W, x = host["c5"]
         N, K = synth.C5_Q8
         q, d = oracle.q8_quantize(x)
         oracle.q4k_q8_gemv(W, q, d, N, K)
-        steps += 1
-        if time.time() - t0 >= budget_s:
-            break
-    dt = time.time() - t0
-    return {"value": round(wb * steps / dt / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": f"{steps} whole steps of the same workload (all four stages, f64 oracle) in {dt:.1f}s"}
+    return {"c1": (c1, wb["c1"]), "c2": (c2, wb["c2"]), "c3": (c3, wb["c3"]), "c4": (c4, wb["c4"]),
+            "c5": (c5, wb["c5"])}
 
 
-def traffic_entry(alg_bytes):
-    """HBM bytes per lm_head launch from committed rocprofv3 counter runs, if
-    they were taken on the current kernel sources."""
+def cpu_baseline(host, budget_s=(1.0, 0.6)):
+    """The oracle as it stands, timed on the host on each workload: on one
+    thread and on all of its OpenMP threads, repeating each config's call
+    until budget_s (one thread, all threads) seconds have passed (at least
+    one call).  `value` is the whole step's weight GB/s on all threads (the
+    sum of the configs' per-call times)."""
+    import oracle
+    calls = oracle_config_calls(host)
+    all_threads = oracle.num_threads()
+    per = {}
+    t_start = time.time()
+    for name, (fn, nbytes) in calls.items():
+        row = {"weight_bytes": nbytes}
+        for label, threads, budget in (("one_thread", 1, budget_s[0]), ("all_threads", all_threads, budget_s[1])):
+            oracle.set_num_threads(threads)
+            n = 0
+            t0 = time.perf_counter()
+            while True:
+                fn()
+                n += 1
+                if time.perf_counter() - t0 >= budget:
+                    break
+            ms = (time.perf_counter() - t0) * 1e3 / n
+            row[label] = {"threads": threads, "ms_per_call": round(ms, 3), "calls_per_s": round(1e3 / ms, 2),
+                          "weight_GBps": round(nbytes / ms / 1e6, 3), "calls_timed": n}
+        per[name] = row
+    oracle.set_num_threads(all_threads)
+    step_ms = sum(r["all_threads"]["ms_per_call"] for r in per.values())
+    wb = sum(weight_bytes().values())
+    return {"value": round(wb / step_ms / 1e6, 3), "unit": "GB/s", "cores": all_threads, "kind": "oracle",
+            "cpu_model": cpu_model(), "host_cpus": len(os.sched_getaffinity(0)),
+            "sample": (f"each of the five workloads' oracle calls (f64) repeated for >= {budget_s[0]} s on one "
+                       f"thread and >= {budget_s[1]} s on {all_threads} threads ({time.time() - t_start:.1f} s in "
+                       f"all); value = the whole step's weight bytes / the sum of the per-config times on "
+                       f"{all_threads} threads"),
+            "per_config": per}
+
+
+def c5_q8_accuracy(gq, host, v):
+    """The Q8 path's result (GPU, config 5) against the exact-x f64 result
+    (reported, not gated; the pages quote cosine 0.9887 for their DP4A path
+    against 0.9999 for the float one)."""
+    import oracle
+    import synth
+    W, x = host["c5"]
+    N, K = synth.C5_Q8
+    gq.q8_quantize(v["c5x"], xq=v["xq"], xd=v["xd"])
+    y8 = gq.q4k_q8_gemv(v["c5W"], v["xq"], v["xd"], N, K).cpu().numpy().astype(np.float64)
+    exact = oracle.q4k_gemv(W, x, N, K)
+    q, d = oracle.q8_quantize(x)
+    q8hat = oracle.q4k_q8_gemv(W, q, d, N, K)
+    cos = float(np.dot(y8, exact) / (np.linalg.norm(y8) * np.linalg.norm(exact)))
+    return {"cosine_vs_exact_x": round(cos, 6),
+            "e_inf_vs_exact_x": float(f"{np.max(np.abs(y8 - exact)) / np.max(np.abs(exact)):.3e}"),
+            "e_inf_vs_oracle_q8_path": float(f"{np.max(np.abs(y8 - q8hat)) / np.max(np.abs(q8hat)):.3e}"),
+            "oracle_q8_cosine_vs_exact_x": round(float(np.dot(q8hat, exact) / (np.linalg.norm(q8hat) *
+                                                                               np.linalg.norm(exact))), 6)}
+
+
+CONFIG_KERNELS = {
+    # config: (breakdown entry, weight bytes per call, the read launches its ceiling counts, label)
+    "c1": ("c1_q4k_gemv_1024x1024_in_cache", ("c1",), "Q4_K 1024x1024 (in cache: 590 KB, not HBM-bound)"),
+    "c2": ("c2_q4k_gemv_triple", ("c2a", "c2b", "c2c"), "Q4_K 4096x2560 + 2560x9728 + 9728x2560 back to back"),
+    "c3": ("lm_head_argmax_248320x1024", ("c3",), "lm_head Q6_K 248320x1024 + argmax"),
+    "c4": ("ffn_f32_swiglu+q6k", ("c4g", "c4d"), "SwiGLU 2x Q4_K 9728x2560 + Q6_K 2560x9728 (two launches)"),
+    "c5": ("c5_q8_quantize+q4k_q8_gemv_28672x8192", ("c5",), "Q8 quantize + Q4_K x Q8 28672x8192 (two launches)"),
+}
+
+
+def read_sizes():
+    import synth
+    sz = {}
+    N, K = synth.C1_Q4K
+    sz["c1"] = N * K // 256 * 144
+    for tag, (N, K) in zip(("c2a", "c2b", "c2c"), synth.C2_Q4K):
+        sz[tag] = N * K // 256 * 144
+    N, K = synth.C3_LM_HEAD
+    sz["c3"] = N * K // 256 * 210
+    N, K = synth.C4_SWIGLU
+    sz["c4g"] = 2 * N * K // 256 * 144
+    sz["c4d"] = K * N // 256 * 210
+    N, K = synth.C5_Q8
+    sz["c5"] = N * K // 256 * 144
+    return sz
+
+
+def config_summary(kern, ceil, cpu):
+    """Per-config figures from the breakdown, the read ceilings and the CPU
+    oracle timings."""
+    sz = read_sizes()
+    wb = weight_bytes()
+    out = {}
+    for name, (entry, reads, label) in CONFIG_KERNELS.items():
+        k = kern.get(entry)
+        if k is None:
+            continue
+        us = k["us"]
+        read_us = sum(ceil[sz[r]]["us"] for r in reads) if ceil else None
+        row = {"workload": label, "us_per_call": us, "gemv_per_s": round(1e6 / us, 1),
+               "weight_GBps": round(wb[name] / us / 1e3, 1),
+               "frac_hbm_peak": round(wb[name] / us / 1e3 / HBM_PEAK_GBS, 4),
+               "read_ceiling_us": round(read_us, 2) if read_us else None,
+               "frac_read_ceiling": round(read_us / us, 4) if read_us else None}
+        if name == "c1":
+            row["in_cache"] = True
+        if cpu:
+            c = cpu["per_config"][name]
+            row["oracle_ms_per_call"] = {"one_thread": c["one_thread"]["ms_per_call"],
+                                         "all_threads": c["all_threads"]["ms_per_call"]}
+            row["gpu_vs_oracle_all_threads"] = round(c["all_threads"]["ms_per_call"] * 1e3 / us, 1)
+        out[name] = row
+    return out
+
+
+def traffic_entry(alg_bytes, path=None):
+    """HBM bytes per launch from a committed rocprofv3 counter record (the
+    lm_head's by default), if it was taken on the current kernel sources."""
     try:
-        with open(PROFILE_TRAFFIC) as f:
+        with open(path or PROFILE_TRAFFIC) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -590,9 +822,11 @@ def main():
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic (seeded GGUF Q4_K/Q6_K blocks, f32 activations)",
-        "config": {"workload": "decode hot path: Q4_K 4096x2560+2560x9728+9728x2560; Q6_K lm_head 248320x1024 "
-                               "+ argmax; SwiGLU 2x Q4_K 9728x2560 + Q6_K 2560x9728; Q8 quantize + Q4_K "
-                               "28672x8192", "weight_bytes_per_step": step_bytes,
+        "config": {"workload": "decode hot path: Q4_K 1024x1024; Q4_K 4096x2560+2560x9728+9728x2560; Q6_K lm_head "
+                               "248320x1024 + argmax; SwiGLU 2x Q4_K 9728x2560 + Q6_K 2560x9728; Q8 quantize + "
+                               "Q4_K x Q8 28672x8192", "weight_bytes_per_step": step_bytes,
+                   "value_is": "weight bytes of the whole step / step time (every config's GEMVs; see configs "
+                               "for each one)",
                    "weight_copies": 2, "parallelism": "single GPU"},
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "lm_head_argmax_calls_per_s": round(1e6 / lm_us, 1),
@@ -603,10 +837,28 @@ def main():
         "wall_s": round(wall, 3),
         "roofline": roofline,
     }
+    kern, ceil, cpu = None, None, None
     if not args.no_breakdown:
-        result["kernels"] = breakdown(gq, sets, v)
+        kern = breakdown(gq, sets, v)
+        sizes = sorted(set(read_sizes().values()))
+        ceil = read_ceiling(gq, dev, sizes, in_cache=(read_sizes()["c1"],))
+        for k in kern.values():   # each kernel against a read of its matrix bytes
+            wbk = k.get("weight_bytes")
+            if wbk in ceil:
+                k["frac_read_ceiling"] = round(ceil[wbk]["us"] / k["us"], 4)
+        for tag, _, alg_b, path in traffic_kernels()[1:]:
+            entry = {"swiglu_gemv_9728x2560": "swiglu_gemv_9728x2560", "q6k_gemv_2560x9728": "q6k_gemv_2560x9728",
+                     "q4k_q8_gemv_28672x8192": "q4k_q8_gemv_28672x8192"}[tag]
+            if entry in kern:
+                kern[entry]["traffic"] = traffic_entry(alg_b, path)
+        result["kernels"] = kern
+        result["read_ceiling"] = {str(S): c for S, c in ceil.items()}
+        result["c5_q8_accuracy"] = c5_q8_accuracy(gq, host, {**v, "c5W": sets[0]["c5W"]})
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(host)
+        cpu = cpu_baseline(host)
+        result["cpu_baseline"] = cpu
+    if kern is not None:
+        result["configs"] = config_summary(kern, ceil, cpu)
     print(json.dumps(result), flush=True)
 
 

@@ -20,7 +20,7 @@ import threading
 __all__ = [
     "GemvqError", "lib", "exported_names", "header_names",
     "q4k_gemv", "q4k_gemv_multi", "q6k_gemv", "q8_quantize", "q4k_q8_gemv", "swiglu_gemv",
-    "lm_head_argmax", "lm_head_argmax_timed", "lm_head_argmax_masked", "lm_head_argmax_noalloc", "lm_head_argmax_ws_bytes", "q4k_q8_isums", "strerror", "tile_geometry",
+    "lm_head_argmax", "lm_head_argmax_timed", "lm_head_argmax_masked", "lm_head_argmax_noalloc", "lm_head_argmax_ws_bytes", "q4k_q8_isums", "strerror", "tile_geometry", "stream_read",
     "q6k_q8_gemv", "q6k_q8_isums", "swiglu_q8_gemv", "swiglu_q8_ws_bytes", "rms_norm_q8", "q4k_q8_gemv_batch", "q6k_q8_gemv_batch", "add_rms_norm_q8",
     "Q4K_BLOCK_BYTES", "Q6K_BLOCK_BYTES", "LIB_PATH", "HEADER_PATH",
 ]
@@ -69,6 +69,7 @@ _SIGS = {
     "gemvq_q4k_q8_isums": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P]),
     "gemvq_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "gemvq_tile_geometry": (ctypes.c_int, [ctypes.c_int, _I64, _I64, _P]),
+    "gemvq_stream_read": (ctypes.c_int, [_P, _I64, ctypes.c_int, _P, _P]),
 }
 
 
@@ -112,6 +113,16 @@ def tile_geometry(kind: int, N: int, K: int) -> dict:
     return {"waves": out[0], "rows_tile": out[1], "tiles": out[2], "wave_local": out[3],
             "x_in_lds": out[4], "lds_bytes": out[5], "steps": out[6], "wave_unit": out[7],
             "resident": out[8], "phase": out[9], "grid": out[10]}
+
+
+def stream_read(buf, grid: int, sink, stream=None) -> None:
+    """Plain streaming read of a whole device tensor (measurement hook)."""
+    torch = _torch()
+    if not isinstance(buf, torch.Tensor) or buf.device.type != "cuda" or not buf.is_contiguous():
+        raise TypeError("buf: expected a contiguous device tensor")
+    nbytes = buf.numel() * buf.element_size()
+    _check("gemvq_stream_read", lib().gemvq_stream_read(buf.data_ptr(), nbytes - nbytes % 16, int(grid),
+                                                         sink.data_ptr(), _stream(buf, stream)))
 
 
 def strerror(status: int) -> str:

@@ -2268,6 +2268,32 @@ hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s)
     return hipGetLastError();
 }
 
+// Plain streaming read, the measured ceiling the GEMVs are compared with:
+// every byte of p[0, n16 * 16) is read once with 16-byte loads, four in
+// flight per thread, grid-stride over the whole buffer, and folded into one
+// word that is stored only if it equals a value no seeded input produces
+// (so the loads cannot be dropped and nothing is written in practice).
+__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4 *__restrict__ p, int64_t n16,
+                                                          uint32_t *__restrict__ sink)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    for (; i + 3 * stride < n16; i += 4 * stride) {
+        const u32x4 v0 = p[i], v1 = p[i + stride], v2 = p[i + 2 * stride], v3 = p[i + 3 * stride];
+        acc ^= v0 ^ v1 ^ v2 ^ v3;
+    }
+    for (; i < n16; i += stride) acc ^= p[i];
+    const uint32_t w = acc.x ^ acc.y ^ acc.z ^ acc.w;
+    if (w == 0x9E3779B9u) sink[threadIdx.x] = w;
+}
+
+hipError_t launch_stream_read(const void *p, int64_t bytes, int grid, uint32_t *sink, hipStream_t s)
+{
+    hipLaunchKernelGGL(stream_read_kernel, dim3(grid), dim3(256), 0, s, (const u32x4 *)p, bytes / 16, sink);
+    return hipGetLastError();
+}
+
 hipError_t launch_q8_quantize(const float *x, int8_t *xq, uint16_t *xd, int64_t K, hipStream_t s)
 {
     const int threads = 256;

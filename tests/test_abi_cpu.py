@@ -280,3 +280,14 @@ def test_lm_head_argmax_noalloc_rejections():
     _rejected(L.lm_head_argmax_noalloc(A, B, A + 64, None, 4, 256, None), gq.ERR_ALIAS)   # idx inside W
     _rejected(L.lm_head_argmax_noalloc(A, B, B + 16, None, 4, 256, None), gq.ERR_ALIAS)   # idx inside x
     _rejected(L.lm_head_argmax_noalloc(A, B, C, C, 4, 256, None), gq.ERR_ALIAS)           # max == idx
+
+
+def test_stream_read_rejections():
+    L = gq.lib()
+    _rejected(L.gemvq_stream_read(None, 1024, 256, C, None), gq.ERR_NULL)
+    _rejected(L.gemvq_stream_read(A, 1024, 256, None, None), gq.ERR_NULL)
+    _rejected(L.gemvq_stream_read(A, 0, 256, C, None), gq.ERR_SHAPE)
+    _rejected(L.gemvq_stream_read(A, 1000, 256, C, None), gq.ERR_SHAPE)
+    _rejected(L.gemvq_stream_read(A, 1024, 0, C, None), gq.ERR_SHAPE)
+    _rejected(L.gemvq_stream_read(A + 8, 1024, 256, C, None), gq.ERR_ALIGN)
+    _rejected(L.gemvq_stream_read(A, 1024, 256, A + 512, None), gq.ERR_ALIAS)

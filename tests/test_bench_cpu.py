@@ -39,7 +39,7 @@ def test_traffic_record(tmp_path, monkeypatch):
     # the fetch counter reads half the true bytes, split over two instances per dispatch
     fetch_rows = [(CAL, d, known_kib / 4) for d in (1, 2) for _ in range(2)]
     fetch_rows += [(LM, d, 50_000.0) for d in (3, 4) for _ in range(2)]
-    fetch_rows += [(OTHER, 5, 1.0)]
+    fetch_rows += [(OTHER, 5, 1.0)]     # not a recorded kernel in this database
     write_rows = [(CAL, 1, known_kib), (LM, 3, 10.0), (LM, 4, 30.0)]
     fdb, wdb = str(tmp_path / "f.db"), str(tmp_path / "w.db")
     _db(fdb, "FETCH_SIZE", fetch_rows)
@@ -72,3 +72,24 @@ def test_stale_traffic_record_is_ignored(tmp_path, monkeypatch):
     p.write_text(json.dumps({"kernel_source_hash": "not-this-source", "bytes_per_launch": 123}))
     monkeypatch.setattr(bench, "PROFILE_TRAFFIC", str(p))
     assert bench.traffic_entry(0) is None
+
+
+def test_traffic_records_for_every_recorded_kernel(tmp_path, monkeypatch):
+    """Each recorded kernel present in the databases gets its own record
+    (bytes per launch against its algorithmic bytes)."""
+    known_kib = (bench.CALIB_MIB << 20) / 1024
+    sw = "void gemvq::gemv_kernel<3, 0, 2, true, true>(gemvq::GemvArgs)"
+    c5 = "void gemvq::gemv_wave_kernel<2, 0, 2>(gemvq::GemvArgs)"
+    fetch_rows = [(CAL, 1, known_kib / 2), (LM, 2, 100.0), (sw, 3, 500.0), (c5, 4, 700.0)]
+    write_rows = [(CAL, 1, known_kib), (LM, 2, 1.0), (sw, 3, 2.0), (c5, 4, 3.0)]
+    fdb, wdb = str(tmp_path / "f.db"), str(tmp_path / "w.db")
+    _db(fdb, "FETCH_SIZE", fetch_rows)
+    _db(wdb, "WRITE_SIZE", write_rows)
+    kernels = [(tag, pat, alg, str(tmp_path / (tag + ".json"))) for tag, pat, alg, _ in bench.traffic_kernels()]
+    monkeypatch.setattr(bench, "traffic_kernels", lambda: kernels)
+    bench.write_traffic(fdb, wdb, "cmd")
+    got = {p.name for p in tmp_path.glob("*.json")}
+    assert got == {"lm_head_argmax.json", "swiglu_gemv_9728x2560.json", "q4k_q8_gemv_28672x8192.json"}
+    t = json.loads((tmp_path / "swiglu_gemv_9728x2560.json").read_text())
+    assert t["hbm_fetch_bytes_per_launch"] == 2 * 500 * 1024 and t["hbm_write_bytes_per_launch"] == 2 * 1024
+    assert t["traffic_over_algorithmic"] == pytest.approx((1000 * 1024 + 2048) / t["algorithmic_bytes_per_launch"], abs=1e-4)
