@@ -7,7 +7,8 @@ enqueued on one stream:
   2. Q4_K GEMV  4096x2560, 2560x9728, 9728x2560 (4B-class decode shapes)
   3. lm_head Q6_K 248,320 x 1024 GEMV + fused first-index argmax (4-byte result)
   4. fused gate/up SwiGLU GEMV (2 x Q4_K 9728x2560) + ffn_down Q6_K 2560x9728
-  5. Q8 quantize of an f32[8192] activation + Q4_K x Q8 GEMV 28672x8192
+  5. Q8 quantize of an f32[8192] activation + Q4_K x Q8 GEMV 28672x8192 (one
+     launch: q4k_q8_gemv_from_f32 quantizes in the GEMV's prologue)
 Weights are seeded synthetic data with the workloads' distributions.  Two
 copies of every weight buffer alternate between steps, so each buffer is
 re-read only after ~0.85 GB of other traffic and the 256 MB Infinity Cache
@@ -151,9 +152,8 @@ def step_calls(gq, s, v):
                                   v["h"].data_ptr(), N, K, st)))
     calls.append((L.q6k_gemv, (s["c4Wd"].data_ptr(), v["h"].data_ptr(), v["yd"].data_ptr(), K, N, st)))
     N, K = synth.C5_Q8
-    calls.append((L.q8_quantize, (v["c5x"].data_ptr(), v["xq"].data_ptr(), v["xd"].data_ptr(), K, st)))
-    calls.append((L.q4k_q8_gemv, (s["c5W"].data_ptr(), v["xq"].data_ptr(), v["xd"].data_ptr(),
-                                  v["c5y"].data_ptr(), N, K, st)))
+    calls.append((L.q4k_q8_gemv_from_f32, (s["c5W"].data_ptr(), v["c5x"].data_ptr(), v["xq"].data_ptr(),
+                                           v["xd"].data_ptr(), v["c5y"].data_ptr(), N, K, st)))
     return calls, lm
 
 
@@ -179,8 +179,7 @@ def run_step(gq, s, v):
     gq.swiglu_gemv(s["c4Wg"], s["c4Wu"], v["c4x"], N, K, h=v["h"])
     gq.q6k_gemv(s["c4Wd"], v["h"], K, N, y=v["yd"])
     N, K = synth.C5_Q8
-    gq.q8_quantize(v["c5x"], xq=v["xq"], xd=v["xd"])
-    gq.q4k_q8_gemv(s["c5W"], v["xq"], v["xd"], N, K, y=v["c5y"])
+    gq.q4k_q8_gemv_from_f32(s["c5W"], v["c5x"], N, K, xq=v["xq"], xd=v["xd"], y=v["c5y"])
 
 
 def graph_step_ms(gq, sets, v, steps):
@@ -390,6 +389,9 @@ def breakdown(gq, sets, v, reps=24):
         gq.q4k_q8_gemv(w[0], v["xq"], v["xd"], N, K, y=v["c5y"])
     timeit("c5_q8_quantize+q4k_q8_gemv_28672x8192", c5, ws,
            N * K // 256 * 144 + 4 * K + 2 * (K + K // 16) + 4 * N, N * K // 256 * 144)
+    timeit("c5_q4k_q8_gemv_from_f32_28672x8192",
+           lambda w: gq.q4k_q8_gemv_from_f32(w[0], v["c5x"], N, K, xq=v["xq"], xd=v["xd"], y=v["c5y"]), ws,
+           N * K // 256 * 144 + 4 * K + K + K // 16 + 4 * N, N * K // 256 * 144)
     timeit("q4k_gemv_28672x8192", lambda w: gq.q4k_gemv(w[0], v["c5x"], N, K, y=v["c5y"]), ws,
            N * K // 256 * 144 + 4 * (N + K), N * K // 256 * 144)
     del ws
@@ -663,8 +665,8 @@ def c5_q8_accuracy(gq, host, v):
     import synth
     W, x = host["c5"]
     N, K = synth.C5_Q8
-    gq.q8_quantize(v["c5x"], xq=v["xq"], xd=v["xd"])
-    y8 = gq.q4k_q8_gemv(v["c5W"], v["xq"], v["xd"], N, K).cpu().numpy().astype(np.float64)
+    y8, _, _ = gq.q4k_q8_gemv_from_f32(v["c5W"], v["c5x"], N, K, xq=v["xq"], xd=v["xd"])
+    y8 = y8.cpu().numpy().astype(np.float64)
     exact = oracle.q4k_gemv(W, x, N, K)
     q, d = oracle.q8_quantize(x)
     q8hat = oracle.q4k_q8_gemv(W, q, d, N, K)
@@ -682,7 +684,8 @@ CONFIG_KERNELS = {
     "c2": ("c2_q4k_gemv_triple", ("c2a", "c2b", "c2c"), "Q4_K 4096x2560 + 2560x9728 + 9728x2560 back to back"),
     "c3": ("lm_head_argmax_248320x1024", ("c3",), "lm_head Q6_K 248320x1024 + argmax"),
     "c4": ("ffn_f32_swiglu+q6k", ("c4g", "c4d"), "SwiGLU 2x Q4_K 9728x2560 + Q6_K 2560x9728 (two launches)"),
-    "c5": ("c5_q8_quantize+q4k_q8_gemv_28672x8192", ("c5",), "Q8 quantize + Q4_K x Q8 28672x8192 (two launches)"),
+    "c5": ("c5_q4k_q8_gemv_from_f32_28672x8192", ("c5",),
+           "Q8 quantize + Q4_K x Q8 28672x8192 (one launch: the quantization in the GEMV's prologue)"),
 }
 
 
@@ -824,7 +827,7 @@ def main():
         "vs_baseline": None, "dtype": "f32", "data": "synthetic (seeded GGUF Q4_K/Q6_K blocks, f32 activations)",
         "config": {"workload": "decode hot path: Q4_K 1024x1024; Q4_K 4096x2560+2560x9728+9728x2560; Q6_K lm_head "
                                "248320x1024 + argmax; SwiGLU 2x Q4_K 9728x2560 + Q6_K 2560x9728; Q8 quantize + "
-                               "Q4_K x Q8 28672x8192", "weight_bytes_per_step": step_bytes,
+                               "Q4_K x Q8 28672x8192 (one launch)", "weight_bytes_per_step": step_bytes,
                    "value_is": "weight bytes of the whole step / step time (every config's GEMVs; see configs "
                                "for each one)",
                    "weight_copies": 2, "parallelism": "single GPU"},

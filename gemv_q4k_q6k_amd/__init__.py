@@ -21,7 +21,7 @@ __all__ = [
     "GemvqError", "lib", "exported_names", "header_names",
     "q4k_gemv", "q4k_gemv_multi", "q6k_gemv", "q8_quantize", "q4k_q8_gemv", "swiglu_gemv",
     "lm_head_argmax", "lm_head_argmax_timed", "lm_head_argmax_masked", "lm_head_argmax_noalloc", "lm_head_argmax_ws_bytes", "q4k_q8_isums", "strerror", "tile_geometry", "stream_read",
-    "q6k_q8_gemv", "q6k_q8_isums", "swiglu_q8_gemv", "swiglu_q8_ws_bytes", "rms_norm_q8", "q4k_q8_gemv_batch", "q6k_q8_gemv_batch", "add_rms_norm_q8",
+    "q6k_q8_gemv", "q4k_q8_gemv_from_f32", "q6k_q8_isums", "swiglu_q8_gemv", "swiglu_q8_ws_bytes", "rms_norm_q8", "q4k_q8_gemv_batch", "q6k_q8_gemv_batch", "add_rms_norm_q8",
     "Q4K_BLOCK_BYTES", "Q6K_BLOCK_BYTES", "LIB_PATH", "HEADER_PATH",
 ]
 
@@ -53,6 +53,7 @@ _SIGS = {
     "q8_quantize": (ctypes.c_int, [_P, _P, _P, _I64, _P]),
     "q4k_q8_gemv": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _P]),
     "swiglu_gemv": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _P]),
+    "q4k_q8_gemv_from_f32": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _P]),
     "q6k_q8_gemv": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _P]),
     "q4k_q8_gemv_batch": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, ctypes.c_int, _P]),
     "q6k_q8_gemv_batch": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, ctypes.c_int, _P]),
@@ -247,6 +248,20 @@ def q4k_q8_gemv(W, xq, xd, N: int, K: int, y=None, stream=None):
     _check("q4k_q8_gemv", lib().q4k_q8_gemv(W.data_ptr(), xq.data_ptr(), xd.data_ptr(), y.data_ptr(), N, K,
                                             _stream(xq, stream)))
     return y
+
+
+def q4k_q8_gemv_from_f32(W, x, N: int, K: int, xq=None, xd=None, y=None, stream=None):
+    """q8_quantize(x) then q4k_q8_gemv in one call (one launch where the
+    wave-unit kernel runs the shape).  Returns (y, xq, xd)."""
+    torch = _torch()
+    _weights(W, N, K, Q4K_BLOCK_BYTES)
+    _dev_tensor(x, torch.float32, K, "x")
+    xq = _out(xq, x.device, torch.int8, K, "xq")
+    xd = _out(xd, x.device, torch.int16, K // 32, "xd")
+    y = _out(y, x.device, torch.float32, N, "y")
+    _check("q4k_q8_gemv_from_f32", lib().q4k_q8_gemv_from_f32(W.data_ptr(), x.data_ptr(), xq.data_ptr(), xd.data_ptr(),
+                                                              y.data_ptr(), N, K, _stream(x, stream)))
+    return y, xq, xd
 
 
 def q6k_q8_gemv(W, xq, xd, N: int, K: int, y=None, stream=None):

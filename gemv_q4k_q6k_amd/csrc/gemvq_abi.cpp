@@ -229,6 +229,25 @@ int q4k_q8_gemv(const void *W, const int8_t *xq, const uint16_t *xd, float *y, i
     return status_of(gemvq::launch_q4k_q8_gemv(W, xq, xd, y, N, K, cus, (hipStream_t)stream));
 }
 
+int q4k_q8_gemv_from_f32(const void *W, const float *x, int8_t *xq, uint16_t *xd, float *y, int64_t N, int64_t K,
+                         void *stream)
+{
+    if (!W || !x || !xq || !xd || !y) return GEMVQ_ERR_NULL;
+    size_t wb = 0;
+    if (int st = check_shape(N, K, 144, &wb)) return st;
+    if (!aligned(W, 16) || !aligned(x, 16) || !aligned(xq, 16) || !aligned(xd, 4) || !aligned(y, 4))
+        return GEMVQ_ERR_ALIGN;
+    const size_t ny = (size_t)N * 4, nx = (size_t)K * 4, nq = (size_t)K, nd = (size_t)(K / 32) * 2;
+    // outputs overlap neither the inputs nor each other
+    if (overlap(y, ny, W, wb) || overlap(y, ny, x, nx) || overlap(y, ny, xq, nq) || overlap(y, ny, xd, nd) ||
+        overlap(xq, nq, W, wb) || overlap(xq, nq, x, nx) || overlap(xq, nq, xd, nd) || overlap(xd, nd, W, wb) ||
+        overlap(xd, nd, x, nx))
+        return GEMVQ_ERR_ALIAS;
+    int cus = 0;
+    if (int st = device_cus(&cus)) return st;
+    return status_of(gemvq::launch_q4k_q8_gemv_from_f32(W, x, xq, xd, y, N, K, cus, (hipStream_t)stream));
+}
+
 int q6k_q8_gemv(const void *W, const int8_t *xq, const uint16_t *xd, float *y, int64_t N, int64_t K, void *stream)
 {
     if (!W || !xq || !xd || !y) return GEMVQ_ERR_NULL;

@@ -948,7 +948,13 @@ constexpr int wave_max_threads() { return (is_q8(KIND) || KIND == kQ4K) ? 1024 :
 constexpr int kWaveMaxThreads = 1024;   // the largest of wave_max_threads
 constexpr int kHalvesWaves = 8;          // waves per CU of the two-half (STEPS = 2) wave-unit kernel
 
-template <int KIND, int EPI, int STEPS>
+// QUANT (Q4_K x Q8 only): the activation arrives as f32 (a.x) and every
+// workgroup quantizes it to Q8 in its prologue, with the encoder every Q8
+// producer uses (q8_scale, q8_code, q8_scale_bits), so its codes and scales
+// equal q8_quantize's bit for bit; workgroup 0 also writes them to a.hq and
+// a.hd.  The codes go to LDS as the int8 activation, the scales to LDS past
+// them.
+template <int KIND, int EPI, int STEPS, bool QUANT = false>
 __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_wave_kernel(GemvArgs a)
 {
     // one unit in flight per wave (the next unit's loads are issued as soon
@@ -1034,7 +1040,7 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_wave_kernel(Gem
         fx_preload<KIND>(xg0, a.x, K, tid);
         fx_preload<KIND>(xg1, a.x, K, tid + (int)blockDim.x);
     }
-    constexpr int kXRegs = kFx ? 0 : (is_q8(KIND) ? 1 : 2);
+    constexpr int kXRegs = (kFx || QUANT) ? 0 : (is_q8(KIND) ? 1 : 2);
     const int step = is_q8(KIND) ? 16 : 4;
     const int esz = is_q8(KIND) ? 1 : 4;
     const uint8_t *src = is_q8(KIND) ? (const uint8_t *)a.xq : (const uint8_t *)a.x;
@@ -1043,6 +1049,13 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_wave_kernel(Gem
     for (int r = 0; r < kXRegs; ++r) {
         const int i = (tid + r * (int)blockDim.x) * step;
         if (i < K) xr[r] = *(const u32x4 *)(src + (size_t)i * esz);
+    }
+    // QUANT: thread t takes values [16t, 16t + 16) of x, half of a 32-value
+    // Q8 block (its partner is the adjacent lane); the first round is loaded
+    // before the weights
+    float xv[QUANT ? 16 : 1];
+    if constexpr (QUANT) {
+        if (tid * 16 < K) load_x_f32(xv, a.x + 16 * tid, 16);
     }
     int unit[kPhase];
     RawSet<KIND> ring[kPhase][STEPS];
@@ -1065,7 +1078,36 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_wave_kernel(Gem
         fetch_mask(d, unit[d], u_end - 1);
     }
     if (tid == 0) s_next = (uint32_t)(kPhase * waves);
-    if constexpr (kFx) {
+    // QUANT: the scales sit in LDS past the padded codes
+    const uint16_t *xd_src = a.xd;
+    if constexpr (QUANT) {
+        uint16_t *s_xd = (uint16_t *)(smem + lds_pad((uint32_t)K));
+        xd_src = s_xd;
+        for (int t = tid; t * 16 < K; t += (int)blockDim.x) {   // pairs (t, t ^ 1) share an iteration
+            if (t != tid) load_x_f32(xv, a.x + 16 * t, 16);
+            float m = 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(xv[i]));
+            m = fmaxf(m, dpp_f<kDppQuadXor1>(m));   // the block's other half (lane ^ 1)
+            const float d = q8_scale(m);
+            uint32_t w[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                uint32_t acc = 0u;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc |= ((uint32_t)(q8_code(xv[4 * k + j], d) & 0xFF)) << (8 * j);
+                w[k] = acc;
+            }
+            const u32x4 codes = u32x4{w[0], w[1], w[2], w[3]};
+            *(u32x4 *)(smem + lds_pad(16u * (uint32_t)t)) = codes;
+            const uint16_t dbits = q8_scale_bits(d);
+            if ((t & 1) == 0) s_xd[t >> 1] = dbits;
+            if (blockIdx.x == 0) {
+                *(u32x4 *)(a.hq + 16 * t) = codes;
+                if ((t & 1) == 0) a.hd[t >> 1] = dbits;
+            }
+        }
+    } else if constexpr (kFx) {
         fx_stage_all<KIND>(smem, a.x, K, xg0, xg1);
     } else {
 #pragma unroll
@@ -1084,7 +1126,7 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_wave_kernel(Gem
     } else if constexpr (is_q8(KIND)) {
 #pragma unroll
         for (int st = 0; st < STEPS; ++st) {
-            load_x<true>(xs[st].v, (const int8_t *)smem, a.xd, b + 16 * st, part);
+            load_x<true>(xs[st].v, (const int8_t *)smem, xd_src, b + 16 * st, part);
             finish_x(xs[st].v);
         }
     } else {
@@ -2102,6 +2144,32 @@ hipError_t launch_q4k_q8_gemv(const void *W, const int8_t *xq, const uint16_t *x
     a.xd = xd;
     a.y = y;
     return launch<kQ4KQ8, kStore>(pl, a, cus, s);
+}
+
+hipError_t launch_q4k_q8_gemv_from_f32(const void *W, const float *x, int8_t *xq, uint16_t *xd, float *y, int64_t N,
+                                       int64_t K, int cus, hipStream_t s)
+{
+    Plan pl = make_plan(N, K, kQ4KQ8, cus);
+    if (pl.wave_local && !pl.rows_kernel) {
+        // wave-unit kernel: the quantization runs in its prologue; the
+        // scales take K/16 bytes of LDS past the codes
+        GemvArgs a = base_args(pl, N);
+        a.W = (const uint8_t *)W;
+        a.x = x;
+        a.hq = xq;
+        a.hd = xd;
+        a.y = y;
+        pl.lds_bytes = ((pl.lds_bytes + 15) & ~(size_t)15) + (size_t)(K / 16);
+        if (pl.steps == 2)
+            return launch_per_cu(gemv_wave_kernel<kQ4KQ8, kStore, 2, true>, kHalvesWaves, pl, a, cus, s, Timing{});
+        return launch_per_cu(gemv_wave_kernel<kQ4KQ8, kStore, 1, true>, wave_max_threads<kQ4KQ8>() / 64, pl, a, cus,
+                             s, Timing{});
+    }
+    // other shapes: the quantize launch, then the GEMV on its output (the
+    // same codes, the same GEMV)
+    const hipError_t e = launch_q8_quantize(x, xq, xd, K, s);
+    if (e != hipSuccess) return e;
+    return launch_q4k_q8_gemv(W, xq, xd, y, N, K, cus, s);
 }
 
 hipError_t launch_swiglu_q8_gemv(const void *Wg, const void *Wu, const float *x, float *h, int8_t *hq, uint16_t *hd,

@@ -83,6 +83,9 @@ hipError_t launch_q4k_q8_gemv(const void *W, const int8_t *xq, const uint16_t *x
                               int cus, hipStream_t s);
 hipError_t launch_q6k_q8_gemv(const void *W, const int8_t *xq, const uint16_t *xd, float *y, int64_t N, int64_t K,
                               int cus, hipStream_t s);
+// q4k_q8_gemv_from_f32: quantize x (writing xq, xd) and run the Q4_K x Q8 GEMV
+hipError_t launch_q4k_q8_gemv_from_f32(const void *W, const float *x, int8_t *xq, uint16_t *xd, float *y, int64_t N,
+                                       int64_t K, int cus, hipStream_t s);
 // mask: nullptr, or the banned-row bitmask of lm_head_argmax_masked
 hipError_t launch_lm_head_argmax(const void *W, const float *x, const uint32_t *mask, uint32_t *out_idx,
                                  float *out_max, void *ws, int64_t N, int64_t K, int cus, hipStream_t s,

@@ -111,6 +111,23 @@ int q4k_q8_gemv(const void *W, const int8_t *xq, const uint16_t *xd, float *y,
                 int64_t N, int64_t K, void *stream);
 
 /*
+ * q8_quantize followed by q4k_q8_gemv as one call on an f32 activation (the
+ * problem statement's configuration: activations quantized on the device to
+ * Q8, then int8 dot products; memra-engine decode.rs `ffn_swiglu_decode`
+ * quantizes the activation right before the pre-quantized GEMV).  Where
+ * q4k_q8_gemv runs its wave-unit kernel (K/256 a power of two up to 16, or
+ * K = 8192), every workgroup quantizes x in its own prologue, with the
+ * encoder q8_quantize uses, while its first weight loads are in flight, and
+ * no separate quantize launch exists; other shapes run the two launches.
+ * Either way xq, xd receive exactly q8_quantize(x) and y exactly
+ * q4k_q8_gemv(W, xq, xd) (bit for bit).
+ *   W: Q4_K N x K.  x: float[K], finite.  xq: int8[K] (16-B aligned).
+ *   xd: uint16[K/32].  y: float[N].  Outputs overlap no input and each other.
+ */
+int q4k_q8_gemv_from_f32(const void *W, const float *x, int8_t *xq, uint16_t *xd, float *y,
+                         int64_t N, int64_t K, void *stream);
+
+/*
  * Q6_K x Q8 integer-dot GEMV, the int8 ffn_down: on the pages' q8 fast path
  * the down projection consumes an already quantized activation (memra-engine
  * decode.rs `ffn_swiglu_decode`: the SwiGLU epilogue emits the q8 form of its

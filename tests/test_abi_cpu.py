@@ -291,3 +291,20 @@ def test_stream_read_rejections():
     _rejected(L.gemvq_stream_read(A, 1024, 0, C, None), gq.ERR_SHAPE)
     _rejected(L.gemvq_stream_read(A + 8, 1024, 256, C, None), gq.ERR_ALIGN)
     _rejected(L.gemvq_stream_read(A, 1024, 256, A + 512, None), gq.ERR_ALIAS)
+
+
+def test_q4k_q8_gemv_from_f32_rejections():
+    L = gq.lib()
+    N, K = 64, 512
+    _rejected(L.q4k_q8_gemv_from_f32(None, B, C, D, E, N, K, None), gq.ERR_NULL)
+    _rejected(L.q4k_q8_gemv_from_f32(A, B, None, D, E, N, K, None), gq.ERR_NULL)
+    _rejected(L.q4k_q8_gemv_from_f32(A, B, C, D, None, N, K, None), gq.ERR_NULL)
+    _rejected(L.q4k_q8_gemv_from_f32(A, B, C, D, E, N, 300, None), gq.ERR_SHAPE)
+    _rejected(L.q4k_q8_gemv_from_f32(A + 4, B, C, D, E, N, K, None), gq.ERR_ALIGN)
+    _rejected(L.q4k_q8_gemv_from_f32(A, B + 4, C, D, E, N, K, None), gq.ERR_ALIGN)
+    _rejected(L.q4k_q8_gemv_from_f32(A, B, C + 8, D, E, N, K, None), gq.ERR_ALIGN)
+    _rejected(L.q4k_q8_gemv_from_f32(A, B, C, D + 2, E, N, K, None), gq.ERR_ALIGN)
+    _rejected(L.q4k_q8_gemv_from_f32(A, B, C, D, B + 16, N, K, None), gq.ERR_ALIAS)      # y inside x
+    _rejected(L.q4k_q8_gemv_from_f32(A, B, A + 256, D, E, N, K, None), gq.ERR_ALIAS)     # xq inside W
+    _rejected(L.q4k_q8_gemv_from_f32(A, B, C, C + 16, E, N, K, None), gq.ERR_ALIAS)      # xd inside xq
+    _rejected(L.q4k_q8_gemv_from_f32(A, B, C, D, D, N, K, None), gq.ERR_ALIAS)           # y over xd

@@ -931,3 +931,25 @@ def test_lm_head_argmax_wide_range(dev, N):
     print(f"wide lm_head N={N}: idx {idx}, oracle {oracle.argmax_first(yhat)}, gap {gap:.3e}", flush=True)
     if gap > 1e-3:
         assert idx == oracle.argmax_first(yhat)
+
+
+@pytest.mark.parametrize("N,K", [(28_672, 8192), (100, 8192), (3, 8192), (1000, 1024), (1003, 1024), (7, 256),
+                                 (333, 2560), (50, 9728)])
+def test_q4k_q8_gemv_from_f32(dev, N, K):
+    """Quantize + Q4_K x Q8 GEMV in one call: the codes and scales are
+    q8_quantize's and the oracle's bit for bit, y is q4k_q8_gemv's on them
+    bit for bit (one launch on wave-unit shapes, two elsewhere), and within
+    the parity bound of the oracle's Q8 path."""
+    r = synth.rng_for(6100 + N + K)
+    W = synth.q4k_weights(r, N, K)
+    x = synth.activation_outliers(r, K)
+    dW, dx = up(W, dev), up(x, dev)
+    print(f"q4k_q8_gemv_from_f32 N={N} K={K}", flush=True)
+    y, xq, xd = gq().q4k_q8_gemv_from_f32(dW, dx, N, K)
+    q, d = oracle.q8_quantize(x)
+    assert np.array_equal(xq.cpu().numpy(), q)
+    assert np.array_equal(xd.cpu().numpy().view(np.uint16), d)
+    xq2, xd2 = gq().q8_quantize(dx)
+    assert torch.equal(xq2, xq) and torch.equal(xd2, xd)
+    assert torch.equal(gq().q4k_q8_gemv(dW, xq, xd, N, K), y)
+    check_f32(f"q4k_q8_from_f32 {N}x{K}", y.cpu().numpy(), oracle.q4k_q8_gemv(W, q, d, N, K))
