@@ -501,10 +501,11 @@ __device__ __forceinline__ uint32_t fx4_sums_off(int K) { return 3u * lds_pad((u
 __device__ __forceinline__ uint32_t fx4_exps_off(int K) { return fx4_sums_off(K) + 4u * (uint32_t)(K / 16); }
 
 // Group g (16 values v, in registers) of the activation: its f32 sum (added
-// in index order, as sum16 does) and its fixed-point bytes; the four groups
-// of a part sit in one quad of lanes and share their largest |x| by DPP.
-// Call with whole quads active.
-__device__ void fx4_stage_group(unsigned char *smem, int K, int g, const float (&v)[16])
+// in index order, as sum16 does) and its fixed-point bytes.  The four groups
+// of one 64-value part sit in one quad of lanes and share the part's largest
+// |x| by DPP; the quad's first lane (lead) writes the part's exponent at index
+// eidx.  Call with whole quads active.
+__device__ void fx_stage_group(unsigned char *smem, int K, int g, int eidx, bool lead, const float (&v)[16])
 {
     float t = 0.f, m = 0.f;
 #pragma unroll
@@ -535,7 +536,7 @@ __device__ void fx4_stage_group(unsigned char *smem, int K, int g, const float (
     *(u32x4 *)(smem + o) = u32x4{hi[0], hi[1], hi[2], hi[3]};
     *(u32x4 *)(smem + stride + o) = u32x4{mid[0], mid[1], mid[2], mid[3]};
     *(u32x4 *)(smem + 2 * stride + o) = u32x4{lo[0], lo[1], lo[2], lo[3]};
-    if ((g & 3) == 0) ((int *)(smem + fx4_exps_off(K)))[g >> 2] = e;
+    if (lead) ((int *)(smem + fx4_exps_off(K)))[eidx] = e;
 }
 
 // Lane slice of part c of block b from the staged fixed-point activation.
@@ -564,47 +565,11 @@ __device__ __forceinline__ void fx4_load(Q4KFX &xs, const unsigned char *smem, i
 
 // The same layout for Q6_K parts (tile kernel): part slot t (block t >> 4,
 // part (t >> 2) & 3, group t & 3 of the part) is 16-element group g of the
-// activation; the exponent sits at the part's index 4*block + part.  One
-// thread per slot, values in registers, whole quads active.
+// activation; the exponent sits at the part's index 4*block + part = t >> 2.
 __device__ __forceinline__ int fx6_group_of_slot(int t)
 {
     const int blk = t >> 4, u = (t >> 2) & 3, sg = t & 3;
     return 16 * blk + 8 * (u >> 1) + 2 * sg + (u & 1);
-}
-
-__device__ void fx6_stage_slot(unsigned char *smem, int K, int t, const float (&v)[16])
-{
-    const int g = fx6_group_of_slot(t);
-    float sum = 0.f, m = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        sum += v[i];
-        m = fmaxf(m, fabsf(v[i]));
-    }
-    ((float *)(smem + fx4_sums_off(K)))[g] = sum;
-    m = fmaxf(m, dpp_f<kDppQuadXor1>(m));
-    m = fmaxf(m, dpp_f<kDppQuadXor2>(m));
-    const int e = (m > 0.f && m <= 3.402823466e38f) ? 22 - __builtin_amdgcn_frexp_expf(m) : 0;
-    uint32_t hi[4], mid[4], lo[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        int X[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) X[j] = (int)rintf(__builtin_amdgcn_ldexpf(v[4 * k + j], e));
-        const uint32_t p01 = __builtin_amdgcn_perm((uint32_t)X[1], (uint32_t)X[0], 0x05010400u);
-        const uint32_t p23 = __builtin_amdgcn_perm((uint32_t)X[3], (uint32_t)X[2], 0x05010400u);
-        const uint32_t r01 = __builtin_amdgcn_perm((uint32_t)X[1], (uint32_t)X[0], 0x07030602u);
-        const uint32_t r23 = __builtin_amdgcn_perm((uint32_t)X[3], (uint32_t)X[2], 0x07030602u);
-        lo[k] = __builtin_amdgcn_perm(p23, p01, 0x05040100u);
-        mid[k] = __builtin_amdgcn_perm(p23, p01, 0x07060302u);
-        hi[k] = __builtin_amdgcn_perm(r23, r01, 0x05040100u);
-    }
-    const uint32_t stride = lds_pad((uint32_t)K);
-    const uint32_t o = lds_pad(16u * (uint32_t)g);
-    *(u32x4 *)(smem + o) = u32x4{hi[0], hi[1], hi[2], hi[3]};
-    *(u32x4 *)(smem + stride + o) = u32x4{mid[0], mid[1], mid[2], mid[3]};
-    *(u32x4 *)(smem + 2 * stride + o) = u32x4{lo[0], lo[1], lo[2], lo[3]};
-    if ((t & 3) == 0) ((int *)(smem + fx4_exps_off(K)))[t >> 2] = e;
 }
 
 __device__ __forceinline__ void fx6_load(Q6KFX &xs, const unsigned char *smem, int K, int b, int u)
@@ -639,8 +604,8 @@ __device__ __forceinline__ void fx_stage_all(unsigned char *smem, const float *x
 {
     const int slots = K / 16, tid = (int)threadIdx.x, bd = (int)blockDim.x;
     auto stage = [&](int t, const float (&v)[16]) {
-        if constexpr (KIND == kQ6K) fx6_stage_slot(smem, K, t, v);
-        else fx4_stage_group(smem, K, t, v);
+        if constexpr (KIND == kQ6K) fx_stage_group(smem, K, fx6_group_of_slot(t), t >> 2, (t & 3) == 0, v);
+        else fx_stage_group(smem, K, t, t >> 2, (t & 3) == 0, v);
     };
     if (tid < slots) stage(tid, xg0);
     if (tid + bd < slots) stage(tid + bd, xg1);
