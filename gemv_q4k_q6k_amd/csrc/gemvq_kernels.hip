@@ -700,15 +700,17 @@ __global__ __launch_bounds__(RES ? kResThreads : kMaxThreads) void gemv_kernel(G
     // many short-lived workgroups are bound by start-up, which the
     // conversion lengthens (measured slower at 2560 x 9728 and 9728 x 2560).
     constexpr bool kFx = tile_fx(KIND, XLDS, RES);
-    // The resident SwiGLU pair runs its whole activation path (loads, fixed-
-    // point staging, barrier, slice) before it issues the weight loads.  A
-    // barrier after the weight loads completes only once every wave has
-    // issued all of them, and issue is throttled by the memory pipeline, so
-    // the dot products could start only when most of the stream had arrived
-    // (measured with device timestamps: x ready ~4 us into a ~8 us launch).
-    // The other kinds measured as fast or faster with their weight loads
-    // first.
-    constexpr bool kXFirst = RES && XLDS && KIND == kSwiglu;
+    // A resident workgroup with a fixed-point activation issues its first
+    // tile's weight loads, converts x while they are in flight, and issues the
+    // remaining tiles once the slice is in registers.  Issue is throttled by
+    // the memory pipeline (a wave waits at each load until the CU accepts it),
+    // so with every tile issued first the conversion started only once most
+    // of the stream was out, and the dot products waited for it; with x
+    // converted before any weight load the stream started late.  Measured
+    // with device timestamps at 2560 x 9728 (Q6_K) and 9728 x 2560 (SwiGLU):
+    // x staged at ~2.8 us instead of ~4.2 (all tiles first) and 7.6 -> 6.8,
+    // 8.7 -> 8.3 us per call.  The other forms issue every tile first.
+    constexpr int kPre = (RES && kFx) ? 1 : kPhase;   // tiles fetched before the conversion
     float xg0[16], xg1[16];
     if constexpr (kFx) {
         fx_preload<KIND>(xg0, a.x, K, tid);
@@ -738,10 +740,8 @@ __global__ __launch_bounds__(RES ? kResThreads : kMaxThreads) void gemv_kernel(G
             load_x(xs.v, a.x, xb, part);
     }
     RawSet<KIND> ring[kPhase];
-    if constexpr (!kXFirst) {
 #pragma unroll
-        for (int d = 0; d < kPhase; ++d) fetch(ring[d], t_begin + d);
-    }
+    for (int d = 0; d < kPre; ++d) fetch(ring[d], t_begin + d);
 
     // ---- activation slice into registers (through LDS when several rows of
     // a tile share it).  The two branches keep the source pointer's address
@@ -785,10 +785,8 @@ __global__ __launch_bounds__(RES ? kResThreads : kMaxThreads) void gemv_kernel(G
             finish_x(xs.v, (const float *)nullptr, xb, part);
         }
     }
-    if constexpr (kXFirst) {
 #pragma unroll
-        for (int d = 0; d < kPhase; ++d) fetch(ring[d], t_begin + d);
-    }
+    for (int d = kPre; d < kPhase; ++d) fetch(ring[d], t_begin + d);
     // LDS is reused for row reductions below (the resident form keeps them
     // in a region of their own, past the staged activation)
     if constexpr (!RES) __syncthreads();
@@ -812,6 +810,20 @@ __global__ __launch_bounds__(RES ? kResThreads : kMaxThreads) void gemv_kernel(G
             if (part == 0 && lane_on) rb[(o * a.rows_tile + p) * a.nb + b] = q;
         }
     };
+    // epilogue of one row from its sums r (one lane per row)
+    auto row_epi = [&](int64_t row, const float (&r)[2]) {
+        if constexpr (EPI == kQ8Emit) {
+            // the SwiGLU product exactly as the store epilogue writes it
+            const float g = r[0], u = r[1];
+            const float hv = g * u / (1.0f + expf(-g));
+            s_h[row - r_begin] = hv;
+            if (a.y) a.y[row] = hv;
+        } else {
+            uint32_t mw = 0;
+            if constexpr (EPI == kArgmaxMasked) mw = a.mask[row >> 5];
+            emit_row<KIND, EPI>(a, row, r, best, mw);
+        }
+    };
     // row pr of tile t from its block sums in rb: added in column order
     // (loads issued four at a time), then the epilogue
     auto row_out = [&](const float *rb, int t, int pr) {
@@ -830,17 +842,36 @@ __global__ __launch_bounds__(RES ? kResThreads : kMaxThreads) void gemv_kernel(G
             for (; c < a.nb; ++c) acc += src[c];
             r[o] = acc;
         }
-        if constexpr (EPI == kQ8Emit) {
-            // the SwiGLU product exactly as the store epilogue writes it
-            const float g = r[0], u = r[1];
-            const float hv = g * u / (1.0f + expf(-g));
-            s_h[row - r_begin] = hv;
-            if (a.y) a.y[row] = hv;
-        } else {
-            uint32_t mw = 0;
-            if constexpr (EPI == kArgmaxMasked) mw = a.mask[row >> 5];
-            emit_row<KIND, EPI>(a, row, r, best, mw);
+        row_epi(row, r);
+    };
+    // The same row summed by an aligned group of L lanes (4, 8 or 16; lane s
+    // of the group): lane s adds columns s, s + L, s + 2L, ... in that order,
+    // the group's partial sums are then added by group_sum (a fixed pairing,
+    // the same bits in every lane), and lane 0 of the group runs the
+    // epilogue.  Loads are unconditional (column 0 stands in past the row's
+    // end) and contribute +0 there: a partial sum that starts at +0 is never
+    // -0, so adding +0 leaves it unchanged.  Uniform across the group.
+    auto row_out_group = [&](const float *rb, int t, int pr, int s, int L) {
+        const int64_t row = (int64_t)t * a.rows_tile + pr;
+        if (row >= a.N) return;
+        float r[2];
+#pragma unroll
+        for (int o = 0; o < OUTS; ++o) {
+            const float *src = rb + (o * a.rows_tile + pr) * a.nb;
+            float acc = 0.f;
+            for (int c0 = s; c0 < a.nb; c0 += 4 * L) {
+                float v[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int c = c0 + i * L;
+                    v[i] = src[c < a.nb ? c : 0];
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc += c0 + i * L < a.nb ? v[i] : 0.f;
+            }
+            r[o] = group_sum(acc, L);
         }
+        if (s == 0) row_epi(row, r);
     };
     // dot, row reduction and epilogue of tile t (workgroup-uniform control flow)
     auto process = [&](const RawSet<KIND> &rs, int t) {
@@ -858,10 +889,13 @@ __global__ __launch_bounds__(RES ? kResThreads : kMaxThreads) void gemv_kernel(G
         for (int d = 0; d < kPhase; ++d)
             if (t_begin + d < t_end) block_sums(ring[d], t_begin + d, red + d * red_stride);   // uniform
         __syncthreads();
+        // a group of lanes per row, sized so each lane adds a few columns
         const int nrows = kPhase * a.rows_tile;
-        for (int j = tid; j < nrows; j += (int)blockDim.x) {
+        const int lg = a.nb <= 16 ? 2 : (a.nb <= 32 ? 3 : 4);
+        const int L = 1 << lg, s = tid & (L - 1);
+        for (int j = tid >> lg; j < nrows; j += (int)blockDim.x >> lg) {
             const int d = j / a.rows_tile;
-            if (t_begin + d < t_end) row_out(red + d * red_stride, t_begin + d, j - d * a.rows_tile);
+            if (t_begin + d < t_end) row_out_group(red + d * red_stride, t_begin + d, j - d * a.rows_tile, s, L);
         }
         if constexpr (is_argmax(EPI)) {
             // every wave folds its threads' keys first (all lanes active here)
