@@ -528,8 +528,10 @@ def traffic_kernels():
     out.append(("q6k_gemv_2560x9728", r"gemv_kernel<1, 0, \d, true, true>", K * N // 256 * 210 + 4 * (N + K),
                 os.path.join(ROOT, "profiles", "traffic_q6k_gemv_2560x9728.json")))
     N, K = synth.C5_Q8
-    out.append(("q4k_q8_gemv_28672x8192", r"gemv_wave_kernel<2, 0, 2>", N * K // 256 * 144 + K + K // 16 + 4 * N,
-                os.path.join(ROOT, "profiles", "traffic_q4k_q8_gemv_28672x8192.json")))
+    # f32 x in, its Q8 codes and scales out (one workgroup writes them), y out
+    out.append(("c5_q4k_q8_gemv_from_f32_28672x8192", r"gemv_wave_kernel<2, 0, 2, true>",
+                N * K // 256 * 144 + 4 * K + K + K // 16 + 4 * N,
+                os.path.join(ROOT, "profiles", "traffic_q4k_q8_gemv_from_f32_28672x8192.json")))
     return out
 
 
@@ -849,11 +851,9 @@ def main():
             wbk = k.get("weight_bytes")
             if wbk in ceil:
                 k["frac_read_ceiling"] = round(ceil[wbk]["us"] / k["us"], 4)
-        for tag, _, alg_b, path in traffic_kernels()[1:]:
-            entry = {"swiglu_gemv_9728x2560": "swiglu_gemv_9728x2560", "q6k_gemv_2560x9728": "q6k_gemv_2560x9728",
-                     "q4k_q8_gemv_28672x8192": "q4k_q8_gemv_28672x8192"}[tag]
-            if entry in kern:
-                kern[entry]["traffic"] = traffic_entry(alg_b, path)
+        for tag, _, alg_b, path in traffic_kernels()[1:]:   # tag: the kernel's entry in the breakdown
+            if tag in kern:
+                kern[tag]["traffic"] = traffic_entry(alg_b, path)
         result["kernels"] = kern
         result["read_ceiling"] = {str(S): c for S, c in ceil.items()}
         result["c5_q8_accuracy"] = c5_q8_accuracy(gq, host, {**v, "c5W": sets[0]["c5W"]})

@@ -79,7 +79,7 @@ def test_traffic_records_for_every_recorded_kernel(tmp_path, monkeypatch):
     (bytes per launch against its algorithmic bytes)."""
     known_kib = (bench.CALIB_MIB << 20) / 1024
     sw = "void gemvq::gemv_kernel<3, 0, 2, true, true>(gemvq::GemvArgs)"
-    c5 = "void gemvq::gemv_wave_kernel<2, 0, 2>(gemvq::GemvArgs)"
+    c5 = "void gemvq::gemv_wave_kernel<2, 0, 2, true>(gemvq::GemvArgs)"
     fetch_rows = [(CAL, 1, known_kib / 2), (LM, 2, 100.0), (sw, 3, 500.0), (c5, 4, 700.0)]
     write_rows = [(CAL, 1, known_kib), (LM, 2, 1.0), (sw, 3, 2.0), (c5, 4, 3.0)]
     fdb, wdb = str(tmp_path / "f.db"), str(tmp_path / "w.db")
@@ -89,7 +89,7 @@ def test_traffic_records_for_every_recorded_kernel(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "traffic_kernels", lambda: kernels)
     bench.write_traffic(fdb, wdb, "cmd")
     got = {p.name for p in tmp_path.glob("*.json")}
-    assert got == {"lm_head_argmax.json", "swiglu_gemv_9728x2560.json", "q4k_q8_gemv_28672x8192.json"}
+    assert got == {"lm_head_argmax.json", "swiglu_gemv_9728x2560.json", "c5_q4k_q8_gemv_from_f32_28672x8192.json"}
     t = json.loads((tmp_path / "swiglu_gemv_9728x2560.json").read_text())
     assert t["hbm_fetch_bytes_per_launch"] == 2 * 500 * 1024 and t["hbm_write_bytes_per_launch"] == 2 * 1024
     assert t["traffic_over_algorithmic"] == pytest.approx((1000 * 1024 + 2048) / t["algorithmic_bytes_per_launch"], abs=1e-4)
