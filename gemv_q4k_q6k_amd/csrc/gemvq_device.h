@@ -238,11 +238,13 @@ __device__ __forceinline__ float q4k_dot(const Q4KRaw &r, const Q4KX &x, int c)
     return (dl * qxl - ml * x.sxl) + (dh * qxh - mh * x.sxh);
 }
 
-// Activation slice of a Q4_K part in fixed point (row-stream kernel): the
-// part's 64 values (x[256b + 64c + i], i < 64: the low sub-block's 32, then
-// the high one's) share one scale, X_i = rint(x_i * 2^(22-E)) with E the
-// binary exponent of the part's largest |x| (|X_i| <= 2^22, rounding error
-// at most 2^-23 of that value), split into a signed high byte and unsigned
+// Activation slice of a Q4_K part in fixed point (row-stream and resident
+// SwiGLU tile kernels): the part's 64 values (x[256b + 64c + i], i < 64: the
+// low sub-block's 32, then the high one's) share one scale,
+// X_i = rint(x_i * 2^(22-E)) with E the binary exponent of the part's largest
+// |x| (frexp: largest |x| = f 2^E, 1/2 <= f < 1, so |X_i| <= 2^22 and the
+// rounding error 2^(E-23) is at most 2^-22 of that value), split into a
+// signed high byte and unsigned
 // middle and low bytes, four elements to a dword (dwords 0..7 low sub-block,
 // 8..15 high).  e = E - 22 undoes the scale; sxl and sxh are the f32 sums
 // of the two sub-blocks for the min term.
@@ -449,9 +451,9 @@ __device__ __forceinline__ float q6k_dot(const Q6KRaw &r, const Q6KX &x, int u)
 // Activation slice of a Q6_K part in fixed point (wave-unit kernel).  The
 // part's 64 values (groups s = 0..3, x[128n + 32s + l0 + i], i < 16) share
 // one scale: X_i = rint(x_i * 2^(22-E)) with E the binary exponent of the
-// part's largest |x|, so |X_i| <= 2^22 and the rounding error is at most
-// 2^-23 of that largest value.  Each X_i is split into three bytes,
-// X_i = 65536*hi + 256*mid + lo (hi signed, mid and lo unsigned), four
+// part's largest |x| (frexp), so |X_i| <= 2^22 and the rounding error,
+// 2^(E-23), is at most 2^-22 of that largest value.  Each X_i is split into
+// three bytes, X_i = 65536*hi + 256*mid + lo (hi signed, mid and lo unsigned), four
 // elements to a dword, so a group's dot product with the 6-bit quants is
 // three exact integer dot products.  m[s] = -32 * sum_s * 2^(22-E) takes the
 // quants' offset off in the scaled domain, and e = E - 22 undoes the scale
