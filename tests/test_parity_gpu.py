@@ -328,6 +328,46 @@ def test_lm_head_ragged_last_unit(dev):
                 assert idx == min(pos), (pos, idx)
 
 
+@pytest.mark.parametrize("N", [65_536, 248_320])
+def test_lm_head_argmax_every_unit_counts(dev, N):
+    """Every unit of the matrix is read, and read as its own rows: on a
+    matrix of equal rows (every row the same Q6_K bytes), one row at a time
+    gets its fp16 d doubled -- the unique maximum -- at positions spread over
+    the whole matrix and dense over its last 15% (the last rounds of the
+    unit deal, and the ragged end); the argmax must return that row every
+    time.  With all rows equal it returns row 0."""
+    K = 1024
+    nb = K // 256
+    assert gq().tile_geometry(gq().KIND_Q6K, N, K)["wave_unit"] == 1
+    r = synth.rng_for(4242)
+    W1 = synth.q6k_weights(r, 1, K)
+    x = synth.activation(r, K)
+    y0 = float(oracle.q6k_gemv(W1, x, 1, K)[0])
+    if y0 < 0:
+        x = -x
+    assert abs(y0) > 1e-3
+    d = W1.reshape(nb, 210)[:, 208:210].copy().view(np.float16)
+    boosted = W1.reshape(nb, 210).copy()
+    boosted[:, 208:210] = (d.astype(np.float32) * 2).astype(np.float16).view(np.uint8).reshape(nb, 2)
+    dW = up(np.repeat(W1.reshape(1, -1), N, axis=0), dev)
+    dx = up(x, dev)
+    ws = _ws(dev, N, K)
+    base_row = dW[0].clone()
+    hot = up(boosted.reshape(-1), dev)
+    assert int(gq().lm_head_argmax(dW, dx, N, K, ws).item()) == 0
+    rng = np.random.default_rng(N)
+    tail = np.linspace(int(N * 0.85), N - 1, 24 if N > 100_000 else 48).astype(int)
+    targets = sorted(set([0, 1, 4, 15, 16, N // 3, N // 2, N - 2, N - 1] + tail.tolist()
+                         + rng.integers(0, N, 8).tolist()))
+    for t in targets:
+        dW[t] = hot
+        idx = int(gq().lm_head_argmax(dW, dx, N, K, ws).item())
+        dW[t] = base_row
+        assert idx == t, (N, t, idx)
+    assert int(torch.count_nonzero(ws[:4096]).item()) == 0
+    print(f"N={N}: {len(targets)} planted maxima found", flush=True)
+
+
 def _q6k_row_with_d(row, nb, dbits):
     row = row.copy().reshape(nb, 210)
     row[:, 208] = dbits & 0xFF
