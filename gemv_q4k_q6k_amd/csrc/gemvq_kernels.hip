@@ -98,14 +98,16 @@ template <> struct TileSlice<kSwiglu, true> { using T = FX4Slice; };
 
 // Activation form of the tile kernel when it stages x in LDS: fixed point
 // (true) or f32.  Q6_K always takes fixed point (its f32 dot needs two more
-// byte permutes per four weights).  The resident SwiGLU pair takes it too:
-// its two dot products per quarter block make it VALU-bound once the weight
+// byte permutes per four weights).  The resident Q4_K forms (single matrix
+// and SwiGLU pair) take it too: their dot products run after the weight
 // stream has arrived (f32: ~1.75 VALU operations per weight, fixed point
-// ~1.1), while a single resident Q4_K matrix keeps f32, which measured
-// faster there (the conversion sits on its start-up path).
+// ~1.1), and the conversion runs under the first tile's loads.  Measured
+// against the f32 form at 2560 x 9728, 9728 x 2560 and 4096 x 2560:
+// 5.94 -> 5.12, 5.60 -> 5.05 and 4.40 -> 4.01 us.  The ring form keeps f32:
+// its many short-lived workgroups each pay the conversion at start-up.
 constexpr bool tile_fx(int kind, bool xlds, bool res)
 {
-    return xlds && (kind == kQ6K || (res && kind == kSwiglu));
+    return xlds && (kind == kQ6K || (res && (kind == kSwiglu || kind == kQ4K)));
 }
 
 // Layout of the activation staged in LDS: 16 bytes of padding after every
@@ -1767,10 +1769,11 @@ static bool plan_in_wave(Plan &pl, int64_t N, int64_t K, int kind)
     // has room for them without spilling
     const bool halves = pl.nb == 32 && kind == kQ4KQ8;
     // The row-stream kernel wins (measured) for f32 Q4_K rows of two halves,
-    // and for one-step rows of a single matrix when each CU gets a couple of
-    // dozen rows at most; with more rows per CU, longer rows or the SwiGLU
-    // pair, the tile kernel's shorter start-up wins.
-    const bool stream = (kind == kQ4K && pl.nb == 32) || (pl.nb < 16 && kind != kSwiglu && N <= 6144);
+    // and for one-step rows of a single Q6_K or Q8 matrix when each CU gets a
+    // couple of dozen rows at most; with more rows per CU, longer rows, the
+    // SwiGLU pair or a single f32 Q4_K matrix (resident fixed-point tile:
+    // 4096 x 2560 4.48 -> 4.01 us), the tile kernel wins.
+    const bool stream = (kind == kQ4K && pl.nb == 32) || (pl.nb < 16 && kind != kSwiglu && kind != kQ4K && N <= 6144);
     if (!fits && !halves && !stream) return false;
     if (!fits && !halves) return plan_rows(pl, N, K, kind);
     // gemv_wave_kernel: the row's lanes are a power-of-two group (or two halves)

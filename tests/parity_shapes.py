@@ -38,7 +38,7 @@ def kernel_path(kind, N, K):
 
 TILE_PATHS = {"tile-res-lds", "tile-res", "tile-ring-lds", "tile-ring"}
 REQUIRED_PATHS = {
-    gq.KIND_Q4K: {"wave1", "rows1", "rows2"} | TILE_PATHS,
+    gq.KIND_Q4K: {"wave1", "rows2"} | TILE_PATHS,   # short single-matrix rows run the tile kernel
     gq.KIND_Q6K: {"wave1", "rows1"} | TILE_PATHS,
     gq.KIND_SWIGLU: {"wave1"} | TILE_PATHS,
     gq.KIND_Q4K_Q8: {"wave1", "wave2", "rows1"} | TILE_PATHS,

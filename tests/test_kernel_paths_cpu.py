@@ -15,7 +15,7 @@ def test_parity_cases_cover_every_path(kind):
 
 @pytest.mark.parametrize("kind,N,K,path", [
     (gq.KIND_Q6K, 248_320, 1024, "wave1"),      # lm_head
-    (gq.KIND_Q4K, 4096, 2560, "rows1"),
+    (gq.KIND_Q4K, 4096, 2560, "tile-res-lds"),
     (gq.KIND_Q4K, 9728, 2560, "tile-res-lds"),
     (gq.KIND_Q4K, 2560, 9728, "tile-res-lds"),
     (gq.KIND_SWIGLU, 9728, 2560, "tile-res-lds"),
