@@ -271,6 +271,47 @@ def test_lm_head_argmax_seed_sweep(dev):
     assert checked == 200
 
 
+def test_lm_head_argmax_full_vocab_x_sweep(dev, c3_full):
+    """200 activations at the full vocabulary (248,320 x 1024, the launch the
+    benchmark times, about 242 units per CU): the seed-0 matrix with x drawn
+    per seed.  The oracle's index decides when its top-2 gap exceeds 1e-3;
+    otherwise the first-index argmax of the device's own Q6_K GEMV must
+    (same row values).  Seeds with s % 100 == 99 copy the oracle's max row
+    over a later row (an earlier one if it is the last): the smaller index
+    must win."""
+    W, _, dW, _ = c3_full
+    N, K = synth.C3_LM_HEAD
+    ws = _ws(dev, N, K)
+    by_gap = by_self = ties = 0
+    for seed in range(200):
+        x = synth.activation(synth.rng_for(30_000 + seed), K)
+        dx = up(x, dev)
+        yhat = oracle.q6k_gemv(W, x, N, K)
+        i = oracle.argmax_first(yhat)
+        if seed % 100 == 99:
+            rr = np.random.default_rng(40_000 + seed)
+            j = int(rr.integers(i + 1, N)) if i < N - 1 else int(rr.integers(0, i))
+            saved = dW[j].clone()
+            dW[j] = dW[i]
+            idx = int(gq().lm_head_argmax(dW, dx, N, K, ws).item())
+            dW[j] = saved
+            assert idx == min(i, j), (seed, idx, i, j)
+            ties += 1
+            continue
+        idx = int(gq().lm_head_argmax(dW, dx, N, K, ws).item())
+        if oracle.top2_gap(yhat) > 1e-3:
+            assert idx == i, (seed, idx, i)
+            by_gap += 1
+        else:
+            y = gq().q6k_gemv(dW, dx, N, K).cpu().numpy()
+            assert idx == int(np.argmax(y)), (seed, idx)
+            by_self += 1
+    assert int(torch.count_nonzero(ws[:4096]).item()) == 0
+    print(f"full-vocabulary sweep: {by_gap} by the oracle's gap, {by_self} by the device's own logits, "
+          f"{ties} planted ties", flush=True)
+    assert by_gap + by_self + ties == 200
+
+
 def test_lm_head_constructed_ties(dev):
     """Exact ties at planned positions: same wave, same workgroup, different
     workgroups, index 0, index N-1, more than two copies; all rows equal."""
