@@ -950,6 +950,11 @@ template <int KIND>
 constexpr int wave_max_threads() { return (is_q8(KIND) || KIND == kQ4K) ? 1024 : 768; }
 constexpr int kWaveMaxThreads = 1024;   // the largest of wave_max_threads
 constexpr int kHalvesWaves = 8;          // waves per CU of the two-half (STEPS = 2) wave-unit kernel
+// The same kernel quantizing x in its prologue runs 16: the prologue's work
+// is shared by more waves (28,672 x 8192, duplicated builds interleaved:
+// 25.12 / 25.20 us with 8 waves, 24.66 / 24.64 with 16; the plain Q8 launch
+// goes the other way, 23.9 against 24.4 us).
+constexpr int kQuantHalvesWaves = 16;
 
 // QUANT (Q4_K x Q8 only): the activation arrives as f32 (a.x) and every
 // workgroup quantizes it to Q8 in its prologue, with the encoder every Q8
@@ -2165,7 +2170,7 @@ hipError_t launch_q4k_q8_gemv_from_f32(const void *W, const float *x, int8_t *xq
         a.y = y;
         pl.lds_bytes = ((pl.lds_bytes + 15) & ~(size_t)15) + (size_t)(K / 16);
         if (pl.steps == 2)
-            return launch_per_cu(gemv_wave_kernel<kQ4KQ8, kStore, 2, true>, kHalvesWaves, pl, a, cus, s, Timing{});
+            return launch_per_cu(gemv_wave_kernel<kQ4KQ8, kStore, 2, true>, kQuantHalvesWaves, pl, a, cus, s, Timing{});
         return launch_per_cu(gemv_wave_kernel<kQ4KQ8, kStore, 1, true>, wave_max_threads<kQ4KQ8>() / 64, pl, a, cus,
                              s, Timing{});
     }
