@@ -19,6 +19,13 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+// No multiply is fused into an add unless the code says so (fmaf): with the
+// compiler free to contract, two kernels built from the same device code
+// (another tile geometry template, the multi-output form, the Q8-emitting
+// epilogue) could round a row differently, and the library promises equal
+// bits wherever the row arithmetic is the same.
+#pragma clang fp contract(off)
+
 namespace gemvq {
 
 constexpr int kQK = 256;

@@ -149,7 +149,13 @@ def test_decode_step_graph_replays(dev):
         (junk * 2).sum().item()
         torch.cuda.synchronize()
         for k in og:
-            assert torch.equal(og[k], oe[k]), (rep, k)
+            if not torch.equal(og[k], oe[k]):
+                a_, b_ = og[k].cpu(), oe[k].cpu()
+                ne = (a_ != b_) if a_.dtype.is_floating_point is False else ~((a_ == b_) | (a_.isnan() & b_.isnan()))
+                where = torch.nonzero(ne).flatten()[:6].tolist()
+                detail = [(i, float(a_[i]), float(b_[i])) for i in where]
+                raise AssertionError(f"replay {rep}, output {k}: {int(ne.sum())} of {a_.numel()} elements differ "
+                                     f"between the replay and the eager calls, first {detail}")
         for w in (ws, ws2):
             assert int(torch.count_nonzero(w[:4096]).item()) == 0, rep
         check_against_oracle(rep, og)
