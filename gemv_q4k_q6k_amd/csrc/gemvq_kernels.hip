@@ -650,9 +650,14 @@ __device__ __forceinline__ void fx_preload(float (&v)[16], const float *x, int K
 // of the matrix is in flight at once.  Every tile's block sums then go to a
 // buffer of their own and one barrier precedes the row sums, which are
 // added in the same order as in the ring form (same bits).
-template <int KIND, int EPI, int PHASE, bool XLDS, bool RES = false>
-__global__ __launch_bounds__(RES ? kResThreads : kMaxThreads) void gemv_kernel(GemvArgs a)
+// MULTI (CU-resident Q4_K store only): up to kMaxMulti matrices of the same
+// K sharing x, their tiles numbered one matrix after the other (a.ustart[m]
+// is matrix m's first tile; a tile holds rows of one matrix only), each with
+// its own output and optional residual.
+template <int KIND, int EPI, int PHASE, bool XLDS, bool RES, bool MULTI>
+__device__ __forceinline__ void gemv_tile_body(GemvArgs a)
 {
+    static_assert(!MULTI || (RES && KIND == kQ4K && EPI == kStore), "multi-output tiles: resident Q4_K store");
     constexpr int kPhase = PHASE;
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int BYTES = Traits<KIND>::kBytes;
@@ -673,7 +678,20 @@ __global__ __launch_bounds__(RES ? kResThreads : kMaxThreads) void gemv_kernel(G
     const int64_t tile_stride = (int64_t)a.rows_tile * a.nb * BYTES;   // bytes per tile
     const uint32_t lane_off = (uint32_t)((p * a.nb + b) * BYTES);      // < tile_stride
 
+    // multi-output: the matrix of tile t (workgroup-uniform)
+    auto mat_of = [&](int t) {
+        int m = 0;
+        if constexpr (MULTI) {
+#pragma unroll
+            for (int j = 1; j < kMaxMulti; ++j) m += t >= a.ustart[j] ? 1 : 0;
+        }
+        return m;
+    };
     auto valid_tile = [&](int t) {
+        if constexpr (MULTI) {
+            const int m = mat_of(t);
+            return lane_on && t < t_end && (int64_t)(t - a.ustart[m]) * a.rows_tile + p < a.Nm[m];
+        }
         return lane_on && t < t_end && (t < a.tiles - 1 || p < last_rows);
     };
     // Loads are unconditional so no branch surrounds them (a branch, even a
@@ -684,6 +702,11 @@ __global__ __launch_bounds__(RES ? kResThreads : kMaxThreads) void gemv_kernel(G
     auto fetch = [&](RawSet<KIND> &rs, int t) {
         const int tt = t < t_end ? t : t_end - 1;
         const uint32_t off = valid_tile(t) ? lane_off : 0u;
+        if constexpr (MULTI) {
+            const int m = mat_of(tt);
+            q4k_load(rs.r[0], a.Wm[m] + (int64_t)(tt - a.ustart[m]) * tile_stride, off, part);
+            return;
+        }
         const int64_t tb = (int64_t)tt * tile_stride;
         if constexpr (is_q6(KIND)) {
             q6k_load(rs.r[0], a.W + tb, off, part);
@@ -856,7 +879,13 @@ __global__ __launch_bounds__(RES ? kResThreads : kMaxThreads) void gemv_kernel(G
     // end) and contribute +0 there: a partial sum that starts at +0 is never
     // -0, so adding +0 leaves it unchanged.  Uniform across the group.
     auto row_out_group = [&](const float *rb, int t, int pr, int s, int L) {
-        const int64_t row = (int64_t)t * a.rows_tile + pr;
+        int64_t row = (int64_t)t * a.rows_tile + pr;
+        int m = 0;
+        if constexpr (MULTI) {
+            m = mat_of(t);
+            row = (int64_t)(t - a.ustart[m]) * a.rows_tile + pr;
+            if (row >= a.Nm[m]) return;
+        }
         if (row >= a.N) return;
         float r[2];
 #pragma unroll
@@ -875,7 +904,13 @@ __global__ __launch_bounds__(RES ? kResThreads : kMaxThreads) void gemv_kernel(G
             }
             r[o] = group_sum(acc, L);
         }
-        if (s == 0) row_epi(row, r);
+        if constexpr (MULTI) {
+            // the residual (possibly the output itself) is read before the
+            // output is written, by the same lane
+            if (s == 0) a.ym[m][row] = a.rm[m] ? r[0] + a.rm[m][row] : r[0];
+        } else {
+            if (s == 0) row_epi(row, r);
+        }
     };
     // dot, row reduction and epilogue of tile t (workgroup-uniform control flow)
     auto process = [&](const RawSet<KIND> &rs, int t) {
@@ -929,6 +964,19 @@ __global__ __launch_bounds__(RES ? kResThreads : kMaxThreads) void gemv_kernel(G
         argmax_finish(a, best, tid < a.rows_tile ? tid : -1, a.rows_tile);
     }
     if constexpr (EPI == kQ8Emit) q8_emit_finish(a, s_h, r_begin, r_end);
+}
+
+template <int KIND, int EPI, int PHASE, bool XLDS, bool RES = false>
+__global__ __launch_bounds__(RES ? kResThreads : kMaxThreads) void gemv_kernel(GemvArgs a)
+{
+    gemv_tile_body<KIND, EPI, PHASE, XLDS, RES, false>(a);
+}
+
+// CU-resident tiles of several Q4_K matrices sharing x (q4k_gemv_multi).
+template <int PHASE>
+__global__ __launch_bounds__(kResThreads) void gemv_kernel_multi(GemvArgs a)
+{
+    gemv_tile_body<kQ4K, kStore, PHASE, true, true, true>(a);
 }
 
 // ------------------------------------------------------ wave-unit kernel
@@ -2298,12 +2346,85 @@ hipError_t launch_lm_head_argmax(const void *W, const float *x, const uint32_t *
     return launch<kQ6K, kArgmax>(pl, a, cus, s, tm);
 }
 
+// Multi-output launch on CU-resident tiles, where one matrix of all the
+// rows would take that form: waves per workgroup w in {4, 8, 12}, each
+// matrix's rows in tiles of its own (R = 64w / (4 nb) rows), the w whose
+// busiest CU has the fewest rows with its tiles all in flight (at most
+// kResMaxPhase) and x staged in LDS.  False if there is none.
+static bool launch_multi_resident(const void *const *W, const int64_t *N, float *const *y, const float *const *r,
+                                  int count, const float *x, int64_t total, int64_t K, int cus, hipStream_t s,
+                                  hipError_t &err)
+{
+    const Plan single = make_plan(total, K, kQ4K, cus);
+    if (single.wave_local || !single.resident) return false;
+    Plan pl = single;
+    int64_t best_rows = INT64_MAX, best_tiles = 0, best_per = 0;
+    int best_w = 0;
+    for (int w = 4; w <= kResThreads / 64; w += 4) {
+        const int rows = 64 * w / pl.lanes_row;
+        if (rows < 2) continue;   // x is staged in LDS only when rows share it
+        int64_t tiles = 0;
+        for (int m = 0; m < count; ++m) tiles += (N[m] + rows - 1) / rows;
+        const int64_t per = (tiles + cus - 1) / cus;
+        if (per > kResMaxPhase) continue;
+        const size_t red = (size_t)per * rows * pl.nb * 4;
+        const size_t staged = (tile_staged_bytes(K, kQ4K, true) + 15) & ~(size_t)15;
+        if (staged + red > 65536) continue;
+        if (per * rows < best_rows) {
+            best_rows = per * rows;
+            best_w = w;
+            best_tiles = tiles;
+            best_per = per;
+        }
+    }
+    if (!best_w) return false;
+    pl.waves = best_w;
+    pl.threads = 64 * best_w;
+    pl.rows_tile = pl.threads / pl.lanes_row;
+    pl.phase = (int)best_per;
+    pl.tiles = best_tiles;
+    pl.grid = (int)((best_tiles + best_per - 1) / best_per);
+    pl.x_in_lds = 1;
+    pl.red_off = (tile_staged_bytes(K, kQ4K, true) + 15) & ~(size_t)15;
+    pl.lds_bytes = pl.red_off + (size_t)best_per * pl.rows_tile * pl.nb * 4;
+    GemvArgs a = base_args(pl, total);
+    a.x = x;
+    int64_t t = 0;
+    for (int m = 0; m < kMaxMulti; ++m) {
+        a.ustart[m] = m < count ? (int)t : INT32_MAX;
+        a.Wm[m] = m < count ? (const uint8_t *)W[m] : nullptr;
+        a.ym[m] = m < count ? y[m] : nullptr;
+        a.rm[m] = (m < count && r) ? r[m] : nullptr;
+        a.Nm[m] = m < count ? N[m] : 0;
+        if (m < count) t += (N[m] + pl.rows_tile - 1) / pl.rows_tile;
+    }
+    a.ustart[kMaxMulti] = INT32_MAX;
+    a.W = a.Wm[0];
+    a.y = a.ym[0];
+    a.tiles_q = (int)(pl.tiles / pl.grid);
+    a.tiles_r = (int)(pl.tiles % pl.grid);
+    switch (pl.phase) {
+    case 1: launch_on(gemv_kernel_multi<1>, pl, a, s, Timing{}); break;
+    case 2: launch_on(gemv_kernel_multi<2>, pl, a, s, Timing{}); break;
+    case 3: launch_on(gemv_kernel_multi<3>, pl, a, s, Timing{}); break;
+    default: launch_on(gemv_kernel_multi<kResMaxPhase>, pl, a, s, Timing{}); break;
+    }
+    err = hipGetLastError();
+    return true;
+}
+
 hipError_t launch_q4k_gemv_multi(const void *const *W, const int64_t *N, float *const *y, const float *const *r,
                                  int count, const float *x, int64_t K, int cus, hipStream_t s)
 {
-    // one row-stream plan for the stacked matrices (every row inside one wave)
     int64_t total = 0;
     for (int m = 0; m < count; ++m) total += N[m];
+    // CU-resident tiles where one matrix of all the rows would take them
+    // (q, k and v of 4096 + 1024 + 1024 rows at K = 2560, graph replay:
+    // 6.82 us on the row-stream kernel, 6.26 us on 8-wave resident tiles;
+    // 4 waves with 5 tiles each measured 0.2 us slower)
+    hipError_t err = hipSuccess;
+    if (launch_multi_resident(W, N, y, r, count, x, total, K, cus, s, err)) return err;
+    // otherwise one row-stream plan for the stacked matrices (every row inside one wave)
     Plan pl{};
     plan_rows(pl, total, K, kQ4K);
     GemvArgs a = base_args(pl, total);

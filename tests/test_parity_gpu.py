@@ -684,6 +684,9 @@ def test_lm_head_argmax_masked_c3_full(dev, c3_full):
     ((777, 1, 3, 300), 8192, "some"),        # ragged, four matrices, two-step rows
     ((5, 7), 256, "inplace"),
     ((100, 200), 14336, "some"),             # the largest K
+    ((777, 1, 3, 300), 2560, "some"),        # CU-resident tiles: ragged, four matrices, a 1-row one
+    ((4096, 1024, 1024), 2560, "inplace"),   # CU-resident tiles, residuals in place
+    ((1000, 2000), 4352, "none"),            # CU-resident tiles, 17 super-blocks a row
 ])
 def test_q4k_gemv_multi(dev, Ns, K, res):
     r = synth.rng_for(sum(Ns) + K)
@@ -708,19 +711,23 @@ def test_q4k_gemv_multi(dev, Ns, K, res):
         check_f32(f"multi {Ns} K={K} {res} [{i}]", y.cpu().numpy(), yhat)
 
 
-def test_q4k_gemv_multi_matches_single_rows(dev):
-    """For shapes whose single GEMV runs the same row-stream kernel (two-step
-    rows, K = 8192), each output is bit-identical to that tensor's own
-    q4k_gemv."""
+@pytest.mark.parametrize("K,Ns,path", [
+    (8192, (777, 1, 300), "rows2"),             # row-stream kernel, two-step rows
+    (2560, (4096, 1024, 1024), "tile-res-lds"),  # CU-resident tiles (fixed-point x)
+])
+def test_q4k_gemv_multi_matches_single(dev, K, Ns, path):
+    """Where each single GEMV runs the same kernel form as the multi-output
+    launch (row-stream two-step rows; CU-resident fixed-point tiles, whose
+    row arithmetic does not depend on the tile geometry), each output is
+    bit-identical to that tensor's own q4k_gemv."""
     import parity_shapes as ps
-    K = 8192
-    Ns = (777, 1, 300)
-    r = synth.rng_for(9)
+    r = synth.rng_for(9 + K)
     Ws = [up(synth.q4k_weights(r, N, K), dev) for N in Ns]
     dx = up(synth.activation(r, K), dev)
     out = gq().q4k_gemv_multi(Ws, list(Ns), dx, K)
+    assert ps.kernel_path(gq().KIND_Q4K, sum(Ns), K) == path
     for W, N, y in zip(Ws, Ns, out):
-        assert ps.kernel_path(gq().KIND_Q4K, N, K) == "rows2"
+        assert ps.kernel_path(gq().KIND_Q4K, N, K) == path
         assert torch.equal(y, gq().q4k_gemv(W, dx, N, K))
 
 
