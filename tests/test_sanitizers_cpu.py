@@ -1,7 +1,7 @@
 """Address and undefined-behaviour sanitizer runs of the host code (CPU only).
 
-Two drivers under tests/sanitize/, each built here with the sanitizers on and
-run to completion:
+Two test programs under tests/sanitize/, each built here with the sanitizers
+on and run to completion:
 
 * the C oracle: every function on exact-size heap buffers over shapes from one
   super-block to K = 32768, with 1 and 2 OpenMP threads (gcc,
@@ -12,7 +12,7 @@ run to completion:
   the geometry hook.  hipcc instruments the host pass only; device code is
   built as for the product.
 
-A sanitizer report aborts the driver (-fno-sanitize-recover=all), so a zero
+A sanitizer report aborts the program (-fno-sanitize-recover=all), so a zero
 exit status means a clean run.
 """
 import os
