@@ -528,6 +528,17 @@ def traffic_kernels():
                 os.path.join(ROOT, "profiles", "traffic_swiglu_gemv_9728x2560.json")))
     out.append(("q6k_gemv_2560x9728", r"gemv_kernel<1, 0, \d, true, true>", K * N // 256 * 210 + 4 * (N + K),
                 os.path.join(ROOT, "profiles", "traffic_q6k_gemv_2560x9728.json")))
+    # config 2: 4096x2560 is the step's only three-tile resident instantiation;
+    # 2560x9728 and 9728x2560 share one (two tiles) and equal byte counts, so
+    # one record, under both breakdown entries ('+'-joined tag), covers both
+    N, K = synth.C2_Q4K[0]
+    out.append(("q4k_gemv_4096x2560", r"gemv_kernel<0, 0, 3, true, true>", N * K // 256 * 144 + 4 * (N + K),
+                os.path.join(ROOT, "profiles", "traffic_q4k_gemv_4096x2560.json")))
+    N, K = synth.C2_Q4K[1]
+    assert tuple(synth.C2_Q4K[2]) == (K, N)
+    out.append(("q4k_gemv_2560x9728+q4k_gemv_9728x2560", r"gemv_kernel<0, 0, 2, true, true>",
+                N * K // 256 * 144 + 4 * (N + K),
+                os.path.join(ROOT, "profiles", "traffic_q4k_gemv_2560x9728_and_9728x2560.json")))
     N, K = synth.C5_Q8
     # f32 x in, its Q8 codes and scales out (one workgroup writes them), y out
     out.append(("c5_q4k_q8_gemv_from_f32_28672x8192", r"gemv_wave_kernel<2, 0, 2, true>",
@@ -853,9 +864,10 @@ def main():
             wbk = k.get("weight_bytes")
             if wbk in ceil:
                 k["frac_read_ceiling"] = round(ceil[wbk]["us"] / k["us"], 4)
-        for tag, _, alg_b, path in traffic_kernels()[1:]:   # tag: the kernel's entry in the breakdown
-            if tag in kern:
-                kern[tag]["traffic"] = traffic_entry(alg_b, path)
+        for tag, _, alg_b, path in traffic_kernels()[1:]:   # tag: the kernel's entries in the breakdown
+            for t in tag.split("+"):
+                if t in kern:
+                    kern[t]["traffic"] = traffic_entry(alg_b, path)
         result["kernels"] = kern
         result["read_ceiling"] = {str(S): c for S, c in ceil.items()}
         result["c5_q8_accuracy"] = c5_q8_accuracy(gq, host, {**v, "c5W": sets[0]["c5W"]})
