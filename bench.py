@@ -748,6 +748,16 @@ def config_summary(kern, ceil, cpu):
     return out
 
 
+def attach_traffic(kern):
+    """Each recorded kernel's HBM bytes per launch (None if its record is
+    stale) under its breakdown entries; a '+'-joined tag names several
+    entries that share one kernel instantiation and one record."""
+    for tag, _, alg_b, path in traffic_kernels()[1:]:
+        for t in tag.split("+"):
+            if t in kern:
+                kern[t]["traffic"] = traffic_entry(alg_b, path)
+
+
 def traffic_entry(alg_bytes, path=None):
     """HBM bytes per launch from a committed rocprofv3 counter record (the
     lm_head's by default), if it was taken on the current kernel sources."""
@@ -864,10 +874,7 @@ def main():
             wbk = k.get("weight_bytes")
             if wbk in ceil:
                 k["frac_read_ceiling"] = round(ceil[wbk]["us"] / k["us"], 4)
-        for tag, _, alg_b, path in traffic_kernels()[1:]:   # tag: the kernel's entries in the breakdown
-            for t in tag.split("+"):
-                if t in kern:
-                    kern[t]["traffic"] = traffic_entry(alg_b, path)
+        attach_traffic(kern)
         result["kernels"] = kern
         result["read_ceiling"] = {str(S): c for S, c in ceil.items()}
         result["c5_q8_accuracy"] = c5_q8_accuracy(gq, host, {**v, "c5W": sets[0]["c5W"]})

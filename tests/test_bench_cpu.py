@@ -93,3 +93,17 @@ def test_traffic_records_for_every_recorded_kernel(tmp_path, monkeypatch):
     t = json.loads((tmp_path / "swiglu_gemv_9728x2560.json").read_text())
     assert t["hbm_fetch_bytes_per_launch"] == 2 * 500 * 1024 and t["hbm_write_bytes_per_launch"] == 2 * 1024
     assert t["traffic_over_algorithmic"] == pytest.approx((1000 * 1024 + 2048) / t["algorithmic_bytes_per_launch"], abs=1e-4)
+
+
+def test_shared_traffic_record_reaches_every_entry(tmp_path, monkeypatch):
+    """A record whose tag joins several breakdown entries with '+' is
+    attached to each of them; entries without a record are left alone."""
+    rec = tmp_path / "pair.json"
+    rec.write_text(json.dumps({"kernel_source_hash": bench.kernel_source_hash(), "bytes_per_launch": 1234}))
+    monkeypatch.setattr(bench, "traffic_kernels",
+                        lambda: [("lm_head_argmax", "x", 1, str(tmp_path / "none.json")),
+                                 ("a_1x2+a_2x1", "y", 1000, str(rec))])
+    kern = {"a_1x2": {"us": 1.0}, "a_2x1": {"us": 2.0}, "b": {"us": 3.0}}
+    bench.attach_traffic(kern)
+    assert kern["a_1x2"]["traffic"] == 1234 and kern["a_2x1"]["traffic"] == 1234
+    assert "traffic" not in kern["b"]
