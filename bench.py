@@ -720,11 +720,41 @@ def read_sizes():
     return sz
 
 
+def config_algorithmic_bytes():
+    """Bytes a config must move per call: its weights plus the f32 vectors
+    it reads and writes (config 4: h written and read back between the two
+    launches; config 5, one launch: x read, the Q8 codes and fp16 scales
+    written once, the GEMV reading them from LDS, y written)."""
+    import synth
+    wb = weight_bytes()
+    N, K = synth.C1_Q4K
+    out = {"c1": wb["c1"] + 4 * (N + K)}
+    out["c2"] = wb["c2"] + sum(4 * (N + K) for N, K in synth.C2_Q4K)
+    N, K = synth.C3_LM_HEAD
+    out["c3"] = wb["c3"] + 4 * K + 4
+    N, K = synth.C4_SWIGLU
+    out["c4"] = wb["c4"] + 4 * K + 2 * 4 * N + 4 * K
+    N, K = synth.C5_Q8
+    out["c5"] = wb["c5"] + 4 * K + K + K // 16 + 4 * N
+    return out
+
+
+def device_facts(dev):
+    """The device's own account of itself (torch's view of
+    hipGetDeviceProperties), for the report."""
+    import torch
+    pr = torch.cuda.get_device_properties(dev)
+    keys = ("name", "gcnArchName", "multi_processor_count", "warp_size", "total_memory", "L2_cache_size",
+            "shared_memory_per_multiprocessor", "shared_memory_per_block", "max_threads_per_multi_processor")
+    return {k: getattr(pr, k) for k in keys if hasattr(pr, k)}
+
+
 def config_summary(kern, ceil, cpu):
     """Per-config figures from the breakdown, the read ceilings and the CPU
     oracle timings."""
     sz = read_sizes()
     wb = weight_bytes()
+    alg = config_algorithmic_bytes()
     out = {}
     for name, (entry, reads, label) in CONFIG_KERNELS.items():
         k = kern.get(entry)
@@ -734,6 +764,7 @@ def config_summary(kern, ceil, cpu):
         read_us = sum(ceil[sz[r]]["us"] for r in reads) if ceil else None
         row = {"workload": label, "us_per_call": us, "gemv_per_s": round(1e6 / us, 1),
                "weight_GBps": round(wb[name] / us / 1e3, 1),
+               "algorithmic_bytes": alg[name], "algorithmic_GBps": round(alg[name] / us / 1e3, 1),
                "frac_hbm_peak": round(wb[name] / us / 1e3 / HBM_PEAK_GBS, 4),
                "read_ceiling_us": round(read_us, 2) if read_us else None,
                "frac_read_ceiling": round(read_us / us, 4) if read_us else None}
@@ -862,6 +893,7 @@ def main():
         "graph_ms_per_step": round(gms, 4),
         "graph_value": round(step_bytes / (gms * 1e-3) / 1e9, 1),
         "self_check_ok": parity_ok,
+        "device": device_facts(dev),
         "wall_s": round(wall, 3),
         "roofline": roofline,
     }

@@ -107,3 +107,15 @@ def test_shared_traffic_record_reaches_every_entry(tmp_path, monkeypatch):
     bench.attach_traffic(kern)
     assert kern["a_1x2"]["traffic"] == 1234 and kern["a_2x1"]["traffic"] == 1234
     assert "traffic" not in kern["b"]
+
+
+def test_config_algorithmic_bytes():
+    """Per-config bytes: the weights plus the vectors each config moves
+    (x and y; config 4's h written and read back; config 5's Q8 codes and
+    scales written once by its single launch)."""
+    alg = bench.config_algorithmic_bytes()
+    assert alg["c1"] == 589_824 + 4_096 + 4_096
+    assert alg["c2"] == 33_914_880 + 124_928
+    assert alg["c3"] == bench.lm_head_algorithmic_bytes() == 208_588_800 + 4_096 + 4
+    assert alg["c4"] == 48_445_440 + 10_240 + 77_824 + 10_240
+    assert alg["c5"] == 132_120_576 + 32_768 + 8_192 + 512 + 114_688
