@@ -368,6 +368,15 @@ def breakdown(gq, sets, v, reps=24):
            N * K // 256 * 210 + 4 * (N + K), N * K // 256 * 210)
     timeit("lm_head_argmax_248320x1024", lambda w: gq.lm_head_argmax(w[0], v["c3x"], N, K, v["ws"], out_idx=v["idx"]),
            ws, lm_head_algorithmic_bytes(), N * K // 256 * 210)
+    # the masked variant: a seeded ban mask over ~1% of the vocabulary, one
+    # 4-byte mask word per 32 rows read with the weights
+    banned = np.random.default_rng(11).random(N) < 0.01
+    mask = torch.from_numpy(np.packbits(np.concatenate([banned, np.zeros((-N) % 32, bool)]),
+                                        bitorder="little").view(np.int32)).to(v["c3x"].device)
+    ws_m = torch.zeros_like(v["ws"])
+    timeit("lm_head_argmax_masked_248320x1024",
+           lambda w: gq.lm_head_argmax_masked(w[0], v["c3x"], mask, N, K, ws_m, out_idx=v["idx"]),
+           ws, lm_head_algorithmic_bytes() + 4 * ((N + 31) // 32), N * K // 256 * 210)
     del ws
     N, K = synth.C4_SWIGLU
     ws = list(zip(copies(s0["c4Wg"]), copies(s0["c4Wu"])))
