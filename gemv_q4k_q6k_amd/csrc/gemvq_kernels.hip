@@ -71,6 +71,12 @@ struct GemvArgs {
     int batch_round;
     // tile kernel: byte offset of the row-reduction buffer in LDS
     uint32_t red_off;
+    // threads per workgroup (blockDim.x), set by the launch.  The tile and
+    // batch kernels read it from here: blockDim.x comes from the implicit
+    // kernel arguments through a vector load that the compiler may issue
+    // after the weight loads, and vector-memory counters retire in order, so
+    // its wait then waited for every weight load issued before it.
+    int threads;
 };
 
 // ------------------------------------------------------- activation setup
@@ -225,6 +231,34 @@ __device__ __forceinline__ void load_x(Q8X &xs, const int8_t *qsrc, const uint16
         xs.dl = (float)__builtin_bit_cast(_Float16, dsrc[j]);
         xs.dh = (float)__builtin_bit_cast(_Float16, dsrc[j + 1]);
     }
+}
+
+// The fp16 scale words of a lane's Q8 slice, loaded on their own so that
+// they can go out with the activation codes, before any weight load: the
+// two scales of Q8X part c of block b (one dword: scales 8b+2c, 8b+2c+1), or
+// the four of Q6Q8X part u (two dwords: scales 8b+4n .. 8b+4n+3).  The
+// scale array is 4-byte aligned.
+__device__ __forceinline__ void load_xd(uint32_t (&w)[2], const uint16_t *dsrc, const Q8X *, int b, int c)
+{
+    w[0] = *(const uint32_t *)(dsrc + 8 * b + 2 * c);
+    w[1] = 0u;
+}
+__device__ __forceinline__ void load_xd(uint32_t (&w)[2], const uint16_t *dsrc, const Q6Q8X *, int b, int u)
+{
+    const uint32_t *dp = (const uint32_t *)(dsrc + 8 * b + 4 * (u >> 1));
+    w[0] = dp[0];
+    w[1] = dp[1];
+}
+// The slice's scales from those words (the same values load_x reads).
+__device__ __forceinline__ void set_xd(Q8X &xs, const uint32_t (&w)[2])
+{
+    xs.dl = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[0] & 0xFFFFu));
+    xs.dh = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[0] >> 16));
+}
+__device__ __forceinline__ void set_xd(Q6Q8X &xs, const uint32_t (&w)[2])
+{
+    xs.d2[0] = w[0];
+    xs.d2[1] = w[1];
 }
 
 // Integer sums of the slice's two Q8 blocks.
@@ -462,7 +496,7 @@ __device__ void q8_emit_finish(const GemvArgs &a, const float *s_h, int64_t r0, 
     __syncthreads();   // every row of the range is in LDS
     if (r1 <= r0) return;
     const int l = threadIdx.x & 31;
-    const int hw = (int)(threadIdx.x >> 5), nhw = (int)(blockDim.x >> 5);
+    const int hw = (int)(threadIdx.x >> 5), nhw = a.threads >> 5;
     uint32_t *cnt = (uint32_t *)a.ws;
     uint32_t *vals = (uint32_t *)(a.ws + a.emit_vals_off);
     const int64_t jb = r0 >> 5, je = (r1 - 1) >> 5;
@@ -663,6 +697,17 @@ __device__ __forceinline__ void gemv_tile_body(GemvArgs a)
     constexpr int BYTES = Traits<KIND>::kBytes;
     constexpr int OUTS = Traits<KIND>::kOuts;
     const int tid = threadIdx.x;
+    // threads per workgroup.  The int8 kinds, the argmax epilogues and the Q8
+    // emission take it from the arguments (their blockDim.x read was a vector
+    // load issued after the weight loads; see GemvArgs::threads).  The f32
+    // kinds read blockDim.x where it is used, as a scalar load whose round
+    // trip sits between the activation loads and the weights: at K = 9728
+    // that head start for the activation measured 0.35-0.45 us faster than
+    // without it (2560 x 9728 Q4_K and Q6_K), at K = 2560 0.2-0.25 us slower.
+    auto nthr = [&]() -> int {
+        if constexpr (is_q8(KIND) || is_argmax(EPI) || EPI == kQ8Emit) return a.threads;
+        else return (int)blockDim.x;
+    };
     const int p = (int)__umulhi((uint32_t)tid, a.lanes_row_magic);   // row within the tile
     const int rr = tid - p * a.lanes_row;     // lane within the row
     const int b = rr >> 2;                    // super-block column
@@ -741,7 +786,7 @@ __device__ __forceinline__ void gemv_tile_body(GemvArgs a)
     float xg0[16], xg1[16];
     if constexpr (kFx) {
         fx_preload<KIND>(xg0, a.x, K, tid);
-        fx_preload<KIND>(xg1, a.x, K, tid + (int)blockDim.x);
+        fx_preload<KIND>(xg1, a.x, K, tid + nthr());
     }
     // float4 (or 16 int8) staged per thread through registers; a resident
     // workgroup has 768 threads, so 4 cover K <= 12288 in f32
@@ -753,7 +798,7 @@ __device__ __forceinline__ void gemv_tile_body(GemvArgs a)
         const int esz = is_q8(KIND) ? 1 : 4;
 #pragma unroll
         for (int r = 0; r < kXRegs; ++r) {
-            const int i = (tid + r * (int)blockDim.x) * step;
+            const int i = (tid + r * nthr()) * step;
             if (i < K) xr[r] = *(const u32x4 *)(src + (size_t)i * esz);
         }
     }
@@ -762,10 +807,15 @@ __device__ __forceinline__ void gemv_tile_body(GemvArgs a)
     if constexpr (!XLDS) {
         // each lane reads its own slice (no other lane of the tile shares it)
         if constexpr (is_q8(KIND))
-            load_x(xs.v, a.xq, a.xd, xb, part);
+            load_x(xs.v, a.xq, nullptr, xb, part);
         else
             load_x(xs.v, a.x, xb, part);
     }
+    // the lane's Q8 scale words go out with the codes, before the weights: a
+    // scale load issued after them would wait for every one of them
+    uint32_t xdw[2];
+    if constexpr (is_q8(KIND)) load_xd(xdw, a.xd, &xs.v, xb, part);
+    if constexpr (!XLDS && is_q8(KIND)) set_xd(xs.v, xdw);
     RawSet<KIND> ring[kPhase];
 #pragma unroll
     for (int d = 0; d < kPre; ++d) fetch(ring[d], t_begin + d);
@@ -789,24 +839,27 @@ __device__ __forceinline__ void gemv_tile_body(GemvArgs a)
         const int esz = is_q8(KIND) ? 1 : 4;
 #pragma unroll
         for (int r = 0; r < kXRegs; ++r) {
-            const int i = (tid + r * (int)blockDim.x) * step;
+            const int i = (tid + r * nthr()) * step;
             if (i < K) *(u32x4 *)(smem + lds_pad((uint32_t)(i * esz))) = xr[r];
         }
-        for (int i = (tid + kXRegs * (int)blockDim.x) * step; i < K; i += (int)blockDim.x * step)
+        for (int i = (tid + kXRegs * nthr()) * step; i < K; i += nthr() * step)
             *(u32x4 *)(smem + lds_pad((uint32_t)(i * esz))) = *(const u32x4 *)(src + (size_t)i * esz);
         __syncthreads();
     }
     if constexpr (kFx) {
         // slice loaded above
     } else if constexpr (is_q8(KIND)) {
-        if constexpr (XLDS) load_x<true>(xs.v, (const int8_t *)smem, a.xd, xb, part);
+        if constexpr (XLDS) {
+            load_x<true>(xs.v, (const int8_t *)smem, nullptr, xb, part);
+            set_xd(xs.v, xdw);
+        }
         finish_x(xs.v);
     } else {
         if constexpr (XLDS) {
             // K/16 sums of 16 consecutive activation values, once per workgroup
             const float *sx = (const float *)smem;
             float *ssum = (float *)(smem + lds_pad(4u * (uint32_t)K));
-            for (int g = tid; g < K / 16; g += blockDim.x) ssum[g] = sum16(x_at<true>(sx, 16 * g));
+            for (int g = tid; g < K / 16; g += nthr()) ssum[g] = sum16(x_at<true>(sx, 16 * g));
             __syncthreads();
             load_x<true>(xs.v, sx, xb, part);
             finish_x(xs.v, (const float *)ssum, xb, part);
@@ -882,9 +935,19 @@ __device__ __forceinline__ void gemv_tile_body(GemvArgs a)
         int64_t row = (int64_t)t * a.rows_tile + pr;
         int m = 0;
         if constexpr (MULTI) {
+            // the matrix's fields picked by constant index: the lane groups of
+            // a wave hold rows of different tiles, and a lane-varying index
+            // into the argument arrays loads them with waited vector loads
             m = mat_of(t);
-            row = (int64_t)(t - a.ustart[m]) * a.rows_tile + pr;
-            if (row >= a.Nm[m]) return;
+            int us = a.ustart[0];
+            int64_t nm = a.Nm[0];
+#pragma unroll
+            for (int j = 1; j < kMaxMulti; ++j) {
+                us = m == j ? a.ustart[j] : us;
+                nm = m == j ? a.Nm[j] : nm;
+            }
+            row = (int64_t)(t - us) * a.rows_tile + pr;
+            if (row >= nm) return;
         }
         if (row >= a.N) return;
         float r[2];
@@ -907,7 +970,14 @@ __device__ __forceinline__ void gemv_tile_body(GemvArgs a)
         if constexpr (MULTI) {
             // the residual (possibly the output itself) is read before the
             // output is written, by the same lane
-            if (s == 0) a.ym[m][row] = a.rm[m] ? r[0] + a.rm[m][row] : r[0];
+            float *ym = a.ym[0];
+            const float *rm = a.rm[0];
+#pragma unroll
+            for (int j = 1; j < kMaxMulti; ++j) {
+                ym = m == j ? a.ym[j] : ym;
+                rm = m == j ? a.rm[j] : rm;
+            }
+            if (s == 0) ym[row] = rm ? r[0] + rm[row] : r[0];
         } else {
             if (s == 0) row_epi(row, r);
         }
@@ -932,7 +1002,7 @@ __device__ __forceinline__ void gemv_tile_body(GemvArgs a)
         const int nrows = kPhase * a.rows_tile;
         const int lg = a.nb <= 16 ? 2 : (a.nb <= 32 ? 3 : 4);
         const int L = 1 << lg, s = tid & (L - 1);
-        for (int j = tid >> lg; j < nrows; j += (int)blockDim.x >> lg) {
+        for (int j = tid >> lg; j < nrows; j += nthr() >> lg) {
             const int d = j / a.rows_tile;
             if (t_begin + d < t_end) row_out_group(red + d * red_stride, t_begin + d, j - d * a.rows_tile, s, L);
         }
@@ -940,7 +1010,7 @@ __device__ __forceinline__ void gemv_tile_body(GemvArgs a)
             // every wave folds its threads' keys first (all lanes active here)
             const int lane = tid & 63;
             best = wave_max_key(best);
-            argmax_finish(a, best, lane == 0 ? (tid >> 6) : -1, (int)(blockDim.x >> 6));
+            argmax_finish(a, best, lane == 0 ? (tid >> 6) : -1, (int)(nthr() >> 6));
         }
         if constexpr (EPI == kQ8Emit) q8_emit_finish(a, s_h, r_begin, r_end);
         return;
@@ -1113,6 +1183,14 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_wave_kernel(Gem
     if constexpr (QUANT) {
         if (tid * 16 < K) load_x_f32(xv, a.x + 16 * tid, 16);
     }
+    // Q8 activation without QUANT: the lane's scale words of each step go out
+    // before the weights (a scale load issued after them waits for all of them)
+    uint32_t xdw[(is_q8(KIND) && !QUANT) ? STEPS : 1][2];
+    if constexpr (is_q8(KIND) && !QUANT) {
+#pragma unroll
+        for (int st = 0; st < STEPS; ++st)
+            load_xd(xdw[st], a.xd, (const decltype(XSlice<KIND>::v) *)nullptr, b + 16 * st, part);
+    }
     int unit[kPhase];
     RawSet<KIND> ring[kPhase][STEPS];
     // masked argmax: each unit's mask word (the word of the lane's row,
@@ -1189,7 +1267,12 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_wave_kernel(Gem
     } else if constexpr (is_q8(KIND)) {
 #pragma unroll
         for (int st = 0; st < STEPS; ++st) {
-            load_x<true>(xs[st].v, (const int8_t *)smem, xd_src, b + 16 * st, part);
+            if constexpr (QUANT) {
+                load_x<true>(xs[st].v, (const int8_t *)smem, xd_src, b + 16 * st, part);
+            } else {
+                load_x<true>(xs[st].v, (const int8_t *)smem, nullptr, b + 16 * st, part);
+                set_xd(xs[st].v, xdw[st]);
+            }
             finish_x(xs[st].v);
         }
     } else {
@@ -1554,18 +1637,27 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_batch_kernel(GemvArgs a)
             q4k_load(rs.r[0], a.W + tb, off, part);
     };
 
+    // every vector's Q8 scale words of the lane go out first: loaded after the
+    // weights, each waited for every weight load, one vector after another
+    XSlice<KIND> xs[M];
+    const int xb = lane_on ? b : 0;
+    uint32_t xdw[M][2];
+#pragma unroll
+    for (int j = 0; j < M; ++j) {
+        const int jv = j < a.batch ? j : a.batch - 1;
+        load_xd(xdw[j], a.xd + (size_t)jv * (K / 32), &xs[j].v, xb, part);
+    }
+
     RawSet<KIND> ring[kPhase];
 #pragma unroll
     for (int d = 0; d < kPhase; ++d) fetch(ring[d], t_begin + d);
 
     // activation slices, staged a.batch_round vectors at a time; a vector
     // occupies K + K/16 bytes of LDS (lds_pad layout)
-    XSlice<KIND> xs[M];
-    const int xb = lane_on ? b : 0;
     const int vbytes = K + K / 16;
     for (int j0 = 0; j0 < M; j0 += a.batch_round) {   // workgroup-uniform
         const int nv = M - j0 < a.batch_round ? M - j0 : a.batch_round;
-        for (int i = tid * 16; i < nv * K; i += (int)blockDim.x * 16) {
+        for (int i = tid * 16; i < nv * K; i += a.threads * 16) {
             const int jj = i / K, kk = i - jj * K;
             const int jv = j0 + jj < a.batch ? j0 + jj : a.batch - 1;
             *(u32x4 *)(smem + jj * vbytes + lds_pad((uint32_t)kk)) = *(const u32x4 *)(a.xq + (size_t)jv * K + kk);
@@ -1574,9 +1666,8 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_batch_kernel(GemvArgs a)
 #pragma unroll
         for (int j = 0; j < M; ++j) {
             if (j >= j0 && j < j0 + nv) {
-                const int jv = j < a.batch ? j : a.batch - 1;
-                load_x<true>(xs[j].v, (const int8_t *)(smem + (j - j0) * vbytes), a.xd + (size_t)jv * (K / 32), xb,
-                             part);
+                load_x<true>(xs[j].v, (const int8_t *)(smem + (j - j0) * vbytes), nullptr, xb, part);
+                set_xd(xs[j].v, xdw[j]);
                 finish_x(xs[j].v);
             }
         }
@@ -1602,12 +1693,12 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_batch_kernel(GemvArgs a)
             if (part == 0 && lane_on) rb[(j * P + p) * a.nb + b] = q;
         }
         __syncthreads();
-        // P * M <= 2 * blockDim.x (a row has at least 4 lanes and M <= 8):
+        // P * M <= 2 * a.threads (a row has at least 4 lanes and M <= 8):
         // two fixed passes, so the number of stores per tile is static and
         // the ring loads keep their counted waits
 #pragma unroll
         for (int it = 0; it < 2; ++it) {
-            const int i = tid + it * (int)blockDim.x;
+            const int i = tid + it * a.threads;
             const int j = i / P, pr = i - j * P;
             const int64_t row = (int64_t)t * P + pr;
             if (t < t_end && j < a.batch && row < a.N) {
@@ -2041,8 +2132,10 @@ static GemvArgs base_args(const Plan &pl, int64_t N)
 // end are recorded into them (hipExtLaunchKernel), so their elapsed time is
 // the kernel's duration.
 template <typename Kern>
-static void launch_on(Kern k, const Plan &pl, const GemvArgs &a, hipStream_t s, const Timing &tm)
+static void launch_on(Kern k, const Plan &pl, const GemvArgs &a_in, hipStream_t s, const Timing &tm)
 {
+    GemvArgs a = a_in;
+    a.threads = pl.threads;
     if (tm.start || tm.stop)
         hipExtLaunchKernelGGL(k, dim3(pl.grid), dim3(pl.threads), (uint32_t)pl.lds_bytes, s, tm.start, tm.stop, 0u, a);
     else
