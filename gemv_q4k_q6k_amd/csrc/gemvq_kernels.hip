@@ -697,17 +697,8 @@ __device__ __forceinline__ void gemv_tile_body(GemvArgs a)
     constexpr int BYTES = Traits<KIND>::kBytes;
     constexpr int OUTS = Traits<KIND>::kOuts;
     const int tid = threadIdx.x;
-    // threads per workgroup.  The int8 kinds, the argmax epilogues and the Q8
-    // emission take it from the arguments (their blockDim.x read was a vector
-    // load issued after the weight loads; see GemvArgs::threads).  The f32
-    // kinds read blockDim.x where it is used, as a scalar load whose round
-    // trip sits between the activation loads and the weights: at K = 9728
-    // that head start for the activation measured 0.35-0.45 us faster than
-    // without it (2560 x 9728 Q4_K and Q6_K), at K = 2560 0.2-0.25 us slower.
-    auto nthr = [&]() -> int {
-        if constexpr (is_q8(KIND) || is_argmax(EPI) || EPI == kQ8Emit) return a.threads;
-        else return (int)blockDim.x;
-    };
+    // threads per workgroup, from the arguments (see GemvArgs::threads)
+    auto nthr = [&]() -> int { return a.threads; };
     const int p = (int)__umulhi((uint32_t)tid, a.lanes_row_magic);   // row within the tile
     const int rr = tid - p * a.lanes_row;     // lane within the row
     const int b = rr >> 2;                    // super-block column
@@ -817,6 +808,16 @@ __device__ __forceinline__ void gemv_tile_body(GemvArgs a)
     if constexpr (is_q8(KIND)) load_xd(xdw, a.xd, &xs.v, xb, part);
     if constexpr (!XLDS && is_q8(KIND)) set_xd(xs.v, xdw);
     RawSet<KIND> ring[kPhase];
+    // A large activation (K > 4096: 40 KB or more of f32, the same for every
+    // CU) gets a head start of ~0.2 us (s_sleep 8 = 512 cycles) before the
+    // first tile's weight loads, so it is not queued behind them and the
+    // conversion starts earlier.  Measured at 2560 x 9728 (Q4_K, Q6_K) against
+    // issuing the weights at once: 5.7-5.9 -> 5.2-5.3 us (Q4_K) and 7.07 ->
+    // 6.58 us (Q6_K); s_sleep 4 and 16 did less well over the FFN and the
+    // attention projections.  Small activations arrive quickly without it.
+    if constexpr (RES && kFx) {
+        if (K > 4096) __builtin_amdgcn_s_sleep(8);
+    }
 #pragma unroll
     for (int d = 0; d < kPre; ++d) fetch(ring[d], t_begin + d);
 
