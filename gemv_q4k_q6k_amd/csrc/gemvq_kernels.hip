@@ -808,7 +808,7 @@ __device__ __forceinline__ void gemv_tile_body(GemvArgs a)
     if constexpr (is_q8(KIND)) load_xd(xdw, a.xd, &xs.v, xb, part);
     if constexpr (!XLDS && is_q8(KIND)) set_xd(xs.v, xdw);
     RawSet<KIND> ring[kPhase];
-    // A large activation (K > 4096: 40 KB or more of f32, the same for every
+    // A large activation (K > 4096: over 16 KB of f32, the same for every
     // CU) gets a head start of ~0.2 us (s_sleep 8 = 512 cycles) before the
     // first tile's weight loads, so it is not queued behind them and the
     // conversion starts earlier.  Measured at 2560 x 9728 (Q4_K, Q6_K) against
