@@ -36,6 +36,7 @@ constexpr uint32_t kNoIndex = 0xFFFFFFFFu;
 
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // f16 "magic" conversion: OR-ing a 10-bit integer m into the mantissa of
 // 1024.0h (0x6400) gives the exact half value 1024 + m.  Two such halves per

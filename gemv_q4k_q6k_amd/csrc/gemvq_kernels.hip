@@ -478,6 +478,43 @@ __device__ __forceinline__ int8_t q8_encode(float v, uint16_t &dbits)
     return (int8_t)q8_code(v, d);
 }
 
+// The codes q8_code gives for NV values of one block (scale d), packed four
+// to a word (value 4k + j in byte j of word k), with one division per block
+// instead of one per value.  Each quotient is taken as q = v * (1/d), both
+// products rounded to nearest: |q - v/d| <= (2^-23 + 2^-48) |v/d|, and the
+// correctly rounded v/d that q8_code rounds is within 2^-24 |v/d| of v/d.
+// Since |v/d| <= 127 (1 + 2^-23), q and q8_code's quotient differ by less than
+// 2^-15, so both round to the same integer unless a half-integer lies within
+// that distance.  A value whose q has a fractional part within 2^-13 of 0.5
+// (or is not a number), or a block whose d is zero, subnormal or not finite,
+// takes q8_code itself for all NV values.  The codes are q8_code's bit for
+// bit (checked on the CPU against the exact division over adversarial
+// quotients next to every k + 0.5).
+template <int NV>
+__device__ __forceinline__ void q8_codes_fast(const float (&v)[NV], float d, uint32_t (&w)[NV / 4])
+{
+    const float y = 1.0f / d;
+    bool slow = !(d >= 0x1p-126f && d <= 0x1p+126f);
+    int c[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const float q = v[i] * y;
+        const float t = truncf(q);
+        const float f = fabsf(q - t);   // exact for |q| < 2^23
+        slow = slow || !(fabsf(f - 0.5f) >= 0x1p-13f);
+        const float r = f >= 0.5f ? t + copysignf(1.0f, q) : t;   // half away from zero, as roundf
+        c[i] = (int)fminf(fmaxf(r, -127.0f), 127.0f);
+    }
+    if (slow) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) c[i] = q8_code(v[i], d);
+    }
+#pragma unroll
+    for (int k = 0; k < NV / 4; ++k)
+        w[k] = (uint32_t)(c[4 * k] & 0xFF) | ((uint32_t)(c[4 * k + 1] & 0xFF) << 8) |
+               ((uint32_t)(c[4 * k + 2] & 0xFF) << 16) | ((uint32_t)(c[4 * k + 3] & 0xFF) << 24);
+}
+
 // Q8 encoding of the rows a workgroup of the tile kernel computed, [r0, r1)
 // (values in LDS).  A 32-row block that lies inside the range is encoded
 // right here.  A block shared with other workgroups goes through the
@@ -1177,12 +1214,13 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_wave_kernel(Gem
         const int i = (tid + r * (int)blockDim.x) * step;
         if (i < K) xr[r] = *(const u32x4 *)(src + (size_t)i * esz);
     }
-    // QUANT: thread t takes values [16t, 16t + 16) of x, half of a 32-value
-    // Q8 block (its partner is the adjacent lane); the first round is loaded
+    // QUANT: thread t takes values [8t, 8t + 8) of x, a quarter of a 32-value
+    // Q8 block (the quad t & ~3 holds the block), so every wave of a 1024-thread
+    // workgroup shares the encoding at K = 8192; the first round is loaded
     // before the weights
-    float xv[QUANT ? 16 : 1];
+    float xv[QUANT ? 8 : 1];
     if constexpr (QUANT) {
-        if (tid * 16 < K) load_x_f32(xv, a.x + 16 * tid, 16);
+        if (tid * 8 < K) load_x_f32(xv, a.x + 8 * tid, 8);
     }
     // Q8 activation without QUANT: the lane's scale words of each step go out
     // before the weights (a scale load issued after them waits for all of them)
@@ -1225,28 +1263,23 @@ __global__ __launch_bounds__(wave_max_threads<KIND>()) void gemv_wave_kernel(Gem
     if constexpr (QUANT) {
         uint16_t *s_xd = (uint16_t *)(smem + lds_pad((uint32_t)K));
         xd_src = s_xd;
-        for (int t = tid; t * 16 < K; t += (int)blockDim.x) {   // pairs (t, t ^ 1) share an iteration
-            if (t != tid) load_x_f32(xv, a.x + 16 * t, 16);
+        for (int t = tid; t * 8 < K; t += (int)blockDim.x) {   // quads (t & ~3 .. t | 3) share an iteration
+            if (t != tid) load_x_f32(xv, a.x + 8 * t, 8);
             float m = 0.f;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(xv[i]));
-            m = fmaxf(m, dpp_f<kDppQuadXor1>(m));   // the block's other half (lane ^ 1)
+            for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(xv[i]));
+            m = fmaxf(m, dpp_f<kDppQuadXor1>(m));   // the block's other quarters
+            m = fmaxf(m, dpp_f<kDppQuadXor2>(m));
             const float d = q8_scale(m);
-            uint32_t w[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                uint32_t acc = 0u;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc |= ((uint32_t)(q8_code(xv[4 * k + j], d) & 0xFF)) << (8 * j);
-                w[k] = acc;
-            }
-            const u32x4 codes = u32x4{w[0], w[1], w[2], w[3]};
-            *(u32x4 *)(smem + lds_pad(16u * (uint32_t)t)) = codes;
+            uint32_t w[2];
+            q8_codes_fast<8>(xv, d, w);
+            const u32x2 codes = u32x2{w[0], w[1]};
+            *(u32x2 *)(smem + lds_pad(8u * (uint32_t)t)) = codes;
             const uint16_t dbits = q8_scale_bits(d);
-            if ((t & 1) == 0) s_xd[t >> 1] = dbits;
+            if ((t & 3) == 0) s_xd[t >> 2] = dbits;
             if (blockIdx.x == 0) {
-                *(u32x4 *)(a.hq + 16 * t) = codes;
-                if ((t & 1) == 0) a.hd[t >> 1] = dbits;
+                *(u32x2 *)(a.hq + 8 * t) = codes;
+                if ((t & 3) == 0) a.hd[t >> 2] = dbits;
             }
         }
     } else if constexpr (kFx) {

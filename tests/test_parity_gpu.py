@@ -1043,3 +1043,62 @@ def test_q4k_q8_gemv_from_f32(dev, N, K):
     assert torch.equal(xq2, xq) and torch.equal(xd2, xd)
     assert torch.equal(gq().q4k_q8_gemv(dW, xq, xd, N, K), y)
     check_f32(f"q4k_q8_from_f32 {N}x{K}", y.cpu().numpy(), oracle.q4k_q8_gemv(W, q, d, N, K))
+
+
+def _halfway_activation(r, K):
+    """Q8 blocks whose quotients x/d sit on or next to a rounding boundary
+    k + 0.5, where a quotient formed any other way than by the correctly
+    rounded division could round to another code.  Blocks cycle through:
+    a block maximum of 127 * 2^e (scale exactly 2^e) with values
+    (k + 0.5) 2^e moved by -1, 0 or +1 ulp; an irregular maximum with values
+    near (k + 0.5) amax / 127 (formed in f64, rounded to f32, moved by up to
+    3 ulps, kept within the maximum); an all-zero block; plain N(0, 1).  Every block scale is a finite fp16."""
+    x = np.empty(K, np.float32)
+    for j in range(K // 32):
+        kind = j % 4
+        if kind == 0:
+            e = int(r.integers(-14, 11))   # the scale 2^e stays a finite fp16
+            k = r.integers(0, 127, 32).astype(np.float64)
+            v = ((k + 0.5) * 2.0 ** e).astype(np.float32)
+            for i, st in enumerate(r.integers(-1, 2, 32)):
+                if st:
+                    v[i] = np.nextafter(v[i], np.float32(np.inf if st > 0 else -np.inf))
+            v[0] = np.float32(127.0 * 2.0 ** e)
+            v *= np.where(r.random(32) < 0.5, -1, 1).astype(np.float32)
+        elif kind == 1:
+            amax = np.float32(r.uniform(0.5, 2.0) * 2.0 ** int(r.integers(-8, 14)))
+            k = r.integers(0, 127, 32).astype(np.float64)
+            v = ((k + 0.5) * float(amax) / 127.0).astype(np.float32)
+            for i, st in enumerate(r.integers(-3, 4, 32)):
+                for _ in range(abs(int(st))):
+                    v[i] = np.nextafter(v[i], np.float32(np.inf if st > 0 else -np.inf))
+            v = np.minimum(v, amax)
+            v[0] = amax
+            v *= np.where(r.random(32) < 0.5, -1, 1).astype(np.float32)
+        elif kind == 2:
+            v = np.zeros(32, np.float32)
+        else:
+            v = r.standard_normal(32).astype(np.float32)
+        x[32 * j:32 * j + 32] = v
+    return x
+
+
+@pytest.mark.parametrize("N,K", [(28_672, 8192), (100, 8192), (1000, 1024), (7, 256)])
+def test_q4k_q8_gemv_from_f32_halfway(dev, N, K):
+    """The one-launch quantize + Q4_K x Q8 GEMV on activations whose
+    quotients lie on or next to the code boundaries k + 0.5: codes and
+    scales are the oracle's and q8_quantize's bit for bit, and y is
+    q4k_q8_gemv's on them bit for bit."""
+    r = synth.rng_for(6900 + N + K)
+    W = synth.q4k_weights(r, N, K)
+    x = _halfway_activation(r, K)
+    dW, dx = up(W, dev), up(x, dev)
+    print(f"q4k_q8_gemv_from_f32 halfway N={N} K={K}", flush=True)
+    y, xq, xd = gq().q4k_q8_gemv_from_f32(dW, dx, N, K)
+    q, d = oracle.q8_quantize(x)
+    assert np.array_equal(xq.cpu().numpy(), q)
+    assert np.array_equal(xd.cpu().numpy().view(np.uint16), d)
+    xq2, xd2 = gq().q8_quantize(dx)
+    assert torch.equal(xq2, xq) and torch.equal(xd2, xd)
+    assert torch.equal(gq().q4k_q8_gemv(dW, xq, xd, N, K), y)
+    assert bool(torch.isfinite(y).all())
