@@ -283,15 +283,16 @@ def graph_us(fn, ws, reps=24):
     return float(np.median(trials))
 
 
-READ_GRIDS = (256, 512, 1024, 2048, 4096, 8192)
+READ_SHAPES = tuple((1024, g) for g in (128, 256, 512, 1024, 2048, 4096)) + \
+              tuple((256, g) for g in (1024, 2048, 4096, 8192, 16384))   # (threads, grid)
 
 
 def read_ceiling(gq, dev, sizes, in_cache=()):
     """Streaming-read time of each byte count: the library's plain read
     kernel (16-byte loads, grid-stride) over slices of one pool, rotating
     through >= 640 MB of slices (sizes listed in in_cache: one slice, read
-    again and again, as the in-cache config it matches), best of a few
-    grids.  {bytes: {"us", "GBps", "grid", "in_cache"}}."""
+    again and again, as the in-cache config it matches), best over workgroup
+    sizes and grids.  {bytes: {"us", "GBps", "grid", "threads", "in_cache"}}."""
     import torch
     pool = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     sink = torch.zeros(256, dtype=torch.int32, device=dev)
@@ -302,12 +303,12 @@ def read_ceiling(gq, dev, sizes, in_cache=()):
         n = 1 if S in in_cache else max(2, min(pool.numel() // stride, -(-MIN_ROTATE_BYTES // S16)))
         bufs = [(pool[i * stride:i * stride + S16],) for i in range(n)]
         best = None
-        for grid in READ_GRIDS:
-            us = graph_us(lambda w, grid=grid: gq.stream_read(w[0], grid, sink), bufs)
+        for thr, grid in READ_SHAPES:
+            us = graph_us(lambda w, grid=grid, thr=thr: gq.stream_read(w[0], grid, sink, threads=thr), bufs)
             if best is None or us < best[0]:
-                best = (us, grid)
+                best = (us, grid, thr)
         out[S] = {"us": round(best[0], 2), "GBps": round(S16 / best[0] / 1e3, 1), "grid": best[1],
-                  "in_cache": S in in_cache}
+                  "threads": best[2], "in_cache": S in in_cache}
     del pool
     torch.cuda.empty_cache()
     return out

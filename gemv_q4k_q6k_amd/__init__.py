@@ -70,7 +70,7 @@ _SIGS = {
     "gemvq_q4k_q8_isums": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P]),
     "gemvq_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "gemvq_tile_geometry": (ctypes.c_int, [ctypes.c_int, _I64, _I64, _P]),
-    "gemvq_stream_read": (ctypes.c_int, [_P, _I64, ctypes.c_int, _P, _P]),
+    "gemvq_stream_read": (ctypes.c_int, [_P, _I64, ctypes.c_int, ctypes.c_int, _P, _P]),
 }
 
 
@@ -116,14 +116,15 @@ def tile_geometry(kind: int, N: int, K: int) -> dict:
             "resident": out[8], "phase": out[9], "grid": out[10]}
 
 
-def stream_read(buf, grid: int, sink, stream=None) -> None:
-    """Plain streaming read of a whole device tensor (measurement hook)."""
+def stream_read(buf, grid: int, sink, stream=None, threads: int = 1024) -> None:
+    """Plain streaming read of a whole device tensor by `grid` workgroups of
+    `threads` (256 or 1024) threads (measurement hook)."""
     torch = _torch()
     if not isinstance(buf, torch.Tensor) or buf.device.type != "cuda" or not buf.is_contiguous():
         raise TypeError("buf: expected a contiguous device tensor")
     nbytes = buf.numel() * buf.element_size()
     _check("gemvq_stream_read", lib().gemvq_stream_read(buf.data_ptr(), nbytes - nbytes % 16, int(grid),
-                                                         sink.data_ptr(), _stream(buf, stream)))
+                                                         int(threads), sink.data_ptr(), _stream(buf, stream)))
 
 
 def strerror(status: int) -> str:

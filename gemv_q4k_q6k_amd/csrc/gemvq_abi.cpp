@@ -446,13 +446,14 @@ int lm_head_argmax_masked(const void *W, const float *x, const uint32_t *mask, u
     return lm_head_argmax_impl(W, x, mask, out_idx, out_max, workspace, ws_bytes, N, K, stream, gemvq::Timing{});
 }
 
-int gemvq_stream_read(const void *p, int64_t bytes, int grid, uint32_t *sink, void *stream)
+int gemvq_stream_read(const void *p, int64_t bytes, int grid, int threads, uint32_t *sink, void *stream)
 {
     if (!p || !sink) return GEMVQ_ERR_NULL;
     if (bytes < 16 || bytes % 16 != 0 || grid < 1 || grid > 65536) return GEMVQ_ERR_SHAPE;
+    if (threads != 256 && threads != 1024) return GEMVQ_ERR_SHAPE;
     if (!aligned(p, 16) || !aligned(sink, 4)) return GEMVQ_ERR_ALIGN;
     if (overlap(sink, 1024, p, (size_t)bytes)) return GEMVQ_ERR_ALIAS;
-    return status_of(gemvq::launch_stream_read(p, bytes, grid, sink, (hipStream_t)stream));
+    return status_of(gemvq::launch_stream_read(p, bytes, grid, threads, sink, (hipStream_t)stream));
 }
 
 int gemvq_q4k_q8_isums(const void *W, const int8_t *xq, int32_t *isums, int64_t N, int64_t K, void *stream)

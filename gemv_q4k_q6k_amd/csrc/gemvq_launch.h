@@ -96,7 +96,7 @@ hipError_t launch_q8_quantize(const float *x, int8_t *xq, uint16_t *xd, int64_t 
 // measurement hook: read bytes (a multiple of 16) at p once with `grid`
 // workgroups of 256 threads; sink: uint32[256], written only on an
 // impossible fold value
-hipError_t launch_stream_read(const void *p, int64_t bytes, int grid, uint32_t *sink, hipStream_t s);
+hipError_t launch_stream_read(const void *p, int64_t bytes, int grid, int threads, uint32_t *sink, hipStream_t s);
 // zero `bytes` (a multiple of 16, at most 65536) at a 16-byte aligned device address with a fill kernel
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s);
 hipError_t launch_q6k_q8_isums(const void *W, const int8_t *xq, int32_t *isums, int64_t N, int64_t K, hipStream_t s);

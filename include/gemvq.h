@@ -351,14 +351,15 @@ int gemvq_tile_geometry(int kind, int64_t N, int64_t K, int64_t out[11]);
 /*
  * Measurement hook: a plain streaming read of `bytes` (a multiple of 16,
  * 16-B aligned) at device address p, each byte read once with 16-byte
- * loads by `grid` workgroups of 256 threads (grid-stride).  It is the
- * ceiling the GEMVs' achieved bandwidth is compared with at the same byte
- * count (its best time over a few grids).  sink: device uint32[256], written
- * only if the folded data equals one fixed value (in practice never).
- * Returns GEMVQ_ERR_SHAPE for bytes < 16, not a multiple of 16, or grid
- * outside [1, 65536].
+ * loads by `grid` workgroups of `threads` threads (256 or 1024;
+ * grid-stride).  It is the ceiling the GEMVs' achieved bandwidth is
+ * compared with at the same byte count (its best time over workgroup sizes
+ * and grids).  sink: device uint32[256], written only if the folded data
+ * equals one fixed value (in practice never).
+ * Returns GEMVQ_ERR_SHAPE for bytes < 16, not a multiple of 16, grid
+ * outside [1, 65536] or threads other than 256 and 1024.
  */
-int gemvq_stream_read(const void *p, int64_t bytes, int grid, uint32_t *sink, void *stream);
+int gemvq_stream_read(const void *p, int64_t bytes, int grid, int threads, uint32_t *sink, void *stream);
 
 /* Static description of a status code (never NULL). */
 const char *gemvq_strerror(int status);

@@ -37,13 +37,14 @@ int main()
            "noalloc null x");
     expect(q4k_q8_gemv_from_f32(P(A), F(B), nullptr, (uint16_t *)P(D), F(E), 4, 256, nullptr), GEMVQ_ERR_NULL,
            "from_f32 null xq");
-    expect(gemvq_stream_read(nullptr, 1024, 256, (uint32_t *)P(C), nullptr), GEMVQ_ERR_NULL, "stream_read null");
+    expect(gemvq_stream_read(nullptr, 1024, 256, 1024, (uint32_t *)P(C), nullptr), GEMVQ_ERR_NULL, "stream_read null");
     // shapes
     for (int64_t K : {0, 255, 300, 32768 + 256}) expect(q4k_gemv(P(A), F(B), F(C), 4, K, nullptr), GEMVQ_ERR_SHAPE, "K");
     expect(q6k_gemv(P(A), F(B), F(C), 0, 256, nullptr), GEMVQ_ERR_SHAPE, "N = 0");
     expect(q6k_gemv(P(A), F(B), F(C), (int64_t)1 << 40, 256, nullptr), GEMVQ_ERR_SHAPE, "N too large");
     expect(q8_quantize(F(A), (int8_t *)P(B), (uint16_t *)P(C), 33, nullptr), GEMVQ_ERR_SHAPE, "q8 K % 32");
-    expect(gemvq_stream_read(P(A), 1000, 256, (uint32_t *)P(C), nullptr), GEMVQ_ERR_SHAPE, "stream_read bytes");
+    expect(gemvq_stream_read(P(A), 1000, 256, 1024, (uint32_t *)P(C), nullptr), GEMVQ_ERR_SHAPE, "stream_read bytes");
+    expect(gemvq_stream_read(P(A), 1024, 256, 512, (uint32_t *)P(C), nullptr), GEMVQ_ERR_SHAPE, "stream_read threads");
     // alignment
     expect(q4k_gemv(P(A + 4), F(B), F(C), 4, 256, nullptr), GEMVQ_ERR_ALIGN, "q4k W 16 B");
     expect(q6k_gemv(P(A + 2), F(B), F(C), 4, 256, nullptr), GEMVQ_ERR_ALIGN, "q6k W 4 B");

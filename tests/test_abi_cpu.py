@@ -284,13 +284,15 @@ def test_lm_head_argmax_noalloc_rejections():
 
 def test_stream_read_rejections():
     L = gq.lib()
-    _rejected(L.gemvq_stream_read(None, 1024, 256, C, None), gq.ERR_NULL)
-    _rejected(L.gemvq_stream_read(A, 1024, 256, None, None), gq.ERR_NULL)
-    _rejected(L.gemvq_stream_read(A, 0, 256, C, None), gq.ERR_SHAPE)
-    _rejected(L.gemvq_stream_read(A, 1000, 256, C, None), gq.ERR_SHAPE)
-    _rejected(L.gemvq_stream_read(A, 1024, 0, C, None), gq.ERR_SHAPE)
-    _rejected(L.gemvq_stream_read(A + 8, 1024, 256, C, None), gq.ERR_ALIGN)
-    _rejected(L.gemvq_stream_read(A, 1024, 256, A + 512, None), gq.ERR_ALIAS)
+    _rejected(L.gemvq_stream_read(None, 1024, 256, 1024, C, None), gq.ERR_NULL)
+    _rejected(L.gemvq_stream_read(A, 1024, 256, 1024, None, None), gq.ERR_NULL)
+    _rejected(L.gemvq_stream_read(A, 0, 256, 1024, C, None), gq.ERR_SHAPE)
+    _rejected(L.gemvq_stream_read(A, 1000, 256, 1024, C, None), gq.ERR_SHAPE)
+    _rejected(L.gemvq_stream_read(A, 1024, 0, 1024, C, None), gq.ERR_SHAPE)
+    _rejected(L.gemvq_stream_read(A, 1024, 256, 512, C, None), gq.ERR_SHAPE)
+    _rejected(L.gemvq_stream_read(A, 1024, 256, 0, C, None), gq.ERR_SHAPE)
+    _rejected(L.gemvq_stream_read(A + 8, 1024, 256, 1024, C, None), gq.ERR_ALIGN)
+    _rejected(L.gemvq_stream_read(A, 1024, 256, 1024, A + 512, None), gq.ERR_ALIAS)
 
 
 def test_q4k_q8_gemv_from_f32_rejections():
