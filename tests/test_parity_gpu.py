@@ -1045,6 +1045,26 @@ def test_q4k_q8_gemv_from_f32(dev, N, K):
     check_f32(f"q4k_q8_from_f32 {N}x{K}", y.cpu().numpy(), oracle.q4k_q8_gemv(W, q, d, N, K))
 
 
+@pytest.mark.parametrize("K", [256, 512, 1024, 2048, 4096, 8192])
+@pytest.mark.parametrize("N", [1, 15, 255, 257, 4097])
+def test_q4k_q8_gemv_from_f32_ragged(dev, N, K):
+    """The one-launch quantize + Q4_K x Q8 GEMV over every K it serves and
+    ragged N (fewer units than waves, a ragged last unit, units left over
+    after the first two per wave): codes and scales are the oracle's bit for
+    bit, and y is q4k_q8_gemv's on them bit for bit."""
+    r = synth.rng_for(7300 + N + K)
+    W = synth.q4k_weights(r, N, K)
+    x = synth.activation_outliers(r, K)
+    dW, dx = up(W, dev), up(x, dev)
+    print(f"q4k_q8_gemv_from_f32 ragged N={N} K={K}", flush=True)
+    y, xq, xd = gq().q4k_q8_gemv_from_f32(dW, dx, N, K)
+    q, d = oracle.q8_quantize(x)
+    assert np.array_equal(xq.cpu().numpy(), q)
+    assert np.array_equal(xd.cpu().numpy().view(np.uint16), d)
+    assert torch.equal(gq().q4k_q8_gemv(dW, xq, xd, N, K), y)
+    check_f32(f"q4k_q8_from_f32 ragged {N}x{K}", y.cpu().numpy(), oracle.q4k_q8_gemv(W, q, d, N, K))
+
+
 def _halfway_activation(r, K):
     """Q8 blocks whose quotients x/d sit on or next to a rounding boundary
     k + 0.5, where a quotient formed any other way than by the correctly
