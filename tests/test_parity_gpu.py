@@ -1046,12 +1046,13 @@ def test_q4k_q8_gemv_from_f32(dev, N, K):
 
 
 @pytest.mark.parametrize("K", [256, 512, 1024, 2048, 4096, 8192])
-@pytest.mark.parametrize("N", [1, 15, 255, 257, 4097])
+@pytest.mark.parametrize("N", [1, 15, 64, 136, 255, 257, 4097])
 def test_q4k_q8_gemv_from_f32_ragged(dev, N, K):
     """The one-launch quantize + Q4_K x Q8 GEMV over every K it serves and
     ragged N (fewer units than waves, a ragged last unit, units left over
-    after the first two per wave): codes and scales are the oracle's bit for
-    bit, and y is q4k_q8_gemv's on them bit for bit."""
+    after the first two per wave, grids of 64 and 136 workgroups that take
+    the XCD-contiguous order as the full grid does): codes and scales are
+    the oracle's bit for bit, and y is q4k_q8_gemv's on them bit for bit."""
     r = synth.rng_for(7300 + N + K)
     W = synth.q4k_weights(r, N, K)
     x = synth.activation_outliers(r, K)
